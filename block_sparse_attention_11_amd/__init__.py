@@ -1,0 +1,228 @@
+"""Python binding of libkpage.so: KPage-style block-sparse attention on MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI declared in include/kpage.h; every step of
+the computation runs in the library's HIP kernels.  The functions keep the C
+names.  Tensors are torch tensors on the GPU (device memory and streams only).
+
+The library must have been built (``python -m block_sparse_attention_11_amd.build``
+or ``__graft_entry__.build()``); importing works without it, but every call
+raises ``KpageError`` when the shared object is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkpage.so")
+
+KPAGE_OK, KPAGE_ERR_INVALID, KPAGE_ERR_UNSUPPORTED, KPAGE_ERR_OOM, KPAGE_ERR_HIP = range(5)
+STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "OOM", 4: "HIP"}
+
+TABLES = {
+    "fwd_route": (0, np.int32), "fwd_walk_ptr": (1, np.int64), "fwd_walk": (2, np.int32),
+    "fwd_nfull": (3, np.int32), "fwd_valid": (4, np.uint32), "q64_queue": (5, np.int32),
+    "q128_queue": (6, np.int32), "owner_ptr": (7, np.int64), "owners": (8, np.int32),
+    "owner_aligned": (9, np.uint8), "revq_ptr": (10, np.int64), "revq": (11, np.int32),
+    "qwalk_ptr": (12, np.int64), "qwalk": (13, np.int32), "adj": (14, np.uint64),
+    "bwd_queue": (15, np.int32),
+}
+
+EXPORTED_SYMBOLS = (
+    "kpage_plan", "kpage_plan_upload", "kpage_attn_fwd", "kpage_bwd_workspace_size", "kpage_attn_bwd",
+    "kpage_plan_stats", "kpage_plan_export", "kpage_plan_destroy", "kpage_last_error",
+)
+
+
+class KpageError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"kpage {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class KpageProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("n_q_blocks", ctypes.c_int32), ("n_kv_blocks", ctypes.c_int32),
+        ("seq_q", ctypes.c_int64), ("seq_kv", ctypes.c_int64), ("per_head", ctypes.c_int32),
+        ("q_valid", ctypes.c_void_p), ("kv_valid", ctypes.c_void_p), ("kv_offset", ctypes.c_void_p),
+        ("q2k_ptr", ctypes.c_void_p), ("q2k_idx", ctypes.c_void_p),
+    ]
+
+
+class KpagePlanOpts(ctypes.Structure):
+    _fields_ = [("q_group", ctypes.c_int32), ("align_q128", ctypes.c_int32), ("align_q64", ctypes.c_int32)]
+
+
+class KpagePairStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("useful", "whole_block", "paged_m128", "nominal", "scheduled", "bwd_physical", "bwd_useful_check")]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library; raises KpageError when it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise KpageError(KPAGE_ERR_HIP, f"{LIB_PATH} is missing: build the HIP library first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.kpage_plan.argtypes = [ctypes.POINTER(KpageProblem), ctypes.POINTER(KpagePlanOpts), ctypes.POINTER(vp)]
+        L.kpage_plan_upload.argtypes = [vp, vp]
+        L.kpage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp]
+        L.kpage_bwd_workspace_size.argtypes = [vp, ctypes.POINTER(sz)]
+        L.kpage_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, f32, vp]
+        L.kpage_plan_stats.argtypes = [vp, ctypes.POINTER(KpagePairStats)]
+        L.kpage_plan_export.argtypes = [vp, i32, vp, ctypes.POINTER(sz)]
+        L.kpage_plan_destroy.argtypes = [vp]
+        L.kpage_plan_destroy.restype = None
+        L.kpage_last_error.restype = ctypes.c_char_p
+        for name in EXPORTED_SYMBOLS:
+            if name not in ("kpage_plan_destroy", "kpage_last_error"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib_handle = L
+    return _lib_handle
+
+
+def kpage_last_error() -> str:
+    return lib().kpage_last_error().decode()
+
+
+def _check(status: int):
+    if status != KPAGE_OK:
+        raise KpageError(status, kpage_last_error())
+
+
+class Plan:
+    """Owns a kpage_plan_t handle plus the shape facts the binding checks tensors against."""
+
+    def __init__(self, handle, batch, heads, head_dim, seq_q, seq_kv):
+        self.handle = handle
+        self.batch, self.heads, self.head_dim = batch, heads, head_dim
+        self.seq_q, self.seq_kv = seq_q, seq_kv
+
+    def close(self):
+        if self.handle:
+            lib().kpage_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _arr(x, dtype):
+    return np.ascontiguousarray(np.asarray(x, dtype=dtype))
+
+
+def kpage_plan(problem, align_q64: int = 0, align_q128: int = 0, q_group: int = 0) -> Plan:
+    """Plan for ``problem`` (any object with the workloads.Workload descriptor attributes)."""
+    qv = _arr(problem.q_valid, np.int32)
+    kvv = _arr(problem.kv_valid, np.int32)
+    ko = _arr(problem.kv_offset, np.int64)
+    ptr = _arr(problem.q2k_ptr, np.int64)
+    idx = _arr(problem.q2k_idx, np.int32)
+    if idx.size == 0:
+        idx = np.zeros(1, dtype=np.int32)
+    p = KpageProblem(
+        batch=problem.batch, heads=problem.heads, head_dim=problem.head_dim,
+        n_q_blocks=problem.n_q, n_kv_blocks=problem.n_kv, seq_q=problem.seq_q, seq_kv=problem.seq_kv,
+        per_head=1 if problem.per_head else 0,
+        q_valid=qv.ctypes.data, kv_valid=kvv.ctypes.data, kv_offset=ko.ctypes.data,
+        q2k_ptr=ptr.ctypes.data, q2k_idx=idx.ctypes.data)
+    opts = KpagePlanOpts(q_group=q_group, align_q128=align_q128, align_q64=align_q64)
+    h = ctypes.c_void_p()
+    _check(lib().kpage_plan(ctypes.byref(p), ctypes.byref(opts), ctypes.byref(h)))
+    return Plan(h, problem.batch, problem.heads, problem.head_dim, problem.seq_q, problem.seq_kv)
+
+
+def kpage_plan_stats(plan: Plan) -> dict:
+    s = KpagePairStats()
+    _check(lib().kpage_plan_stats(plan.handle, ctypes.byref(s)))
+    return {n: int(getattr(s, n)) for n, _ in KpagePairStats._fields_}
+
+
+def kpage_plan_export(plan: Plan, table: str) -> np.ndarray:
+    tid, dtype = TABLES[table]
+    n = ctypes.c_size_t(0)
+    _check(lib().kpage_plan_export(plan.handle, tid, None, ctypes.byref(n)))
+    out = np.zeros(n.value // np.dtype(dtype).itemsize, dtype=dtype)
+    if n.value:
+        _check(lib().kpage_plan_export(plan.handle, tid, out.ctypes.data, ctypes.byref(n)))
+    return out
+
+
+def kpage_bwd_workspace_size(plan: Plan) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().kpage_bwd_workspace_size(plan.handle, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dev(t, rows, plan: Plan, name, dtype):
+    import torch
+    want = (plan.batch, plan.heads, rows) + ((plan.head_dim,) if dtype == torch.bfloat16 else ())
+    if not t.is_cuda or t.dtype != dtype or tuple(t.shape) != want or not t.is_contiguous():
+        raise KpageError(KPAGE_ERR_INVALID, f"{name}: need a contiguous {dtype} CUDA tensor of shape {want}, "
+                                            f"got {tuple(t.shape)} {t.dtype} on {t.device}")
+    return t.data_ptr()
+
+
+def kpage_plan_upload(plan: Plan, stream=None):
+    _check(lib().kpage_plan_upload(plan.handle, _stream_ptr(stream)))
+
+
+def kpage_attn_fwd(plan: Plan, q, k, v, o, lse, softmax_scale: float, stream=None):
+    import torch
+    bf = torch.bfloat16
+    args = (_dev(q, plan.seq_q, plan, "q", bf), _dev(k, plan.seq_kv, plan, "k", bf),
+            _dev(v, plan.seq_kv, plan, "v", bf), _dev(o, plan.seq_q, plan, "o", bf),
+            _dev(lse, plan.seq_q, plan, "lse", torch.float32))
+    _check(lib().kpage_attn_fwd(plan.handle, *args, ctypes.c_float(softmax_scale), _stream_ptr(stream)))
+
+
+def kpage_attn_bwd(plan: Plan, q, k, v, o, lse, do, dq, dk, dv, workspace, softmax_scale: float, stream=None):
+    import torch
+    bf = torch.bfloat16
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise KpageError(KPAGE_ERR_INVALID, "workspace must be a contiguous CUDA tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = (_dev(q, plan.seq_q, plan, "q", bf), _dev(k, plan.seq_kv, plan, "k", bf),
+            _dev(v, plan.seq_kv, plan, "v", bf), _dev(o, plan.seq_q, plan, "o", bf),
+            _dev(lse, plan.seq_q, plan, "lse", torch.float32), _dev(do, plan.seq_q, plan, "do", bf),
+            _dev(dq, plan.seq_q, plan, "dq", bf), _dev(dk, plan.seq_kv, plan, "dk", bf),
+            _dev(dv, plan.seq_kv, plan, "dv", bf))
+    _check(lib().kpage_attn_bwd(plan.handle, *args, workspace.data_ptr(), ctypes.c_size_t(ws_bytes),
+                                ctypes.c_float(softmax_scale), _stream_ptr(stream)))
+
+
+# ---- convenience wrappers (allocation of outputs only) ----
+
+def attn_fwd(plan: Plan, q, k, v, softmax_scale: float, stream=None):
+    import torch
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    kpage_attn_fwd(plan, q, k, v, o, lse, softmax_scale, stream)
+    return o, lse
+
+
+def attn_bwd(plan: Plan, q, k, v, o, lse, do, softmax_scale: float, stream=None, workspace=None):
+    import torch
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(kpage_bwd_workspace_size(plan), dtype=torch.uint8, device=q.device)
+    kpage_attn_bwd(plan, q, k, v, o, lse, do, dq, dk, dv, workspace, softmax_scale, stream)
+    return dq, dk, dv

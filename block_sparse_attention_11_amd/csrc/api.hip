@@ -1,0 +1,369 @@
+// C ABI: plan handle, descriptor validation, device uploads and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "device.hpp"
+#include "kpage.h"
+#include "plan.hpp"
+
+using namespace kpage;
+
+struct kpage_plan {
+  Problem P;
+  FwdTables F;
+  BwdTables B;
+  PairStats S;
+  bool fwd_on_device = false;
+  bool bwd_on_device = false;
+  // forward device tables
+  FwdItem *d_items128 = nullptr, *d_items64 = nullptr;
+  int n_items128 = 0, n_items64 = 0;
+  int32_t *d_pages = nullptr;
+  uint32_t *d_valid = nullptr;
+  // backward device tables
+  BwdItem *d_bitems = nullptr;
+  int n_bitems = 0;
+  int32_t *d_owners = nullptr, *d_qpages = nullptr, *d_uncovered = nullptr, *d_qvalid = nullptr;
+  uint32_t *d_kmask = nullptr, *d_qmask = nullptr;
+  uint64_t *d_adj = nullptr;
+  int64_t *d_uncovered_ptr = nullptr;
+  std::vector<void *> allocations;
+};
+typedef struct kpage_plan PlanT;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kpage_status fail(kpage_status s, const std::string &msg) {
+  g_last_error = msg;
+  return s;
+}
+
+kpage_status hip_fail(hipError_t e, const char *what) {
+  return fail(KPAGE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <class T>
+kpage_status upload(PlanT *pl, const std::vector<T> &host, T **dev, hipStream_t stream) {
+  const size_t bytes = std::max<size_t>(host.size() * sizeof(T), sizeof(T));
+  void *p = nullptr;
+  hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) return fail(KPAGE_ERR_OOM, std::string("hipMalloc: ") + hipGetErrorString(e));
+  pl->allocations.push_back(p);
+  if (!host.empty()) {
+    e = hipMemcpyAsync(p, host.data(), host.size() * sizeof(T), hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  }
+  *dev = static_cast<T *>(p);
+  return KPAGE_OK;
+}
+
+// Copy a walk table with every dummy slot (-1) pointed at the first page of its
+// own walk, so the kernels always load finite data; the row masks keep those
+// slots out of the result.  `ptr` lists walk boundaries.
+std::vector<int32_t> redirect_dummies(const std::vector<int32_t> &walk, const std::vector<int64_t> &ptr) {
+  std::vector<int32_t> out(walk);
+  for (size_t i = 0; i + 1 < ptr.size(); ++i) {
+    const int64_t a = ptr[i], b = ptr[i + 1];
+    if (b <= a) continue;
+    const int32_t first = walk[a];
+    for (int64_t j = a; j < b; ++j)
+      if (out[j] < 0) out[j] = first;
+  }
+  return out;
+}
+
+kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
+  if (pl->fwd_on_device) return KPAGE_OK;
+  const Problem &P = pl->P;
+  const FwdTables &F = pl->F;
+  const int nq = P.n_q;
+  std::vector<int32_t> pages = redirect_dummies(F.walk, F.walk_ptr);
+  std::vector<FwdItem> it128, it64;
+  auto make = [&](int bh, int q) {
+    const int g = P.slot_of(bh);
+    FwdItem x{};
+    x.walk_off = F.walk_ptr[size_t(g) * (nq + 1) + q];
+    x.walk_len = int32_t(F.walk_ptr[size_t(g) * (nq + 1) + q + 1] - x.walk_off);
+    x.bh = bh;
+    x.q = q;
+    x.n_full = F.nfull[size_t(g) * nq + q];
+    x.c_q = P.q_valid[size_t(g) * nq + q];
+    return x;
+  };
+  for (size_t i = 0; i < F.q128_queue.size(); i += 2) it128.push_back(make(F.q128_queue[i], F.q128_queue[i + 1]));
+  for (size_t i = 0; i < F.q64_queue.size(); i += 2) it64.push_back(make(F.q64_queue[i], F.q64_queue[i + 1]));
+  // blocks without valid rows still own their output rows: append cleanup items (empty walk)
+  for (int bh = 0; bh < P.batch * P.heads; ++bh)
+    for (int q = 0; q < nq; ++q)
+      if (P.q_valid[size_t(P.slot_of(bh)) * nq + q] == 0) it64.push_back(make(bh, q));
+  kpage_status s;
+  if ((s = upload(pl, pages, &pl->d_pages, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, F.valid, &pl->d_valid, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, it128, &pl->d_items128, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, it64, &pl->d_items64, stream)) != KPAGE_OK) return s;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  pl->n_items128 = int(it128.size());
+  pl->n_items64 = int(it64.size());
+  pl->fwd_on_device = true;
+  return KPAGE_OK;
+}
+
+void ensure_backward_on_host(PlanT *pl) {
+  if (!pl->B.built) build_backward(pl->P, &pl->B, &pl->S);
+}
+
+kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
+  ensure_backward_on_host(pl);
+  if (pl->bwd_on_device) return KPAGE_OK;
+  const Problem &P = pl->P;
+  const BwdTables &B = pl->B;
+  const int nq = P.n_q, nk = P.n_kv;
+  const size_t n_own = B.aligned.size();
+  // row masks of owner pages (K/V sizes) and of Q-walk pages (Q sizes)
+  std::vector<uint32_t> kmask(n_own * kOwnerSlots, 0);
+  std::vector<uint32_t> qmask(B.qwalk.size(), 0);
+  for (int g = 0; g < P.slots; ++g) {
+    const int32_t *ck = &P.kv_valid[size_t(g) * nk];
+    const int64_t *ok = &P.kv_offset[size_t(g) * nk];
+    std::vector<std::pair<int64_t, int>> starts;  // (first page, block)
+    for (int k = 0; k < nk; ++k)
+      if (ck[k] > 0) starts.emplace_back(ok[k] / kPageRows, k);
+    std::sort(starts.begin(), starts.end());
+    for (int64_t t = B.owner_ptr[g]; t < B.owner_ptr[g + 1]; ++t) {
+      for (int i = 0; i < kOwnerSlots; ++i) {
+        const int32_t pg = B.owners[size_t(t) * kOwnerSlots + i];
+        if (pg < 0) continue;
+        auto itb = std::upper_bound(starts.begin(), starts.end(), std::make_pair(int64_t(pg), 1 << 30));
+        const int k = std::prev(itb)->second;
+        const int j = int(pg - ok[k] / kPageRows);
+        const int c = ck[k];
+        kmask[size_t(t) * kOwnerSlots + i] = (j + 1) * kPageRows <= c ? kFullMask : ((1u << (c % kPageRows)) - 1u);
+      }
+      for (int64_t e = B.qwalk_ptr[t]; e < B.qwalk_ptr[t + 1]; ++e) {
+        const int32_t qp = B.qwalk[e];
+        if (qp < 0) continue;
+        const int c = P.q_valid[size_t(g) * nq + qp / 8];
+        const int j = qp % 8;
+        qmask[e] = (j + 1) * kPageRows <= c ? kFullMask : ((1u << (c % kPageRows)) - 1u);
+      }
+    }
+  }
+  std::vector<int32_t> qpages = redirect_dummies(B.qwalk, B.qwalk_ptr);
+  std::vector<int32_t> owners(B.owners);
+  std::vector<BwdItem> items;
+  for (size_t i = 0; i < B.bwd_queue.size(); i += 2) {
+    const int bh = B.bwd_queue[i], t_local = B.bwd_queue[i + 1];
+    const int g = P.slot_of(bh);
+    const int64_t t = B.owner_ptr[g] + t_local;
+    BwdItem x{};
+    x.qwalk_off = B.qwalk_ptr[t];
+    x.n_steps = int32_t((B.qwalk_ptr[t + 1] - B.qwalk_ptr[t]) / 8);
+    x.bh = bh;
+    x.owner = int32_t(t);
+    x.aligned = B.aligned[t];
+    items.push_back(x);
+  }
+  kpage_status s;
+  if ((s = upload(pl, items, &pl->d_bitems, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, owners, &pl->d_owners, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, kmask, &pl->d_kmask, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, qpages, &pl->d_qpages, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, qmask, &pl->d_qmask, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, B.adj, &pl->d_adj, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, B.uncovered, &pl->d_uncovered, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, B.uncovered_ptr, &pl->d_uncovered_ptr, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, P.q_valid, &pl->d_qvalid, stream)) != KPAGE_OK) return s;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  pl->n_bitems = int(items.size());
+  pl->bwd_on_device = true;
+  return KPAGE_OK;
+}
+
+bool bad_scale(float s) { return !(s > 0.f) || !std::isfinite(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char *kpage_last_error(void) { return g_last_error.c_str(); }
+
+kpage_status kpage_plan(const kpage_problem *problem, const kpage_plan_opts *opts, kpage_plan_t **out) {
+  if (!out) return fail(KPAGE_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  PlanT *pl = new (std::nothrow) PlanT();
+  if (!pl) return fail(KPAGE_ERR_OOM, "host allocation failed");
+  std::string err;
+  int a64 = 16, a128 = 8;
+  kpage_status s = load_problem(problem, opts, &pl->P, &a64, &a128, &err);
+  if (s != KPAGE_OK) {
+    delete pl;
+    return fail(s, err);
+  }
+  pl->F.align64 = a64;
+  pl->F.align128 = a128;
+  try {
+    build_forward(pl->P, &pl->F, &pl->S);
+  } catch (const std::bad_alloc &) {
+    delete pl;
+    return fail(KPAGE_ERR_OOM, "host allocation failed while planning");
+  }
+  *out = pl;
+  g_last_error.clear();
+  return KPAGE_OK;
+}
+
+kpage_status kpage_plan_upload(kpage_plan_t *plan, void *stream) {
+  if (!plan) return fail(KPAGE_ERR_INVALID, "plan is NULL");
+  return ensure_forward_on_device(plan, static_cast<hipStream_t>(stream));
+}
+
+kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, const void *v, void *o, float *lse,
+                            float softmax_scale, void *stream) {
+  if (!plan) return fail(KPAGE_ERR_INVALID, "plan is NULL");
+  if (!q || !k || !v || !o || !lse) return fail(KPAGE_ERR_INVALID, "tensor pointer is NULL");
+  if (bad_scale(softmax_scale)) return fail(KPAGE_ERR_INVALID, "softmax_scale must be positive and finite");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  kpage_status s = ensure_forward_on_device(plan, st);
+  if (s != KPAGE_OK) return s;
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.pages = plan->d_pages;
+  a.valid = plan->d_valid;
+  a.seq_q = plan->P.seq_q;
+  a.seq_kv = plan->P.seq_kv;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.items = plan->d_items128;
+  a.n_items = plan->n_items128;
+  hipError_t e = launch_fwd(a, plan->P.head_dim, 128, st);
+  if (e != hipSuccess) return hip_fail(e, "forward launch (M128 route)");
+  a.items = plan->d_items64;
+  a.n_items = plan->n_items64;
+  e = launch_fwd(a, plan->P.head_dim, 64, st);
+  if (e != hipSuccess) return hip_fail(e, "forward launch (M64 route)");
+  return KPAGE_OK;
+}
+
+kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes) {
+  if (!plan || !bytes) return fail(KPAGE_ERR_INVALID, "plan or bytes is NULL");
+  const size_t rows = size_t(plan->P.batch) * plan->P.heads * size_t(plan->P.seq_q);
+  // fp32 dQ accumulator [BH, seq_q, d] followed by fp32 row sums D [BH, seq_q]
+  *bytes = rows * size_t(plan->P.head_dim) * 4 + rows * 4;
+  return KPAGE_OK;
+}
+
+kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, const void *v, const void *o,
+                            const float *lse, const void *dO, void *dq, void *dk, void *dv, void *workspace,
+                            size_t workspace_bytes, float softmax_scale, void *stream) {
+  if (!plan) return fail(KPAGE_ERR_INVALID, "plan is NULL");
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
+    return fail(KPAGE_ERR_INVALID, "tensor or workspace pointer is NULL");
+  if (bad_scale(softmax_scale)) return fail(KPAGE_ERR_INVALID, "softmax_scale must be positive and finite");
+  size_t need = 0;
+  kpage_bwd_workspace_size(plan, &need);
+  if (workspace_bytes < need) return fail(KPAGE_ERR_INVALID, "workspace smaller than kpage_bwd_workspace_size()");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  kpage_status s = ensure_backward_on_device(plan, st);
+  if (s != KPAGE_OK) return s;
+  const Problem &P = plan->P;
+  const size_t rows = size_t(P.batch) * P.heads * size_t(P.seq_q);
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dO; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dq_acc = static_cast<float *>(workspace);
+  a.delta = static_cast<float *>(workspace) + rows * size_t(P.head_dim);
+  a.items = plan->d_bitems;
+  a.n_items = plan->n_bitems;
+  a.owners = plan->d_owners;
+  a.owner_kmask = plan->d_kmask;
+  a.qpages = plan->d_qpages;
+  a.qmask = plan->d_qmask;
+  a.adj = plan->d_adj;
+  a.uncovered = plan->d_uncovered;
+  a.uncovered_ptr = plan->d_uncovered_ptr;
+  a.q_valid = plan->d_qvalid;
+  a.seq_q = P.seq_q;
+  a.seq_kv = P.seq_kv;
+  a.heads = P.heads;
+  a.n_q = P.n_q;
+  a.per_head = P.per_head ? 1 : 0;
+  a.bh_count = P.batch * P.heads;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipError_t e = launch_bwd(a, P.head_dim, st);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return KPAGE_OK;
+}
+
+kpage_status kpage_plan_stats(const kpage_plan_t *plan, kpage_pair_stats *out) {
+  if (!plan || !out) return fail(KPAGE_ERR_INVALID, "plan or out is NULL");
+  out->useful = plan->S.useful;
+  out->whole_block = plan->S.whole_block;
+  out->paged_m128 = plan->S.paged_m128;
+  out->nominal = plan->S.nominal;
+  out->scheduled = plan->S.scheduled;
+  out->bwd_physical = plan->S.bwd_physical;
+  out->bwd_useful_check = plan->S.bwd_useful_check;
+  return KPAGE_OK;
+}
+
+kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf, size_t *bytes) {
+  if (!plan || !bytes) return fail(KPAGE_ERR_INVALID, "plan or bytes is NULL");
+  if (table_id < 0 || table_id >= KPAGE_T_COUNT) return fail(KPAGE_ERR_INVALID, "unknown table id");
+  if (table_id >= KPAGE_T_OWNER_PTR) ensure_backward_on_host(plan);
+  const void *src = nullptr;
+  size_t n = 0;
+  switch (table_id) {
+#define KPAGE_TABLE(id, vec) \
+  case id:                   \
+    src = vec.data();        \
+    n = vec.size() * sizeof(vec[0]); \
+    break;
+    KPAGE_TABLE(KPAGE_T_FWD_ROUTE, plan->F.route)
+    KPAGE_TABLE(KPAGE_T_FWD_WALK_PTR, plan->F.walk_ptr)
+    KPAGE_TABLE(KPAGE_T_FWD_WALK, plan->F.walk)
+    KPAGE_TABLE(KPAGE_T_FWD_NFULL, plan->F.nfull)
+    KPAGE_TABLE(KPAGE_T_FWD_VALID, plan->F.valid)
+    KPAGE_TABLE(KPAGE_T_Q64_QUEUE, plan->F.q64_queue)
+    KPAGE_TABLE(KPAGE_T_Q128_QUEUE, plan->F.q128_queue)
+    KPAGE_TABLE(KPAGE_T_OWNER_PTR, plan->B.owner_ptr)
+    KPAGE_TABLE(KPAGE_T_OWNERS, plan->B.owners)
+    KPAGE_TABLE(KPAGE_T_OWNER_ALIGNED, plan->B.aligned)
+    KPAGE_TABLE(KPAGE_T_REVQ_PTR, plan->B.revq_ptr)
+    KPAGE_TABLE(KPAGE_T_REVQ, plan->B.revq)
+    KPAGE_TABLE(KPAGE_T_QWALK_PTR, plan->B.qwalk_ptr)
+    KPAGE_TABLE(KPAGE_T_QWALK, plan->B.qwalk)
+    KPAGE_TABLE(KPAGE_T_ADJ, plan->B.adj)
+    KPAGE_TABLE(KPAGE_T_BWD_QUEUE, plan->B.bwd_queue)
+#undef KPAGE_TABLE
+  }
+  if (!host_buf) {
+    *bytes = n;
+    return KPAGE_OK;
+  }
+  if (*bytes < n) return fail(KPAGE_ERR_INVALID, "host buffer too small for the table");
+  if (n) std::memcpy(host_buf, src, n);
+  *bytes = n;
+  return KPAGE_OK;
+}
+
+void kpage_plan_destroy(kpage_plan_t *plan) {
+  if (!plan) return;
+  if (!plan->allocations.empty()) {
+    (void)hipDeviceSynchronize();
+    for (void *p : plan->allocations) (void)hipFree(p);
+  }
+  delete plan;
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Device-side work descriptors and kernel launchers shared by the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace kpage {
+
+// One forward work item: a query block of one (batch, head) and its page walk.
+struct FwdItem {
+  int64_t walk_off;  // first entry of the walk in the device page table (multiple of the step size)
+  int32_t bh;        // b * heads + h
+  int32_t q;         // query block
+  int32_t walk_len;  // pages, a multiple of the pages per step (0: nothing selected)
+  int32_t n_full;    // pages of the fully valid prefix
+  int32_t c_q;       // valid query rows (0 only for cleanup items of empty blocks)
+  int32_t pad;
+};
+
+struct FwdArgs {
+  const void *q, *k, *v;
+  void *o;
+  float *lse;
+  const FwdItem *items;
+  const int32_t *pages;     // walk entries; dummy slots point at a real page of the same walk
+  const uint32_t *valid;    // two 16-bit row masks per word, indexed by walk position / 2
+  int64_t seq_q, seq_kv;
+  int32_t n_items;
+  float scale;              // softmax scale
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+// One backward work item: a K/V owner of one (batch, head) and its Q-page steps.
+struct BwdItem {
+  int64_t qwalk_off;   // first Q page entry (multiple of 8)
+  int32_t bh;
+  int32_t owner;       // global owner index (row of the owner table)
+  int32_t n_steps;
+  int32_t aligned;     // 1: the owner is one block of 8 contiguous pages
+};
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  float *dq_acc;              // fp32 [BH, seq_q, d]
+  float *delta;               // fp32 [BH, seq_q]: rowsum(dO * O)
+  const BwdItem *items;
+  const int32_t *owners;      // [n_own][8] page ids, -1 empty
+  const uint32_t *owner_kmask;// [n_own][8] 16-bit row masks of the owner pages (0 for empty slots)
+  const int32_t *qpages;      // Q-page walk entries, dummy slots point at a real page
+  const uint32_t *qmask;      // row mask per Q-page entry (0 for dummies)
+  const uint64_t *adj;        // adjacency word per step
+  const int32_t *uncovered;   // K/V pages outside every footprint, per slot
+  const int64_t *uncovered_ptr;
+  const int32_t *q_valid;     // [slots][n_q]
+  int64_t seq_q, seq_kv;
+  int32_t n_items, heads, n_q, per_head, bh_count;
+  float scale, scale_log2;
+};
+
+hipError_t launch_fwd(const FwdArgs &a, int head_dim, int route, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &a, int head_dim, hipStream_t stream);
+
+}  // namespace kpage

@@ -1,0 +1,328 @@
+// Host planner: Page16 walks, Q64/Q128 routes and queues, validity words,
+// K/V owners, reverse-Q lists, Q-page walks and page-pair adjacency words.
+//
+// KPage paper: section 3.2.1 (Page16 count p = ceil(c / 16), full pages of the
+// selected blocks first, then one partial tail per partial block, then dummy
+// pages), 3.2.2 (routes by c_q with 64 rows as the threshold; one queue per
+// route, longer walks first; walks padded to whole iterations of 16 or 8 pages),
+// 3.2.4 (two 16-bit page masks per 32-bit word), 3.3.1 (owners of eight page
+// slots, full blocks aligned to their own owner, partial blocks packed without
+// crossing an owner), 3.3.2 (reverse-Q lists from an owner x Q bitmap; full Q
+// blocks first, then pages of partial Q blocks), 3.3.3 (one 64-bit adjacency
+// word per 8 x 8 page step), 3.4 (metadata depends only on the graph and the
+// valid-row counts) and 4.4 (pair-capacity accounting).
+#include "plan.hpp"
+
+#include <algorithm>
+#include <sstream>
+#include <tuple>
+
+namespace kpage {
+
+namespace {
+
+inline int pages_of(int c) { return (c + kPageRows - 1) / kPageRows; }
+inline uint32_t tail_mask(int c) { return (1u << (c % kPageRows)) - 1u; }
+inline uint32_t page_mask(int c, int j) {  // mask of page j of a block with c valid rows
+  return (j + 1) * kPageRows <= c ? kFullMask : tail_mask(c);
+}
+
+template <class T>
+std::string str(const T &v) {
+  std::ostringstream os;
+  os << v;
+  return os.str();
+}
+
+}  // namespace
+
+kpage_status load_problem(const kpage_problem *p, const kpage_plan_opts *o, Problem *out, int *align64,
+                          int *align128, std::string *err) {
+  if (!p) { *err = "problem is NULL"; return KPAGE_ERR_INVALID; }
+  if (p->batch < 1 || p->heads < 1) { *err = "batch and heads must be >= 1"; return KPAGE_ERR_INVALID; }
+  if (p->head_dim != 64 && p->head_dim != 128) {
+    *err = "head_dim " + str(p->head_dim) + " not supported (64 or 128)";
+    return KPAGE_ERR_UNSUPPORTED;
+  }
+  if (p->n_q_blocks < 1 || p->n_kv_blocks < 1) { *err = "n_q_blocks and n_kv_blocks must be >= 1"; return KPAGE_ERR_INVALID; }
+  if (p->seq_q != int64_t(kBlockRows) * p->n_q_blocks) { *err = "seq_q must equal 128 * n_q_blocks"; return KPAGE_ERR_INVALID; }
+  if (p->seq_kv < kPageRows || p->seq_kv % kPageRows) { *err = "seq_kv must be a positive multiple of 16"; return KPAGE_ERR_INVALID; }
+  if (p->per_head != 0 && p->per_head != 1) { *err = "per_head must be 0 or 1"; return KPAGE_ERR_INVALID; }
+  if (!p->q_valid || !p->kv_valid || !p->q2k_ptr || (!p->q2k_idx)) {
+    *err = "q_valid, kv_valid, q2k_ptr and q2k_idx are required";
+    return KPAGE_ERR_INVALID;
+  }
+  int a64 = 16, a128 = 8;
+  if (o) {
+    if (o->q_group != 0) { *err = "only q_group = 0 (one Q group) is implemented"; return KPAGE_ERR_UNSUPPORTED; }
+    if (o->align_q64) a64 = o->align_q64;
+    if (o->align_q128) a128 = o->align_q128;
+    if (a64 < 16 || a64 % 16 || a128 < 8 || a128 % 8) {
+      *err = "align_q64 must be a multiple of 16 and align_q128 a multiple of 8";
+      return KPAGE_ERR_INVALID;
+    }
+  }
+  *align64 = a64;
+  *align128 = a128;
+  Problem &P = *out;
+  P.batch = p->batch; P.heads = p->heads; P.head_dim = p->head_dim;
+  P.n_q = p->n_q_blocks; P.n_kv = p->n_kv_blocks;
+  P.seq_q = p->seq_q; P.seq_kv = p->seq_kv;
+  P.per_head = p->per_head == 1;
+  P.slots = P.per_head ? P.batch * P.heads : 1;
+  const size_t G = P.slots, nq = P.n_q, nk = P.n_kv;
+  P.q_valid.assign(p->q_valid, p->q_valid + G * nq);
+  P.kv_valid.assign(p->kv_valid, p->kv_valid + G * nk);
+  P.q2k_ptr.assign(p->q2k_ptr, p->q2k_ptr + G * (nq + 1));
+  P.kv_offset.resize(G * nk);
+  for (size_t g = 0; g < G; ++g)
+    for (size_t k = 0; k < nk; ++k)
+      P.kv_offset[g * nk + k] = p->kv_offset ? p->kv_offset[g * nk + k] : int64_t(kBlockRows) * int64_t(k);
+  for (int32_t c : P.q_valid)
+    if (c < 0 || c > kBlockRows) { *err = "q_valid outside [0,128]"; return KPAGE_ERR_INVALID; }
+  for (int32_t c : P.kv_valid)
+    if (c < 0 || c > kBlockRows) { *err = "kv_valid outside [0,128]"; return KPAGE_ERR_INVALID; }
+  int64_t nnz = 0;
+  for (size_t g = 0; g < G; ++g)
+    for (size_t q = 0; q < nq; ++q) {
+      int64_t a = P.q2k_ptr[g * (nq + 1) + q], b = P.q2k_ptr[g * (nq + 1) + q + 1];
+      if (a < 0 || b < a) { *err = "q2k_ptr must be non-negative and non-decreasing within a row"; return KPAGE_ERR_INVALID; }
+      nnz = std::max(nnz, b);
+    }
+  P.q2k_idx.assign(p->q2k_idx, p->q2k_idx + nnz);
+  // footprints: page aligned, inside seq_kv, pairwise disjoint
+  const int64_t n_pages = P.seq_kv / kPageRows;
+  std::vector<int32_t> owner_block(n_pages);
+  for (size_t g = 0; g < G; ++g) {
+    std::fill(owner_block.begin(), owner_block.end(), -1);
+    for (size_t k = 0; k < nk; ++k) {
+      int64_t off = P.kv_offset[g * nk + k];
+      int c = P.kv_valid[g * nk + k];
+      if (off < 0 || off % kPageRows) { *err = "kv_offset must be a non-negative multiple of 16"; return KPAGE_ERR_INVALID; }
+      if (off + int64_t(kPageRows) * pages_of(c) > P.seq_kv) { *err = "a K/V block footprint exceeds seq_kv"; return KPAGE_ERR_INVALID; }
+      for (int j = 0; j < pages_of(c); ++j) {
+        int64_t pg = off / kPageRows + j;
+        if (owner_block[pg] >= 0) { *err = "K/V block page footprints overlap"; return KPAGE_ERR_INVALID; }
+        owner_block[pg] = int32_t(k);
+      }
+    }
+    std::vector<int32_t> seen(nk, -1);
+    for (size_t q = 0; q < nq; ++q) {
+      int64_t a = P.q2k_ptr[g * (nq + 1) + q], b = P.q2k_ptr[g * (nq + 1) + q + 1];
+      for (int64_t e = a; e < b; ++e) {
+        int32_t k = P.q2k_idx[e];
+        if (k < 0 || k >= P.n_kv) { *err = "q2k_idx entry outside [0, n_kv)"; return KPAGE_ERR_INVALID; }
+        if (seen[k] == int32_t(q)) { *err = "duplicate K/V block in a selection list"; return KPAGE_ERR_INVALID; }
+        seen[k] = int32_t(q);
+      }
+    }
+  }
+  return KPAGE_OK;
+}
+
+void build_forward(const Problem &P, FwdTables *T, PairStats *S) {
+  const int G = P.slots, nq = P.n_q, nk = P.n_kv;
+  const int BH = P.batch * P.heads;
+  std::vector<int> bh_per_slot(G, 0);
+  for (int bh = 0; bh < BH; ++bh) bh_per_slot[P.slot_of(bh)]++;
+  T->route.assign(size_t(G) * nq, 0);
+  T->nfull.assign(size_t(G) * nq, 0);
+  T->unpadded.assign(size_t(G) * nq, 0);
+  T->walk_ptr.assign(size_t(G) * (nq + 1), 0);
+  T->walk.clear();
+  T->valid.clear();
+  std::vector<uint32_t> masks;
+  for (int g = 0; g < G; ++g) {
+    const int32_t *cq = &P.q_valid[size_t(g) * nq];
+    const int32_t *ck = &P.kv_valid[size_t(g) * nk];
+    const int64_t *ok = &P.kv_offset[size_t(g) * nk];
+    const uint64_t mult = uint64_t(bh_per_slot[g]);
+    for (int q = 0; q < nq; ++q) {
+      T->walk_ptr[size_t(g) * (nq + 1) + q] = int64_t(T->walk.size());
+      if (cq[q] == 0) continue;
+      const int route = cq[q] <= 64 ? 64 : 128;
+      const int per_step = route == 64 ? T->align64 : T->align128;
+      const int64_t a = P.q2k_ptr[size_t(g) * (nq + 1) + q], b = P.q2k_ptr[size_t(g) * (nq + 1) + q + 1];
+      const size_t start = T->walk.size();
+      masks.clear();
+      uint64_t useful = 0, psum = 0;
+      // full pages of every selected block, in selection order
+      for (int64_t e = a; e < b; ++e) {
+        const int k = P.q2k_idx[e];
+        const int32_t base = int32_t(ok[k] / kPageRows);
+        for (int j = 0; j < ck[k] / kPageRows; ++j) {
+          T->walk.push_back(base + j);
+          masks.push_back(kFullMask);
+        }
+        useful += uint64_t(cq[q]) * uint64_t(ck[k]);
+        psum += uint64_t(pages_of(ck[k]));
+      }
+      const int n_full = int(T->walk.size() - start);
+      // then the partial tail of every partial block, in selection order
+      for (int64_t e = a; e < b; ++e) {
+        const int k = P.q2k_idx[e];
+        if (ck[k] % kPageRows) {
+          T->walk.push_back(int32_t(ok[k] / kPageRows) + ck[k] / kPageRows);
+          masks.push_back(tail_mask(ck[k]));
+        }
+      }
+      const int unpadded = int(T->walk.size() - start);
+      while ((T->walk.size() - start) % per_step) {
+        T->walk.push_back(-1);
+        masks.push_back(0);
+      }
+      for (size_t i = 0; i + 1 < masks.size(); i += 2) T->valid.push_back(masks[i] | (masks[i + 1] << 16));
+      T->route[size_t(g) * nq + q] = route;
+      T->nfull[size_t(g) * nq + q] = n_full;
+      T->unpadded[size_t(g) * nq + q] = unpadded;
+      const uint64_t M = uint64_t(route == 64 ? 64 : 128);
+      const uint64_t len = uint64_t(T->walk.size() - start);
+      S->useful += mult * useful;
+      S->whole_block += mult * uint64_t(kBlockRows) * kBlockRows * uint64_t(b - a);
+      S->paged_m128 += mult * uint64_t(kBlockRows) * kPageRows * psum;
+      S->nominal += mult * M * kPageRows * psum;
+      S->scheduled += mult * M * kPageRows * len;
+    }
+    T->walk_ptr[size_t(g) * (nq + 1) + nq] = int64_t(T->walk.size());
+  }
+  // per-route queues: longest unpadded walk first, then (bh, q) ascending
+  for (int route : {64, 128}) {
+    std::vector<std::tuple<int, int, int>> ent;
+    for (int bh = 0; bh < BH; ++bh) {
+      const int g = P.slot_of(bh);
+      for (int q = 0; q < nq; ++q)
+        if (T->route[size_t(g) * nq + q] == route) ent.emplace_back(-T->unpadded[size_t(g) * nq + q], bh, q);
+    }
+    std::sort(ent.begin(), ent.end());
+    auto &out = route == 64 ? T->q64_queue : T->q128_queue;
+    out.clear();
+    for (auto &x : ent) {
+      out.push_back(std::get<1>(x));
+      out.push_back(std::get<2>(x));
+    }
+  }
+}
+
+void build_backward(const Problem &P, BwdTables *T, PairStats *S) {
+  const int G = P.slots, nq = P.n_q, nk = P.n_kv;
+  const int BH = P.batch * P.heads;
+  std::vector<int> bh_per_slot(G, 0);
+  for (int bh = 0; bh < BH; ++bh) bh_per_slot[P.slot_of(bh)]++;
+  *T = BwdTables();
+  T->owner_ptr.push_back(0);
+  T->revq_ptr.push_back(0);
+  T->qwalk_ptr.push_back(0);
+  T->uncovered_ptr.push_back(0);
+  S->bwd_physical = 0;
+  S->bwd_useful_check = 0;
+  std::vector<std::vector<int>> steps_of(G);
+  const int64_t n_pages = P.seq_kv / kPageRows;
+  for (int g = 0; g < G; ++g) {
+    const int32_t *cq = &P.q_valid[size_t(g) * nq];
+    const int32_t *ck = &P.kv_valid[size_t(g) * nk];
+    const int64_t *ok = &P.kv_offset[size_t(g) * nk];
+    const uint64_t mult = uint64_t(bh_per_slot[g]);
+    // owners: full blocks first (each its own aligned owner), then partial blocks next-fit
+    std::vector<std::vector<int32_t>> own;
+    std::vector<std::vector<int32_t>> own_blocks;
+    std::vector<int32_t> owner_of(nk, -1);
+    for (int k = 0; k < nk; ++k) {
+      if (ck[k] != kBlockRows) continue;
+      owner_of[k] = int32_t(own.size());
+      own.emplace_back();
+      own_blocks.push_back({k});
+      for (int j = 0; j < kOwnerSlots; ++j) own.back().push_back(int32_t(ok[k] / kPageRows) + j);
+    }
+    int cur = -1;
+    for (int k = 0; k < nk; ++k) {
+      if (ck[k] == 0 || ck[k] == kBlockRows) continue;
+      const int p = pages_of(ck[k]);
+      if (cur < 0 || kOwnerSlots - int(own[cur].size()) < p) {
+        own.emplace_back();
+        own_blocks.emplace_back();
+        cur = int(own.size()) - 1;
+      }
+      owner_of[k] = cur;
+      own_blocks[cur].push_back(k);
+      for (int j = 0; j < p; ++j) own[cur].push_back(int32_t(ok[k] / kPageRows) + j);
+    }
+    const int n_own = int(own.size());
+    // per-page block and row mask, for adjacency and the visited-pair check
+    std::vector<int32_t> page_block(n_pages, -1);
+    for (int k = 0; k < nk; ++k)
+      for (int j = 0; j < pages_of(ck[k]); ++j) page_block[ok[k] / kPageRows + j] = k;
+    for (int64_t pg = 0; pg < n_pages; ++pg)
+      if (page_block[pg] < 0) T->uncovered.push_back(int32_t(pg));
+    T->uncovered_ptr.push_back(int64_t(T->uncovered.size()));
+    // graph edges (c_q > 0, c_k > 0) as a dense bit matrix and the owner x Q bitmap
+    std::vector<uint8_t> edge(size_t(nq) * nk, 0);
+    std::vector<uint8_t> bitmap(size_t(n_own) * nq, 0);
+    for (int q = 0; q < nq; ++q) {
+      if (cq[q] == 0) continue;
+      const int64_t a = P.q2k_ptr[size_t(g) * (nq + 1) + q], b = P.q2k_ptr[size_t(g) * (nq + 1) + q + 1];
+      for (int64_t e = a; e < b; ++e) {
+        const int k = P.q2k_idx[e];
+        if (ck[k] == 0) continue;
+        edge[size_t(q) * nk + k] = 1;
+        bitmap[size_t(owner_of[k]) * nq + q] = 1;
+      }
+    }
+    for (int t = 0; t < n_own; ++t) {
+      auto &pages = own[t];
+      const uint8_t al = (own_blocks[t].size() == 1 && pages.size() == size_t(kOwnerSlots)) ? 1 : 0;
+      while (pages.size() < size_t(kOwnerSlots)) pages.push_back(-1);
+      std::vector<int32_t> R;
+      for (int q = 0; q < nq; ++q)
+        if (bitmap[size_t(t) * nq + q]) R.push_back(q);
+      T->revq.insert(T->revq.end(), R.begin(), R.end());
+      T->revq_ptr.push_back(int64_t(T->revq.size()));
+      const size_t w0 = T->qwalk.size();
+      for (int q : R)
+        if (cq[q] == kBlockRows)
+          for (int j = 0; j < 8; ++j) T->qwalk.push_back(8 * q + j);
+      for (int q : R)
+        if (cq[q] > 0 && cq[q] < kBlockRows)
+          for (int j = 0; j < pages_of(cq[q]); ++j) T->qwalk.push_back(8 * q + j);
+      while ((T->qwalk.size() - w0) % 8) T->qwalk.push_back(-1);
+      T->qwalk_ptr.push_back(int64_t(T->qwalk.size()));
+      const int n_steps = int((T->qwalk.size() - w0) / 8);
+      for (int s = 0; s < n_steps; ++s) {
+        uint64_t word = 0;
+        for (int j = 0; j < 8; ++j) {
+          const int32_t qp = T->qwalk[w0 + 8 * s + j];
+          if (qp < 0) continue;
+          const int qb = qp / 8;
+          const uint32_t qm = page_mask(cq[qb], qp % 8);
+          for (int i = 0; i < 8; ++i) {
+            const int32_t kp = pages[i];
+            if (kp < 0) continue;
+            const int kb = page_block[kp];
+            if (!edge[size_t(qb) * nk + kb]) continue;
+            word |= uint64_t(1) << (8 * j + i);
+            const uint32_t km = page_mask(ck[kb], int(kp - ok[kb] / kPageRows));
+            S->bwd_useful_check += mult * uint64_t(__builtin_popcount(qm)) * uint64_t(__builtin_popcount(km));
+          }
+        }
+        T->adj.push_back(word);
+      }
+      S->bwd_physical += mult * uint64_t(kBlockRows) * kBlockRows * uint64_t(n_steps);
+      T->owners.insert(T->owners.end(), pages.begin(), pages.end());
+      T->aligned.push_back(al);
+      steps_of[g].push_back(n_steps);
+    }
+    T->owner_ptr.push_back(T->owner_ptr.back() + n_own);
+  }
+  std::vector<std::tuple<int, int, int>> ent;
+  for (int bh = 0; bh < BH; ++bh) {
+    const int g = P.slot_of(bh);
+    for (size_t t = 0; t < steps_of[g].size(); ++t) ent.emplace_back(-steps_of[g][t], bh, int(t));
+  }
+  std::sort(ent.begin(), ent.end());
+  for (auto &x : ent) {
+    T->bwd_queue.push_back(std::get<1>(x));
+    T->bwd_queue.push_back(std::get<2>(x));
+  }
+  T->built = true;
+}
+
+}  // namespace kpage

@@ -1,0 +1,68 @@
+// Host-side planner of the KPage page tables (KPage paper, sections 3.2-3.4).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "kpage.h"
+
+namespace kpage {
+
+constexpr int kPageRows = 16;
+constexpr int kBlockRows = 128;
+constexpr int kOwnerSlots = 8;
+constexpr uint32_t kFullMask = 0xFFFFu;
+
+struct Problem {
+  int batch = 0, heads = 0, head_dim = 0, n_q = 0, n_kv = 0, slots = 0;
+  int64_t seq_q = 0, seq_kv = 0;
+  bool per_head = false;
+  std::vector<int32_t> q_valid, kv_valid;   // [slots][n]
+  std::vector<int64_t> kv_offset;           // [slots][n_kv]
+  std::vector<int64_t> q2k_ptr;             // [slots][n_q + 1]
+  std::vector<int32_t> q2k_idx;
+  int slot_of(int bh) const { return per_head ? bh : 0; }
+};
+
+struct PairStats {
+  uint64_t useful = 0, whole_block = 0, paged_m128 = 0, nominal = 0, scheduled = 0;
+  uint64_t bwd_physical = 0, bwd_useful_check = 0;
+};
+
+// Forward tables, concatenated over graph slots.
+struct FwdTables {
+  int align64 = 16, align128 = 8;
+  std::vector<int32_t> route;       // [slots][n_q]
+  std::vector<int64_t> walk_ptr;    // [slots][n_q + 1]
+  std::vector<int32_t> walk;        // page ids, -1 dummy
+  std::vector<int32_t> nfull;       // [slots][n_q]
+  std::vector<uint32_t> valid;      // 2 page masks per word
+  std::vector<int32_t> q64_queue;   // pairs (bh, q)
+  std::vector<int32_t> q128_queue;  // pairs (bh, q)
+  std::vector<int32_t> unpadded;    // [slots][n_q] real pages per walk
+};
+
+// Backward tables, concatenated over graph slots.
+struct BwdTables {
+  bool built = false;
+  std::vector<int64_t> owner_ptr;   // [slots + 1]
+  std::vector<int32_t> owners;      // [n_own][8]
+  std::vector<uint8_t> aligned;     // [n_own]
+  std::vector<int64_t> revq_ptr;    // [n_own + 1]
+  std::vector<int32_t> revq;
+  std::vector<int64_t> qwalk_ptr;   // [n_own + 1]
+  std::vector<int32_t> qwalk;
+  std::vector<uint64_t> adj;        // one word per step
+  std::vector<int32_t> bwd_queue;   // pairs (bh, owner within slot)
+  std::vector<int64_t> uncovered_ptr;  // [slots + 1] K/V pages outside every block footprint
+  std::vector<int32_t> uncovered;
+};
+
+// Validates the C descriptor and copies it.  Returns KPAGE_OK or an error with `err` set.
+kpage_status load_problem(const kpage_problem *p, const kpage_plan_opts *o, Problem *out, int *align64,
+                          int *align128, std::string *err);
+void build_forward(const Problem &p, FwdTables *t, PairStats *s);
+void build_backward(const Problem &p, BwdTables *t, PairStats *s);
+
+}  // namespace kpage

@@ -1,0 +1,188 @@
+/*
+ * kpage.h -- C ABI of a gfx950 (MI355X) implementation of KPage-style
+ * block-sparse attention over flattened T x H x W video token layouts.
+ *
+ * Source: "KPage: Cross-Block Page Compaction for Hardware-Efficient Sparse
+ * Attention" (arXiv 2610.28096).  Section numbers below refer to that paper.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are caller-owned device buffers, bf16 (bfloat16), contiguous
+ *    [batch, heads, rows, head_dim], 16-byte aligned:
+ *      Q, O, dO, dQ : rows = seq_q  (= 128 * n_q_blocks; query block q owns
+ *                                    rows [128 q, 128 q + 128), valid rows first)
+ *      K, V, dK, dV : rows = seq_kv (K/V block k owns rows
+ *                                    [kv_offset[k], kv_offset[k] + kv_valid[k]))
+ *    LSE is fp32 [batch, heads, seq_q] (natural log).
+ *  - Every row of K and V that lies inside a block's 16-row page footprint
+ *    must hold finite values, padded rows included (section 3.2.4: padding is
+ *    masked before the row maximum; the paper zeroes it, a finite value is
+ *    enough for exact results).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    device work is asynchronous on that stream; kernel faults surface at the
+ *    caller's next synchronisation.
+ *  - No exception crosses the ABI.  A non-OK status leaves a thread-local
+ *    message readable with kpage_last_error().  Descriptor errors are reported
+ *    before any device work is enqueued.
+ */
+#ifndef KPAGE_H
+#define KPAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KPAGE_OK = 0,
+  KPAGE_ERR_INVALID = 1,      /* malformed descriptor, pointer or size           */
+  KPAGE_ERR_UNSUPPORTED = 2,  /* well formed but outside what is implemented     */
+  KPAGE_ERR_OOM = 3,          /* host or device allocation failed                */
+  KPAGE_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed      */
+} kpage_status;
+
+typedef struct kpage_plan kpage_plan_t;
+
+/*
+ * Problem descriptor (host memory, read only during kpage_plan()).
+ * Section 3.4.1: per-head Q block sizes c^Q, K/V block sizes c^K and
+ * Page16-aligned offsets o^K with disjoint page footprints, and the ordered
+ * per-query-block lists K_q of selected K/V blocks.  The shared blk128 layout
+ * is the special case n_q = n_kv, c^Q = c^K, o^K = 128 k.
+ *
+ * G = 1 graph slot when per_head == 0 (one layout and graph for every
+ * (batch, head)), G = batch * heads when per_head == 1 (slot b * heads + h).
+ */
+typedef struct {
+  int32_t batch, heads, head_dim;   /* head_dim in {64, 128}                         */
+  int32_t n_q_blocks, n_kv_blocks;  /* >= 1                                          */
+  int64_t seq_q, seq_kv;            /* seq_q == 128 * n_q_blocks; seq_kv % 16 == 0    */
+  int32_t per_head;                 /* 0 or 1                                        */
+  const int32_t *q_valid;           /* [G][n_q]  valid rows per Q block, in [0,128]  */
+  const int32_t *kv_valid;          /* [G][n_kv] valid rows per K/V block, in [0,128]*/
+  const int64_t *kv_offset;         /* [G][n_kv] first row, % 16 == 0; NULL: 128 k   */
+  const int64_t *q2k_ptr;           /* [G][n_q + 1] offsets into q2k_idx (CSR rows)  */
+  const int32_t *q2k_idx;           /* K/V block ids in [0, n_kv), unique per row    */
+} kpage_problem;
+
+/*
+ * Planner options (NULL = defaults).  Section 3.2.2: the Q64 path consumes 16
+ * pages per iteration and the Q128 path 8, so walks are padded with dummy pages
+ * to a multiple of align_q64 / align_q128 (defaults 16 / 8; multiples of those
+ * values are accepted).  q_group is the Q-group size of section 3.3.2; only 0
+ * (one group) is implemented.
+ */
+typedef struct {
+  int32_t q_group;
+  int32_t align_q128;
+  int32_t align_q64;
+} kpage_plan_opts;
+
+/* Section 4.4 pair-capacity accounting, summed over batch, heads and non-empty
+ * query blocks (see kpage_plan_stats). */
+typedef struct {
+  uint64_t useful;            /* sum over edges of c_q * c_k                         */
+  uint64_t whole_block;       /* 128 * 128 per selected block                        */
+  uint64_t paged_m128;        /* 128 * 16 * pages of the selected blocks              */
+  uint64_t nominal;           /* M_q * 16 * pages, M_q = 64 or 128 by route           */
+  uint64_t scheduled;         /* M_q * 16 * walk length including dummy pages        */
+  uint64_t bwd_physical;      /* 128 * 128 per backward step (lazy; 0 until built)   */
+  uint64_t bwd_useful_check;  /* valid pairs visited by backward; equals useful      */
+} kpage_pair_stats;
+
+/*
+ * Build the forward metadata (section 3.4): Page16 walks of every query block
+ * (full pages of K_q in order, then one tail page per partial block, then dummy
+ * pages), Q64/Q128 routes (section 3.2.2), per-route work queues ordered by
+ * descending walk length, validity words (two 16-bit page masks per uint32,
+ * section 3.2.4) and the index of the end of the fully valid prefix.
+ * Host-only: no device memory is touched here; tables are copied to the device
+ * on first use (kpage_plan_upload or the first attention call).
+ * Returns KPAGE_ERR_INVALID for a malformed descriptor, KPAGE_ERR_UNSUPPORTED
+ * for head_dim not in {64,128} or q_group != 0.  *out is owned by the caller
+ * and released with kpage_plan_destroy().
+ */
+kpage_status kpage_plan(const kpage_problem *problem, const kpage_plan_opts *opts,
+                        kpage_plan_t **out);
+
+/* Copy the forward tables to the current HIP device on `stream` (idempotent). */
+kpage_status kpage_plan_upload(kpage_plan_t *plan, void *stream);
+
+/*
+ * Forward attention, section 3.2: for every (b, h) and query block q with
+ * c_q > 0, O = softmax(scale * Q K_J^T) V_J over exactly the valid key rows J
+ * of the selected blocks (masking before the row maximum, eq. 3), and
+ * LSE = log sum exp.  K/V pages are gathered straight into LDS tiles; no
+ * compacted copy is written to device memory.  Rows outside the valid prefix
+ * of a block, blocks with c_q = 0 and rows with no valid key get O = 0 and
+ * LSE = -inf.  q, k, v, o: bf16 device pointers; lse: fp32 device pointer.
+ */
+kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, const void *v,
+                            void *o, float *lse, float softmax_scale, void *stream);
+
+/* Bytes of device workspace kpage_attn_bwd needs (fp32 dQ accumulator and row sums). */
+kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes);
+
+/*
+ * Backward attention, section 3.3: gradients of sum(O * dO) under the forward
+ * definition, computed over K/V-owned tiles (owners of 8 Page16 slots, no
+ * logical block crossing an owner), their reverse-Q neighbourhoods packed into
+ * 8-page Q steps, and one 64-bit page-pair adjacency word per step that
+ * restores the original graph.  The backward metadata is built on the first
+ * call (lazily, section 3.4).  o and lse are the forward outputs; workspace is
+ * a caller-owned device buffer of at least kpage_bwd_workspace_size() bytes.
+ * Invalid rows of dQ (by Q sizes) and of dK/dV (by K/V sizes), and rows of
+ * blocks with no edge, are written as 0.
+ */
+kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, const void *v,
+                            const void *o, const float *lse, const void *dO,
+                            void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                            float softmax_scale, void *stream);
+
+/* Pair statistics (host memory).  Backward fields are filled once the backward
+ * metadata exists (after kpage_attn_bwd or an export of a backward table). */
+kpage_status kpage_plan_stats(const kpage_plan_t *plan, kpage_pair_stats *out);
+
+/* Plan tables for offline comparison.  Element types: */
+enum {
+  KPAGE_T_FWD_ROUTE = 0,      /* int32 [G][n_q]: 0, 64 or 128                         */
+  KPAGE_T_FWD_WALK_PTR = 1,   /* int64 [G][n_q + 1]: offsets into FWD_WALK            */
+  KPAGE_T_FWD_WALK = 2,       /* int32 page ids (row / 16), -1 = dummy                */
+  KPAGE_T_FWD_NFULL = 3,      /* int32 [G][n_q]: length of the fully valid prefix     */
+  KPAGE_T_FWD_VALID = 4,      /* uint32: word i of a walk at FWD_WALK_PTR / 2 + i     */
+  KPAGE_T_Q64_QUEUE = 5,      /* int32 [n][2]: (b * heads + h, q)                     */
+  KPAGE_T_Q128_QUEUE = 6,     /* int32 [n][2]                                         */
+  KPAGE_T_OWNER_PTR = 7,      /* int64 [G + 1]: offsets into OWNERS                   */
+  KPAGE_T_OWNERS = 8,         /* int32 [n_own][8]: K/V page ids, -1 = empty slot      */
+  KPAGE_T_OWNER_ALIGNED = 9,  /* uint8 [n_own]: one block of 8 contiguous pages       */
+  KPAGE_T_REVQ_PTR = 10,      /* int64 [n_own + 1]                                    */
+  KPAGE_T_REVQ = 11,          /* int32 Q block ids, ascending per owner               */
+  KPAGE_T_QWALK_PTR = 12,     /* int64 [n_own + 1]: offsets into QWALK (multiple of 8)*/
+  KPAGE_T_QWALK = 13,         /* int32 Q page ids (8 q + j), -1 = dummy               */
+  KPAGE_T_ADJ = 14,           /* uint64: step s of owner t at QWALK_PTR[t] / 8 + s    */
+  KPAGE_T_BWD_QUEUE = 15,     /* int32 [n][2]: (b * heads + h, owner within its slot) */
+  KPAGE_T_COUNT = 16
+};
+
+/*
+ * Copy table `table_id` into host_buf.  With host_buf == NULL, *bytes receives
+ * the size.  Otherwise *bytes must be at least that size (KPAGE_ERR_INVALID if
+ * not) and receives the number of bytes written.  Backward tables trigger the
+ * host part of the lazy backward build.
+ */
+kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf, size_t *bytes);
+
+/* Release a plan and its device tables (NULL is ignored).  Synchronises the
+ * device before freeing device memory that kernels may still read. */
+void kpage_plan_destroy(kpage_plan_t *plan);
+
+/* Message of the last non-OK status on this thread ("" if none). */
+const char *kpage_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KPAGE_H */

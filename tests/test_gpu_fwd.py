@@ -1,0 +1,194 @@
+"""Forward parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (bf16 inputs, fp32 accumulation): O max-abs <= 1e-2; LSE relative error
+<= 1e-3, taken against max(1, |LSE|) so rows with LSE near 0 are not ill-conditioned;
+rows the oracle marks empty (LSE = -inf) must be exactly O = 0 and LSE = -inf.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_11_amd as K
+from oracle import oracle_fwd
+from tests.problems import make_problem, random_tensors
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+O_ATOL = 1e-2
+LSE_RTOL = 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_fwd(problem, q, k, v, plan=None):
+    dev = torch.device("cuda", 0)
+    plan = plan or K.kpage_plan(problem)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o, lse = K.attn_fwd(plan, qd, kd, vd, problem.scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def check(O, L, Oref, Lref, label):
+    done = ~np.isnan(Lref)
+    empty = done & np.isneginf(Lref)
+    live = done & ~empty
+    assert np.all(np.isneginf(L[empty])), f"{label}: rows without keys must have LSE = -inf"
+    assert np.all(O[empty] == 0), f"{label}: rows without keys must have O = 0"
+    assert np.all(np.isfinite(L[live])), f"{label}: non-finite LSE on a live row"
+    err_o = np.abs(O[live] - Oref[live]).max() if live.any() else 0.0
+    err_l = (np.abs(L[live] - Lref[live]) / np.maximum(1.0, np.abs(Lref[live]))).max() if live.any() else 0.0
+    _say(f"  {label}: rows={int(live.sum())} empty={int(empty.sum())} O max-abs={err_o:.3e} LSE rel={err_l:.3e}")
+    assert err_o <= O_ATOL, (label, err_o)
+    assert err_l <= LSE_RTOL, (label, err_l)
+
+
+def padded_rows(w, side):
+    """Row indices that hold no token (shared layouts: every block spans 128 rows)."""
+    c = w.q_valid[0] if side == "q" else w.kv_valid[0]
+    rows = [np.arange(128 * b + int(n), 128 * b + 128) for b, n in enumerate(c)]
+    return torch.from_numpy(np.concatenate(rows))
+
+
+def _all_rows(w, label):
+    _say(f"[fwd] {label}: B={w.batch} H={w.heads} d={w.head_dim} n_q={w.n_q} n_kv={w.n_kv}")
+    O, L = gpu_fwd(w, w.q, w.k, w.v)
+    Oref, Lref = oracle_fwd(w, w.q, w.k, w.v)
+    check(O, L, Oref, Lref, label)
+
+
+def _sampled(w, label, per_head=24, seed=0):
+    rng = np.random.default_rng(seed)
+    items = []
+    for h in range(w.heads):
+        qs = rng.choice(w.n_q, size=min(per_head, w.n_q), replace=False)
+        items += [(0, h, int(q)) for q in qs]
+    _say(f"[fwd] {label}: B={w.batch} H={w.heads} n_q={w.n_q}, {len(items)} sampled blocks")
+    O, L = gpu_fwd(w, w.q, w.k, w.v)
+    Oref, Lref = oracle_fwd(w, w.q, w.k, w.v, items=items)
+    check(O, L, Oref, Lref, label)
+
+
+def test_fwd_tiny_3d_layout_d64_all_rows():
+    _all_rows(make_workload(1), "tiny 5x6x10 d=64")
+
+
+def test_fwd_padding_free_two_heads_all_rows():
+    _all_rows(make_workload(2, heads=[0, 1]), "16x32x32 two heads")
+
+
+def test_fwd_3d_padded_two_heads_all_rows():
+    _all_rows(make_workload(3, heads=[0, 1]), "21x30x52 two heads")
+
+
+def test_fwd_vsa_topk_sampled():
+    _sampled(make_workload(4, heads=[0, 1]), "21x45x80 top-87, two heads", per_head=40)
+
+
+def test_fwd_independent_partitions_sampled():
+    _sampled(make_workload(5, heads=[0, 1]), "SVG2-like partitions, two heads", per_head=60)
+
+
+def test_fwd_3d_padded_full_heads_sampled():
+    """All 40 heads in one launch, as the benchmark runs it; sampled query blocks checked."""
+    _sampled(make_workload(3), "21x30x52 all 40 heads", per_head=6)
+
+
+def test_fwd_padding_free_full_heads_sampled():
+    _sampled(make_workload(2), "16x32x32 all 24 heads", per_head=8)
+
+
+EDGE_CASES = {
+    # every tail length, both routes, walks of several stages with dummies
+    "tails-1-to-15": ([128, 64, 65, 1, 127], [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 128, 16, 17],
+                      [list(range(18)), list(range(0, 18, 2)), list(range(1, 18, 3)), [15, 0], list(range(17, -1, -1))]),
+    # empty selections, empty blocks on both sides, a block with one valid key
+    "empty-and-single": ([128, 0, 40, 128, 64], [0, 1, 128, 0],
+                         [[0], [1, 2], [], [1], [0, 3]]),
+    # one query block that needs many stages
+    "long-walk": ([100, 30], [128] * 20 + [77] * 5, [list(range(25)), list(range(24, -1, -1))]),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE_CASES))
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_edge_cases(name, d):
+    cq, ck, rows = EDGE_CASES[name]
+    p = make_problem(cq, ck, rows, heads=3, head_dim=d, sort_rows=False)
+    t = random_tensors(p, seed=len(name) + d)
+    _say(f"[fwd] edge case {name} d={d}")
+    O, L = gpu_fwd(p, t["q"], t["k"], t["v"])
+    Oref, Lref = oracle_fwd(p, t["q"], t["k"], t["v"])
+    check(O, L, Oref, Lref, f"{name} d={d}")
+
+
+def test_fwd_independent_offsets_with_gaps():
+    """K/V blocks at shuffled Page16 offsets with unused pages between footprints."""
+    ck = [50, 128, 3, 97, 16, 0, 33]
+    off = [448, 0, 160, 192, 128, 0, 320]
+    rows = [[0, 1, 2], [3, 4, 6], [6, 0], [1, 3, 5], [2]]
+    p = make_problem([128, 64, 90, 20, 128], ck, rows, heads=2, head_dim=128, kv_offset=off, seq_kv=512,
+                     sort_rows=False)
+    t = random_tensors(p, seed=5)
+    _say("[fwd] shuffled offsets with gaps")
+    O, L = gpu_fwd(p, t["q"], t["k"], t["v"])
+    Oref, Lref = oracle_fwd(p, t["q"], t["k"], t["v"])
+    check(O, L, Oref, Lref, "offsets with gaps")
+
+
+def test_fwd_padding_contents_do_not_matter():
+    """Finite garbage in padded rows gives bit-identical outputs (masking is a select before the max)."""
+    w = make_workload(3, heads=[0])
+    _say("[fwd] padded-row garbage invariance")
+    O1, L1 = gpu_fwd(w, w.q, w.k, w.v)
+    g = torch.Generator().manual_seed(3)
+    q, k, v = w.q.clone(), w.k.clone(), w.v.clone()
+    for x, rows in ((q, padded_rows(w, "q")), (k, padded_rows(w, "kv")), (v, padded_rows(w, "kv"))):
+        garbage = (100 * torch.randn(x.shape, generator=g)).to(torch.bfloat16)
+        x[:, :, rows] = garbage[:, :, rows]
+    O2, L2 = gpu_fwd(w, q, k, v)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_fwd_selection_order_does_not_matter():
+    w = make_workload(3, heads=[0, 1])
+    _say("[fwd] K_q permutation")
+    O1, L1 = gpu_fwd(w, w.q, w.k, w.v)
+    rng = np.random.default_rng(1)
+    idx = w.q2k_idx.copy()
+    for q in range(w.n_q):
+        a, b = w.q2k_ptr[0, q], w.q2k_ptr[0, q + 1]
+        idx[a:b] = rng.permutation(idx[a:b])
+    w.q2k_idx = idx
+    O2, L2 = gpu_fwd(w, w.q, w.k, w.v)
+    assert np.abs(O1 - O2).max() <= O_ATOL
+    fin = np.isfinite(L1)
+    assert np.array_equal(fin, np.isfinite(L2))
+    assert (np.abs(L1[fin] - L2[fin]) / np.maximum(1, np.abs(L1[fin]))).max() <= LSE_RTOL
+
+
+def test_fwd_is_deterministic_and_plan_is_reusable():
+    w = make_workload(3, heads=[0, 1])
+    plan = K.kpage_plan(w)
+    _say("[fwd] determinism and plan reuse")
+    O1, L1 = gpu_fwd(w, w.q, w.k, w.v, plan=plan)
+    O2, L2 = gpu_fwd(w, w.q, w.k, w.v, plan=plan)
+    assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def test_fwd_rejects_bad_arguments_before_launch():
+    w = make_workload(1)
+    plan = K.kpage_plan(w)
+    dev = torch.device("cuda", 0)
+    q, k, v = w.q.to(dev), w.k.to(dev), w.v.to(dev)
+    with pytest.raises(K.KpageError):
+        K.attn_fwd(plan, q, k, v, -1.0)
+    with pytest.raises(K.KpageError):
+        K.attn_fwd(plan, q[:, :1].contiguous(), k, v, w.scale)
