@@ -1,0 +1,160 @@
+"""Benchmark: KPage block-sparse attention forward + backward on one MI355X.
+
+One step is the whole hot path on one batch: kpage_attn_fwd then kpage_attn_bwd on
+the 3D-padded video layout (21 x 30 x 52 tokens in 4 x 4 x 8 tiles -> 336 blocks of
+128 rows, 43008 physical rows, 40 heads, d = 128, bf16; window (1,2,2) plus 4 random
+blocks per query block).  Planning (page tables, routes, owners) is built once before
+the timed region and reused, as the method intends.
+
+Reported value: useful TFLOP/s of the step = 14 * d * (valid query-key pairs) / time
+(2 forward GEMMs + 5 backward GEMMs per valid pair); the forward alone is reported
+beside it with 4 * d * pairs.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0
+METRIC = "useful TFLOP/s (4·d·valid pairs) fwd & fwd+bwd; % bf16 MFMA peak"
+WORKLOAD = 3
+
+
+def _cpu_baseline(heads=(0, 1)):
+    """The fp64 CPU oracle on a bounded sample: forward + backward of a few heads."""
+    import numpy as np  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    from oracle import oracle_bwd
+    from workloads import make_workload
+
+    w = make_workload(WORKLOAD, heads=list(heads), with_do=True)
+    from oracle import oracle_plan  # noqa: F401  (pair count of the sample from the oracle planner)
+    pairs = oracle_plan(w).stats["useful"]
+    t0 = time.perf_counter()
+    oracle_bwd(w, w.q, w.k, w.v, w.do)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": round(14 * w.head_dim * pairs / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"oracle forward+backward (fp64 numpy) of {len(heads)} of 40 heads of the same workload, "
+                  f"{dt:.1f} s wall, scaled per valid pair",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by head with no exchange, and multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_11_amd as K
+    from workloads import make_workload
+
+    dev = torch.device("cuda", 0)
+    w = make_workload(WORKLOAD, with_do=True)
+    d = w.head_dim
+    t0 = time.perf_counter()
+    plan = K.kpage_plan(w)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(K.kpage_bwd_workspace_size(plan), dtype=torch.uint8, device=dev)
+    t0 = time.perf_counter()
+    K.kpage_plan_upload(plan)
+    K.kpage_attn_bwd(plan, q, k, v, o, lse, do, dq, dk, dv, ws, w.scale)  # builds the lazy backward plan
+    torch.cuda.synchronize()
+    bwd_plan_ms = (time.perf_counter() - t0) * 1e3
+    stats = K.kpage_plan_stats(plan)
+
+    def step():
+        K.kpage_attn_fwd(plan, q, k, v, o, lse, w.scale)
+        K.kpage_attn_bwd(plan, q, k, v, o, lse, do, dq, dk, dv, ws, w.scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K.kpage_timing_enable(plan, True)
+    for name in K.KERNELS:
+        K.kpage_timing_read(plan, name)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    kern = {name: K.kpage_timing_read(plan, name) for name in K.KERNELS}
+    K.kpage_timing_enable(plan, False)
+    ms_step = total_ms / args.steps
+    pairs = stats["useful"]
+    fwd_ms = sum(kern[n][0] for n in ("fwd_q128", "fwd_q64")) / args.steps
+    bwd_ms = sum(kern[n][0] for n in ("bwd_pre", "bwd_zero", "bwd_main", "bwd_post")) / args.steps
+    value = 14 * d * pairs / (ms_step * 1e-3) / 1e12
+    fwd_tflops = 4 * d * pairs / (fwd_ms * 1e-3) / 1e12
+
+    # dominant kernel: the K/V-owned backward, 10 * d flops per valid pair (5 GEMMs)
+    main_ms, main_n = kern["bwd_main"]
+    main_avg = main_ms / max(main_n, 1)
+    achieved = 10 * d * pairs / (main_avg * 1e-3) / 1e12
+    roofline = {"kernel": "kpage_bwd_main", "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "avg_ms": round(main_avg, 4), "launches": main_n,
+                "algorithmic": "10*d*useful_pairs per launch"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "3d-padded 21x30x52 (4x4x8 tiles, 336 blocks, 43008 rows), 40 heads, d=128, "
+                               "window (1,2,2) + 4 random blocks, fwd+bwd",
+                   "batch": 1, "heads": w.heads, "head_dim": d, "tokens": 21 * 30 * 52, "seq_physical": w.seq_q},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd": {"ms": round(fwd_ms, 4), "useful_tflops": round(fwd_tflops, 2),
+                "pct_bf16_peak": round(100 * fwd_tflops / PEAK_BF16_TFLOPS, 2)},
+        "bwd_ms": round(bwd_ms, 4),
+        "kernel_ms_per_step": {n: round(kern[n][0] / args.steps, 4) for n in K.KERNELS},
+        "pairs": {kk: stats[kk] for kk in ("useful", "whole_block", "paged_m128", "nominal", "scheduled",
+                                             "bwd_physical")},
+        "plan_ms": {"forward": round(plan_ms, 2), "backward_lazy_incl_first_call": round(bwd_plan_ms, 2)},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

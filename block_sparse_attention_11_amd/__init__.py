@@ -33,8 +33,11 @@ TABLES = {
 
 EXPORTED_SYMBOLS = (
     "kpage_plan", "kpage_plan_upload", "kpage_attn_fwd", "kpage_bwd_workspace_size", "kpage_attn_bwd",
-    "kpage_plan_stats", "kpage_plan_export", "kpage_plan_destroy", "kpage_last_error",
+    "kpage_plan_stats", "kpage_plan_export", "kpage_plan_destroy", "kpage_timing_enable", "kpage_timing_read",
+    "kpage_last_error",
 )
+
+KERNELS = {"fwd_q128": 0, "fwd_q64": 1, "bwd_pre": 2, "bwd_zero": 3, "bwd_main": 4, "bwd_post": 5}
 
 
 class KpageError(RuntimeError):
@@ -80,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.kpage_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, f32, vp]
         L.kpage_plan_stats.argtypes = [vp, ctypes.POINTER(KpagePairStats)]
         L.kpage_plan_export.argtypes = [vp, i32, vp, ctypes.POINTER(sz)]
+        L.kpage_timing_enable.argtypes = [vp, i32]
+        L.kpage_timing_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.kpage_plan_destroy.argtypes = [vp]
         L.kpage_plan_destroy.restype = None
         L.kpage_last_error.restype = ctypes.c_char_p
@@ -158,6 +163,17 @@ def kpage_plan_export(plan: Plan, table: str) -> np.ndarray:
     if n.value:
         _check(lib().kpage_plan_export(plan.handle, tid, out.ctypes.data, ctypes.byref(n)))
     return out
+
+
+def kpage_timing_enable(plan: Plan, enable: bool = True):
+    _check(lib().kpage_timing_enable(plan.handle, 1 if enable else 0))
+
+
+def kpage_timing_read(plan: Plan, kernel: str):
+    """(total milliseconds, launches) of one kernel since the last read (waits for its events)."""
+    ms, n = ctypes.c_double(0), ctypes.c_int64(0)
+    _check(lib().kpage_timing_read(plan.handle, KERNELS[kernel], ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)
 
 
 def kpage_bwd_workspace_size(plan: Plan) -> int:

@@ -14,6 +14,64 @@
 
 using namespace kpage;
 
+namespace {
+
+// HIP event pairs around every launch, pooled and kept per kernel id until read.
+class EventTimer final : public LaunchTimer {
+ public:
+  ~EventTimer() override {
+    for (auto &k : pending_)
+      for (auto &p : k) {
+        (void)hipEventDestroy(p.first);
+        (void)hipEventDestroy(p.second);
+      }
+    for (hipEvent_t e : pool_) (void)hipEventDestroy(e);
+  }
+  void before(int kid, hipStream_t s) override {
+    hipEvent_t e = take();
+    (void)hipEventRecord(e, s);
+    open_[kid] = e;
+  }
+  void after(int kid, hipStream_t s) override {
+    hipEvent_t e = take();
+    (void)hipEventRecord(e, s);
+    pending_[kid].emplace_back(open_[kid], e);
+  }
+  // sum of elapsed milliseconds and launch count of one kernel; returns false on a HIP error
+  bool read(int kid, double *ms, int64_t *n) {
+    double total = 0;
+    for (auto &p : pending_[kid]) {
+      float t = 0;
+      if (hipEventSynchronize(p.second) != hipSuccess || hipEventElapsedTime(&t, p.first, p.second) != hipSuccess)
+        return false;
+      total += t;
+      pool_.push_back(p.first);
+      pool_.push_back(p.second);
+    }
+    *ms = total;
+    *n = int64_t(pending_[kid].size());
+    pending_[kid].clear();
+    return true;
+  }
+
+ private:
+  hipEvent_t take() {
+    if (pool_.empty()) {
+      hipEvent_t e = nullptr;
+      (void)hipEventCreate(&e);
+      return e;
+    }
+    hipEvent_t e = pool_.back();
+    pool_.pop_back();
+    return e;
+  }
+  std::vector<hipEvent_t> pool_;
+  hipEvent_t open_[KPAGE_K_COUNT] = {};
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending_[KPAGE_K_COUNT];
+};
+
+}  // namespace
+
 struct kpage_plan {
   Problem P;
   FwdTables F;
@@ -33,7 +91,9 @@ struct kpage_plan {
   uint32_t *d_kmask = nullptr, *d_qmask = nullptr;
   uint64_t *d_adj = nullptr;
   int64_t *d_uncovered_ptr = nullptr;
+  int max_uncovered = 0;
   std::vector<void *> allocations;
+  EventTimer *timer = nullptr;
 };
 typedef struct kpage_plan PlanT;
 
@@ -185,6 +245,8 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   pl->n_bitems = int(items.size());
+  for (int g = 0; g < P.slots; ++g)
+    pl->max_uncovered = std::max(pl->max_uncovered, int(B.uncovered_ptr[g + 1] - B.uncovered_ptr[g]));
   pl->bwd_on_device = true;
   return KPAGE_OK;
 }
@@ -245,11 +307,11 @@ kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, co
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.items = plan->d_items128;
   a.n_items = plan->n_items128;
-  hipError_t e = launch_fwd(a, plan->P.head_dim, 128, st);
+  hipError_t e = launch_fwd(a, plan->P.head_dim, 128, st, plan->timer);
   if (e != hipSuccess) return hip_fail(e, "forward launch (M128 route)");
   a.items = plan->d_items64;
   a.n_items = plan->n_items64;
-  e = launch_fwd(a, plan->P.head_dim, 64, st);
+  e = launch_fwd(a, plan->P.head_dim, 64, st, plan->timer);
   if (e != hipSuccess) return hip_fail(e, "forward launch (M64 route)");
   return KPAGE_OK;
 }
@@ -257,8 +319,8 @@ kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, co
 kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes) {
   if (!plan || !bytes) return fail(KPAGE_ERR_INVALID, "plan or bytes is NULL");
   const size_t rows = size_t(plan->P.batch) * plan->P.heads * size_t(plan->P.seq_q);
-  // fp32 dQ accumulator [BH, seq_q, d] followed by fp32 row sums D [BH, seq_q]
-  *bytes = rows * size_t(plan->P.head_dim) * 4 + rows * 4;
+  // fp32 dQ accumulator [BH, seq_q, d], then fp32 D = rowsum(dO * O) and LSE * log2(e), each [BH, seq_q]
+  *bytes = rows * size_t(plan->P.head_dim) * 4 + 2 * rows * 4;
   return KPAGE_OK;
 }
 
@@ -298,9 +360,10 @@ kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, co
   a.n_q = P.n_q;
   a.per_head = P.per_head ? 1 : 0;
   a.bh_count = P.batch * P.heads;
+  a.max_uncovered = plan->max_uncovered;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipError_t e = launch_bwd(a, P.head_dim, st);
+  hipError_t e = launch_bwd(a, P.head_dim, st, plan->timer);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return KPAGE_OK;
 }
@@ -357,8 +420,30 @@ kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf,
   return KPAGE_OK;
 }
 
+kpage_status kpage_timing_enable(kpage_plan_t *plan, int enable) {
+  if (!plan) return fail(KPAGE_ERR_INVALID, "plan is NULL");
+  if (enable && !plan->timer) plan->timer = new (std::nothrow) EventTimer();
+  if (enable && !plan->timer) return fail(KPAGE_ERR_OOM, "host allocation failed");
+  if (!enable && plan->timer) {
+    delete plan->timer;
+    plan->timer = nullptr;
+  }
+  return KPAGE_OK;
+}
+
+kpage_status kpage_timing_read(kpage_plan_t *plan, int kernel_id, double *total_ms, int64_t *launches) {
+  if (!plan || !total_ms || !launches) return fail(KPAGE_ERR_INVALID, "plan, total_ms or launches is NULL");
+  if (kernel_id < 0 || kernel_id >= KPAGE_K_COUNT) return fail(KPAGE_ERR_INVALID, "unknown kernel id");
+  *total_ms = 0;
+  *launches = 0;
+  if (!plan->timer) return KPAGE_OK;
+  if (!plan->timer->read(kernel_id, total_ms, launches)) return fail(KPAGE_ERR_HIP, "reading HIP events failed");
+  return KPAGE_OK;
+}
+
 void kpage_plan_destroy(kpage_plan_t *plan) {
   if (!plan) return;
+  delete plan->timer;
   if (!plan->allocations.empty()) {
     (void)hipDeviceSynchronize();
     for (void *p : plan->allocations) (void)hipFree(p);

@@ -56,10 +56,18 @@ struct BwdArgs {
   const int32_t *q_valid;     // [slots][n_q]
   int64_t seq_q, seq_kv;
   int32_t n_items, heads, n_q, per_head, bh_count;
+  int32_t max_uncovered;      // largest count of uncovered K/V pages over the graph slots
   float scale, scale_log2;
 };
 
-hipError_t launch_fwd(const FwdArgs &a, int head_dim, int route, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs &a, int head_dim, hipStream_t stream);
+// Optional per-launch timing: called right before and right after each kernel launch.
+struct LaunchTimer {
+  virtual void before(int kernel_id, hipStream_t stream) = 0;
+  virtual void after(int kernel_id, hipStream_t stream) = 0;
+  virtual ~LaunchTimer() = default;
+};
+
+hipError_t launch_fwd(const FwdArgs &a, int head_dim, int route, hipStream_t stream, LaunchTimer *timer);
+hipError_t launch_bwd(const BwdArgs &a, int head_dim, hipStream_t stream, LaunchTimer *timer);
 
 }  // namespace kpage

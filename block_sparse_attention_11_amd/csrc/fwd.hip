@@ -388,14 +388,17 @@ __global__ __launch_bounds__(256, 1) void kpage_fwd_kernel(FwdArgs args) {
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs &a, int head_dim, int route, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs &a, int head_dim, int route, hipStream_t stream, LaunchTimer *timer) {
   if (a.n_items <= 0) return hipSuccess;
+  const int kid = route == 128 ? 0 : 1;
   dim3 grid(a.n_items), block(256);
+  if (timer) timer->before(kid, stream);
   if (head_dim == 128 && route == 128) hipLaunchKernelGGL((kpage_fwd_kernel<128, 8>), grid, block, 0, stream, a);
   else if (head_dim == 128 && route == 64) hipLaunchKernelGGL((kpage_fwd_kernel<128, 16>), grid, block, 0, stream, a);
   else if (head_dim == 64 && route == 128) hipLaunchKernelGGL((kpage_fwd_kernel<64, 8>), grid, block, 0, stream, a);
   else if (head_dim == 64 && route == 64) hipLaunchKernelGGL((kpage_fwd_kernel<64, 16>), grid, block, 0, stream, a);
   else return hipErrorInvalidValue;
+  if (timer) timer->after(kid, stream);
   return hipGetLastError();
 }
 

@@ -178,6 +178,26 @@ kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf,
  * device before freeing device memory that kernels may still read. */
 void kpage_plan_destroy(kpage_plan_t *plan);
 
+/*
+ * Kernel timing.  With timing enabled on a plan, every kernel launch the plan
+ * makes is bracketed by a pair of HIP events recorded on the launch stream.
+ * kpage_timing_read() waits for those events, returns the summed milliseconds
+ * and the number of launches of one kernel since the last read, and resets that
+ * kernel's record.  Kernel ids below.  Disabled by default; enabling it adds two
+ * event records per launch and nothing else.
+ */
+enum {
+  KPAGE_K_FWD_Q128 = 0,  /* forward, M128 x N128 route                            */
+  KPAGE_K_FWD_Q64 = 1,   /* forward, M64 x N256 route and empty-block cleanup      */
+  KPAGE_K_BWD_PRE = 2,   /* rowsum(dO * O), scaled LSE, dQ accumulator clear       */
+  KPAGE_K_BWD_ZERO = 3,  /* dK/dV pages outside every block footprint              */
+  KPAGE_K_BWD_MAIN = 4,  /* K/V-owned backward                                      */
+  KPAGE_K_BWD_POST = 5,  /* dQ accumulator to bf16                                  */
+  KPAGE_K_COUNT = 6
+};
+kpage_status kpage_timing_enable(kpage_plan_t *plan, int enable);
+kpage_status kpage_timing_read(kpage_plan_t *plan, int kernel_id, double *total_ms, int64_t *launches);
+
 /* Message of the last non-OK status on this thread ("" if none). */
 const char *kpage_last_error(void);
 
