@@ -28,7 +28,7 @@ METRIC = "useful TFLOP/s (4·d·valid pairs) fwd & fwd+bwd; % bf16 MFMA peak"
 WORKLOAD = 3
 
 
-def _cpu_baseline(heads=(0, 1)):
+def _cpu_baseline(heads=(0, 1, 2, 3)):
     """The fp64 CPU oracle on a bounded sample: forward + backward of a few heads."""
     import numpy as np  # noqa: F401
     from threadpoolctl import threadpool_info
