@@ -140,6 +140,30 @@ std::vector<int32_t> redirect_dummies(const std::vector<int32_t> &walk, const st
   return out;
 }
 
+// Launch order for MI355X's 8 XCDs.  The dispatcher hands workgroup i to XCD i % 8
+// and each XCD has its own 4 MB L2, so position 8 j + x holds the j-th item of XCD
+// x's share, and the share of XCD x is the x-th contiguous eighth of `seq`.  With
+// `seq` in head-major, spatially ordered form, the workgroups resident on one XCD
+// work on one head and on neighbouring blocks at a time: their page gathers reuse
+// that XCD's L2, and the chip as a whole keeps about 8 heads' K/V live in the
+// memory-side cache instead of all of them.  The plan's queues (longest walk
+// first) keep their order for export; this permutation only decides which
+// workgroup runs which item.
+constexpr int kXcds = 8;
+
+template <class T>
+std::vector<T> xcd_interleave(const std::vector<T> &seq) {
+  const size_t n = seq.size(), m = n / kXcds, r = n % kXcds;
+  std::vector<T> out(n);
+  size_t start = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    const size_t cnt = m + (size_t(x) < r ? 1 : 0);
+    for (size_t j = 0; j < cnt; ++j) out[j * kXcds + x] = seq[start + j];
+    start += cnt;
+  }
+  return out;
+}
+
 kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   if (pl->fwd_on_device) return KPAGE_OK;
   const Problem &P = pl->P;
@@ -160,10 +184,15 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   };
   for (size_t i = 0; i < F.q128_queue.size(); i += 2) it128.push_back(make(F.q128_queue[i], F.q128_queue[i + 1]));
   for (size_t i = 0; i < F.q64_queue.size(); i += 2) it64.push_back(make(F.q64_queue[i], F.q64_queue[i + 1]));
+  auto head_major = [](const FwdItem &a, const FwdItem &b) { return a.bh != b.bh ? a.bh < b.bh : a.q < b.q; };
+  std::stable_sort(it128.begin(), it128.end(), head_major);
+  std::stable_sort(it64.begin(), it64.end(), head_major);
   // blocks without valid rows still own their output rows: append cleanup items (empty walk)
   for (int bh = 0; bh < P.batch * P.heads; ++bh)
     for (int q = 0; q < nq; ++q)
       if (P.q_valid[size_t(P.slot_of(bh)) * nq + q] == 0) it64.push_back(make(bh, q));
+  it128 = xcd_interleave(it128);
+  it64 = xcd_interleave(it64);
   kpage_status s;
   if ((s = upload(pl, pages, &pl->d_pages, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, F.valid, &pl->d_valid, stream)) != KPAGE_OK) return s;
@@ -232,6 +261,10 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
     x.aligned = B.aligned[t];
     items.push_back(x);
   }
+  std::stable_sort(items.begin(), items.end(), [](const BwdItem &a, const BwdItem &b) {
+    return a.bh != b.bh ? a.bh < b.bh : a.owner < b.owner;
+  });
+  items = xcd_interleave(items);
   kpage_status s;
   if ((s = upload(pl, items, &pl->d_bitems, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, owners, &pl->d_owners, stream)) != KPAGE_OK) return s;
