@@ -84,6 +84,7 @@ struct kpage_plan {
   int n_items128 = 0, n_items64 = 0;
   int32_t *d_pages = nullptr;
   uint32_t *d_valid = nullptr;
+  int32_t *d_redo = nullptr;  // per launch position of either route: item needs the exact pass
   // backward device tables
   BwdItem *d_bitems = nullptr;
   int n_bitems = 0;
@@ -198,6 +199,9 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   if ((s = upload(pl, F.valid, &pl->d_valid, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, it128, &pl->d_items128, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, it64, &pl->d_items64, stream)) != KPAGE_OK) return s;
+  // the routes run one after the other on the stream, so they share one flag array
+  if ((s = upload(pl, std::vector<int32_t>(std::max(it128.size(), it64.size()), 0), &pl->d_redo, stream)) != KPAGE_OK)
+    return s;
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   pl->n_items128 = int(it128.size());
@@ -334,6 +338,7 @@ kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, co
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.pages = plan->d_pages;
   a.valid = plan->d_valid;
+  a.redo = plan->d_redo;
   a.seq_q = plan->P.seq_q;
   a.seq_kv = plan->P.seq_kv;
   a.scale = softmax_scale;

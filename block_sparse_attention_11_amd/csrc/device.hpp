@@ -25,6 +25,7 @@ struct FwdArgs {
   const int32_t *pages;     // walk entries; dummy slots point at a real page of the same walk
   const uint32_t *valid;    // two 16-bit row masks per word, indexed by walk position / 2
   int64_t seq_q, seq_kv;
+  int32_t *redo;            // per launch position: 1 when the item needs the exact rescaling pass
   int32_t n_items;
   float scale;              // softmax scale
   float scale_log2;         // softmax scale * log2(e)

@@ -1,23 +1,25 @@
 // Forward KPage attention for gfx950 (MI355X, CDNA4).
 //
 // KPage paper, section 3.2: every work item is one query block of one
-// (batch, head).  Its K/V page walk is consumed one stage at a time: 8 Page16
-// regions (128 key rows) for the M128 x N128 route, 16 (256 key rows) for the
-// M64 x N256 route.  Each page is a contiguous 16-row run of the original K/V
+// (batch, head).  Its K/V page walk is consumed in tiles of 8 Page16 regions
+// (128 key rows).  Each page is a contiguous 16-row run of the original K/V
 // tensors and is copied straight from global memory into LDS with 16-byte
 // direct-to-LDS loads (section 3.2.3); no compacted copy exists in HBM.  The
-// consumer is an ordinary flash-attention step on the assembled tile: bf16
-// MFMA for Q K^T and P V with fp32 accumulation, and an online softmax
-// (section 3.2.4: invalid rows are set to -inf before the row maximum, and only
-// on stages at or past the end of the fully valid prefix).
+// consumer is a flash-attention step on the assembled tile: bf16 MFMA for
+// Q K^T and P V with fp32 accumulation, and an online softmax (section 3.2.4:
+// invalid rows are set to -inf before the row maximum, and only on tiles at or
+// past the end of the fully valid prefix).
 //
-// Work split inside a 256-thread workgroup (4 waves of 64 lanes): each wave
-// owns a 64-query x 64-key sub-tile of every stage.  M128: waves (w & 1) pick
-// the query half and (w >> 1) the key half.  M64: all four waves share the 64
-// query rows and take one key quarter each.  Every wave keeps its own running
-// maximum, sum and output, and the waves are merged once at the end.
+// Work split.  A workgroup has 8 waves, two per SIMD, so that one wave's
+// vector work can issue while the other's matrix work runs.  Every wave owns 32
+// query rows of the item and a fixed key range of every tile, walked as
+// sub-tiles of 32 keys.  Route M128 x N128 (section 3.2.2): 4 query groups x 2
+// key halves, 2 sub-tiles per wave per tile.  Route M64 x N256: 2 query groups
+// x 4 key quarters, 1 sub-tile per wave per tile, so the route's 16-page
+// iteration is two tiles.  Each wave keeps its own running maximum, sum and
+// output; the waves that share query rows are merged once at the end.
 //
-// Matrix layout per wave (v_mfma_f32_32x32x16_bf16):
+// Matrix layout per wave (v_mfma_f32_32x32x16_bf16, 32 cycles each):
 //   S^T (key x query) = K . Q^T : A = K rows from LDS, B = Q rows kept in VGPRs.
 //     A lane then holds 16 keys of one query column, so the row maximum is a
 //     lane-local reduction plus one exchange with lane ^ 32.
@@ -25,7 +27,23 @@
 //     accumulators (same lane layout), A = V read transposed from LDS with
 //     ds_read_b64_tr_b16.  The output column of a lane is again its own query,
 //     so the per-query rescaling needs no cross-lane traffic.
+//
+// Software pipeline.  Sub-tile i is processed in three parts that run in
+// different sub-iterations: its scores S_i = K_i Q^T (MFMA), its softmax (VALU)
+// and its product P_i V_i (MFMA).  Sub-iteration i issues the MFMAs of S_{i+1}
+// and of P_{i-1} V_{i-1} and, between them, the softmax of S_i.
+//
+// Running maximum.  In the fast kernel a query's maximum is fixed by the first
+// sub-tile that has a valid key for it and never moves again: probabilities are
+// exp2(s - m) with a stale m, so the output accumulators are never rescaled
+// inside the loop (which keeps them in the matrix-core registers).  This is
+// exact as long as later scores exceed m by less than 2^64 (no overflow of P,
+// O or l in fp32); an item where some score rises further sets a flag and is
+// recomputed by the second kernel, which raises the maximum whenever a
+// sub-tile exceeds it by more than 2^8 and rescales O and l then.
 #include <hip/hip_runtime.h>
+
+#include <utility>
 
 #include "device.hpp"
 
@@ -43,7 +61,11 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef const __attribute__((address_space(4))) int32_t c_i32;
 typedef const __attribute__((address_space(4))) uint32_t c_u32;
 
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLimit = 64.0f;  // fast kernel: largest rise of a score over the fixed maximum (base 2)
+constexpr float kRaise = 8.0f;   // exact kernel: raise the maximum only past this margin (base 2)
 
 // s_waitcnt immediates for gfx9: vmcnt[3:0] + vmcnt_hi[15:14], expcnt[6:4], lgkmcnt[11:8].
 template <int N>
@@ -58,24 +80,20 @@ __device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
 // chunk slots, conflict-free for both 32- and 64-bank LDS.
 __device__ __forceinline__ int vswz(int row) { return (0xAC60 >> (4 * (row & 3))) & 0xF; }
 
-template <int D, int G>
-__device__ __forceinline__ void load_stage(const char *kh, const char *vh, c_i32 *walk, lds_char *kb,
-                                           lds_char *vb, int wave, int lane) {
-  constexpr int CH = D / 8;                    // 16-byte chunks per row
-  constexpr int PER_WAVE = G * 16 * CH / 256;  // direct loads per wave per tensor
-  constexpr int ROWS_PER_INST = 64 / CH;
-#pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int inst = wave * PER_WAVE + i;      // wave-uniform
-    const int64_t page = walk[(inst * ROWS_PER_INST) >> 4];
-    const int row = inst * ROWS_PER_INST + lane / CH;
-    const int pos = lane % CH;
-    const int64_t rbase = (page * 16 + (row & 15)) * (D * 2);
-    const int ck = pos ^ (row & (CH - 1));
-    const int cv = pos ^ (vswz(row) & (CH - 1));
-    __builtin_amdgcn_global_load_lds((const void *)(kh + rbase + ck * 16), (lds_char *)(kb + inst * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void *)(vh + rbase + cv * 16), (lds_char *)(vb + inst * 1024), 16, 0, 0);
-  }
+// max(a, b, c) as one v_max3_f32.  Written out because the compiler otherwise
+// canonicalises MFMA results (v_max x, x, x) before every fmaxf; the inputs here are
+// scores and -inf, never signalling NaNs.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Maximum of x over this lane and lane ^ 32 (v_permlane32_swap: a VALU op, no LDS).
+__device__ __forceinline__ float half_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
 template <int V>
@@ -83,22 +101,80 @@ struct ic {
   static constexpr int value = V;
 };
 
-template <int D, int G>
-__global__ __launch_bounds__(256, 1) void kpage_fwd_kernel(FwdArgs args) {
+// Page `wave` of tile `tile`: the page this wave copies (one scalar load).
+__device__ __forceinline__ int32_t tile_page(c_i32 *walk, int tile, int wave) { return walk[8 * tile + wave]; }
+
+// This wave's page (rows 16 wave .. 16 wave + 15) of one tile of K or V, global ->
+// LDS, 16 bytes per lane.  K chunks are swizzled by row & (CH - 1), V chunks by
+// vswz(row).
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_page(const char *src, int32_t page, lds_char *dst, int wave, int lane) {
+  constexpr int CH = D / 8;                    // 16-byte chunks per row
+  constexpr int PER_WAVE = 16 * CH / 64;       // direct loads per wave
+  constexpr int ROWS_PER_INST = 64 / CH;
+  const char *pbase = src + (int64_t)page * (16 * D * 2);  // wave-uniform: scalar base address
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int inst = wave * PER_WAVE + i;      // wave-uniform
+    const int row = inst * ROWS_PER_INST + lane / CH;
+    const int pos = lane % CH;
+    const int c = IS_V ? pos ^ (vswz(row) & (CH - 1)) : pos ^ (row & (CH - 1));
+    const uint32_t off = (uint32_t)((row & 15) * (D * 2) + c * 16);
+    __builtin_amdgcn_global_load_lds((const void *)(pbase + off), (lds_char *)(dst + inst * 1024), 16, 0, 0);
+  }
+}
+
+// Runs body(parity, flag, x) for x in [a, b), with parity = x & 1 as a compile-time
+// value, so that LDS double buffers are addressed with constants.
+template <class Flag, class Body>
+__device__ __forceinline__ void for_range(Flag flag, int a, int b, Body &&body) {
+  int x = a;
+  if ((x & 1) && x < b) {
+    body(ic<1>{}, flag, x);
+    ++x;
+  }
+  for (; x + 1 < b; x += 2) {
+    body(ic<0>{}, flag, x);
+    body(ic<1>{}, flag, x + 1);
+  }
+  if (x < b) body(ic<0>{}, flag, x);
+}
+
+template <int... I, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F &&f) {
+  (f(ic<I>{}), ...);
+}
+// f(ic<0>{}), ..., f(ic<N-1>{}): every index is a compile-time constant.
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+// MASK values of a sub-iteration: no masking, a runtime check, or masking always.
+constexpr int kMaskNone = 0, kMaskCheck = 1, kMaskAlways = 2;
+
+template <int D, int ROUTE, bool EXACT>
+__global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int DS = D / 16;         // MFMA k-steps over the head dimension
   constexpr int ND = D / 32;         // 32-wide output blocks over the head dimension
-  constexpr int M = G == 8 ? 128 : 64;
-  constexpr int NBUF = G == 8 ? 2 : 1;
-  constexpr int STAGE_BYTES = G * 16 * D * 2;
+  constexpr int M = ROUTE;           // query rows of the work item
+  constexpr int NQG = M / 32;        // query groups of 32 rows
+  constexpr int NKG = kWaves / NQG;  // key groups per tile
+  constexpr int KW = 128 / NKG;      // keys of a tile per wave
+  constexpr int NH = KW / 32;        // 32-key sub-tiles per wave per tile
+  constexpr int TILE_BYTES = 128 * D * 2;
+  constexpr int LOADS = 16 * CH / 64;  // direct loads per wave per tile and tensor
 
-  __shared__ __attribute__((aligned(1024))) char kbuf0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kbuf1[NBUF == 2 ? STAGE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[NBUF == 2 ? STAGE_BYTES : 16];
-  __shared__ float stat_m[4][64];
-  __shared__ float stat_l[4][64];
+  // K tiles 0/1, then V tiles 0/1; at the end the per-wave partial outputs
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
+  __shared__ float stat_m[kWaves][32];
+  __shared__ float stat_l[kWaves][32];
+  __shared__ int redo_any;
 
+  if (EXACT && args.redo[blockIdx.x] == 0) return;
+
+  char *kbuf0 = smem, *kbuf1 = smem + TILE_BYTES, *vbuf0 = smem + 2 * TILE_BYTES, *vbuf1 = smem + 3 * TILE_BYTES;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -108,226 +184,375 @@ __global__ __launch_bounds__(256, 1) void kpage_fwd_kernel(FwdArgs args) {
   const FwdItem it = args.items[blockIdx.x];
   const int bh = it.bh;
   const int cq = it.c_q;
-  const int n_stages = it.walk_len / G;
-  const int full_stages = it.n_full / G;
-  const int qhalf = G == 8 ? (wave & 1) : 0;
-  const int kvq = G == 8 ? (wave >> 1) : wave;
-  const int kvbase = 64 * kvq;       // first key row of this wave inside a stage
+  const int n_tiles = it.walk_len / 8;
+  const int n_sub = n_tiles * NH;
+  const int full_tiles = it.n_full / 8;  // tiles inside the fully valid prefix
+  const int qg = wave % NQG;
+  const int keyoff = (wave / NQG) * KW;  // first key of this wave in a tile
 
   const char *kh = (const char *)args.k + (int64_t)bh * args.seq_kv * D * 2;
   const char *vh = (const char *)args.v + (int64_t)bh * args.seq_kv * D * 2;
   c_i32 *walk = (c_i32 *)(args.pages + it.walk_off);
   c_u32 *vwords = (c_u32 *)(args.valid + (it.walk_off >> 1));
 
-  // per-wave fp32 partial output for the final merge, placed over the free stage buffers
-  auto part_of = [&](int w) -> lds_char * {
-    if (NBUF == 2)
-      return w == 0 ? (lds_char *)kbuf0 : w == 1 ? (lds_char *)kbuf1 : w == 2 ? (lds_char *)vbuf0 : (lds_char *)vbuf1;
-    return (w < 2 ? (lds_char *)kbuf0 : (lds_char *)vbuf0) + (w & 1) * (64 * D * 4);
-  };
-
-  if (n_stages > 0) load_stage<D, G>(kh, vh, walk, (lds_char *)kbuf0, (lds_char *)vbuf0, wave, lane);
-
-  // Q rows of this wave as MFMA B operands: qreg[b][s] = Q[q0 + 32b + l32][16s + 8g .. +8]
-  bf16x8 qreg[2][DS];
+  // Q rows of this wave as MFMA B operands: qreg[s] = Q[q0 + l32][16s + 8g .. +8]
+  bf16x8 qreg[DS];
   {
-    const int q0 = 128 * it.q + 64 * qhalf;
+    const int q0 = 128 * it.q + 32 * qg;
     const bf16x8 *qh = (const bf16x8 *)((const char *)args.q + ((int64_t)bh * args.seq_q + q0) * D * 2);
+    const bool ok = 32 * qg + l32 < cq;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const bool ok = 64 * qhalf + 32 * b + l32 < cq;
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        bf16x8 x = qh[(32 * b + l32) * (D / 8) + 2 * s + g];
-        if (!ok) x = bf16x8{};
-        qreg[b][s] = x;
-      }
+    for (int s = 0; s < DS; ++s) {
+      bf16x8 x = qh[l32 * (D / 8) + 2 * s + g];
+      if (!ok) x = bf16x8{};
+      qreg[s] = x;
     }
   }
+  if (n_tiles > 0) load_page<D, false>(kh, tile_page(walk, 0, wave), (lds_char *)kbuf0, wave, lane);
+  if (n_tiles > 1) load_page<D, false>(kh, tile_page(walk, 1, wave), (lds_char *)kbuf1, wave, lane);
+  if (ROUTE == 128 && n_tiles > 0) load_page<D, true>(vh, tile_page(walk, 0, wave), (lds_char *)vbuf0, wave, lane);
 
-  f32x16 oacc[ND][2];
+  f32x16 oacc[ND];
 #pragma unroll
-  for (int n = 0; n < ND; ++n)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) oacc[n][b] = f32x16{};
-  float m_run[2] = {kNegInf, kNegInf};
-  float l_run[2] = {0.f, 0.f};
+  for (int n = 0; n < ND; ++n) oacc[n] = f32x16{};
+  float m2 = kNegInf;    // running maximum of the scaled scores (base-2 units)
+  float l_run = 0.f;     // this lane's part of the running sum
+  bool over = false;     // fast kernel: a score rose past the fixed maximum + kLimit
   const float c2 = args.scale_log2;
 
   // lane-constant parts of the LDS addresses
-  const int k_row_off = l32 * D * 2;
-  const int k_swz = lane & (CH - 1) & 31;
+  const int k_row_off = (keyoff + l32) * D * 2;
+  const int k_swz = lane & (CH - 1);
   const int sl = lane & 15;
   const int mgrp = lane >> 4;
-  const int v_row_off = (4 * g + (sl >> 2)) * D * 2;
+  const int v_row_off = (keyoff + 4 * g + (sl >> 2)) * D * 2;
   const int v_chunk_lane = 2 * (mgrp & 1) + ((sl & 3) >> 1);
   const int v_swz = vswz(sl >> 2) & (CH - 1);
   const int v_byte = (sl & 1) * 8;
 
-  // One stage of the walk, reading LDS buffer BUF (a compile-time choice, so the
-  // compiler can tell the prefetch into the other buffer apart from these reads).
-  auto stage = [&](auto bufc, int st) {
-    constexpr int BUF = decltype(bufc)::value;
-    lds_char *kcur = BUF ? (lds_char *)kbuf1 : (lds_char *)kbuf0;
-    lds_char *vcur = BUF ? (lds_char *)vbuf1 : (lds_char *)vbuf0;
-    lds_char *knext = BUF ? (lds_char *)kbuf0 : (lds_char *)kbuf1;
-    lds_char *vnext = BUF ? (lds_char *)vbuf0 : (lds_char *)vbuf1;
-    if (NBUF == 1 && st > 0) load_stage<D, G>(kh, vh, walk + st * G, kcur, vcur, wave, lane);
-    // validity words of this wave's two 32-key blocks (only read past the full prefix)
-    uint32_t words[2] = {0xFFFFFFFFu, 0xFFFFFFFFu};
-    const bool masked = st >= full_stages;
-    if (masked) {
-      words[0] = vwords[st * (G / 2) + 2 * kvq];
-      words[1] = vwords[st * (G / 2) + 2 * kvq + 1];
-    }
-    wait_vmcnt<0>();
-    wait_lgkm0();
-    barrier();
-    if (NBUF == 2 && st + 1 < n_stages) load_stage<D, G>(kh, vh, walk + (st + 1) * G, knext, vnext, wave, lane);
-    const lds_char *kt = kcur + kvbase * D * 2;
-    const lds_char *vt = vcur + kvbase * D * 2;
+  // Scores and probabilities ping-pong between two register sets selected by the
+  // parity of the sub-tile index (a compile-time value at every call site).
+  f32x16 sacc[2];       // [parity]: scores of the sub-tile in softmax / of the next one
+  bf16x8 pacc[2][2];    // [parity][hh]: probabilities of a sub-tile
 
-    // S^T = K Q^T for the wave's 64 keys x 64 queries
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+  auto read_v_op = [&](const lds_char *vrow) __attribute__((always_inline)) -> bf16x8 {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)vrow);
+    const s16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(vrow + 8 * D * 2));
+    const bf16x4 lo_b = __builtin_bit_cast(bf16x4, lo), hi_b = __builtin_bit_cast(bf16x4, hi);
+    return bf16x8{lo_b[0], lo_b[1], lo_b[2], lo_b[3], hi_b[0], hi_b[1], hi_b[2], hi_b[3]};
+  };
+  // S^T of one sub-tile (32 keys x 32 queries) from the K tile in `kt`
+  auto qk = [&](const lds_char *kt, int half, f32x16 &acc) __attribute__((always_inline)) {
+    acc = f32x16{};
+    const lds_char *base = kt + k_row_off + half * 32 * D * 2;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
+      const bf16x8 kop = *(const __attribute__((address_space(3))) bf16x8 *)(base + (((2 * s + g) ^ k_swz) * 16));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[s], acc, 0, 0, 0);
+    }
+  };
+  // O^T += V^T P^T for one sub-tile from the V tile in `vt`
+  auto pv = [&](const lds_char *vt, int half, const bf16x8 *p) __attribute__((always_inline)) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const lds_char *src = kt + a * 32 * D * 2 + k_row_off + (((2 * s + g) ^ k_swz) * 16);
-        const bf16x8 kop = *(const __attribute__((address_space(3))) bf16x8 *)src;
+    for (int hh = 0; hh < 2; ++hh) {
+      const lds_char *vrow = vt + v_row_off + (32 * half + 16 * hh) * D * 2;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[b][s], acc[a][b], 0, 0, 0);
+      for (int n = 0; n < ND; ++n) {
+        const bf16x8 vop = read_v_op(vrow + ((4 * n + v_chunk_lane) ^ v_swz) * 16 + v_byte);
+        oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, p[hh], oacc[n], 0, 0, 0);
       }
     }
-
-    // exact masking of invalid key rows on stages past the fully valid prefix
-    if (masked) {
+  };
+  // exact masking of invalid key rows of sub-tile `sub` (its 32 keys = one validity word)
+  auto mask = [&](int sub, f32x16 &sc) __attribute__((always_inline)) {
+    const int tile = sub / NH, half = sub % NH;
+    const uint32_t word = vwords[tile * 4 + (keyoff >> 5) + half] >> (4 * g);
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const uint32_t word = words[a] >> (4 * g);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int bit = (r & 3) + 8 * ((r >> 2) & 1) + 16 * (r >> 3);
-          if (!((word >> bit) & 1u)) {
-            acc[a][0][r] = kNegInf;
-            acc[a][1][r] = kNegInf;
-          }
-        }
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int bit = (r & 3) + 8 * ((r >> 2) & 1) + 16 * (r >> 3);
+      sc[r] = ((word >> bit) & 1u) ? sc[r] : kNegInf;
     }
-
-    // online softmax per query column (lane-local over 32 keys, then lane ^ 32)
-    bf16x8 pb[2][2][2];  // [a][b][hh]
+  };
+  float alpha = 1.f;  // exact kernel: rescale factor owed by the last softmax
+  bool pending = false;
+  // softmax of sc into p_out (the sequential form: exact kernel and peeled sub-iterations)
+  auto softmax = [&](const f32x16 &sc, bf16x8 *p_out) __attribute__((always_inline)) {
+    float mx = kNegInf;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[a][b][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m_run[b], mx);
-      const float muse = mnew == kNegInf ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f((m_run[b] - muse) * c2);
-      m_run[b] = mnew;
-      const float nm = -muse * c2;
-      float rs = 0.f;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[a][b][8 * hh + e], c2, nm));
-            rs += p;
-            pb[a][b][hh][e] = (__bf16)p;
-          }
-      l_run[b] = l_run[b] * alpha + rs;
-#pragma unroll
-      for (int n = 0; n < ND; ++n) oacc[n][b] *= alpha;
+    for (int r = 0; r < 16; r += 2) mx = max3(mx, sc[r], sc[r + 1]);
+    mx = half_max(mx) * c2;
+    if (EXACT) {
+      const bool up = mx > m2 + kRaise;
+      const float mnew = up ? mx : m2;
+      alpha = up ? __builtin_amdgcn_exp2f(m2 - mnew) : 1.f;
+      m2 = mnew;
+      pending = __builtin_amdgcn_ballot_w64(up) != 0;
+    } else {
+      const bool first = m2 == kNegInf;
+      over = over || (!first && mx > m2 + kLimit);
+      m2 = first ? mx : m2;
     }
-
-    // O^T += V^T P^T
+    const float nm = m2 == kNegInf ? 0.f : -m2;
+    float rs = 0.f;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const lds_char *vrow = vt + (32 * a + 16 * hh) * D * 2 + v_row_off;
-#pragma unroll
-        for (int n = 0; n < ND; ++n) {
-          const int chunk = ((4 * n + v_chunk_lane) ^ v_swz) * 16 + v_byte;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4 *)(vrow + chunk));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4 *)(vrow + 8 * D * 2 + chunk));
-          const bf16x4 lo_b = __builtin_bit_cast(bf16x4, lo);
-          const bf16x4 hi_b = __builtin_bit_cast(bf16x4, hi);
-          const bf16x8 vop = {lo_b[0], lo_b[1], lo_b[2], lo_b[3], hi_b[0], hi_b[1], hi_b[2], hi_b[3]};
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-            oacc[n][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[a][b][hh], oacc[n][b], 0, 0, 0);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * hh + e], c2, nm));
+        rs += p;
+        p_out[hh][e] = (__bf16)p;
       }
-    if (NBUF == 1) {
-      wait_lgkm0();
-      barrier();
+    l_run = EXACT ? l_run * alpha + rs : l_run + rs;
+  };
+  auto rescale = [&]() __attribute__((always_inline)) {
+    if (EXACT && pending) {
+#pragma unroll
+      for (int n = 0; n < ND; ++n) oacc[n] *= alpha;
+      pending = false;
     }
   };
 
-  if (NBUF == 2) {
-    for (int st = 0; st < n_stages; st += 2) {
-      stage(ic<0>{}, st);
-      if (st + 1 < n_stages) stage(ic<1>{}, st + 1);
+  // Full sub-iteration of the fast kernel, hand-interleaved: the DS MFMAs of S_{i+1}
+  // and the 2 ND MFMAs of P_{i-1} V_{i-1} alternate one per chunk, and the softmax
+  // of S_i is cut into slices placed between them.  A scheduling fence closes every
+  // second chunk, so the order written here is the order issued.  K and V operands
+  // are read from LDS two products ahead of their MFMAs.
+  auto fused = [&](auto par, const lds_char *kb, int khalf, const lds_char *vb, int vhalf)
+                   __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    constexpr int VOPS = 2 * ND, NM = DS + VOPS;
+    constexpr int PRE = 2, SLICES = 7;  // softmax slices 0, 1 (the maximum) run before the first MFMA
+    static_assert(DS == VOPS, "QK and PV products alternate one to one");
+    const f32x16 &sc = sacc[P];
+    f32x16 &sn = sacc[1 - P];
+    bf16x8 *po = pacc[P];
+    const bf16x8 *pp = pacc[1 - P];
+    bf16x8 kop[DS], vop[VOPS];
+    const lds_char *kbase = kb + k_row_off + khalf * 32 * D * 2;
+    const lds_char *vbase = vb + v_row_off + vhalf * 32 * D * 2;
+    auto read_k = [&](auto s_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_c)::value;
+      kop[S] = *(const __attribute__((address_space(3))) bf16x8 *)(kbase + (((2 * S + g) ^ k_swz) * 16));
+    };
+    auto read_v = [&](auto j_c) __attribute__((always_inline)) {
+      constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
+      vop[J] = read_v_op(vbase + 16 * HH * D * 2 + ((4 * N + v_chunk_lane) ^ v_swz) * 16 + v_byte);
+    };
+    float mx = kNegInf, nm = 0.f, rs0 = 0.f, rs1 = 0.f;
+    // slices 0, 1: maximum of 8 scores each; 2: column maximum and the fixed maximum;
+    // 3..6: probabilities of 4 scores (exp2, two partial row sums, bf16 packs)
+    auto slice = [&](auto k_c) __attribute__((always_inline)) {
+      constexpr int K = decltype(k_c)::value;
+      if constexpr (K < 2) {
+        constexpr int Q = 8 * K;
+        float m = max3(mx, sc[Q], sc[Q + 1]);
+        m = max3(m, sc[Q + 2], sc[Q + 3]);
+        m = max3(m, sc[Q + 4], sc[Q + 5]);
+        mx = max3(m, sc[Q + 6], sc[Q + 7]);
+      } else if constexpr (K == 2) {
+        const float m = half_max(mx) * c2;
+        const bool first = m2 == kNegInf;
+        over = over || (!first && m > m2 + kLimit);
+        m2 = first ? m : m2;
+        nm = m2 == kNegInf ? 0.f : -m2;
+      } else {
+        constexpr int R = 4 * (K - 3);
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_fmaf(sc[R + e], c2, nm);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = __builtin_amdgcn_exp2f(p[e]);
+        rs0 += p[0];
+        rs1 += p[1];
+        rs0 += p[2];
+        rs1 += p[3];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) po[R / 8][R % 8 + e] = (__bf16)p[e];
+      }
+    };
+    read_k(ic<0>{});
+    read_k(ic<1>{});
+    read_v(ic<0>{});
+    read_v(ic<1>{});
+    static_for<PRE>(slice);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NM>([&](auto c_c) __attribute__((always_inline)) {
+      constexpr int C = decltype(c_c)::value, KK = C / 2;
+      if constexpr (C % 2 == 0) {
+        if constexpr (KK + 2 < DS) read_k(ic<KK + 2>{});
+        sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[KK], qreg[KK], KK == 0 ? f32x16{} : sn, 0, 0, 0);
+      } else {
+        constexpr int HH = KK / ND, N = KK % ND;
+        if constexpr (KK + 2 < VOPS) read_v(ic<KK + 2>{});
+        oacc[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[KK], pp[HH], oacc[N], 0, 0, 0);
+      }
+      static_for<SLICES - PRE>([&](auto k_c) __attribute__((always_inline)) {
+        constexpr int K = decltype(k_c)::value;
+        if constexpr (K * NM / (SLICES - PRE) == C) slice(ic<K + PRE>{});
+      });
+      if constexpr (C % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    });
+    l_run += rs0 + rs1;
+  };
+
+  // Sub-iteration i: S_{i+1} (if HAS_QK), softmax of S_i, P_{i-1} V_{i-1} (if HAS_PV).
+  // PAR = i & 1.  KB / VB: LDS tiles holding the keys of sub-tile i+1 and the values of
+  // sub-tile i-1.  In the exact kernel the rescale owed by sub-tile i-1 runs first,
+  // after P_{i-2} V_{i-2} and before P_{i-1} V_{i-1}.
+  auto step = [&](auto has_qk, auto has_pv, auto par, auto masking, const lds_char *kb, const lds_char *vb,
+                  int i) __attribute__((always_inline)) {
+    constexpr bool HAS_QK = decltype(has_qk)::value;
+    constexpr bool HAS_PV = decltype(has_pv)::value;
+    constexpr int P = decltype(par)::value;
+    constexpr int MASK = decltype(masking)::value;
+    rescale();
+    if (MASK == kMaskAlways || (MASK == kMaskCheck && i / NH >= full_tiles)) mask(i, sacc[P]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!EXACT && HAS_QK && HAS_PV) {
+      fused(par, kb, (i + 1) % NH, vb, (i - 1 + NH) % NH);
+    } else {
+      if (HAS_QK) qk(kb, (i + 1) % NH, sacc[1 - P]);
+      softmax(sacc[P], pacc[P]);
+      if (HAS_PV) pv(vb, (i - 1 + NH) % NH, pacc[1 - P]);
     }
-  } else {
-    for (int st = 0; st < n_stages; ++st) stage(ic<0>{}, st);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr ic<1> T;
+  constexpr ic<0> F;
+  const lds_char *K0 = (const lds_char *)kbuf0, *K1 = (const lds_char *)kbuf1;
+  const lds_char *V0 = (const lds_char *)vbuf0, *V1 = (const lds_char *)vbuf1;
+
+  if (n_sub > 0) {
+    // The steady-state loops run only full sub-iterations (scores of the next
+    // sub-tile, softmax, product of the previous one).  The first and the last
+    // sub-iterations are peeled, and sub-tiles that may need masking run in a loop
+    // of their own, so no loop body carries a branch around its MFMA work.
+    if (NH == 2) {
+      // Sub-tile i = 2t + h lives in tile t.  Before sub-iteration 2t + 1: K_{t+1} and
+      // V_t are resident; K_{t+2} and V_{t+1} are then issued into the buffers of K_t
+      // and V_{t-1}, which no wave reads any more.
+      if (n_tiles > 1) wait_vmcnt<2 * LOADS>(); else wait_vmcnt<LOADS>();
+      barrier();
+      qk(K0, 0, sacc[0]);
+      step(T, F, ic<0>{}, ic<kMaskCheck>{}, K0, V0, 0);  // S_1 comes from the same tile
+      // tile body t: sub-iterations 2t + 1 (softmax of tile t) and 2t + 2 (tile t + 1)
+      auto tile = [&](auto par, auto masking, int t) __attribute__((always_inline)) {
+        constexpr int PT = decltype(par)::value;
+        // page ids first: their scalar loads overlap the wait for the other waves
+        const int32_t kp = tile_page(walk, min(t + 2, n_tiles - 1), wave);
+        const int32_t vp = tile_page(walk, t + 1, wave);
+        wait_vmcnt<0>();
+        barrier();
+        if (t + 2 < n_tiles) load_page<D, false>(kh, kp, (lds_char *)(PT ? kbuf1 : kbuf0), wave, lane);
+        load_page<D, true>(vh, vp, (lds_char *)(PT ? vbuf0 : vbuf1), wave, lane);
+        const lds_char *knext = PT ? K0 : K1;  // K_{t+1}
+        const lds_char *vcur = PT ? V1 : V0;   // V_t
+        step(T, T, ic<1>{}, masking, knext, vcur, 2 * t + 1);
+        step(T, T, ic<0>{}, masking, knext, vcur, 2 * t + 2);
+      };
+      // bodies t < full_tiles - 1 touch only tiles of the valid prefix
+      const int split = min(max(full_tiles - 1, 0), n_tiles - 1);
+      for_range(ic<kMaskNone>{}, 0, split, tile);
+      for_range(ic<kMaskAlways>{}, split, n_tiles - 1, tile);
+      // last tile t = n_tiles - 1: V_t resident after the wait
+      const int t = n_tiles - 1;
+      wait_vmcnt<0>();
+      barrier();
+      const lds_char *vlast = (t & 1) ? V1 : V0;
+      step(F, T, ic<1>{}, ic<kMaskCheck>{}, K0, vlast, 2 * t + 1);
+      rescale();
+      pv(vlast, 1, pacc[1]);
+    } else {
+      // One sub-tile per tile.  Before sub-iteration i: K_{i+1} and V_{i-1} resident;
+      // then K_{i+2} goes into the buffer of K_i and V_i into the buffer of V_{i-2}.
+      if (n_tiles > 1) wait_vmcnt<LOADS>(); else wait_vmcnt<0>();
+      barrier();
+      qk(K0, 0, sacc[0]);
+      wait_vmcnt<0>();
+      barrier();
+      if (n_sub > 2) load_page<D, false>(kh, tile_page(walk, 2, wave), (lds_char *)kbuf0, wave, lane);
+      load_page<D, true>(vh, tile_page(walk, 0, wave), (lds_char *)vbuf0, wave, lane);
+      if (n_sub > 1) {
+        step(T, F, ic<0>{}, ic<kMaskCheck>{}, K1, V1, 0);
+        auto sub = [&](auto par, auto masking, int i) __attribute__((always_inline)) {
+          constexpr int PI = decltype(par)::value;
+          const int32_t kp = tile_page(walk, min(i + 2, n_sub - 1), wave);
+          const int32_t vp = tile_page(walk, i, wave);
+          wait_vmcnt<0>();
+          barrier();
+          if (i + 2 < n_sub) load_page<D, false>(kh, kp, (lds_char *)(PI ? kbuf1 : kbuf0), wave, lane);
+          load_page<D, true>(vh, vp, (lds_char *)(PI ? vbuf1 : vbuf0), wave, lane);
+          step(T, T, par, masking, PI ? K0 : K1, PI ? V0 : V1, i);
+        };
+        const int split = min(max(full_tiles, 1), n_sub - 1);
+        for_range(ic<kMaskNone>{}, 1, split, sub);
+        for_range(ic<kMaskAlways>{}, split, n_sub - 1, sub);
+        // last sub-iteration i = n_sub - 1
+        const int i = n_sub - 1;
+        wait_vmcnt<0>();
+        barrier();
+        load_page<D, true>(vh, tile_page(walk, i, wave), (lds_char *)((i & 1) ? vbuf1 : vbuf0), wave, lane);
+        if (i & 1) step(F, T, ic<1>{}, ic<kMaskCheck>{}, K0, V0, i);
+        else step(F, T, ic<0>{}, ic<kMaskCheck>{}, K0, V1, i);
+      } else {
+        step(F, F, ic<0>{}, ic<kMaskCheck>{}, K1, V1, 0);
+      }
+      rescale();
+      wait_vmcnt<0>();
+      barrier();
+      if ((n_sub - 1) & 1) pv(V1, 0, pacc[1]); else pv(V0, 0, pacc[0]);
+    }
   }
 
   // ---- merge the waves that share query rows, then write O and LSE ----
   wait_vmcnt<0>();
   wait_lgkm0();
+  if (!EXACT && tid == 0) redo_any = 0;
   barrier();
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const float lt = l_run[b] + __shfl_xor(l_run[b], 32);
+  if (!EXACT && __builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) redo_any = 1;
+  {
+    const float lt = l_run + __shfl_xor(l_run, 32);
     if (lane < 32) {
-      stat_m[wave][32 * b + l32] = m_run[b];
-      stat_l[wave][32 * b + l32] = lt;
+      stat_m[wave][l32] = m2;
+      stat_l[wave][l32] = lt;
     }
   }
   wait_lgkm0();
   barrier();
-  lds_char *part = part_of(wave);
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int qr = 32 * b + l32;
+  if (!EXACT) {
+    const int redo = redo_any;
+    if (tid == 0) args.redo[blockIdx.x] = redo;
+    if (redo) return;  // the exact kernel writes this item
+  }
+  // merged maximum and sum of query row qr (0..31) of query group q_g
+  auto merged = [&](int q_g, int qr, float *mt_out) __attribute__((always_inline)) -> float {
     float mt = kNegInf;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const bool partner = G == 8 ? ((w & 1) == qhalf) : true;
-      if (partner) mt = fmaxf(mt, stat_m[w][qr]);
-    }
+    for (int w = q_g; w < kWaves; w += NQG) mt = fmaxf(mt, stat_m[w][qr]);
     float lt = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const bool partner = G == 8 ? ((w & 1) == qhalf) : true;
-      if (partner && stat_m[w][qr] != kNegInf) lt += stat_l[w][qr] * __builtin_amdgcn_exp2f((stat_m[w][qr] - mt) * c2);
-    }
-    const float f = (m_run[b] == kNegInf || lt == 0.f) ? 0.f : __builtin_amdgcn_exp2f((m_run[b] - mt) * c2) / lt;
+    for (int w = q_g; w < kWaves; w += NQG)
+      if (stat_m[w][qr] != kNegInf) lt += stat_l[w][qr] * __builtin_amdgcn_exp2f(stat_m[w][qr] - mt);
+    *mt_out = mt;
+    return lt;
+  };
+  // per-wave fp32 partial output (32 rows x D) over the free tile buffers
+  constexpr int PART_BYTES = 32 * D * 4;
+  {
+    float mt;
+    const float lt = merged(qg, l32, &mt);
+    const float f = (m2 == kNegInf || lt == 0.f) ? 0.f : __builtin_amdgcn_exp2f(m2 - mt) / lt;
+    lds_char *part = (lds_char *)smem + wave * PART_BYTES;
 #pragma unroll
     for (int n = 0; n < ND; ++n) {
-      f32x16 o = oacc[n][b] * f;
+      const f32x16 o = oacc[n] * f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c4 = 8 * n + 2 * j + g;                  // float4 chunk of d = 32n + 8j + 4g
-        const int phys = c4 ^ (qr & (D / 4 - 1));
+        const int phys = c4 ^ (l32 & (D / 4 - 1));
         const f32x4 val = {o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]};
-        *(__attribute__((address_space(3))) f32x4 *)(part + (qr * D + 4 * phys) * 4) = val;
+        *(__attribute__((address_space(3))) f32x4 *)(part + (l32 * D + 4 * phys) * 4) = val;
       }
     }
   }
@@ -337,17 +562,13 @@ __global__ __launch_bounds__(256, 1) void kpage_fwd_kernel(FwdArgs args) {
   const int64_t orow0 = (int64_t)bh * args.seq_q + 128 * it.q;
   const int vrows = cq < M ? cq : M;
   constexpr int GROUPS = D / 8;
-  for (int u = tid; u < 128 * GROUPS; u += 256) {
+  for (int u = tid; u < 128 * GROUPS; u += kThreads) {
     const int row = u / GROUPS, grp = u % GROUPS;
     float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (row < vrows) {
-      const int qr = row & 63;
-      const int qh = row >> 6;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const bool partner = G == 8 ? ((w & 1) == qh) : true;
-        if (!partner) continue;
-        const lds_char *pw = part_of(w);
+      const int qr = row & 31, q_g = row >> 5;
+      for (int w = q_g; w < kWaves; w += NQG) {
+        const lds_char *pw = (const lds_char *)smem + w * PART_BYTES;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int phys = (2 * grp + h) ^ (qr & (D / 4 - 1));
@@ -368,22 +589,20 @@ __global__ __launch_bounds__(256, 1) void kpage_fwd_kernel(FwdArgs args) {
     const int row = tid;
     float lse = kNegInf;
     if (row < vrows) {
-      const int qr = row & 63;
-      const int qh = row >> 6;
-      float mt = kNegInf;
-      for (int w = 0; w < 4; ++w) {
-        const bool partner = G == 8 ? ((w & 1) == qh) : true;
-        if (partner) mt = fmaxf(mt, stat_m[w][qr]);
-      }
-      float lt = 0.f;
-      for (int w = 0; w < 4; ++w) {
-        const bool partner = G == 8 ? ((w & 1) == qh) : true;
-        if (partner && stat_m[w][qr] != kNegInf) lt += stat_l[w][qr] * __builtin_amdgcn_exp2f((stat_m[w][qr] - mt) * c2);
-      }
-      if (mt != kNegInf && lt > 0.f) lse = mt * args.scale + __logf(lt);
+      float mt;
+      const float lt = merged(row >> 5, row & 31, &mt);
+      // LSE = ln(sum exp(scale * s)) = (m2 + log2 l) * ln 2
+      if (mt != kNegInf && lt > 0.f) lse = (mt + __log2f(lt)) * 0.6931471805599453f;
     }
     args.lse[orow0 + row] = lse;
   }
+}
+
+template <int D, int ROUTE>
+void launch_route(const FwdArgs &a, hipStream_t stream) {
+  dim3 grid(a.n_items), block(kThreads);
+  hipLaunchKernelGGL((kpage_fwd_kernel<D, ROUTE, false>), grid, block, 0, stream, a);
+  hipLaunchKernelGGL((kpage_fwd_kernel<D, ROUTE, true>), grid, block, 0, stream, a);
 }
 
 }  // namespace
@@ -391,12 +610,11 @@ __global__ __launch_bounds__(256, 1) void kpage_fwd_kernel(FwdArgs args) {
 hipError_t launch_fwd(const FwdArgs &a, int head_dim, int route, hipStream_t stream, LaunchTimer *timer) {
   if (a.n_items <= 0) return hipSuccess;
   const int kid = route == 128 ? 0 : 1;
-  dim3 grid(a.n_items), block(256);
   if (timer) timer->before(kid, stream);
-  if (head_dim == 128 && route == 128) hipLaunchKernelGGL((kpage_fwd_kernel<128, 8>), grid, block, 0, stream, a);
-  else if (head_dim == 128 && route == 64) hipLaunchKernelGGL((kpage_fwd_kernel<128, 16>), grid, block, 0, stream, a);
-  else if (head_dim == 64 && route == 128) hipLaunchKernelGGL((kpage_fwd_kernel<64, 8>), grid, block, 0, stream, a);
-  else if (head_dim == 64 && route == 64) hipLaunchKernelGGL((kpage_fwd_kernel<64, 16>), grid, block, 0, stream, a);
+  if (head_dim == 128 && route == 128) launch_route<128, 128>(a, stream);
+  else if (head_dim == 128 && route == 64) launch_route<128, 64>(a, stream);
+  else if (head_dim == 64 && route == 128) launch_route<64, 128>(a, stream);
+  else if (head_dim == 64 && route == 64) launch_route<64, 64>(a, stream);
   else return hipErrorInvalidValue;
   if (timer) timer->after(kid, stream);
   return hipGetLastError();

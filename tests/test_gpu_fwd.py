@@ -142,6 +142,39 @@ def test_fwd_edge_cases(name, d):
     check(O, L, Oref, Lref, f"{name} d={d}")
 
 
+def rising_scores_problem(d):
+    """Scores that rise by far more than 2^64 (base 2) after the first tile of every walk.
+
+    Every query has a large component along one direction u; the keys of the first
+    selected block have none, the keys of later blocks a large one, so the row maximum
+    found on the first tile is exceeded by about q.k * scale * log2(e) ~ 100 later on.
+    This drives the forward kernel's exact rescaling pass; the oracle is unaffected.
+    """
+    p = make_problem([128, 100, 50, 20], [128, 128, 77, 128, 33], [[0, 1, 2], [0, 3, 4, 1], [0, 2], [0, 4]],
+                     heads=2, head_dim=d, sort_rows=False)
+    t = random_tensors(p, seed=11)
+    g = torch.Generator().manual_seed(12)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    amp = 30.0 * (128.0 / d) ** 0.5
+    q = t["q"].float() + amp * u
+    k = t["k"].float()
+    k[:, :, 128:] += amp * u          # every key block but block 0
+    for x, c in ((q, p.q_valid[0]), (k, p.kv_valid[0])):
+        for b, n in enumerate(c):
+            x[:, :, 128 * b + int(n):128 * (b + 1)] = 0
+    return p, q.to(torch.bfloat16), k.to(torch.bfloat16), t["v"], t["do"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_large_score_rise_uses_exact_pass(d):
+    p, q, k, v, _ = rising_scores_problem(d)
+    _say(f"[fwd] large score rise d={d}")
+    O, L = gpu_fwd(p, q, k, v)
+    Oref, Lref = oracle_fwd(p, q, k, v)
+    check(O, L, Oref, Lref, f"large score rise d={d}")
+
+
 def test_fwd_independent_offsets_with_gaps():
     """K/V blocks at shuffled Page16 offsets with unused pages between footprints."""
     ck = [50, 128, 3, 97, 16, 0, 33]
