@@ -88,8 +88,8 @@ struct kpage_plan {
   // backward device tables
   BwdItem *d_bitems = nullptr;
   int n_bitems = 0;
-  int32_t *d_owners = nullptr, *d_qpages = nullptr, *d_uncovered = nullptr, *d_qvalid = nullptr;
-  uint32_t *d_kmask = nullptr, *d_qmask = nullptr;
+  int32_t *d_owners = nullptr, *d_qpages = nullptr, *d_uncovered = nullptr;
+  uint32_t *d_kmask = nullptr;
   uint64_t *d_adj = nullptr;
   int64_t *d_uncovered_ptr = nullptr;
   int max_uncovered = 0;
@@ -219,11 +219,11 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
   if (pl->bwd_on_device) return KPAGE_OK;
   const Problem &P = pl->P;
   const BwdTables &B = pl->B;
-  const int nq = P.n_q, nk = P.n_kv;
+  const int nk = P.n_kv;
   const size_t n_own = B.aligned.size();
-  // row masks of owner pages (K/V sizes) and of Q-walk pages (Q sizes)
+  // row masks of owner pages (K/V sizes); query-row validity reaches the kernels
+  // through LSE = -inf of invalid rows
   std::vector<uint32_t> kmask(n_own * kOwnerSlots, 0);
-  std::vector<uint32_t> qmask(B.qwalk.size(), 0);
   for (int g = 0; g < P.slots; ++g) {
     const int32_t *ck = &P.kv_valid[size_t(g) * nk];
     const int64_t *ok = &P.kv_offset[size_t(g) * nk];
@@ -240,13 +240,6 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
         const int j = int(pg - ok[k] / kPageRows);
         const int c = ck[k];
         kmask[size_t(t) * kOwnerSlots + i] = (j + 1) * kPageRows <= c ? kFullMask : ((1u << (c % kPageRows)) - 1u);
-      }
-      for (int64_t e = B.qwalk_ptr[t]; e < B.qwalk_ptr[t + 1]; ++e) {
-        const int32_t qp = B.qwalk[e];
-        if (qp < 0) continue;
-        const int c = P.q_valid[size_t(g) * nq + qp / 8];
-        const int j = qp % 8;
-        qmask[e] = (j + 1) * kPageRows <= c ? kFullMask : ((1u << (c % kPageRows)) - 1u);
       }
     }
   }
@@ -274,11 +267,9 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
   if ((s = upload(pl, owners, &pl->d_owners, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, kmask, &pl->d_kmask, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, qpages, &pl->d_qpages, stream)) != KPAGE_OK) return s;
-  if ((s = upload(pl, qmask, &pl->d_qmask, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, B.adj, &pl->d_adj, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, B.uncovered, &pl->d_uncovered, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, B.uncovered_ptr, &pl->d_uncovered_ptr, stream)) != KPAGE_OK) return s;
-  if ((s = upload(pl, P.q_valid, &pl->d_qvalid, stream)) != KPAGE_OK) return s;
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   pl->n_bitems = int(items.size());
@@ -357,8 +348,8 @@ kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, co
 kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes) {
   if (!plan || !bytes) return fail(KPAGE_ERR_INVALID, "plan or bytes is NULL");
   const size_t rows = size_t(plan->P.batch) * plan->P.heads * size_t(plan->P.seq_q);
-  // fp32 dQ accumulator [BH, seq_q, d], then fp32 D = rowsum(dO * O) and LSE * log2(e), each [BH, seq_q]
-  *bytes = rows * size_t(plan->P.head_dim) * 4 + 2 * rows * 4;
+  // fp32 LSE * log2(e), then fp32 D = rowsum(dO * O), each [BH, seq_q]
+  *bytes = 2 * rows * 4;
   return KPAGE_OK;
 }
 
@@ -373,25 +364,33 @@ kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, co
   kpage_bwd_workspace_size(plan, &need);
   if (workspace_bytes < need) return fail(KPAGE_ERR_INVALID, "workspace smaller than kpage_bwd_workspace_size()");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  kpage_status s = ensure_backward_on_device(plan, st);
+  kpage_status s = ensure_forward_on_device(plan, st);  // the dQ pass walks the forward tables
+  if (s != KPAGE_OK) return s;
+  s = ensure_backward_on_device(plan, st);
   if (s != KPAGE_OK) return s;
   const Problem &P = plan->P;
   const size_t rows = size_t(P.batch) * P.heads * size_t(P.seq_q);
+  // the K/V pass addresses delta as lse2 plus a 32-bit byte offset
+  if (rows * 4 >= (size_t(1) << 31)) return fail(KPAGE_ERR_UNSUPPORTED, "more than 2^29 query rows in one call");
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dO; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.dq_acc = static_cast<float *>(workspace);
-  a.delta = static_cast<float *>(workspace) + rows * size_t(P.head_dim);
+  a.lse2 = static_cast<float *>(workspace);
+  a.delta = static_cast<float *>(workspace) + rows;
   a.items = plan->d_bitems;
   a.n_items = plan->n_bitems;
   a.owners = plan->d_owners;
   a.owner_kmask = plan->d_kmask;
   a.qpages = plan->d_qpages;
-  a.qmask = plan->d_qmask;
   a.adj = plan->d_adj;
   a.uncovered = plan->d_uncovered;
   a.uncovered_ptr = plan->d_uncovered_ptr;
-  a.q_valid = plan->d_qvalid;
+  a.fitems128 = plan->d_items128;
+  a.fitems64 = plan->d_items64;
+  a.n_fitems128 = plan->n_items128;
+  a.n_fitems64 = plan->n_items64;
+  a.pages = plan->d_pages;
+  a.valid = plan->d_valid;
   a.seq_q = P.seq_q;
   a.seq_kv = P.seq_kv;
   a.heads = P.heads;

@@ -1,73 +1,36 @@
 // Backward KPage attention for gfx950 (MI355X, CDNA4).
 //
-// KPage paper, section 3.3: the backward pass is organised around K/V owners.
-// An owner is 8 Page16 slots (128 key rows) holding pages of one or more
-// logical K/V blocks; no block crosses an owner.  Its reverse-Q neighbourhood
-// is visited in steps of 8 query pages (128 query rows), and one 64-bit
-// adjacency word per step (bit 8 j + i: Q slot j, K slot i) removes the page
-// pairs that are not edges of the original graph (section 3.3.3).  dK and dV
-// accumulate in registers over all steps of the owner; dQ goes through an fp32
-// accumulator with atomic adds, scattered by query page id, and a final pass
-// converts it to bf16 (section 3.3.3, last paragraph; section 3.4.1 for the
-// cleanup of rows that hold no token).
+// KPage paper, section 3.3: dK and dV are accumulated by K/V owners.  An owner is
+// 8 Page16 slots (128 key rows) holding pages of one or more logical K/V blocks;
+// no block crosses an owner.  Its reverse-Q neighbourhood is visited in steps of 8
+// query pages (128 query rows), and one 64-bit adjacency word per step (bit 8 j + i:
+// Q slot j, K slot i) removes the page pairs that are not edges of the original
+// graph (section 3.3.3).
+//
+// dQ is computed by a second, Q-owned pass over the forward page walks (section
+// 3.2): each query block recomputes S and dP for its own keys and accumulates
+// dQ = scale dS K in registers, so no query row is written by more than one
+// workgroup and no fp32 accumulator or atomic traffic is needed.  This costs one
+// more S and dP product per pair than an atomic dQ inside the owner loop, but on
+// MI355X the owner loop would otherwise spend its LDS bandwidth on transposed dS
+// and K reads and its memory bandwidth on fp32 atomics.
 //
 // Kernels:
-//   kpage_bwd_pre       D_i = sum_d dO_id O_id, LSE_i * log2(e) (0 for empty
-//                       rows), zero the dQ accumulator.
-//   kpage_bwd_zero      zero dK/dV pages that lie outside every block footprint.
-//   kpage_bwd_main      one work item per (batch*head, owner).
-//   kpage_bwd_post      dQ = bf16(scale * acc), rows past c_q set to 0.
-//
-// Main kernel layout (256 threads, 4 waves, v_mfma_f32_32x32x16_bf16): wave w
-// owns key rows 32w..32w+31 of the owner (its K and V rows stay in VGPRs as MFMA
-// operands, its dK and dV in accumulators).  Per step it computes, for all 128
-// query rows, S = Q K^T with the lane index running over keys and the register
-// index over queries; in that layout P^T and dS^T are directly the A operands
-// of dV += P^T dO and dK += dS^T Q, whose B operands (columns of dO and Q) come
-// from LDS through ds_read_b64_tr_b16.  dS is also written to LDS so that wave
-// w can form dQ for query rows 32w..32w+31 over all 128 keys.
+//   kpage_bwd_pre   D_i = sum_d dO_id O_id and LSE_i * log2(e) (0 for rows without
+//                   keys), 16 threads per row.
+//   kpage_bwd_zero  zero dK/dV pages that lie outside every block footprint.
+//   kpage_bwd_kv    one workgroup per (batch*head, owner): dK, dV.
+//   kpage_bwd_dq    one workgroup per forward work item (query block): dQ.
 #include <hip/hip_runtime.h>
-#include <hip/amd_detail/amd_hip_unsafe_atomics.h>
 
 #include "device.hpp"
+#include "tile_common.hpp"
 
 namespace kpage {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-typedef const __attribute__((address_space(4))) int32_t c_i32;
-typedef const __attribute__((address_space(4))) uint32_t c_u32;
-typedef const __attribute__((address_space(4))) uint64_t c_u64;
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
-
-// XOR swizzle of the 16-byte chunks of row r of a row-major LDS tile.  Any 8
-// (or 16) aligned consecutive rows map one logical chunk to 8 (16) distinct
-// slots (row reads), and any 4 aligned consecutive rows map a chunk pair (quad)
-// to 8 (16) distinct slots (ds_read_b64_tr_b16 reads): conflict-free for both
-// access patterns on 32- and 64-bank LDS.
-__device__ __forceinline__ int swz(int r) {
-  return (((0xAC60 >> (4 * (r & 3))) & 0xF) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 2));
-}
-
-__device__ __forceinline__ bf16x8 tr_read8(const lds_char *p0, const lds_char *p1) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p0);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p1);
-  const bf16x4 a = __builtin_bit_cast(bf16x4, lo), b = __builtin_bit_cast(bf16x4, hi);
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-}
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 
 // ---------------------------------------------------------------------------
 // pre: 16 threads per query row
@@ -78,20 +41,19 @@ __global__ __launch_bounds__(256) void kpage_bwd_pre(BwdArgs a) {
   const int sub = threadIdx.x & 15;
   if (row >= rows) return;
   constexpr int PER = D / 16;  // elements per thread
-  const __bf16 *o = (const __bf16 *)a.o + row * D + sub * PER;
-  const __bf16 *g = (const __bf16 *)a.dout + row * D + sub * PER;
+  typedef __bf16 row_t __attribute__((ext_vector_type(PER)));
+  const row_t o = *(const row_t *)((const __bf16 *)a.o + row * D + sub * PER);
+  const row_t g = *(const row_t *)((const __bf16 *)a.dout + row * D + sub * PER);
   float s = 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) s += (float)o[e] * (float)g[e];
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
-  float *acc = a.dq_acc + row * D + sub * PER;
-#pragma unroll
-  for (int e = 0; e < PER; e += 4) *(f32x4 *)(acc + e) = f32x4{0.f, 0.f, 0.f, 0.f};
   if (sub == 0) {
     a.delta[row] = s;
     const float l = a.lse[row];
-    a.delta[rows + row] = l == -__builtin_inff() ? 0.f : l * kLog2e;
+    // rows without a valid key (and invalid rows) get +inf: exp2(x - lse2) = 0
+    a.lse2[row] = l == kNegInf ? __builtin_inff() : l * kLog2e;
   }
 }
 
@@ -111,75 +73,287 @@ __global__ __launch_bounds__(256) void kpage_bwd_zero(BwdArgs a, int64_t pages_p
   }
 }
 
-// post: 16 threads per query row
+// ---------------------------------------------------------------------------
+// K/V-owned pass.  Wave w owns key rows 32 (w & 3) .. + 31 of the owner (owner
+// slots 2 (w & 3) and 2 (w & 3) + 1) and query rows 64 (w >> 2) .. + 63 of every
+// step.  Its K and V rows stay in VGPRs as MFMA B operands and its dK and dV are
+// accumulators; the two waves of a key group are summed at the end.
+//
+// Per 32-query block: S = Q K^T and dP = dO V^T with the lane index over keys and
+// the register index over queries (A = Q / dO rows read from LDS), so P^T and
+// dS^T are directly the A operands of dV += P^T dO and dK += dS^T Q, whose B
+// operands (columns of dO and Q) are transposed LDS reads of the same tiles.
 template <int D>
-__global__ __launch_bounds__(256) void kpage_bwd_post(BwdArgs a) {
-  const int64_t rows = (int64_t)a.bh_count * a.seq_q;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  if (row >= rows) return;
-  constexpr int PER = D / 16;
-  const int64_t bh = row / a.seq_q;
-  const int64_t r = row % a.seq_q;
-  const int slot = a.per_head ? (int)bh : 0;
-  const bool valid = (r & 127) < a.q_valid[(int64_t)slot * a.n_q + (r >> 7)];
-  const float *acc = a.dq_acc + row * D + sub * PER;
-  __bf16 *out = (__bf16 *)a.dq + row * D + sub * PER;
-  typedef __bf16 row_t __attribute__((ext_vector_type(PER)));
-  row_t v;
+__global__ __launch_bounds__(kThreads, 1) void kpage_bwd_kv(BwdArgs a) {
+  constexpr int DS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int TILE = 128 * D * 2;      // one 128-row tile of Q or dO
+  constexpr int STATS = kWaves * 256;    // per step: 64 floats per wave (lse2, delta, spare)
+
+  // step buffers: [Q 0][dO 0][Q 1][dO 1], then the two stats buffers; at the end the
+  // dK/dV partials of the waves with w >= 4
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
+  __shared__ __attribute__((aligned(256))) char stats[2 * STATS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int sl = lane & 15;
+  const int mgrp = lane >> 4;
+  const int kg = wave & 3;   // key group: owner slots 2 kg, 2 kg + 1
+  const int qh = wave >> 2;  // query half of each step
+
+  const BwdItem it = a.items[blockIdx.x];
+  const int64_t bh = it.bh;
+  const int n_steps = it.n_steps;
+  c_i32 *own = (c_i32 *)(a.owners + (int64_t)it.owner * 8);
+  c_u32 *kmk = (c_u32 *)(a.owner_kmask + (int64_t)it.owner * 8);
+  c_i32 *qpages = (c_i32 *)(a.qpages + it.qwalk_off);
+  c_u64 *adjw = (c_u64 *)(a.adj + (it.qwalk_off >> 3));
+
+  const char *kh = (const char *)a.k + bh * a.seq_kv * D * 2;
+  const char *vh = (const char *)a.v + bh * a.seq_kv * D * 2;
+  const char *qgl = (const char *)a.q + bh * a.seq_q * D * 2;
+  const char *ggl = (const char *)a.dout + bh * a.seq_q * D * 2;
+  const float *l2h = a.lse2 + bh * a.seq_q;
+  const uint32_t stat_off =
+      (uint32_t)(lane & 15) * 4 + ((lane >> 4) & 1) * (uint32_t)((const char *)a.delta - (const char *)a.lse2);
+
+  // step st: Q and dO pages (one page of each per wave), lse2 and delta of that page
+  auto load_step = [&](int st, int buf) __attribute__((always_inline)) {
+    const int32_t page = qpages[8 * st + wave];
+    lds_char *qt = (lds_char *)smem + (2 * buf) * TILE;
+    lds_char *gt = (lds_char *)smem + (2 * buf + 1) * TILE;
+    load_page<D, kSwzBoth>(qgl, page, qt, 16 * wave, lane);
+    load_page<D, kSwzBoth>(ggl, page, gt, 16 * wave, lane);
+    // lanes 0-15: lse2 of the page's rows, 16-31: delta, 32-63: the same again
+    // (delta = lse2 + rows: one scalar base and a 32-bit lane offset)
+    const char *src = (const char *)(l2h + (int64_t)page * 16);
+    const uint32_t off = (uint32_t)xor_imm<0x40000000>(stat_off) ^ 0x40000000u;  // recomputed, not kept
+    __builtin_amdgcn_global_load_lds((const void *)(src + off), (lds_char *)(stats + buf * STATS + wave * 256), 4, 0, 0);
+  };
+
+  // this wave's 32 key rows as MFMA B operands (k = head dim, n = key)
+  const int khalf = l32 >> 4;
+  const int kslot = 2 * kg + khalf;
+  const int32_t mypage_raw = own[kslot];
+  const int32_t mypage = mypage_raw >= 0 ? mypage_raw : own[0];  // empty slots read finite data, masked below
+  const uint32_t mykm = kmk[kslot];
+  const bool kvalid = (mykm >> (l32 & 15)) & 1u;
+  bf16x8 kreg[DS], vreg[DS];
+  {
+    const bf16x8 *kr = (const bf16x8 *)(kh + ((int64_t)mypage * 16 + (l32 & 15)) * (D * 2));
+    const bf16x8 *vr = (const bf16x8 *)(vh + ((int64_t)mypage * 16 + (l32 & 15)) * (D * 2));
 #pragma unroll
-  for (int j = 0; j < PER; ++j) v[j] = (__bf16)(valid ? acc[j] * a.scale : 0.f);
-  *(row_t *)out = v;
+    for (int s = 0; s < DS; ++s) {
+      kreg[s] = kr[2 * s + g];
+      vreg[s] = vr[2 * s + g];
+    }
+  }
+  if (n_steps > 0) load_step(0, 0);
+
+  f32x16 dk[ND], dv[ND];
+#pragma unroll
+  for (int n = 0; n < ND; ++n) {
+    dk[n] = f32x16{};
+    dv[n] = f32x16{};
+  }
+  const float c2 = a.scale_log2;
+  // Lane-constant LDS offsets inside a Q or dO tile.  Row reads of row 64 qh + l32 at
+  // k-step s sit at rd_base ^ 32 s (the swizzle only flips chunk bits); transposed
+  // reads of rows 64 qh + tr_row (+ 8) at head-dim block n sit at tr_base ^ 64 n (and
+  // that + 8 rows, chunk bit 2 flipped).  Query block and buffer are immediates.
+  const int rd_base = chunk_off<kSwzBoth, D>(64 * qh + l32, g);
+  const int tr_base = chunk_off<kSwzBoth, D>(64 * qh + 4 * g + (sl >> 2), 2 * (mgrp & 1) + ((sl & 3) >> 1)) + (sl & 1) * 8;
+
+  auto step = [&](auto buf_c, int st) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const lds_char *qt = (const lds_char *)smem + (2 * BUF) * TILE;
+    const lds_char *gt = (const lds_char *)smem + (2 * BUF + 1) * TILE;
+    // Pair mask of this step.  Query rows without a valid key, invalid rows included,
+    // have lse2 = +inf and drop out by themselves; what is left is key validity and
+    // the adjacency bit of (query page 4 qh + j, this lane's key slot), applied as a
+    // 0 / -inf bias on the exponent.
+    // (the two adjacency bits of this key group are wave-uniform: pick per lane half)
+    const uint64_t adj = adjw[st];
+    float nbias[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t two = (uint32_t)(adj >> (8 * (4 * qh + j) + 2 * kg)) & 3u;
+      nbias[j] = (kvalid && ((two >> khalf) & 1u)) ? 0.f : kNegInf;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<2>([&](auto qb_c) __attribute__((always_inline)) {
+      constexpr int QB = decltype(qb_c)::value;
+      constexpr int RB = 32 * QB * D * 2;  // byte offset of the query block
+      // Register r of a 32 x 32 score block holds query row 32 qb + 8 (r / 4) + 4 g +
+      // r % 4 of the wave's 64 rows; group j4 = r / 4 reads its 4 lse2 / delta values
+      // as one f32x4 from the stats buffer.
+      auto stat4 = [&](int j4, int which) __attribute__((always_inline)) {
+        const int q = 32 * QB + 8 * j4 + 4 * g;
+        const int pg = q >> 4, rin = q & 15;
+        const lds_char *p4 = (const lds_char *)stats + BUF * STATS + ((4 * qh + pg) * 64 + rin) * 4 + which * 64;
+        return *(const __attribute__((address_space(3))) f32x4 *)p4;
+      };
+      // (A) S = Q K^T, operand reads two k-steps ahead; then P = exp2(scale log2e S -
+      // lse2 + bias), kept as bf16 (the A operand of dV += P^T dO)
+      bf16x8 pb[2], sb[2];
+      {
+        f32x16 sp = f32x16{};
+        bf16x8 op[DS];
+        auto rd = [&](auto s_c) __attribute__((always_inline)) {
+          constexpr int S = decltype(s_c)::value;
+          op[S] = lds_read8(qt + RB + xor_imm<32 * S>(rd_base));
+        };
+        rd(ic<0>{});
+        rd(ic<1>{});
+        static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
+          constexpr int S = decltype(s_c)::value;
+          if constexpr (S + 2 < DS) rd(ic<S + 2>{});
+          sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], kreg[S], sp, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const f32x4 l4 = stat4(j4, 0);
+          const float nb = nbias[((32 * QB + 8 * j4) >> 4) & 3];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j4 + e;
+            pb[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sp[r], c2, nb - l4[e]));
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // (B) dP = dO V^T, then (C) dS = P (dP - D) as bf16 (the A operand of dK += dS^T Q).
+      // P enters dS as its bf16 value: the extra rounding is of the order of the final
+      // rounding of dS to bf16.
+      {
+        f32x16 dp = f32x16{};
+        bf16x8 op[DS];
+        auto rd = [&](auto s_c) __attribute__((always_inline)) {
+          constexpr int S = decltype(s_c)::value;
+          op[S] = lds_read8(gt + RB + xor_imm<32 * S>(rd_base));
+        };
+        rd(ic<0>{});
+        rd(ic<1>{});
+        static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
+          constexpr int S = decltype(s_c)::value;
+          if constexpr (S + 2 < DS) rd(ic<S + 2>{});
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], vreg[S], dp, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const f32x4 d4 = stat4(j4, 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j4 + e;
+            sb[r >> 3][r & 7] = (__bf16)((float)pb[r >> 3][r & 7] * (dp[r] - d4[e]));
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // (D) dV += P^T dO and dK += dS^T Q over these 32 query rows (B operands: columns
+      // of dO and Q, transposed reads one product ahead)
+      constexpr int NOPS = 2 * ND;
+      bf16x8 gt_op[NOPS], qt_op[NOPS];
+      auto rdt = [&](auto j_c) __attribute__((always_inline)) {
+        constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
+        constexpr int RH = RB + 16 * HH * D * 2;
+        const int oa = xor_imm<64 * N>(tr_base);
+        const int ob = xor_imm<64>(oa + 8 * D * 2);
+        gt_op[J] = tr_read8(gt + RH + oa, gt + RH + ob);
+        qt_op[J] = tr_read8(qt + RH + oa, qt + RH + ob);
+      };
+      rdt(ic<0>{});
+      static_for<NOPS>([&](auto j_c) __attribute__((always_inline)) {
+        constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
+        if constexpr (J + 1 < NOPS) rdt(ic<J + 1>{});
+        dv[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[HH], gt_op[J], dv[N], 0, 0, 0);
+        dk[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb[HH], qt_op[J], dk[N], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  };
+
+  // one step per iteration; the next step's pages load while this one computes
+  auto iter = [&](auto buf_c, auto, int st) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_c)::value;
+    wait_vmcnt<0>();
+    barrier();  // step st resident for every wave; nobody reads buffer 1 - BUF any more
+    if (st + 1 < n_steps) load_step(st + 1, 1 - BUF);
+    step(buf_c, st);
+  };
+  for_range(ic<0>{}, 0, n_steps, iter);
+
+  // ---- sum the two query halves of each key group, then write dK (scaled) and dV ----
+  wait_vmcnt<0>();
+  barrier();
+  constexpr int PART = 32 * D * 4;  // one 32 x D fp32 block
+  float *part = (float *)((char *)smem + kg * 2 * PART);
+  if (qh == 1) {
+#pragma unroll
+    for (int n = 0; n < ND; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        part[(n * 16 + r) * 64 + lane] = dk[n][r];
+        part[PART / 4 + (n * 16 + r) * 64 + lane] = dv[n][r];
+      }
+  }
+  barrier();
+  if (qh == 0) {
+#pragma unroll
+    for (int n = 0; n < ND; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[n][r] += part[(n * 16 + r) * 64 + lane];
+        dv[n][r] += part[PART / 4 + (n * 16 + r) * 64 + lane];
+      }
+    // lane = head-dim column, register r = key row acc_row(r, g) of the wave's 32 keys
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * kg + acc_row(r, g);
+      const int slot = key >> 4, rin = key & 15;
+      const uint32_t km = kmk[slot];
+      if (km == 0u) continue;  // empty owner slot
+      const int64_t page = own[slot];
+      const bool ok = (km >> rin) & 1u;
+      __bf16 *kdst = (__bf16 *)a.dk + (bh * a.seq_kv + page * 16 + rin) * D + l32;
+      __bf16 *vdst = (__bf16 *)a.dv + (bh * a.seq_kv + page * 16 + rin) * D + l32;
+#pragma unroll
+      for (int n = 0; n < ND; ++n) {
+        kdst[32 * n] = (__bf16)(ok ? dk[n][r] * a.scale : 0.f);
+        vdst[32 * n] = (__bf16)(ok ? dv[n][r] : 0.f);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// main
+// Q-owned dQ pass over the forward page walks.  Same work split as the forward
+// kernel: 8 waves, each with 32 query rows and a key range of every 8-page tile
+// (M128: 4 query groups x 2 key halves, two 32-key sub-tiles per tile; M64: 2 x 4,
+// one sub-tile).  Per sub-tile, in the forward's transposed layout (lane = query):
+//   S^T = K Q^T, dP^T = V dO^T  (A = K / V rows from LDS, B = Q / dO rows in VGPRs),
+//   P^T = exp2(scale log2e S^T - lse2), dS^T = P^T (dP^T - D),
+//   dQ^T += K^T dS^T            (A = K read transposed from LDS, B = dS^T).
+// K tiles use the layout that serves both row and transposed reads.
+template <int D, int ROUTE>
+__global__ __launch_bounds__(kThreads, 1) void kpage_bwd_dq(BwdArgs a, const FwdItem *items) {
+  constexpr int DS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int M = ROUTE;
+  constexpr int NQG = M / 32;
+  constexpr int NKG = kWaves / NQG;
+  constexpr int KW = 128 / NKG;
+  constexpr int NH = KW / 32;
+  constexpr int TILE_BYTES = 128 * D * 2;
 
-template <int D>
-__device__ __forceinline__ void load_qstep(const char *qh, const char *gh, const float *lse2h, const float *delh,
-                                           c_i32 *qp, lds_char *qb, lds_char *gb, lds_char *lb, lds_char *db,
-                                           int wave, int lane) {
-  constexpr int CH = D / 8;
-  constexpr int PER_WAVE = 128 * CH / 256;  // 16-byte direct loads per wave per tensor
-  constexpr int ROWS_PER_INST = 64 / CH;
-#pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int inst = wave * PER_WAVE + i;
-    const int64_t page = qp[(inst * ROWS_PER_INST) >> 4];
-    const int row = inst * ROWS_PER_INST + lane / CH;
-    const int pos = lane % CH;
-    const int c = pos ^ (swz(row) & (CH - 1));
-    const int64_t off = (page * 16 + (row & 15)) * (D * 2) + c * 16;
-    __builtin_amdgcn_global_load_lds((const void *)(qh + off), (lds_char *)(qb + inst * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void *)(gh + off), (lds_char *)(gb + inst * 1024), 16, 0, 0);
-  }
-  // LSE * log2(e) and D of the 128 rows: one 4-byte direct load per lane, waves 0-1 and 2-3
-  {
-    const int half = wave & 1;
-    const int row = 64 * half + lane;
-    // the 4 pages of this half as scalar loads, then a per-lane pick
-    const int64_t p0 = qp[4 * half], p1 = qp[4 * half + 1], p2 = qp[4 * half + 2], p3 = qp[4 * half + 3];
-    const int sel = lane >> 4;
-    const int64_t page = sel == 0 ? p0 : sel == 1 ? p1 : sel == 2 ? p2 : p3;
-    const float *src = (wave < 2 ? lse2h : delh) + page * 16 + (row & 15);
-    lds_char *dst = (wave < 2 ? lb : db) + half * 256;
-    __builtin_amdgcn_global_load_lds((const void *)src, (lds_char *)dst, 4, 0, 0);
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256, 1) void kpage_bwd_main(BwdArgs a) {
-  constexpr int CH = D / 8;
-  constexpr int DS = D / 16;  // k-steps over the head dimension
-  constexpr int ND = D / 32;  // 32-wide output blocks over the head dimension
-  constexpr int TILE = 128 * D * 2;
-
-  __shared__ __attribute__((aligned(1024))) char k_lds[TILE];
-  __shared__ __attribute__((aligned(1024))) char q_lds[TILE];
-  __shared__ __attribute__((aligned(1024))) char g_lds[TILE];
-  __shared__ __attribute__((aligned(1024))) char s_lds[128 * 128 * 2];
-  __shared__ __attribute__((aligned(256))) float lse_lds[128];
-  __shared__ __attribute__((aligned(256))) float del_lds[128];
+  // K tiles 0/1, V tiles 0/1; at the end the per-wave dQ partials
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -189,240 +363,141 @@ __global__ __launch_bounds__(256, 1) void kpage_bwd_main(BwdArgs a) {
   const int sl = lane & 15;
   const int mgrp = lane >> 4;
 
-  const BwdItem it = a.items[blockIdx.x];
+  const FwdItem it = items[blockIdx.x];
   const int64_t bh = it.bh;
-  const int n_steps = it.n_steps;
-  c_i32 *own = (c_i32 *)(a.owners + (int64_t)it.owner * 8);
-  c_u32 *kmk = (c_u32 *)(a.owner_kmask + (int64_t)it.owner * 8);
-  c_i32 *qpages = (c_i32 *)(a.qpages + it.qwalk_off);
-  c_u32 *qmasks = (c_u32 *)(a.qmask + it.qwalk_off);
-  c_u64 *adjw = (c_u64 *)(a.adj + (it.qwalk_off >> 3));
+  const int cq = it.c_q;
+  const int n_tiles = it.walk_len / 8;
+  const int full_tiles = it.n_full / 8;
+  const int qg = wave % NQG;
+  const int keyoff = (wave / NQG) * KW;
 
   const char *kh = (const char *)a.k + bh * a.seq_kv * D * 2;
   const char *vh = (const char *)a.v + bh * a.seq_kv * D * 2;
-  const char *qh = (const char *)a.q + bh * a.seq_q * D * 2;
-  const char *gh = (const char *)a.dout + bh * a.seq_q * D * 2;
-  const int64_t rows_all = (int64_t)a.bh_count * a.seq_q;
-  const float *delh = a.delta + bh * a.seq_q;
-  const float *lse2h = a.delta + rows_all + bh * a.seq_q;
-  float *dqh = a.dq_acc + bh * a.seq_q * D;
+  c_i32 *walk = (c_i32 *)(a.pages + it.walk_off);
+  c_u32 *vwords = (c_u32 *)(a.valid + (it.walk_off >> 1));
 
-  // owner slots: empty slots read the first page (finite data) and are masked out
-  int32_t opage[8];
-  uint32_t okm[8];
-  bool all_k = true;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    okm[i] = kmk[i];
-    opage[i] = own[i] >= 0 ? own[i] : own[0];
-    all_k = all_k && okm[i] == 0xFFFFu;
-  }
-
-  // owner K into LDS (for dQ), rows = slot * 16 + r
+  // this wave's 32 query rows: Q and dO as MFMA B operands, lse2 and delta per lane
+  const int64_t qrow = bh * a.seq_q + 128 * it.q + 32 * qg + l32;
+  const bool qok = 32 * qg + l32 < cq;
+  bf16x8 qreg[DS], greg[DS];
   {
-    constexpr int PER_WAVE = 128 * CH / 256;
-    constexpr int ROWS_PER_INST = 64 / CH;
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int inst = wave * PER_WAVE + i;
-      const int slot = (inst * ROWS_PER_INST) >> 4;
-      int64_t page = opage[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j)
-        if (slot == j) page = opage[j];
-      const int row = inst * ROWS_PER_INST + lane / CH;
-      const int c = (lane % CH) ^ (swz(row) & (CH - 1));
-      __builtin_amdgcn_global_load_lds((const void *)(kh + (page * 16 + (row & 15)) * (D * 2) + c * 16),
-                                       (lds_char *)((lds_char *)k_lds + inst * 1024), 16, 0, 0);
-    }
-  }
-  if (n_steps > 0)
-    load_qstep<D>(qh, gh, lse2h, delh, qpages, (lds_char *)q_lds, (lds_char *)g_lds, (lds_char *)lse_lds,
-                  (lds_char *)del_lds, wave, lane);
-
-  // this wave's 32 key rows as MFMA B operands (k = head dim, j = key)
-  const int kslot = 2 * wave + (l32 >> 4);
-  int64_t mypage = opage[0];
-  uint32_t mykm = okm[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j)
-    if (kslot == j) {
-      mypage = opage[j];
-      mykm = okm[j];
-    }
-  const bool kvalid = (mykm >> (l32 & 15)) & 1u;
-  bf16x8 kreg[DS], vreg[DS];
-  {
-    const bf16x8 *kr = (const bf16x8 *)(kh + (mypage * 16 + (l32 & 15)) * (D * 2));
-    const bf16x8 *vr = (const bf16x8 *)(vh + (mypage * 16 + (l32 & 15)) * (D * 2));
+    const bf16x8 *qp = (const bf16x8 *)((const char *)a.q + qrow * D * 2);
+    const bf16x8 *gp = (const bf16x8 *)((const char *)a.dout + qrow * D * 2);
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      kreg[s] = kr[2 * s + g];
-      vreg[s] = vr[2 * s + g];
+      qreg[s] = qok ? qp[2 * s + g] : bf16x8{};
+      greg[s] = qok ? gp[2 * s + g] : bf16x8{};
     }
   }
-
-  f32x16 dk[ND], dv[ND];
-#pragma unroll
-  for (int n = 0; n < ND; ++n) {
-    dk[n] = f32x16{};
-    dv[n] = f32x16{};
+  const float lse2 = qok ? a.lse2[qrow] : 0.f;
+  const float delta = qok ? a.delta[qrow] : 0.f;
+  if (n_tiles > 0) {
+    load_page<D, kSwzBoth>(kh, tile_page(walk, 0, wave), (lds_char *)smem, 16 * wave, lane);
+    load_page<D, kSwzRow>(vh, tile_page(walk, 0, wave), (lds_char *)smem + 2 * TILE_BYTES, 16 * wave, lane);
   }
-  const float c2 = a.scale_log2;
 
-  // lane-constant parts of LDS addresses
-  const int row_rd = l32;                                   // row reads: row = 32 qb + l32
-  const int tr_row = 4 * g + (sl >> 2);                     // tr reads: row offset inside 16 rows
-  const int tr_col = 2 * (mgrp & 1) + ((sl & 3) >> 1);      // tr reads: chunk inside 4 chunks
+  f32x16 dq[ND];
+#pragma unroll
+  for (int n = 0; n < ND; ++n) dq[n] = f32x16{};
+  const float c2 = a.scale_log2;
+  const int tr_row = 4 * g + (sl >> 2);
+  const int tr_col = 2 * (mgrp & 1) + ((sl & 3) >> 1);
   const int tr_byte = (sl & 1) * 8;
 
-  for (int st = 0; st < n_steps; ++st) {
+  auto sub_tile = [&](const lds_char *kt, const lds_char *vt, int tile, int half, bool masked)
+                      __attribute__((always_inline)) {
+    const int k0 = keyoff + 32 * half;  // first key row of the sub-tile in the tile
+    f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const bf16x8 kop = lds_read8(kt + chunk_off<kSwzBoth, D>(k0 + l32, 2 * s + g));
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[s], s_acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const bf16x8 vop = lds_read8(vt + chunk_off<kSwzRow, D>(k0 + l32, 2 * s + g));
+      dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, greg[s], dp_acc, 0, 0, 0);
+    }
+    uint32_t word = 0xFFFFFFFFu;
+    if (masked) word = vwords[tile * 4 + (k0 >> 5)] >> (4 * g);
+    bf16x8 ds[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int bit = (r & 3) + 8 * ((r >> 2) & 1) + 16 * (r >> 3);
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c2, -lse2));
+      p = ((word >> bit) & 1u) ? p : 0.f;
+      ds[r >> 3][r & 7] = (__bf16)(p * (dp_acc[r] - delta));
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ra = k0 + 16 * hh + tr_row, rb = ra + 8;
+#pragma unroll
+      for (int n = 0; n < ND; ++n) {
+        const int c = 4 * n + tr_col;
+        const bf16x8 kop = tr_read8(kt + chunk_off<kSwzBoth, D>(ra, c) + tr_byte, kt + chunk_off<kSwzBoth, D>(rb, c) + tr_byte);
+        dq[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, ds[hh], dq[n], 0, 0, 0);
+      }
+    }
+  };
+  auto iter = [&](auto buf_c, auto, int t) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const int32_t pnext = tile_page(walk, min(t + 1, n_tiles - 1), wave);
     wait_vmcnt<0>();
-    wait_lgkm0();
-    barrier();
-    // per-step masks: adjacency word and row masks of the 8 query pages
-    const uint64_t adj = adjw[st];
-    uint32_t qm[8];
-    bool all_q = true;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qm[j] = qmasks[8 * st + j];
-      all_q = all_q && qm[j] == 0xFFFFu;
+    barrier();  // tile t resident; buffer 1 - BUF free
+    if (t + 1 < n_tiles) {
+      load_page<D, kSwzBoth>(kh, pnext, (lds_char *)smem + (1 - BUF) * TILE_BYTES, 16 * wave, lane);
+      load_page<D, kSwzRow>(vh, pnext, (lds_char *)smem + (3 - BUF) * TILE_BYTES, 16 * wave, lane);
     }
-    const bool all_valid = all_q && all_k && adj == ~0ull;
-    // per query page: rows of this lane's half (shifted by 4g) that pair with this lane's key
-    uint32_t pm[8];
+    const lds_char *kt = (const lds_char *)smem + BUF * TILE_BYTES;
+    const lds_char *vt = (const lds_char *)smem + (2 + BUF) * TILE_BYTES;
+    const bool masked = t >= full_tiles;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      pm[j] = (kvalid && ((adj >> (8 * j + kslot)) & 1ull)) ? (qm[j] >> (4 * g)) : 0u;
+    for (int h = 0; h < NH; ++h) sub_tile(kt, vt, t, h, masked);
+  };
+  for_range(ic<0>{}, 0, n_tiles, iter);
 
-#pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      // S = Q K^T and dP = dO V^T for query rows 32qb..32qb+31 (lane = key)
-      f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const int r = 32 * qb + row_rd;
-        const int off = r * (D * 2) + (((2 * s + g) ^ (swz(r) & (CH - 1))) * 16);
-        const bf16x8 qop = *(const __attribute__((address_space(3))) bf16x8 *)((lds_char *)q_lds + off);
-        const bf16x8 gop = *(const __attribute__((address_space(3))) bf16x8 *)((lds_char *)g_lds + off);
-        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop, kreg[s], s_acc, 0, 0, 0);
-        dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gop, vreg[s], dp_acc, 0, 0, 0);
-      }
-      // P = exp(scale S - LSE) on valid pairs, dS = P (dP - D)
-      bf16x8 pb[2], sb[2];
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int q0 = 32 * qb + 8 * j4 + 4 * g;
-        const f32x4 l4 = *(const __attribute__((address_space(3))) f32x4 *)((lds_char *)lse_lds + q0 * 4);
-        const f32x4 d4 = *(const __attribute__((address_space(3))) f32x4 *)((lds_char *)del_lds + q0 * 4);
-        const int page = 2 * qb + (j4 >> 1);
-        const uint32_t bits = pm[page] >> (8 * (j4 & 1));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j4 + e;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c2, -l4[e]));
-          if (!all_valid && !((bits >> e) & 1u)) p = 0.f;
-          const float ds = p * (dp_acc[r] - d4[e]);
-          pb[r >> 3][r & 7] = (__bf16)p;
-          sb[r >> 3][r & 7] = (__bf16)ds;
-        }
-      }
-      // dS to LDS for dQ: row = key (32w + l32), columns = query rows
-      {
-        const int kr = 32 * wave + l32;
-#pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const int chunk = (4 * qb + j4) ^ swz(kr);
-          const bf16x4 v = {sb[j4 >> 1][4 * (j4 & 1)], sb[j4 >> 1][4 * (j4 & 1) + 1], sb[j4 >> 1][4 * (j4 & 1) + 2],
-                            sb[j4 >> 1][4 * (j4 & 1) + 3]};
-          *(__attribute__((address_space(3))) bf16x4 *)((lds_char *)s_lds + kr * 256 + chunk * 16 + g * 8) = v;
-        }
-      }
-      // dV += P^T dO and dK += dS^T Q over these 32 query rows
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int rbase = 32 * qb + 16 * hh + tr_row;
-#pragma unroll
-        for (int n = 0; n < ND; ++n) {
-          const int r0 = rbase, r1 = rbase + 8;
-          const int c0 = ((4 * n + tr_col) ^ (swz(r0) & (CH - 1))) * 16 + tr_byte;
-          const int c1 = ((4 * n + tr_col) ^ (swz(r1) & (CH - 1))) * 16 + tr_byte;
-          const bf16x8 gop = tr_read8((lds_char *)g_lds + r0 * (D * 2) + c0, (lds_char *)g_lds + r1 * (D * 2) + c1);
-          const bf16x8 qop = tr_read8((lds_char *)q_lds + r0 * (D * 2) + c0, (lds_char *)q_lds + r1 * (D * 2) + c1);
-          dv[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pb[hh], gop, dv[n], 0, 0, 0);
-          dk[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sb[hh], qop, dk[n], 0, 0, 0);
-        }
-      }
-    }
-    wait_lgkm0();
-    barrier();
-    if (st + 1 < n_steps)
-      load_qstep<D>(qh, gh, lse2h, delh, qpages + 8 * (st + 1), (lds_char *)q_lds, (lds_char *)g_lds,
-                    (lds_char *)lse_lds, (lds_char *)del_lds, wave, lane);
-
-    // dQ for query rows 32w..32w+31: A = dS (tr reads of the key-major dS tile), B = K (tr reads)
-    f32x16 dq[ND];
-#pragma unroll
-    for (int n = 0; n < ND; ++n) dq[n] = f32x16{};
-#pragma unroll
-    for (int ka = 0; ka < 4; ++ka)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r0 = 32 * ka + 16 * hh + tr_row, r1 = r0 + 8;
-        const int sc0 = ((4 * wave + tr_col) ^ swz(r0)) * 16 + tr_byte;
-        const int sc1 = ((4 * wave + tr_col) ^ swz(r1)) * 16 + tr_byte;
-        const bf16x8 sop = tr_read8((lds_char *)s_lds + r0 * 256 + sc0, (lds_char *)s_lds + r1 * 256 + sc1);
-#pragma unroll
-        for (int n = 0; n < ND; ++n) {
-          const int c0 = ((4 * n + tr_col) ^ (swz(r0) & (CH - 1))) * 16 + tr_byte;
-          const int c1 = ((4 * n + tr_col) ^ (swz(r1) & (CH - 1))) * 16 + tr_byte;
-          const bf16x8 kop = tr_read8((lds_char *)k_lds + r0 * (D * 2) + c0, (lds_char *)k_lds + r1 * (D * 2) + c1);
-          dq[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sop, kop, dq[n], 0, 0, 0);
-        }
-      }
-    // scatter-add into the fp32 accumulator by query page (rows without a token are skipped)
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int j = 2 * wave + half;
-      const uint32_t rows = qm[j] >> (4 * g);
-      float *dst = dqh + ((int64_t)qpages[8 * st + j] * 16 + 4 * g) * D + l32;
-#pragma unroll
-      for (int r8 = 0; r8 < 8; ++r8) {
-        const int r = 8 * half + r8;
-        const int rin = 8 * ((r8 >> 2) & 1) + (r8 & 3);  // row inside the page minus 4g
-        if ((rows >> rin) & 1u) {
-#pragma unroll
-          for (int n = 0; n < ND; ++n) unsafeAtomicAdd(dst + rin * D + 32 * n, dq[n][r]);
-        }
-      }
-    }
-  }
-
+  // ---- sum the waves that share query rows, then write dQ = scale * acc (bf16) ----
   wait_vmcnt<0>();
-  // dK (scaled) and dV to their pages; rows past the block's valid count and empty slots handled
+  barrier();
+  constexpr int PART_BYTES = 32 * D * 4;
+  {
+    lds_char *part = (lds_char *)smem + wave * PART_BYTES;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = 32 * wave + 8 * (r >> 2) + 4 * g + (r & 3);
-    const int slot = key >> 4;
-    const int rin = key & 15;
-    uint32_t km = okm[0];
-    int64_t page = opage[0];
+    for (int n = 0; n < ND; ++n)
 #pragma unroll
-    for (int j = 1; j < 8; ++j)
-      if (slot == j) {
-        km = okm[j];
-        page = opage[j];
+      for (int j = 0; j < 4; ++j) {
+        const int c4 = 8 * n + 2 * j + g;  // float4 chunk of d = 32n + 8j + 4g
+        const int phys = c4 ^ (l32 & (D / 4 - 1));
+        const f32x4 val = {dq[n][4 * j], dq[n][4 * j + 1], dq[n][4 * j + 2], dq[n][4 * j + 3]};
+        *(__attribute__((address_space(3))) f32x4 *)(part + (l32 * D + 4 * phys) * 4) = val;
       }
-    if (km == 0u) continue;  // empty owner slot
-    const bool ok = (km >> rin) & 1u;
-    __bf16 *kdst = (__bf16 *)a.dk + (bh * a.seq_kv + page * 16 + rin) * D + l32;
-    __bf16 *vdst = (__bf16 *)a.dv + (bh * a.seq_kv + page * 16 + rin) * D + l32;
+  }
+  barrier();
+  const int64_t orow0 = bh * a.seq_q + 128 * it.q;
+  const int vrows = cq < M ? cq : M;
+  constexpr int GROUPS = D / 8;
+  for (int u = tid; u < 128 * GROUPS; u += kThreads) {
+    const int row = u / GROUPS, grp = u % GROUPS;
+    float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (row < vrows) {
+      const int qr = row & 31, q_g = row >> 5;
+      for (int w = q_g; w < kWaves; w += NQG) {
+        const lds_char *pw = (const lds_char *)smem + w * PART_BYTES;
 #pragma unroll
-    for (int n = 0; n < ND; ++n) {
-      kdst[32 * n] = (__bf16)(ok ? dk[n][r] * a.scale : 0.f);
-      vdst[32 * n] = (__bf16)(ok ? dv[n][r] : 0.f);
+        for (int h = 0; h < 2; ++h) {
+          const int phys = (2 * grp + h) ^ (qr & (D / 4 - 1));
+          const f32x4 x = *(const __attribute__((address_space(3))) f32x4 *)(pw + (qr * D + 4 * phys) * 4);
+          acc8[4 * h] += x[0];
+          acc8[4 * h + 1] += x[1];
+          acc8[4 * h + 2] += x[2];
+          acc8[4 * h + 3] += x[3];
+        }
+      }
     }
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc8[e] * a.scale);
+    *(bf16x8 *)((char *)a.dq + ((orow0 + row) * D + 8 * grp) * 2) = out;
   }
 }
 
@@ -441,11 +516,14 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
   }
   if (a.n_items > 0) {
     if (t) t->before(4, stream);
-    hipLaunchKernelGGL(kpage_bwd_main<D>, dim3(a.n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(kpage_bwd_kv<D>, dim3(a.n_items), dim3(kThreads), 0, stream, a);
     if (t) t->after(4, stream);
   }
   if (t) t->before(5, stream);
-  hipLaunchKernelGGL(kpage_bwd_post<D>, dim3((unsigned)row_blocks), dim3(256), 0, stream, a);
+  if (a.n_fitems128 > 0)
+    hipLaunchKernelGGL((kpage_bwd_dq<D, 128>), dim3(a.n_fitems128), dim3(kThreads), 0, stream, a, a.fitems128);
+  if (a.n_fitems64 > 0)
+    hipLaunchKernelGGL((kpage_bwd_dq<D, 64>), dim3(a.n_fitems64), dim3(kThreads), 0, stream, a, a.fitems64);
   if (t) t->after(5, stream);
   return hipGetLastError();
 }

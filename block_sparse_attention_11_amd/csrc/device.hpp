@@ -44,17 +44,21 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   void *dq, *dk, *dv;
-  float *dq_acc;              // fp32 [BH, seq_q, d]
+  float *lse2;                // fp32 [BH, seq_q]: LSE * log2(e), 0 for rows without keys
   float *delta;               // fp32 [BH, seq_q]: rowsum(dO * O)
+  // K/V-owned pass (dK, dV)
   const BwdItem *items;
   const int32_t *owners;      // [n_own][8] page ids, -1 empty
   const uint32_t *owner_kmask;// [n_own][8] 16-bit row masks of the owner pages (0 for empty slots)
   const int32_t *qpages;      // Q-page walk entries, dummy slots point at a real page
-  const uint32_t *qmask;      // row mask per Q-page entry (0 for dummies)
   const uint64_t *adj;        // adjacency word per step
   const int32_t *uncovered;   // K/V pages outside every footprint, per slot
   const int64_t *uncovered_ptr;
-  const int32_t *q_valid;     // [slots][n_q]
+  // Q-owned pass (dQ): the forward work items and page walks of both routes
+  const FwdItem *fitems128, *fitems64;
+  const int32_t *pages;
+  const uint32_t *valid;
+  int32_t n_fitems128, n_fitems64;
   int64_t seq_q, seq_kv;
   int32_t n_items, heads, n_q, per_head, bh_count;
   int32_t max_uncovered;      // largest count of uncovered K/V pages over the graph slots

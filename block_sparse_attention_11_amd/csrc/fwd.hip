@@ -43,112 +43,16 @@
 // sub-tile exceeds it by more than 2^8 and rescales O and l then.
 #include <hip/hip_runtime.h>
 
-#include <utility>
-
 #include "device.hpp"
+#include "tile_common.hpp"
 
 namespace kpage {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-// read-only tables indexed by wave-uniform values: the constant address space lets
-// them go through scalar loads, which do not hold up the vector-memory counter
-typedef const __attribute__((address_space(4))) int32_t c_i32;
-typedef const __attribute__((address_space(4))) uint32_t c_u32;
-
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr float kNegInf = -__builtin_inff();
 constexpr float kLimit = 64.0f;  // fast kernel: largest rise of a score over the fixed maximum (base 2)
 constexpr float kRaise = 8.0f;   // exact kernel: raise the maximum only past this margin (base 2)
-
-// s_waitcnt immediates for gfx9: vmcnt[3:0] + vmcnt_hi[15:14], expcnt[6:4], lgkmcnt[11:8].
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
-
-// XOR swizzle of 16-byte chunks for V rows: rows 4i..4i+3 get 0, 6, 12, 10.  With
-// it a ds_read_b64_tr_b16 over 4 consecutive rows touches 8 (or 16) distinct
-// chunk slots, conflict-free for both 32- and 64-bank LDS.
-__device__ __forceinline__ int vswz(int row) { return (0xAC60 >> (4 * (row & 3))) & 0xF; }
-
-// max(a, b, c) as one v_max3_f32.  Written out because the compiler otherwise
-// canonicalises MFMA results (v_max x, x, x) before every fmaxf; the inputs here are
-// scores and -inf, never signalling NaNs.
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// Maximum of x over this lane and lane ^ 32 (v_permlane32_swap: a VALU op, no LDS).
-__device__ __forceinline__ float half_max(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
-}
-
-template <int V>
-struct ic {
-  static constexpr int value = V;
-};
-
-// Page `wave` of tile `tile`: the page this wave copies (one scalar load).
-__device__ __forceinline__ int32_t tile_page(c_i32 *walk, int tile, int wave) { return walk[8 * tile + wave]; }
-
-// This wave's page (rows 16 wave .. 16 wave + 15) of one tile of K or V, global ->
-// LDS, 16 bytes per lane.  K chunks are swizzled by row & (CH - 1), V chunks by
-// vswz(row).
-template <int D, bool IS_V>
-__device__ __forceinline__ void load_page(const char *src, int32_t page, lds_char *dst, int wave, int lane) {
-  constexpr int CH = D / 8;                    // 16-byte chunks per row
-  constexpr int PER_WAVE = 16 * CH / 64;       // direct loads per wave
-  constexpr int ROWS_PER_INST = 64 / CH;
-  const char *pbase = src + (int64_t)page * (16 * D * 2);  // wave-uniform: scalar base address
-#pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int inst = wave * PER_WAVE + i;      // wave-uniform
-    const int row = inst * ROWS_PER_INST + lane / CH;
-    const int pos = lane % CH;
-    const int c = IS_V ? pos ^ (vswz(row) & (CH - 1)) : pos ^ (row & (CH - 1));
-    const uint32_t off = (uint32_t)((row & 15) * (D * 2) + c * 16);
-    __builtin_amdgcn_global_load_lds((const void *)(pbase + off), (lds_char *)(dst + inst * 1024), 16, 0, 0);
-  }
-}
-
-// Runs body(parity, flag, x) for x in [a, b), with parity = x & 1 as a compile-time
-// value, so that LDS double buffers are addressed with constants.
-template <class Flag, class Body>
-__device__ __forceinline__ void for_range(Flag flag, int a, int b, Body &&body) {
-  int x = a;
-  if ((x & 1) && x < b) {
-    body(ic<1>{}, flag, x);
-    ++x;
-  }
-  for (; x + 1 < b; x += 2) {
-    body(ic<0>{}, flag, x);
-    body(ic<1>{}, flag, x + 1);
-  }
-  if (x < b) body(ic<0>{}, flag, x);
-}
-
-template <int... I, class F>
-__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F &&f) {
-  (f(ic<I>{}), ...);
-}
-// f(ic<0>{}), ..., f(ic<N-1>{}): every index is a compile-time constant.
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-  static_for_impl(std::make_integer_sequence<int, N>{}, f);
-}
 
 // MASK values of a sub-iteration: no masking, a runtime check, or masking always.
 constexpr int kMaskNone = 0, kMaskCheck = 1, kMaskAlways = 2;
@@ -208,9 +112,9 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
       qreg[s] = x;
     }
   }
-  if (n_tiles > 0) load_page<D, false>(kh, tile_page(walk, 0, wave), (lds_char *)kbuf0, wave, lane);
-  if (n_tiles > 1) load_page<D, false>(kh, tile_page(walk, 1, wave), (lds_char *)kbuf1, wave, lane);
-  if (ROUTE == 128 && n_tiles > 0) load_page<D, true>(vh, tile_page(walk, 0, wave), (lds_char *)vbuf0, wave, lane);
+  if (n_tiles > 0) load_page<D, kSwzRow>(kh, tile_page(walk, 0, wave), (lds_char *)kbuf0, 16 * wave, lane);
+  if (n_tiles > 1) load_page<D, kSwzRow>(kh, tile_page(walk, 1, wave), (lds_char *)kbuf1, 16 * wave, lane);
+  if (ROUTE == 128 && n_tiles > 0) load_page<D, kSwzTr>(vh, tile_page(walk, 0, wave), (lds_char *)vbuf0, 16 * wave, lane);
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -444,8 +348,8 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
         const int32_t vp = tile_page(walk, t + 1, wave);
         wait_vmcnt<0>();
         barrier();
-        if (t + 2 < n_tiles) load_page<D, false>(kh, kp, (lds_char *)(PT ? kbuf1 : kbuf0), wave, lane);
-        load_page<D, true>(vh, vp, (lds_char *)(PT ? vbuf0 : vbuf1), wave, lane);
+        if (t + 2 < n_tiles) load_page<D, kSwzRow>(kh, kp, (lds_char *)(PT ? kbuf1 : kbuf0), 16 * wave, lane);
+        load_page<D, kSwzTr>(vh, vp, (lds_char *)(PT ? vbuf0 : vbuf1), 16 * wave, lane);
         const lds_char *knext = PT ? K0 : K1;  // K_{t+1}
         const lds_char *vcur = PT ? V1 : V0;   // V_t
         step(T, T, ic<1>{}, masking, knext, vcur, 2 * t + 1);
@@ -471,8 +375,8 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
       qk(K0, 0, sacc[0]);
       wait_vmcnt<0>();
       barrier();
-      if (n_sub > 2) load_page<D, false>(kh, tile_page(walk, 2, wave), (lds_char *)kbuf0, wave, lane);
-      load_page<D, true>(vh, tile_page(walk, 0, wave), (lds_char *)vbuf0, wave, lane);
+      if (n_sub > 2) load_page<D, kSwzRow>(kh, tile_page(walk, 2, wave), (lds_char *)kbuf0, 16 * wave, lane);
+      load_page<D, kSwzTr>(vh, tile_page(walk, 0, wave), (lds_char *)vbuf0, 16 * wave, lane);
       if (n_sub > 1) {
         step(T, F, ic<0>{}, ic<kMaskCheck>{}, K1, V1, 0);
         auto sub = [&](auto par, auto masking, int i) __attribute__((always_inline)) {
@@ -481,8 +385,8 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
           const int32_t vp = tile_page(walk, i, wave);
           wait_vmcnt<0>();
           barrier();
-          if (i + 2 < n_sub) load_page<D, false>(kh, kp, (lds_char *)(PI ? kbuf1 : kbuf0), wave, lane);
-          load_page<D, true>(vh, vp, (lds_char *)(PI ? vbuf1 : vbuf0), wave, lane);
+          if (i + 2 < n_sub) load_page<D, kSwzRow>(kh, kp, (lds_char *)(PI ? kbuf1 : kbuf0), 16 * wave, lane);
+          load_page<D, kSwzTr>(vh, vp, (lds_char *)(PI ? vbuf1 : vbuf0), 16 * wave, lane);
           step(T, T, par, masking, PI ? K0 : K1, PI ? V0 : V1, i);
         };
         const int split = min(max(full_tiles, 1), n_sub - 1);
@@ -492,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
         const int i = n_sub - 1;
         wait_vmcnt<0>();
         barrier();
-        load_page<D, true>(vh, tile_page(walk, i, wave), (lds_char *)((i & 1) ? vbuf1 : vbuf0), wave, lane);
+        load_page<D, kSwzTr>(vh, tile_page(walk, i, wave), (lds_char *)((i & 1) ? vbuf1 : vbuf0), 16 * wave, lane);
         if (i & 1) step(F, T, ic<1>{}, ic<kMaskCheck>{}, K0, V0, i);
         else step(F, T, ic<0>{}, ic<kMaskCheck>{}, K0, V1, i);
       } else {

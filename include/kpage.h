@@ -122,17 +122,26 @@ kpage_status kpage_plan_upload(kpage_plan_t *plan, void *stream);
 kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, const void *v,
                             void *o, float *lse, float softmax_scale, void *stream);
 
-/* Bytes of device workspace kpage_attn_bwd needs (fp32 dQ accumulator and row sums). */
+/* Bytes of device workspace kpage_attn_bwd needs: two fp32 values per query row
+ * (LSE * log2(e) and rowsum(dO * O)), i.e. 8 * batch * heads * seq_q. */
 kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes);
 
 /*
  * Backward attention, section 3.3: gradients of sum(O * dO) under the forward
- * definition, computed over K/V-owned tiles (owners of 8 Page16 slots, no
- * logical block crossing an owner), their reverse-Q neighbourhoods packed into
- * 8-page Q steps, and one 64-bit page-pair adjacency word per step that
- * restores the original graph.  The backward metadata is built on the first
- * call (lazily, section 3.4).  o and lse are the forward outputs; workspace is
- * a caller-owned device buffer of at least kpage_bwd_workspace_size() bytes.
+ * definition.  dK and dV are computed over K/V-owned tiles (owners of 8 Page16
+ * slots, no logical block crossing an owner), their reverse-Q neighbourhoods
+ * packed into 8-page Q steps, and one 64-bit page-pair adjacency word per step
+ * that restores the original graph.  dQ is computed by a Q-owned pass over the
+ * forward page walks (each query block recomputes its scores), so every output
+ * row is written by exactly one workgroup and all three gradients are
+ * deterministic.  The backward metadata is built on the first call (lazily,
+ * section 3.4).  o and lse are the forward outputs: a query row with
+ * LSE = -inf (invalid, or without a valid key) contributes nothing, which is how
+ * query-block sizes reach the kernels.  Every row of Q and dO must hold finite
+ * values, padded rows included (they meet zero weights inside the products).
+ * workspace is a caller-owned device buffer of at least
+ * kpage_bwd_workspace_size() bytes, 4-byte aligned; at most 2^29 query rows
+ * (batch * heads * seq_q) per call.
  * Invalid rows of dQ (by Q sizes) and of dK/dV (by K/V sizes), and rows of
  * blocks with no edge, are written as 0.
  */
@@ -189,10 +198,10 @@ void kpage_plan_destroy(kpage_plan_t *plan);
 enum {
   KPAGE_K_FWD_Q128 = 0,  /* forward, M128 x N128 route                            */
   KPAGE_K_FWD_Q64 = 1,   /* forward, M64 x N256 route and empty-block cleanup      */
-  KPAGE_K_BWD_PRE = 2,   /* rowsum(dO * O), scaled LSE, dQ accumulator clear       */
+  KPAGE_K_BWD_PRE = 2,   /* rowsum(dO * O) and LSE * log2(e) per query row         */
   KPAGE_K_BWD_ZERO = 3,  /* dK/dV pages outside every block footprint              */
-  KPAGE_K_BWD_MAIN = 4,  /* K/V-owned backward                                      */
-  KPAGE_K_BWD_POST = 5,  /* dQ accumulator to bf16                                  */
+  KPAGE_K_BWD_KV = 4,    /* K/V-owned pass: dK, dV                                  */
+  KPAGE_K_BWD_DQ = 5,    /* Q-owned pass over the forward walks (both routes): dQ  */
   KPAGE_K_COUNT = 6
 };
 kpage_status kpage_timing_enable(kpage_plan_t *plan, int enable);
