@@ -53,6 +53,26 @@ def _cpu_baseline(heads=(0, 1, 2, 3)):
     }
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bwd_3d_padded_h40.json")
+
+
+def _measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE counter
+    summary (already scaled by the copy calibration), or None when the kernel's sources
+    changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for name in rec["sources"]:
+        with open(os.path.join(ROOT, "block_sparse_attention_11_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def _copy_calibration(mib):
     import torch
     n = mib << 20
@@ -144,7 +164,7 @@ def main():
     achieved = per_pair * d * pairs / (dom_avg * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "avg_ms": round(dom_avg, 4), "launches": dom_n,
+                "traffic": _measured_traffic(dom), "traffic_unit": "HBM bytes per launch (counters)", "avg_ms": round(dom_avg, 4), "launches": dom_n,
                 "algorithmic": f"{per_pair}*d*useful_pairs per launch"}
 
     out = {
