@@ -74,40 +74,41 @@ __global__ __launch_bounds__(256) void kpage_bwd_zero(BwdArgs a, int64_t pages_p
 }
 
 // ---------------------------------------------------------------------------
-// K/V-owned pass.  Wave w owns key rows 32 (w & 3) .. + 31 of the owner (owner
-// slots 2 (w & 3) and 2 (w & 3) + 1) and query rows 64 (w >> 2) .. + 63 of every
-// step.  Its K and V rows stay in VGPRs as MFMA B operands and its dK and dV are
-// accumulators; the two waves of a key group are summed at the end.
+// K/V-owned pass.  One workgroup of 4 waves per (b*h, owner), two workgroups per CU
+// (so the two waves sharing a SIMD belong to different workgroups and drift apart:
+// one's softmax work overlaps the other's MFMAs).  Wave w owns key rows 32 w .. + 31
+// of the owner (owner slots 2 w, 2 w + 1): its K and V rows stay in VGPRs as MFMA B
+// operands and its dK and dV are accumulators.  Each 8-page query step runs as two
+// half-steps of 4 Q pages (64 query rows), double-buffered in LDS.
 //
 // Per 32-query block: S = Q K^T and dP = dO V^T with the lane index over keys and
 // the register index over queries (A = Q / dO rows read from LDS), so P^T and
 // dS^T are directly the A operands of dV += P^T dO and dK += dS^T Q, whose B
 // operands (columns of dO and Q) are transposed LDS reads of the same tiles.
+constexpr int kKvWaves = 4;
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void kpage_bwd_kv(BwdArgs a) {
+__global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
   constexpr int DS = D / 16;
   constexpr int ND = D / 32;
-  constexpr int TILE = 128 * D * 2;      // one 128-row tile of Q or dO
-  constexpr int STATS = kWaves * 256;    // per step: 64 floats per wave (lse2, delta, spare)
+  constexpr int TILE = 64 * D * 2;        // one half-step tile (4 pages) of Q or dO
+  constexpr int STATS = kKvWaves * 256;   // per half-step: 64 floats per page (lse2, delta, spare)
 
-  // step buffers: [Q 0][dO 0][Q 1][dO 1], then the two stats buffers; at the end the
-  // dK/dV partials of the waves with w >= 4
+  // half-step buffers [Q 0][dO 0][Q 1][dO 1] (every offset fits a ds_read immediate)
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
   __shared__ __attribute__((aligned(256))) char stats[2 * STATS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // key group: slots 2 w, 2 w + 1
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int sl = lane & 15;
   const int mgrp = lane >> 4;
-  const int kg = wave & 3;   // key group: owner slots 2 kg, 2 kg + 1
-  const int qh = wave >> 2;  // query half of each step
 
   const BwdItem it = a.items[blockIdx.x];
   const int64_t bh = it.bh;
-  const int n_steps = it.n_steps;
+  const int n_half = 2 * it.n_steps;
   c_i32 *own = (c_i32 *)(a.owners + (int64_t)it.owner * 8);
   c_u32 *kmk = (c_u32 *)(a.owner_kmask + (int64_t)it.owner * 8);
   c_i32 *qpages = (c_i32 *)(a.qpages + it.qwalk_off);
@@ -121,9 +122,10 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_kv(BwdArgs a) {
   const uint32_t stat_off =
       (uint32_t)(lane & 15) * 4 + ((lane >> 4) & 1) * (uint32_t)((const char *)a.delta - (const char *)a.lse2);
 
-  // step st: Q and dO pages (one page of each per wave), lse2 and delta of that page
-  auto load_step = [&](int st, int buf) __attribute__((always_inline)) {
-    const int32_t page = qpages[8 * st + wave];
+  // half-step u (pages 4 (u & 1) .. + 3 of step u / 2): one Q and one dO page per wave,
+  // and the page's lse2 and delta
+  auto load_half = [&](int u, int buf) __attribute__((always_inline)) {
+    const int32_t page = qpages[4 * u + wave];
     lds_char *qt = (lds_char *)smem + (2 * buf) * TILE;
     lds_char *gt = (lds_char *)smem + (2 * buf + 1) * TILE;
     load_page<D, kSwzBoth>(qgl, page, qt, 16 * wave, lane);
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_kv(BwdArgs a) {
 
   // this wave's 32 key rows as MFMA B operands (k = head dim, n = key)
   const int khalf = l32 >> 4;
-  const int kslot = 2 * kg + khalf;
+  const int kslot = 2 * wave + khalf;
   const int32_t mypage_raw = own[kslot];
   const int32_t mypage = mypage_raw >= 0 ? mypage_raw : own[0];  // empty slots read finite data, masked below
   const uint32_t mykm = kmk[kslot];
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_kv(BwdArgs a) {
       vreg[s] = vr[2 * s + g];
     }
   }
-  if (n_steps > 0) load_step(0, 0);
+  if (n_half > 0) load_half(0, 0);
 
   f32x16 dk[ND], dv[ND];
 #pragma unroll
@@ -161,27 +163,29 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_kv(BwdArgs a) {
     dv[n] = f32x16{};
   }
   const float c2 = a.scale_log2;
-  // Lane-constant LDS offsets inside a Q or dO tile.  Row reads of row 64 qh + l32 at
-  // k-step s sit at rd_base ^ 32 s (the swizzle only flips chunk bits); transposed
-  // reads of rows 64 qh + tr_row (+ 8) at head-dim block n sit at tr_base ^ 64 n (and
-  // that + 8 rows, chunk bit 2 flipped).  Query block and buffer are immediates.
-  const int rd_base = chunk_off<kSwzBoth, D>(64 * qh + l32, g);
-  const int tr_base = chunk_off<kSwzBoth, D>(64 * qh + 4 * g + (sl >> 2), 2 * (mgrp & 1) + ((sl & 3) >> 1)) + (sl & 1) * 8;
+  // Lane-constant LDS offsets inside a Q or dO tile.  Row reads of row l32 of a
+  // 32-query block at k-step s sit at rd_base ^ 32 s (the swizzle only flips chunk
+  // bits, and it repeats every 16 rows); transposed reads of rows tr_row and
+  // tr_row + 8 of a 16-row group at head-dim block n sit at tr_base ^ 64 n and at
+  // (tr_base ^ 64 (n ^ 1)) + 8 rows.  Query block, buffer and tile are immediates.
+  const int rd_base = chunk_off<kSwzBoth, D>(l32, g);
+  const int tr_base = chunk_off<kSwzBoth, D>(4 * g + (sl >> 2), 2 * (mgrp & 1) + ((sl & 3) >> 1)) + (sl & 1) * 8;
 
-  auto step = [&](auto buf_c, int st) __attribute__((always_inline)) {
+  auto half_step = [&](auto buf_c, int u) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_c)::value;
     const lds_char *qt = (const lds_char *)smem + (2 * BUF) * TILE;
     const lds_char *gt = (const lds_char *)smem + (2 * BUF + 1) * TILE;
-    // Pair mask of this step.  Query rows without a valid key, invalid rows included,
-    // have lse2 = +inf and drop out by themselves; what is left is key validity and
-    // the adjacency bit of (query page 4 qh + j, this lane's key slot), applied as a
-    // 0 / -inf bias on the exponent.
-    // (the two adjacency bits of this key group are wave-uniform: pick per lane half)
-    const uint64_t adj = adjw[st];
+    // Pair mask.  Query rows without a valid key, invalid rows included, have
+    // lse2 = +inf and drop out by themselves; what is left is key validity and the
+    // adjacency bit of (query page 4 (u & 1) + j, this lane's key slot), applied as a
+    // 0 / -inf bias on the exponent.  The two bits of this key group are
+    // wave-uniform: pick per lane half.
+    const uint64_t adj = adjw[u >> 1];
+    const int jbase = 4 * (u & 1);
     float nbias[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t two = (uint32_t)(adj >> (8 * (4 * qh + j) + 2 * kg)) & 3u;
+      const uint32_t two = (uint32_t)(adj >> (8 * (jbase + j) + 2 * wave)) & 3u;
       nbias[j] = (kvalid && ((two >> khalf) & 1u)) ? 0.f : kNegInf;
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -189,12 +193,12 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_kv(BwdArgs a) {
       constexpr int QB = decltype(qb_c)::value;
       constexpr int RB = 32 * QB * D * 2;  // byte offset of the query block
       // Register r of a 32 x 32 score block holds query row 32 qb + 8 (r / 4) + 4 g +
-      // r % 4 of the wave's 64 rows; group j4 = r / 4 reads its 4 lse2 / delta values
-      // as one f32x4 from the stats buffer.
+      // r % 4 of the half-step; group j4 = r / 4 reads its 4 lse2 / delta values as one
+      // f32x4 from the stats buffer.
       auto stat4 = [&](int j4, int which) __attribute__((always_inline)) {
         const int q = 32 * QB + 8 * j4 + 4 * g;
         const int pg = q >> 4, rin = q & 15;
-        const lds_char *p4 = (const lds_char *)stats + BUF * STATS + ((4 * qh + pg) * 64 + rin) * 4 + which * 64;
+        const lds_char *p4 = (const lds_char *)stats + BUF * STATS + (pg * 64 + rin) * 4 + which * 64;
         return *(const __attribute__((address_space(3))) f32x4 *)p4;
       };
       // (A) S = Q K^T, operand reads two k-steps ahead; then P = exp2(scale log2e S -
@@ -228,8 +232,8 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_kv(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
       // (B) dP = dO V^T, then (C) dS = P (dP - D) as bf16 (the A operand of dK += dS^T Q).
-      // P enters dS as its bf16 value: the extra rounding is of the order of the final
-      // rounding of dS to bf16.
+      // P enters dS as its bf16 value (unpacked with one bit operation): the extra
+      // rounding is of the order of the final rounding of dS to bf16.
       {
         f32x16 dp = f32x16{};
         bf16x8 op[DS];
@@ -251,22 +255,27 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_kv(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * j4 + e;
-            sb[r >> 3][r & 7] = (__bf16)((float)pb[r >> 3][r & 7] * (dp[r] - d4[e]));
+            const uint32_t w = __builtin_bit_cast(u32x4, pb[r >> 3])[(r & 7) >> 1];
+            const float p = __builtin_bit_cast(float, (r & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - d4[e]));
           }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
       // (D) dV += P^T dO and dK += dS^T Q over these 32 query rows (B operands: columns
       // of dO and Q, transposed reads one product ahead)
+      int tro[ND];
+#pragma unroll
+      for (int n = 0; n < ND; ++n) tro[n] = xor_imm_v(tr_base, 64 * n);
       constexpr int NOPS = 2 * ND;
       bf16x8 gt_op[NOPS], qt_op[NOPS];
       auto rdt = [&](auto j_c) __attribute__((always_inline)) {
         constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
         constexpr int RH = RB + 16 * HH * D * 2;
-        const int oa = xor_imm<64 * N>(tr_base);
-        const int ob = xor_imm<64>(oa + 8 * D * 2);
-        gt_op[J] = tr_read8(gt + RH + oa, gt + RH + ob);
-        qt_op[J] = tr_read8(qt + RH + oa, qt + RH + ob);
+        const lds_char *ga = gt + RH + tro[N], *gb = gt + RH + 8 * D * 2 + tro[N ^ 1];
+        const lds_char *qa = qt + RH + tro[N], *qbp = qt + RH + 8 * D * 2 + tro[N ^ 1];
+        gt_op[J] = tr_read8(ga, gb);
+        qt_op[J] = tr_read8(qa, qbp);
       };
       rdt(ic<0>{});
       static_for<NOPS>([&](auto j_c) __attribute__((always_inline)) {
@@ -279,55 +288,32 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_kv(BwdArgs a) {
     });
   };
 
-  // one step per iteration; the next step's pages load while this one computes
-  auto iter = [&](auto buf_c, auto, int st) __attribute__((always_inline)) {
+  // one half-step per iteration; the next one's pages load while this one computes
+  auto iter = [&](auto buf_c, auto, int u) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_c)::value;
     wait_vmcnt<0>();
-    barrier();  // step st resident for every wave; nobody reads buffer 1 - BUF any more
-    if (st + 1 < n_steps) load_step(st + 1, 1 - BUF);
-    step(buf_c, st);
+    barrier();  // half-step u resident for every wave; nobody reads buffer 1 - BUF any more
+    if (u + 1 < n_half) load_half(u + 1, 1 - BUF);
+    half_step(buf_c, u);
   };
-  for_range(ic<0>{}, 0, n_steps, iter);
+  for_range(ic<0>{}, 0, n_half, iter);
 
-  // ---- sum the two query halves of each key group, then write dK (scaled) and dV ----
-  wait_vmcnt<0>();
-  barrier();
-  constexpr int PART = 32 * D * 4;  // one 32 x D fp32 block
-  float *part = (float *)((char *)smem + kg * 2 * PART);
-  if (qh == 1) {
+  // ---- write dK (scaled) and dV by page id ----
+  // lane = head-dim column, register r = key row acc_row(r, g) of the wave's 32 keys
 #pragma unroll
-    for (int n = 0; n < ND; ++n)
+  for (int r = 0; r < 16; ++r) {
+    const int key = 32 * wave + acc_row(r, g);
+    const int slot = key >> 4, rin = key & 15;
+    const uint32_t km = kmk[slot];
+    if (km == 0u) continue;  // empty owner slot
+    const int64_t page = own[slot];
+    const bool ok = (km >> rin) & 1u;
+    __bf16 *kdst = (__bf16 *)a.dk + (bh * a.seq_kv + page * 16 + rin) * D + l32;
+    __bf16 *vdst = (__bf16 *)a.dv + (bh * a.seq_kv + page * 16 + rin) * D + l32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        part[(n * 16 + r) * 64 + lane] = dk[n][r];
-        part[PART / 4 + (n * 16 + r) * 64 + lane] = dv[n][r];
-      }
-  }
-  barrier();
-  if (qh == 0) {
-#pragma unroll
-    for (int n = 0; n < ND; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dk[n][r] += part[(n * 16 + r) * 64 + lane];
-        dv[n][r] += part[PART / 4 + (n * 16 + r) * 64 + lane];
-      }
-    // lane = head-dim column, register r = key row acc_row(r, g) of the wave's 32 keys
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * kg + acc_row(r, g);
-      const int slot = key >> 4, rin = key & 15;
-      const uint32_t km = kmk[slot];
-      if (km == 0u) continue;  // empty owner slot
-      const int64_t page = own[slot];
-      const bool ok = (km >> rin) & 1u;
-      __bf16 *kdst = (__bf16 *)a.dk + (bh * a.seq_kv + page * 16 + rin) * D + l32;
-      __bf16 *vdst = (__bf16 *)a.dv + (bh * a.seq_kv + page * 16 + rin) * D + l32;
-#pragma unroll
-      for (int n = 0; n < ND; ++n) {
-        kdst[32 * n] = (__bf16)(ok ? dk[n][r] * a.scale : 0.f);
-        vdst[32 * n] = (__bf16)(ok ? dv[n][r] : 0.f);
-      }
+    for (int n = 0; n < ND; ++n) {
+      kdst[32 * n] = (__bf16)(ok ? dk[n][r] * a.scale : 0.f);
+      vdst[32 * n] = (__bf16)(ok ? dv[n][r] : 0.f);
     }
   }
 }
@@ -516,7 +502,7 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
   }
   if (a.n_items > 0) {
     if (t) t->before(4, stream);
-    hipLaunchKernelGGL(kpage_bwd_kv<D>, dim3(a.n_items), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(kpage_bwd_kv<D>, dim3(a.n_items), dim3(64 * kKvWaves), 0, stream, a);
     if (t) t->after(4, stream);
   }
   if (t) t->before(5, stream);

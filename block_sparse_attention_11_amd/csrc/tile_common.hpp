@@ -15,6 +15,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 // read-only tables indexed by wave-uniform values: the constant address space lets
 // them go through scalar loads, which do not hold up the vector-memory counter
@@ -108,6 +109,13 @@ constexpr bool swizzle_flip_is_uniform(int base, int n, int flip) {
   for (int r = 0; r < n; ++r)
     if ((swz_of<SWZ, CH>(base + r) ^ swz_of<SWZ, CH>(r)) != flip) return false;
   return true;
+}
+
+// x ^ imm (imm a run-time constant of the caller's unrolled loop) as an opaque VALU op.
+__device__ __forceinline__ int xor_imm_v(int x, int imm) {
+  int r;
+  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(imm), "v"(x));
+  return r;
 }
 
 // One page (16 rows) of a bf16 [rows, D] tensor, global -> LDS rows r0 .. r0 + 15 of a
