@@ -14,17 +14,18 @@ SOURCES = ["csrc/plan.cpp", "csrc/api.hip", "csrc/fwd.hip", "csrc/bwd.hip"]
 OUT = os.path.join(HERE, "libkpage.so")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep hipcc from forming packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
+# Per-source extras.  The backward kernels keep their long-lived dK/dV accumulators
+# in AGPRs by hand and want every other MFMA result in ordinary VGPRs, where the
+# softmax reads it (the default for kernels that may use AGPRs is the opposite).
+EXTRA = {"csrc/bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *FLAGS, "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc"),
-           *[os.path.join(HERE, s) for s in SOURCES], "-o", OUT + ".tmp"]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -33,6 +34,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (per-source flags), then link the library."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    inc = ["-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc")]
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        _run([hipcc, *FLAGS, *EXTRA.get(src, []), *inc, "-c", os.path.join(HERE, src), "-o", obj], verbose)
+        objs.append(obj)
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", OUT + ".tmp"], verbose)
     os.replace(OUT + ".tmp", OUT)
     return OUT
 

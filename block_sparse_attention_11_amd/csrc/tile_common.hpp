@@ -175,6 +175,24 @@ __device__ __forceinline__ float half_max(float x) {
   return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
+// acc += a * b (32 x 32 x 16 bf16 MFMA) with the accumulator pinned to AGPRs, for
+// long-lived accumulators that only MFMAs touch until the end of a kernel.  The
+// leading s_nop covers the VALU-write -> MFMA-read distance for a and b; the caller
+// runs acc_fence() before reading the accumulator with ordinary instructions.
+__device__ __forceinline__ void mfma_acc(f32x16 &acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last mfma_acc and the first ordinary read of its result.
+__device__ __forceinline__ void acc_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// Two floats to packed bf16 (round to nearest even), a in the low half: one
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 // Key row (0..31) inside a 32 x 32 MFMA result block of accumulator register r in
 // lane half g: rows 8 (r / 4) + 4 g + r % 4.
 __device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
