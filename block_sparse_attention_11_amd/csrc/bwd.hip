@@ -74,26 +74,25 @@ __global__ __launch_bounds__(256) void kpage_bwd_zero(BwdArgs a, int64_t pages_p
 }
 
 // ---------------------------------------------------------------------------
-// K/V-owned pass.  One workgroup of 2 waves per (b*h, owner), two workgroups per CU,
-// so every SIMD runs one wave with the whole 512-entry register file.  Wave w owns
-// key rows 64 w .. + 63 of the owner (owner slots 4 w .. 4 w + 3) as two 32-key
-// blocks: their K and V rows stay in registers as MFMA B operands, their dK and dV
-// are accumulators, and every Q / dO operand read from LDS feeds both key blocks.
-// Each 8-page query step runs as two half-steps of 4 Q pages (64 query rows),
-// double-buffered in LDS.
+// K/V-owned pass.  One workgroup of 4 waves per (b*h, owner), two workgroups per CU
+// (so the two waves sharing a SIMD belong to different workgroups and drift apart:
+// one's element-wise work overlaps the other's MFMAs).  Wave w owns key rows
+// 32 w .. + 31 of the owner (owner slots 2 w, 2 w + 1): its K and V rows stay in
+// VGPRs as MFMA B operands and its dK and dV are accumulators.  Each 8-page query
+// step runs as two half-steps of 4 Q pages (64 query rows), double-buffered in LDS.
 //
 // Per 32-query block: S = Q K^T and dP = dO V^T with the lane index over keys and
 // the register index over queries (A = Q / dO rows read from LDS), so P^T and
 // dS^T are directly the A operands of dV += P^T dO and dK += dS^T Q, whose B
 // operands (columns of dO and Q) are transposed LDS reads of the same tiles.
-constexpr int kKvWaves = 2;
+constexpr int kKvWaves = 4;
 
 template <int D>
-__global__ __launch_bounds__(64 * kKvWaves, 1) void kpage_bwd_kv(BwdArgs a) {
+__global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
   constexpr int DS = D / 16;
   constexpr int ND = D / 32;
-  constexpr int TILE = 64 * D * 2;  // one half-step tile (4 pages) of Q or dO
-  constexpr int STATS = 4 * 256;    // per half-step: 64 floats per page (lse2, delta, spare)
+  constexpr int TILE = 64 * D * 2;        // one half-step tile (4 pages) of Q or dO
+  constexpr int STATS = kKvWaves * 256;   // per half-step: 64 floats per page (lse2, delta, spare)
 
   // half-step buffers [Q 0][dO 0][Q 1][dO 1] (every offset fits a ds_read immediate)
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
@@ -101,7 +100,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void kpage_bwd_kv(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // key group: slots 2 w, 2 w + 1
   const int g = lane >> 5;
   const int l32 = lane & 31;
   const int sl = lane & 15;
@@ -124,71 +123,53 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void kpage_bwd_kv(BwdArgs a) {
   const uint32_t stat_off =
       (uint32_t)(lane & 15) * 4 + ((lane >> 4) & 1) * (uint32_t)((const char *)a.delta - (const char *)a.lse2);
 
-  // half-step u (pages 4 (u & 1) .. + 3 of step u / 2): wave w copies pages 2 w and
-  // 2 w + 1 of Q and of dO, and their lse2 and delta
-  auto load_half = [&](const int32_t *pages, int buf) __attribute__((always_inline)) {
+  // half-step u (pages 4 (u & 1) .. + 3 of step u / 2): one Q and one dO page per wave,
+  // and the page's lse2 and delta
+  auto load_half = [&](int32_t page, int buf) __attribute__((always_inline)) {
     lds_char *qt = (lds_char *)smem + (2 * buf) * TILE;
     lds_char *gt = (lds_char *)smem + (2 * buf + 1) * TILE;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int j = 2 * wave + i;
-      const int32_t page = pages[i];
-      load_page<D, kSwzBoth>(qgl, page, qt, 16 * j, lane);
-      load_page<D, kSwzBoth>(ggl, page, gt, 16 * j, lane);
-      // lanes 0-15: lse2 of the page's rows, 16-31: delta, 32-63: the same again
-      // (delta = lse2 + rows: one scalar base and a 32-bit lane offset)
-      const char *src = (const char *)(l2h + (int64_t)page * 16);
-      const uint32_t off = (uint32_t)xor_imm<0x40000000>(stat_off) ^ 0x40000000u;  // recomputed, not kept
-      __builtin_amdgcn_global_load_lds((const void *)(src + off), (lds_char *)(stats + buf * STATS + j * 256), 4, 0, 0);
-    }
+    load_page<D, kSwzBoth>(qgl, page, qt, 16 * wave, lane);
+    load_page<D, kSwzBoth>(ggl, page, gt, 16 * wave, lane);
+    // lanes 0-15: lse2 of the page's rows, 16-31: delta, 32-63: the same again
+    // (delta = lse2 + rows: one scalar base and a 32-bit lane offset)
+    const char *src = (const char *)(l2h + (int64_t)page * 16);
+    const uint32_t off = (uint32_t)xor_imm<0x40000000>(stat_off) ^ 0x40000000u;  // recomputed, not kept
+    __builtin_amdgcn_global_load_lds((const void *)(src + off), (lds_char *)(stats + buf * STATS + wave * 256), 4, 0, 0);
   };
 
-  // this wave's two 32-key blocks as MFMA B operands (k = head dim, n = key)
-  bf16x8 kreg[2][DS], vreg[2][DS];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int slot = 4 * wave + 2 * kb + khalf;
-    const int32_t page_raw = own[slot];
-    const int32_t page = page_raw >= 0 ? page_raw : own[0];  // empty slots read finite data, masked below
+  // this wave's 32 key rows as MFMA B operands (k = head dim, n = key).  Empty owner
+  // slots read finite data of slot 0; their results are never stored.
+  bf16x8 kreg[DS], vreg[DS];
+  {
+    const int32_t page_raw = own[2 * wave + khalf];
+    const int32_t page = page_raw >= 0 ? page_raw : own[0];
     const bf16x8 *kr = (const bf16x8 *)(kh + ((int64_t)page * 16 + (l32 & 15)) * (D * 2));
     const bf16x8 *vr = (const bf16x8 *)(vh + ((int64_t)page * 16 + (l32 & 15)) * (D * 2));
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      kreg[kb][s] = kr[2 * s + g];
-      vreg[kb][s] = vr[2 * s + g];
+      kreg[s] = kr[2 * s + g];
+      vreg[s] = vr[2 * s + g];
     }
   }
-  if (n_half > 0) {
-    const int32_t p0[2] = {qpages[2 * wave], qpages[2 * wave + 1]};
-    load_half(p0, 0);
-  }
+  if (n_half > 0) load_half(qpages[wave], 0);
 
-  f32x16 dk[2][ND], dv[2][ND];
+  f32x16 dk[ND], dv[ND];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int n = 0; n < ND; ++n) {
-      dk[kb][n] = f32x16{};
-      dv[kb][n] = f32x16{};
-    }
-  acc_fence();
+  for (int n = 0; n < ND; ++n) {
+    dk[n] = f32x16{};
+    dv[n] = f32x16{};
+  }
   const float c2 = a.scale_log2;
-  // Lane-constant LDS offsets inside a Q or dO tile (the query block, buffer and tile
-  // are immediates).  Row reads of row l32 of a 32-query block at k-step s sit at
-  // rd_base ^ 32 s (the swizzle only flips chunk bits and repeats every 16 rows).
-  // Transposed reads of rows tr_row and tr_row + 8 of a 16-row group at head-dim block
-  // n sit at tra[n] and at tra[n ^ 1] + 8 rows (row + 8 flips chunk bit 2).
-  const int rd_base = chunk_off<kSwzBoth, D>(l32, g);
-  int tra[ND];
-  {
-    const int tr_row = 4 * g + (sl >> 2);
-    const int tr_col = 2 * (mgrp & 1) + ((sl & 3) >> 1);
-#pragma unroll
-    for (int n = 0; n < ND; ++n) tra[n] = chunk_off<kSwzBoth, D>(tr_row, 4 * n + tr_col) + (sl & 1) * 8;
-  }
-
   // B operand of the extra dP k-step: ones in k = 0, 1 (lanes 0-31), zeros elsewhere
   const uint32_t ones_lo = g ? 0u : 0x3F803F80u;
+  // Lane-constant LDS offsets inside a Q or dO tile.  Row reads of row l32 of a
+  // 32-query block at k-step s sit at rd_base ^ 32 s (the swizzle only flips chunk
+  // bits and repeats every 16 rows).  Transposed reads of rows tr_row and tr_row + 8
+  // of a 16-row group at head-dim block n sit at tr_base ^ 64 n and at
+  // (tr_base ^ 64 (n ^ 1)) + 8 rows (row + 8 flips chunk bit 2).  Query block,
+  // buffer and tile are immediates.
+  const int rd_base = chunk_off<kSwzBoth, D>(l32, g);
+  const int tr_base = chunk_off<kSwzBoth, D>(4 * g + (sl >> 2), 2 * (mgrp & 1) + ((sl & 3) >> 1)) + (sl & 1) * 8;
 
   auto half_step = [&](auto buf_c, int u, uint64_t adj) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_c)::value;
@@ -200,28 +181,14 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void kpage_bwd_kv(BwdArgs a) {
     // and dS of an invalid key reach only that key's own dK / dV rows, which are
     // written as 0.  What is left is the adjacency bit of (query page, key slot); it
     // is all ones on almost every step, so the zeroing of non-edge P blocks runs in a
-    // wave-uniform branch.  The 4 bits of this wave's slots for page j sit at bit
-    // 8 (4 (u & 1) + j) + 4 w of the step's word.
+    // wave-uniform branch.  The 2 bits of this wave's slots for page j sit at bit
+    // 8 (4 (u & 1) + j) + 2 w of the step's word.
     const int jbase = 4 * (u & 1);
-    uint32_t nib = 0xFFFFu;  // 4 bits per page of the half-step
+    uint32_t nib = 0xFFu;  // 2 bits per page of the half-step
 #pragma unroll
-    for (int j = 0; j < 4; ++j) nib &= ~((~(uint32_t)(adj >> (8 * (jbase + j) + 4 * wave)) & 0xFu) << (4 * j));
-    const bool all_edges = nib == 0xFFFFu;
-
-    // operand rotation: op[s] holds what the next MFMA slot s consumes; each slot
-    // refills it for the phase after next (LDS latency hides behind ~8 MFMAs)
-    bf16x8 op[DS];
-    auto rd_row = [&](const lds_char *t, int rb, auto s_c) __attribute__((always_inline)) {
-      constexpr int S = decltype(s_c)::value;
-      op[S] = lds_read8(t + rb + xor_imm<32 * S>(rd_base));
-    };
-    auto rd_tr = [&](const lds_char *t, int rb, auto j_c) __attribute__((always_inline)) {
-      constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
-      const lds_char *p = t + rb + 16 * HH * D * 2;
-      op[J] = tr_read8(p + tra[N], p + 8 * D * 2 + tra[N ^ 1]);
-    };
-    static_for<DS>([&](auto s_c) __attribute__((always_inline)) { rd_row(qt, 0, s_c); });
-
+    for (int j = 0; j < 4; ++j) nib &= ~((~(uint32_t)(adj >> (8 * (jbase + j) + 2 * wave)) & 0x3u) << (2 * j));
+    const bool all_edges = nib == 0xFFu;
+    __builtin_amdgcn_sched_barrier(0);
     static_for<2>([&](auto qb_c) __attribute__((always_inline)) {
       constexpr int QB = decltype(qb_c)::value;
       constexpr int RB = 32 * QB * D * 2;  // byte offset of the query block
@@ -231,127 +198,103 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void kpage_bwd_kv(BwdArgs a) {
         const int q = 32 * QB + 8 * j4 + 4 * g;
         return *(const __attribute__((address_space(3))) f32x4 *)(stb + ((q >> 4) * 64 + (q & 15)) * 4);
       };
-      // The four score-sized products run as separate MFMA chains so that the
-      // element-wise work of one key block hides under the MFMAs of the next:
-      //   T1  S0 = Q K0^T
-      //   T2  S1 = Q K1^T                 | P0 = exp2(scale log2e S0 - lse2)
-      //   T3  dP0 - D = dO V0^T - D       | P1
-      //   T4  dP1 - D                     | dS0 = P0 (dP0 - D)
-      //   T5  dV0, dV1 += P^T dO          | dS1
-      //   T6  dK0, dK1 += dS^T Q
-      // D enters the dP chains as one extra k-step (A = -D split into two bf16,
-      // B = ones), so dS costs one multiply per element.  P and dS are kept as bf16
-      // (A operands of the dV / dK products); P enters dS as its bf16 value, an extra
-      // rounding of the order of dS's own.  Each MFMA slot of T2..T5 carries 16 / (D /
-      // 16) elements of the element-wise work.
-      constexpr int PPS = 8 / DS;  // element pairs per MFMA slot
-      f32x16 acc0, acc1;
-      // P and dS blocks as packed bf16 pairs (hh = rows 16 hh .. + 15 of the block)
-      u32x4 pb0[2], pb1[2], sb0[2], sb1[2];
-      f32x4 st4, st4n;
-      auto p_pair = [&](const f32x16 &sc, u32x4 *dst, auto i_c) __attribute__((always_inline)) {
-        constexpr int I = decltype(i_c)::value, J4 = I / 2;
-        if constexpr (I % 2 == 0) {
-          st4 = st4n;
-          if constexpr (J4 + 1 < 4) st4n = lse4(J4 + 1);
-        }
-        constexpr int E = 2 * (I % 2), R = 4 * J4 + E;
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[R], c2, -st4[E]));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[R + 1], c2, -st4[E + 1]));
-        dst[R >> 3][(R & 7) >> 1] = pack_bf16(p0, p1);
-      };
-      auto ds_pair = [&](const f32x16 &dpd, const u32x4 *pp, u32x4 *dst, auto i_c) __attribute__((always_inline)) {
-        constexpr int I = decltype(i_c)::value;
-        constexpr int R = 2 * I;
-        const uint32_t w = pp[R >> 3][(R & 7) >> 1];
-        const float p0 = __builtin_bit_cast(float, w << 16), p1 = __builtin_bit_cast(float, w & 0xFFFF0000u);
-        dst[R >> 3][(R & 7) >> 1] = pack_bf16(p0 * dpd[R], p1 * dpd[R + 1]);
-      };
-      // zero the P blocks of non-edge (query page, key slot) pairs: pb[hh] holds the
-      // rows of page 2 qb + hh of the half-step
-      auto mask_p = [&](u32x4 *pbk, int kb) __attribute__((always_inline)) {
-        if (!all_edges) {
+      // P and dS as packed bf16 pairs (u32x4 [hh] = rows 16 hh .. + 15 of the block):
+      // the A operands of the dV / dK products
+      u32x4 pb[2], sb[2];
+      // (A) S = Q K^T, operand reads two k-steps ahead; then P = exp2(scale log2e S -
+      // lse2)
+      {
+        f32x16 sp;
+        bf16x8 op[DS];
+        auto rd = [&](auto s_c) __attribute__((always_inline)) {
+          constexpr int S = decltype(s_c)::value;
+          op[S] = lds_read8(qt + RB + xor_imm<32 * S>(rd_base));
+        };
+        rd(ic<0>{});
+        rd(ic<1>{});
+        static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
+          constexpr int S = decltype(s_c)::value;
+          if constexpr (S + 2 < DS) rd(ic<S + 2>{});
+          sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], kreg[S], S == 0 ? f32x16{} : sp, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const bool edge = (nib >> (4 * (2 * QB + hh) + 2 * kb + khalf)) & 1u;
-            if (!edge) pbk[hh] = u32x4{};
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const f32x4 l4 = lse4(j4);
+#pragma unroll
+          for (int e = 0; e < 4; e += 2) {
+            const int r = 4 * j4 + e;
+            pb[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sp[r], c2, -l4[e])),
+                                                        __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r + 1], c2, -l4[e + 1]))));
           }
         }
-      };
-      // A operand of the extra dP k-step: (-D split into bf16 hi + lo) in k = 0, 1 of
-      // lanes 0-31 for query row l32 of the block, zeros elsewhere
-      bf16x8 daug;
-      {
-        const int q = 32 * QB + l32;
-        const float nd = -*(const __attribute__((address_space(3))) float *)(stb + ((q >> 4) * 64 + 16 + (q & 15)) * 4);
-        const __bf16 hi = (__bf16)nd;
-        const __bf16 lo = (__bf16)(nd - (float)hi);
-        daug = bf16x8{hi, lo, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-        if (g) daug = bf16x8{};
+        // zero the P blocks of non-edge (query page, key slot) pairs: pb[hh] holds the
+        // rows of page 2 qb + hh of the half-step
+        if (!all_edges) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            if (!((nib >> (2 * (2 * QB + hh) + khalf)) & 1u)) pb[hh] = u32x4{};
+        }
       }
-      const bf16x8 vaug = __builtin_bit_cast(bf16x8, u32x4{ones_lo, 0u, 0u, 0u});
-
-      // T1: S0
-      static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_c)::value;
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], kreg[0][S], S == 0 ? f32x16{} : acc0, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      // T2: S1 | P0; refill with dO rows
-      st4n = lse4(0);
-      static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_c)::value;
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], kreg[1][S], S == 0 ? f32x16{} : acc1, 0, 0, 0);
-        rd_row(gt, RB, ic<S>{});
-        static_for<PPS>([&](auto k_c) { p_pair(acc0, pb0, ic<S * PPS + decltype(k_c)::value>{}); });
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      mask_p(pb0, 0);
-      // T3: dP0 - D | P1
-      st4n = lse4(0);
-      static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_c)::value;
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], vreg[0][S], S == 0 ? f32x16{} : acc0, 0, 0, 0);
-        static_for<PPS>([&](auto k_c) { p_pair(acc1, pb1, ic<S * PPS + decltype(k_c)::value>{}); });
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(daug, vaug, acc0, 0, 0, 0);
-      mask_p(pb1, 1);
       __builtin_amdgcn_sched_barrier(0);
-      // T4: dP1 - D | dS0; refill with transposed dO for T5 (one slot late, after the
-      // MFMA that read the register)
-      static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_c)::value;
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], vreg[1][S], S == 0 ? f32x16{} : acc1, 0, 0, 0);
-        if constexpr (S > 0) rd_tr(gt, RB, ic<S - 1>{});
-        static_for<PPS>([&](auto k_c) { ds_pair(acc0, pb0, sb0, ic<S * PPS + decltype(k_c)::value>{}); });
+      // (B) dP - D = dO V^T - D, with D as one extra k-step (A = -D split into bf16
+      // hi + lo in k = 0, 1 of lanes 0-31 for query row l32, B = ones), then (C)
+      // dS = P (dP - D).  P enters dS as its bf16 value, an extra rounding of the order
+      // of dS's own.
+      {
+        bf16x8 daug;
+        {
+          const int q = 32 * QB + l32;
+          const float nd = -*(const __attribute__((address_space(3))) float *)(stb + ((q >> 4) * 64 + 16 + (q & 15)) * 4);
+          const float hi = __builtin_bit_cast(float, pack_bf16(nd, 0.f) << 16);
+          const uint32_t w0 = g ? 0u : pack_bf16(hi, nd - hi);
+          daug = __builtin_bit_cast(bf16x8, u32x4{w0, 0u, 0u, 0u});
+        }
+        f32x16 dp;
+        bf16x8 op[DS];
+        auto rd = [&](auto s_c) __attribute__((always_inline)) {
+          constexpr int S = decltype(s_c)::value;
+          op[S] = lds_read8(gt + RB + xor_imm<32 * S>(rd_base));
+        };
+        rd(ic<0>{});
+        rd(ic<1>{});
+        static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
+          constexpr int S = decltype(s_c)::value;
+          if constexpr (S + 2 < DS) rd(ic<S + 2>{});
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], vreg[S], S == 0 ? f32x16{} : dp, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(daug, __builtin_bit_cast(bf16x8, u32x4{ones_lo, 0u, 0u, 0u}), dp,
+                                                     0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-      });
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(daug, vaug, acc1, 0, 0, 0);
-      rd_tr(gt, RB, ic<DS - 1>{});
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const uint32_t w = pb[r >> 3][(r & 7) >> 1];
+          sb[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(__builtin_bit_cast(float, w << 16) * dp[r],
+                                                      __builtin_bit_cast(float, w & 0xFFFF0000u) * dp[r + 1]));
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
-      // T5: dV0, dV1 += P^T dO | dS1; refill with transposed Q for T6
-      static_assert(2 * ND == DS, "one transposed operand per MFMA slot");
-      static_for<DS>([&](auto j_c) __attribute__((always_inline)) {
+      // (D) dV += P^T dO and dK += dS^T Q over these 32 query rows (B operands: columns
+      // of dO and Q, transposed reads one product ahead)
+      constexpr int NOPS = 2 * ND;
+      bf16x8 gt_op[NOPS], qt_op[NOPS];
+      auto rdt = [&](auto j_c) __attribute__((always_inline)) {
         constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
-        mfma_acc(dv[0][N], __builtin_bit_cast(bf16x8, pb0[HH]), op[J]);
-        mfma_acc(dv[1][N], __builtin_bit_cast(bf16x8, pb1[HH]), op[J]);
-        if constexpr (J > 0) rd_tr(qt, RB, ic<J - 1>{});
-        static_for<PPS>([&](auto k_c) { ds_pair(acc1, pb1, sb1, ic<J * PPS + decltype(k_c)::value>{}); });
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      rd_tr(qt, RB, ic<DS - 1>{});
-      __builtin_amdgcn_sched_barrier(0);
-      // T6: dK0, dK1 += dS^T Q; refill with the next query block's Q rows
-      static_for<DS>([&](auto j_c) __attribute__((always_inline)) {
+        constexpr int RH = RB + 16 * HH * D * 2;
+        const int oa = xor_imm<64 * N>(tr_base);
+        const int ob = xor_imm<64 * (N ^ 1)>(tr_base);
+        gt_op[J] = tr_read8(gt + RH + oa, gt + RH + 8 * D * 2 + ob);
+        qt_op[J] = tr_read8(qt + RH + oa, qt + RH + 8 * D * 2 + ob);
+      };
+      rdt(ic<0>{});
+      static_for<NOPS>([&](auto j_c) __attribute__((always_inline)) {
         constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
-        mfma_acc(dk[0][N], __builtin_bit_cast(bf16x8, sb0[HH]), op[J]);
-        mfma_acc(dk[1][N], __builtin_bit_cast(bf16x8, sb1[HH]), op[J]);
-        if constexpr (QB == 0 && J > 0) rd_row(qt, RB + 32 * D * 2, ic<J - 1>{});
+        if constexpr (J + 1 < NOPS) rdt(ic<J + 1>{});
+        dv[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pb[HH]), gt_op[J], dv[N], 0, 0, 0);
+        dk[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sb[HH]), qt_op[J], dk[N], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       });
-      if constexpr (QB == 0) rd_row(qt, RB + 32 * D * 2, ic<DS - 1>{});
-      __builtin_amdgcn_sched_barrier(0);
     });
   };
 
@@ -360,38 +303,34 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void kpage_bwd_kv(BwdArgs a) {
     constexpr int BUF = decltype(buf_c)::value;
     // scalar table reads first and complete, so that no scalar load is in flight
     // while the LDS reads of the half-step wait on their counter
-    const int un = min(u + 1, n_half - 1);
-    const int32_t pn[2] = {qpages[4 * un + 2 * wave], qpages[4 * un + 2 * wave + 1]};
+    const int32_t pn = qpages[4 * min(u + 1, n_half - 1) + wave];
     const uint64_t adj = adjw[u >> 1];
     wait_lgkm0();
     wait_vmcnt<0>();
-    barrier();  // half-step u resident for both waves; nobody reads buffer 1 - BUF any more
+    barrier();  // half-step u resident for every wave; nobody reads buffer 1 - BUF any more
     if (u + 1 < n_half) load_half(pn, 1 - BUF);
     half_step(buf_c, u, adj);
   };
   for_range(ic<0>{}, 0, n_half, iter);
 
   // ---- write dK (scaled) and dV by page id ----
-  // lane = head-dim column, register r = key row acc_row(r, g) of a 32-key block
-  acc_fence();
+  // lane = head-dim column, register r = key row acc_row(r, g) of the wave's 32 keys
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int r = 0; r < 16; ++r) {
+    const int key = 32 * wave + acc_row(r, g);
+    const int slot = key >> 4, rin = key & 15;
+    const uint32_t km = kmk[slot];
+    if (km == 0u) continue;  // empty owner slot
+    const int64_t page = own[slot];
+    const bool ok = (km >> rin) & 1u;
+    __bf16 *kdst = (__bf16 *)a.dk + (bh * a.seq_kv + page * 16 + rin) * D + l32;
+    __bf16 *vdst = (__bf16 *)a.dv + (bh * a.seq_kv + page * 16 + rin) * D + l32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 64 * wave + 32 * kb + acc_row(r, g);
-      const int slot = key >> 4, rin = key & 15;
-      const uint32_t km = kmk[slot];
-      if (km == 0u) continue;  // empty owner slot
-      const int64_t page = own[slot];
-      const bool ok = (km >> rin) & 1u;
-      __bf16 *kdst = (__bf16 *)a.dk + (bh * a.seq_kv + page * 16 + rin) * D + l32;
-      __bf16 *vdst = (__bf16 *)a.dv + (bh * a.seq_kv + page * 16 + rin) * D + l32;
-#pragma unroll
-      for (int n = 0; n < ND; ++n) {
-        kdst[32 * n] = (__bf16)(ok ? dk[kb][n][r] * a.scale : 0.f);
-        vdst[32 * n] = (__bf16)(ok ? dv[kb][n][r] : 0.f);
-      }
+    for (int n = 0; n < ND; ++n) {
+      kdst[32 * n] = (__bf16)(ok ? dk[n][r] * a.scale : 0.f);
+      vdst[32 * n] = (__bf16)(ok ? dv[n][r] : 0.f);
     }
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -137,8 +137,12 @@ __device__ __forceinline__ void load_page(const char *src, int32_t page, lds_cha
     constexpr int FLIP = swz_of<SWZ, CH>(I * ROWS_PER_INST) ^ swz_of<SWZ, CH>(0);
     static_assert(swizzle_flip_is_uniform<SWZ, CH>(I * ROWS_PER_INST, ROWS_PER_INST, FLIP),
                   "swizzle must be linear in the copy index");
-    const uint32_t off = (uint32_t)xor_imm<16 * FLIP>(off0) + I * ROWS_PER_INST * D * 2;
-    __builtin_amdgcn_global_load_lds((const void *)(pbase + off), (lds_char *)(tile + (r0 + I * ROWS_PER_INST) * D * 2),
+    // rows I * ROWS_PER_INST.. of the page: a scalar base, the lane offset unchanged
+    // but for constant chunk bits
+    const char *pi = pbase + I * ROWS_PER_INST * D * 2;
+    asm volatile("" : "+s"(pi));  // keep the base scalar: saddr + 32-bit lane offset
+    const uint32_t off = (uint32_t)xor_imm<16 * FLIP>(off0);
+    __builtin_amdgcn_global_load_lds((const void *)(pi + off), (lds_char *)(tile + (r0 + I * ROWS_PER_INST) * D * 2),
                                      16, 0, 0);
   });
 }
@@ -191,6 +195,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// x, materialised here: an empty volatile asm keeps IR passes from sinking the
+// computation of x past later control flow (the machine scheduler's fences do not
+// bind them), so element-wise work stays in the MFMA slot it was written for.
+__device__ __forceinline__ uint32_t pinned(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // Key row (0..31) inside a 32 x 32 MFMA result block of accumulator register r in

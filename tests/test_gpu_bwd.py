@@ -129,11 +129,12 @@ def test_bwd_independent_offsets_with_gaps():
     check_grads(got, ref, "offsets with gaps", p)
 
 
-def test_bwd_dk_dv_deterministic_dq_stable():
+def test_bwd_gradients_are_deterministic():
+    """Every gradient row is written by exactly one workgroup (no atomics): bitwise repeatable."""
     w = make_workload(3, heads=[0, 1], with_do=True)
     plan = K.kpage_plan(w)
     _say("[bwd] run-to-run")
     a = gpu_fwd_bwd(w, w.q, w.k, w.v, w.do, plan=plan)
     b = gpu_fwd_bwd(w, w.q, w.k, w.v, w.do, plan=plan)
-    assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
-    assert np.abs(a[0] - b[0]).max() <= 1e-2 * np.abs(a[0]).max()
+    for name, x, y in zip(("dQ", "dK", "dV"), a, b):
+        assert np.array_equal(x, y), name
