@@ -19,10 +19,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
-# Per-source extras.  The backward kernels keep their long-lived dK/dV accumulators
-# in AGPRs by hand and want every other MFMA result in ordinary VGPRs, where the
-# softmax reads it (the default for kernels that may use AGPRs is the opposite).
-EXTRA = {"csrc/bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source extras (none at present).
+EXTRA: dict = {}
 
 
 def _run(cmd, verbose):

@@ -16,8 +16,8 @@
 // and K reads and its memory bandwidth on fp32 atomics.
 //
 // Kernels:
-//   kpage_bwd_pre   D_i = sum_d dO_id O_id and LSE_i * log2(e) (0 for rows without
-//                   keys), 16 threads per row.
+//   kpage_bwd_pre   D_i = sum_d dO_id O_id and LSE_i * log2(e) (+inf for rows
+//                   without keys), 16 threads per row.
 //   kpage_bwd_zero  zero dK/dV pages that lie outside every block footprint.
 //   kpage_bwd_kv    one workgroup per (batch*head, owner): dK, dV.
 //   kpage_bwd_dq    one workgroup per forward work item (query block): dQ.
@@ -28,9 +28,6 @@
 
 namespace kpage {
 namespace {
-
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 
 // ---------------------------------------------------------------------------
 // pre: 16 threads per query row
@@ -334,27 +331,33 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Q-owned dQ pass over the forward page walks.  Same work split as the forward
-// kernel: 8 waves, each with 32 query rows and a key range of every 8-page tile
-// (M128: 4 query groups x 2 key halves, two 32-key sub-tiles per tile; M64: 2 x 4,
-// one sub-tile).  Per sub-tile, in the forward's transposed layout (lane = query):
+// Q-owned dQ pass over the forward page walks.  One workgroup of 4 waves per forward
+// work item (query block), two workgroups per CU; the walk is consumed in half-tiles
+// of 4 pages (64 keys), double-buffered in LDS, one K and one V page per wave.  Each
+// wave owns 32 query rows and a key range of every half-tile (M128: 4 query groups,
+// all 64 keys as two 32-key sub-tiles; M64: 2 query groups x 2 key halves, one
+// sub-tile).  Per sub-tile, in the forward's transposed layout (lane = query):
 //   S^T = K Q^T, dP^T = V dO^T  (A = K / V rows from LDS, B = Q / dO rows in VGPRs),
 //   P^T = exp2(scale log2e S^T - lse2), dS^T = P^T (dP^T - D),
 //   dQ^T += K^T dS^T            (A = K read transposed from LDS, B = dS^T).
 // K tiles use the layout that serves both row and transposed reads.
+constexpr int kDqWaves = 4;
+
 template <int D, int ROUTE>
-__global__ __launch_bounds__(kThreads, 1) void kpage_bwd_dq(BwdArgs a, const FwdItem *items) {
+__global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a, const FwdItem *items) {
   constexpr int DS = D / 16;
   constexpr int ND = D / 32;
   constexpr int M = ROUTE;
   constexpr int NQG = M / 32;
-  constexpr int NKG = kWaves / NQG;
-  constexpr int KW = 128 / NKG;
+  constexpr int NKG = kDqWaves / NQG;
+  constexpr int KW = 64 / NKG;  // keys of a half-tile per wave
   constexpr int NH = KW / 32;
-  constexpr int TILE_BYTES = 128 * D * 2;
+  constexpr int HTILE = 64 * D * 2;  // one half-tile of K or V
+  constexpr int PART_BYTES = 32 * D * 4;
+  static_assert(kDqWaves * PART_BYTES <= 4 * HTILE, "dQ partials reuse the tile buffers");
 
-  // K tiles 0/1, V tiles 0/1; at the end the per-wave dQ partials
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
+  // K half-tiles 0/1, V half-tiles 0/1; at the end the per-wave dQ partials
+  __shared__ __attribute__((aligned(1024))) char smem[4 * HTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -367,8 +370,8 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_dq(BwdArgs a, const Fwd
   const FwdItem it = items[blockIdx.x];
   const int64_t bh = it.bh;
   const int cq = it.c_q;
-  const int n_tiles = it.walk_len / 8;
-  const int full_tiles = it.n_full / 8;
+  const int n_half = it.walk_len / 4;
+  const int full_half = it.n_full / 4;
   const int qg = wave % NQG;
   const int keyoff = (wave / NQG) * KW;
 
@@ -390,77 +393,111 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_dq(BwdArgs a, const Fwd
       greg[s] = qok ? gp[2 * s + g] : bf16x8{};
     }
   }
-  const float lse2 = qok ? a.lse2[qrow] : 0.f;
+  const float nlse2 = qok ? -a.lse2[qrow] : kNegInf;
   const float delta = qok ? a.delta[qrow] : 0.f;
-  if (n_tiles > 0) {
-    load_page<D, kSwzBoth>(kh, tile_page(walk, 0, wave), (lds_char *)smem, 16 * wave, lane);
-    load_page<D, kSwzRow>(vh, tile_page(walk, 0, wave), (lds_char *)smem + 2 * TILE_BYTES, 16 * wave, lane);
-  }
+  auto load_half = [&](int32_t page, int buf) __attribute__((always_inline)) {
+    load_page<D, kSwzBoth>(kh, page, (lds_char *)smem + buf * HTILE, 16 * wave, lane);
+    load_page<D, kSwzRow>(vh, page, (lds_char *)smem + (2 + buf) * HTILE, 16 * wave, lane);
+  };
+  if (n_half > 0) load_half(walk[wave], 0);
 
   f32x16 dq[ND];
 #pragma unroll
   for (int n = 0; n < ND; ++n) dq[n] = f32x16{};
   const float c2 = a.scale_log2;
-  const int tr_row = 4 * g + (sl >> 2);
-  const int tr_col = 2 * (mgrp & 1) + ((sl & 3) >> 1);
-  const int tr_byte = (sl & 1) * 8;
+  // Lane-constant LDS offsets of this wave's key range (half-tile, buffer and
+  // sub-tile are immediates): K rows (row l32, k-step s) at rdk ^ 32 s, V rows at
+  // rdv ^ 32 s, transposed K rows tr_row / tr_row + 8 of a 16-row group at head-dim
+  // block n at trk ^ 64 n and (trk ^ 64 (n ^ 1)) + 8 rows.
+  const int rdk = keyoff * D * 2 + chunk_off<kSwzBoth, D>(l32, g);
+  const int rdv = keyoff * D * 2 + chunk_off<kSwzRow, D>(l32, g);
+  const int trk = keyoff * D * 2 + chunk_off<kSwzBoth, D>(4 * g + (sl >> 2), 2 * (mgrp & 1) + ((sl & 3) >> 1)) +
+                  (sl & 1) * 8;
 
-  auto sub_tile = [&](const lds_char *kt, const lds_char *vt, int tile, int half, bool masked)
-                      __attribute__((always_inline)) {
-    const int k0 = keyoff + 32 * half;  // first key row of the sub-tile in the tile
-    f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const bf16x8 kop = lds_read8(kt + chunk_off<kSwzBoth, D>(k0 + l32, 2 * s + g));
-      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[s], s_acc, 0, 0, 0);
+  auto sub_tile = [&](auto buf_c, auto h_c, int u, bool masked) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_c)::value, H = decltype(h_c)::value;
+    constexpr int RB = 32 * H * D * 2;  // byte offset of the sub-tile in the wave's key range
+    const lds_char *kt = (const lds_char *)smem + BUF * HTILE + RB;
+    const lds_char *vt = (const lds_char *)smem + (2 + BUF) * HTILE + RB;
+    f32x16 s_acc, dp_acc;
+    {
+      bf16x8 op[DS];
+      auto rd = [&](auto s_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        op[S] = lds_read8(kt + xor_imm<32 * S>(rdk));
+      };
+      rd(ic<0>{});
+      rd(ic<1>{});
+      static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        if constexpr (S + 2 < DS) rd(ic<S + 2>{});
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], qreg[S], S == 0 ? f32x16{} : s_acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const bf16x8 vop = lds_read8(vt + chunk_off<kSwzRow, D>(k0 + l32, 2 * s + g));
-      dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, greg[s], dp_acc, 0, 0, 0);
+    {
+      bf16x8 op[DS];
+      auto rd = [&](auto s_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        op[S] = lds_read8(vt + xor_imm<32 * S>(rdv));
+      };
+      rd(ic<0>{});
+      rd(ic<1>{});
+      static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        if constexpr (S + 2 < DS) rd(ic<S + 2>{});
+        dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], greg[S], S == 0 ? f32x16{} : dp_acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
+    // key row of register r: 8 (r / 4) + 4 g + r % 4 of the sub-tile; its validity
+    // bit in the sub-tile's word (two 16-bit page masks): (r % 4) + 8 ((r / 4) % 2) +
+    // 16 (r / 8) after a shift by 4 g
     uint32_t word = 0xFFFFFFFFu;
-    if (masked) word = vwords[tile * 4 + (k0 >> 5)] >> (4 * g);
-    bf16x8 ds[2];
+    if (masked) word = vwords[2 * u + ((keyoff + 32 * H) >> 5)] >> (4 * g);
+    u32x4 ds[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int bit = (r & 3) + 8 * ((r >> 2) & 1) + 16 * (r >> 3);
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c2, -lse2));
-      p = ((word >> bit) & 1u) ? p : 0.f;
-      ds[r >> 3][r & 7] = (__bf16)(p * (dp_acc[r] - delta));
-    }
+    for (int r = 0; r < 16; r += 2) {
+      float pp[2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int ra = k0 + 16 * hh + tr_row, rb = ra + 8;
-#pragma unroll
-      for (int n = 0; n < ND; ++n) {
-        const int c = 4 * n + tr_col;
-        const bf16x8 kop = tr_read8(kt + chunk_off<kSwzBoth, D>(ra, c) + tr_byte, kt + chunk_off<kSwzBoth, D>(rb, c) + tr_byte);
-        dq[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, ds[hh], dq[n], 0, 0, 0);
+      for (int e = 0; e < 2; ++e) {
+        const int bit = ((r + e) & 3) + 8 * (((r + e) >> 2) & 1) + 16 * ((r + e) >> 3);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r + e], c2, nlse2));
+        pp[e] = ((word >> bit) & 1u) ? p * (dp_acc[r + e] - delta) : 0.f;
       }
+      ds[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(pp[0], pp[1]));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NOPS = 2 * ND;
+    bf16x8 kop[NOPS];
+    auto rdt = [&](auto j_c) __attribute__((always_inline)) {
+      constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
+      const lds_char *p = kt + 16 * HH * D * 2;
+      kop[J] = tr_read8(p + xor_imm<64 * N>(trk), p + 8 * D * 2 + xor_imm<64 * (N ^ 1)>(trk));
+    };
+    rdt(ic<0>{});
+    static_for<NOPS>([&](auto j_c) __attribute__((always_inline)) {
+      constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
+      if constexpr (J + 1 < NOPS) rdt(ic<J + 1>{});
+      dq[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[J], __builtin_bit_cast(bf16x8, ds[HH]), dq[N], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
-  auto iter = [&](auto buf_c, auto, int t) __attribute__((always_inline)) {
+  auto iter = [&](auto buf_c, auto, int u) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_c)::value;
-    const int32_t pnext = tile_page(walk, min(t + 1, n_tiles - 1), wave);
+    const int32_t pnext = walk[4 * min(u + 1, n_half - 1) + wave];
+    wait_lgkm0();
     wait_vmcnt<0>();
-    barrier();  // tile t resident; buffer 1 - BUF free
-    if (t + 1 < n_tiles) {
-      load_page<D, kSwzBoth>(kh, pnext, (lds_char *)smem + (1 - BUF) * TILE_BYTES, 16 * wave, lane);
-      load_page<D, kSwzRow>(vh, pnext, (lds_char *)smem + (3 - BUF) * TILE_BYTES, 16 * wave, lane);
-    }
-    const lds_char *kt = (const lds_char *)smem + BUF * TILE_BYTES;
-    const lds_char *vt = (const lds_char *)smem + (2 + BUF) * TILE_BYTES;
-    const bool masked = t >= full_tiles;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) sub_tile(kt, vt, t, h, masked);
+    barrier();  // half-tile u resident; buffer 1 - BUF free
+    if (u + 1 < n_half) load_half(pnext, 1 - BUF);
+    const bool masked = u >= full_half;
+    static_for<NH>([&](auto h_c) __attribute__((always_inline)) { sub_tile(buf_c, h_c, u, masked); });
   };
-  for_range(ic<0>{}, 0, n_tiles, iter);
+  for_range(ic<0>{}, 0, n_half, iter);
 
   // ---- sum the waves that share query rows, then write dQ = scale * acc (bf16) ----
   wait_vmcnt<0>();
   barrier();
-  constexpr int PART_BYTES = 32 * D * 4;
   {
     lds_char *part = (lds_char *)smem + wave * PART_BYTES;
 #pragma unroll
@@ -477,12 +514,12 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_bwd_dq(BwdArgs a, const Fwd
   const int64_t orow0 = bh * a.seq_q + 128 * it.q;
   const int vrows = cq < M ? cq : M;
   constexpr int GROUPS = D / 8;
-  for (int u = tid; u < 128 * GROUPS; u += kThreads) {
+  for (int u = tid; u < 128 * GROUPS; u += 64 * kDqWaves) {
     const int row = u / GROUPS, grp = u % GROUPS;
     float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (row < vrows) {
       const int qr = row & 31, q_g = row >> 5;
-      for (int w = q_g; w < kWaves; w += NQG) {
+      for (int w = q_g; w < kDqWaves; w += NQG) {
         const lds_char *pw = (const lds_char *)smem + w * PART_BYTES;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -522,9 +559,9 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
   }
   if (t) t->before(5, stream);
   if (a.n_fitems128 > 0)
-    hipLaunchKernelGGL((kpage_bwd_dq<D, 128>), dim3(a.n_fitems128), dim3(kThreads), 0, stream, a, a.fitems128);
+    hipLaunchKernelGGL((kpage_bwd_dq<D, 128>), dim3(a.n_fitems128), dim3(64 * kDqWaves), 0, stream, a, a.fitems128);
   if (a.n_fitems64 > 0)
-    hipLaunchKernelGGL((kpage_bwd_dq<D, 64>), dim3(a.n_fitems64), dim3(kThreads), 0, stream, a, a.fitems64);
+    hipLaunchKernelGGL((kpage_bwd_dq<D, 64>), dim3(a.n_fitems64), dim3(64 * kDqWaves), 0, stream, a, a.fitems64);
   if (t) t->after(5, stream);
   return hipGetLastError();
 }

@@ -111,13 +111,6 @@ constexpr bool swizzle_flip_is_uniform(int base, int n, int flip) {
   return true;
 }
 
-// x ^ imm (imm a run-time constant of the caller's unrolled loop) as an opaque VALU op.
-__device__ __forceinline__ int xor_imm_v(int x, int imm) {
-  int r;
-  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(imm), "v"(x));
-  return r;
-}
-
 // One page (16 rows) of a bf16 [rows, D] tensor, global -> LDS rows r0 .. r0 + 15 of a
 // tile (r0 % 16 == 0), 16 bytes per lane, laid out with swizzle SWZ.  `page` is
 // wave-uniform, so the page base is a scalar address; each lane adds a 32-bit offset.
@@ -178,16 +171,6 @@ __device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
-
-// acc += a * b (32 x 32 x 16 bf16 MFMA) with the accumulator pinned to AGPRs, for
-// long-lived accumulators that only MFMAs touch until the end of a kernel.  The
-// leading s_nop covers the VALU-write -> MFMA-read distance for a and b; the caller
-// runs acc_fence() before reading the accumulator with ordinary instructions.
-__device__ __forceinline__ void mfma_acc(f32x16 &acc, bf16x8 a, bf16x8 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// Wait states between the last mfma_acc and the first ordinary read of its result.
-__device__ __forceinline__ void acc_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 // Two floats to packed bf16 (round to nearest even), a in the low half: one
 // v_cvt_pk_bf16_f32.
