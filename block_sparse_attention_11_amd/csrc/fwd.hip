@@ -49,25 +49,31 @@
 namespace kpage {
 namespace {
 
-constexpr int kWaves = 8;
+// 4 waves per workgroup, two workgroups per CU; the walk is consumed in 4-page tiles
+// (64 keys), one K and one V page per wave.
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kTilePages = 4;
 constexpr float kLimit = 64.0f;  // fast kernel: largest rise of a score over the fixed maximum (base 2)
 constexpr float kRaise = 8.0f;   // exact kernel: raise the maximum only past this margin (base 2)
+
+// Page of wave j in tile t of a walk (one scalar load).
+__device__ __forceinline__ int32_t fwd_page(c_i32 *walk, int t, int j) { return walk[kTilePages * t + j]; }
 
 // MASK values of a sub-iteration: no masking, a runtime check, or masking always.
 constexpr int kMaskNone = 0, kMaskCheck = 1, kMaskAlways = 2;
 
 template <int D, int ROUTE, bool EXACT>
-__global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
+__global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int DS = D / 16;         // MFMA k-steps over the head dimension
   constexpr int ND = D / 32;         // 32-wide output blocks over the head dimension
   constexpr int M = ROUTE;           // query rows of the work item
   constexpr int NQG = M / 32;        // query groups of 32 rows
   constexpr int NKG = kWaves / NQG;  // key groups per tile
-  constexpr int KW = 128 / NKG;      // keys of a tile per wave
+  constexpr int KW = 16 * kTilePages / NKG;  // keys of a tile per wave
   constexpr int NH = KW / 32;        // 32-key sub-tiles per wave per tile
-  constexpr int TILE_BYTES = 128 * D * 2;
+  constexpr int TILE_BYTES = 16 * kTilePages * D * 2;
   constexpr int LOADS = 16 * CH / 64;  // direct loads per wave per tile and tensor
 
   // K tiles 0/1, then V tiles 0/1; at the end the per-wave partial outputs
@@ -88,9 +94,9 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
   const FwdItem it = args.items[blockIdx.x];
   const int bh = it.bh;
   const int cq = it.c_q;
-  const int n_tiles = it.walk_len / 8;
+  const int n_tiles = it.walk_len / kTilePages;
   const int n_sub = n_tiles * NH;
-  const int full_tiles = it.n_full / 8;  // tiles inside the fully valid prefix
+  const int full_tiles = it.n_full / kTilePages;  // tiles inside the fully valid prefix
   const int qg = wave % NQG;
   const int keyoff = (wave / NQG) * KW;  // first key of this wave in a tile
 
@@ -112,9 +118,9 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
       qreg[s] = x;
     }
   }
-  if (n_tiles > 0) load_page<D, kSwzRow>(kh, tile_page(walk, 0, wave), (lds_char *)kbuf0, 16 * wave, lane);
-  if (n_tiles > 1) load_page<D, kSwzRow>(kh, tile_page(walk, 1, wave), (lds_char *)kbuf1, 16 * wave, lane);
-  if (ROUTE == 128 && n_tiles > 0) load_page<D, kSwzTr>(vh, tile_page(walk, 0, wave), (lds_char *)vbuf0, 16 * wave, lane);
+  if (n_tiles > 0) load_page<D, kSwzRow>(kh, fwd_page(walk, 0, wave), (lds_char *)kbuf0, 16 * wave, lane);
+  if (n_tiles > 1) load_page<D, kSwzRow>(kh, fwd_page(walk, 1, wave), (lds_char *)kbuf1, 16 * wave, lane);
+  if (ROUTE == 128 && n_tiles > 0) load_page<D, kSwzTr>(vh, fwd_page(walk, 0, wave), (lds_char *)vbuf0, 16 * wave, lane);
 
   f32x16 oacc[ND];
 #pragma unroll
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
   // exact masking of invalid key rows of sub-tile `sub` (its 32 keys = one validity word)
   auto mask = [&](int sub, f32x16 &sc) __attribute__((always_inline)) {
     const int tile = sub / NH, half = sub % NH;
-    const uint32_t word = vwords[tile * 4 + (keyoff >> 5) + half] >> (4 * g);
+    const uint32_t word = vwords[tile * (kTilePages / 2) + (keyoff >> 5) + half] >> (4 * g);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int bit = (r & 3) + 8 * ((r >> 2) & 1) + 16 * (r >> 3);
@@ -344,8 +350,8 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
       auto tile = [&](auto par, auto masking, int t) __attribute__((always_inline)) {
         constexpr int PT = decltype(par)::value;
         // page ids first: their scalar loads overlap the wait for the other waves
-        const int32_t kp = tile_page(walk, min(t + 2, n_tiles - 1), wave);
-        const int32_t vp = tile_page(walk, t + 1, wave);
+        const int32_t kp = fwd_page(walk, min(t + 2, n_tiles - 1), wave);
+        const int32_t vp = fwd_page(walk, t + 1, wave);
         wait_vmcnt<0>();
         barrier();
         if (t + 2 < n_tiles) load_page<D, kSwzRow>(kh, kp, (lds_char *)(PT ? kbuf1 : kbuf0), 16 * wave, lane);
@@ -375,14 +381,14 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
       qk(K0, 0, sacc[0]);
       wait_vmcnt<0>();
       barrier();
-      if (n_sub > 2) load_page<D, kSwzRow>(kh, tile_page(walk, 2, wave), (lds_char *)kbuf0, 16 * wave, lane);
-      load_page<D, kSwzTr>(vh, tile_page(walk, 0, wave), (lds_char *)vbuf0, 16 * wave, lane);
+      if (n_sub > 2) load_page<D, kSwzRow>(kh, fwd_page(walk, 2, wave), (lds_char *)kbuf0, 16 * wave, lane);
+      load_page<D, kSwzTr>(vh, fwd_page(walk, 0, wave), (lds_char *)vbuf0, 16 * wave, lane);
       if (n_sub > 1) {
         step(T, F, ic<0>{}, ic<kMaskCheck>{}, K1, V1, 0);
         auto sub = [&](auto par, auto masking, int i) __attribute__((always_inline)) {
           constexpr int PI = decltype(par)::value;
-          const int32_t kp = tile_page(walk, min(i + 2, n_sub - 1), wave);
-          const int32_t vp = tile_page(walk, i, wave);
+          const int32_t kp = fwd_page(walk, min(i + 2, n_sub - 1), wave);
+          const int32_t vp = fwd_page(walk, i, wave);
           wait_vmcnt<0>();
           barrier();
           if (i + 2 < n_sub) load_page<D, kSwzRow>(kh, kp, (lds_char *)(PI ? kbuf1 : kbuf0), 16 * wave, lane);
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(kThreads, 1) void kpage_fwd_kernel(FwdArgs args) {
         const int i = n_sub - 1;
         wait_vmcnt<0>();
         barrier();
-        load_page<D, kSwzTr>(vh, tile_page(walk, i, wave), (lds_char *)((i & 1) ? vbuf1 : vbuf0), 16 * wave, lane);
+        load_page<D, kSwzTr>(vh, fwd_page(walk, i, wave), (lds_char *)((i & 1) ? vbuf1 : vbuf0), 16 * wave, lane);
         if (i & 1) step(F, T, ic<1>{}, ic<kMaskCheck>{}, K0, V0, i);
         else step(F, T, ic<0>{}, ic<kMaskCheck>{}, K0, V1, i);
       } else {
