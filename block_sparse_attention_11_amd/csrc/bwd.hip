@@ -394,7 +394,16 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a, cons
     }
   }
   const float nlse2 = qok ? -a.lse2[qrow] : kNegInf;
-  const float delta = qok ? a.delta[qrow] : 0.f;
+  // D enters the dP^T chain as one extra k-step: A = ones in k = 0, 1 (lanes 0-31),
+  // B = -D of this lane's query split into bf16 hi + lo in k = 0, 1, so the chain
+  // yields dP^T - D and dS^T = P^T (dP^T - D) costs one multiply per element
+  bf16x8 one_aug, nd_aug;
+  {
+    const float nd = qok ? -a.delta[qrow] : 0.f;
+    const float hi = __builtin_bit_cast(float, pack_bf16(nd, 0.f) << 16);
+    nd_aug = __builtin_bit_cast(bf16x8, u32x4{g ? 0u : pack_bf16(hi, nd - hi), 0u, 0u, 0u});
+    one_aug = __builtin_bit_cast(bf16x8, u32x4{g ? 0u : 0x3F803F80u, 0u, 0u, 0u});
+  }
   auto load_half = [&](int32_t page, int buf) __attribute__((always_inline)) {
     load_page<D, kSwzBoth>(kh, page, (lds_char *)smem + buf * HTILE, 16 * wave, lane);
     load_page<D, kSwzRow>(vh, page, (lds_char *)smem + (2 + buf) * HTILE, 16 * wave, lane);
@@ -449,23 +458,33 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a, cons
         dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], greg[S], S == 0 ? f32x16{} : dp_acc, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       });
+      dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(one_aug, nd_aug, dp_acc, 0, 0, 0);
     }
     // key row of register r: 8 (r / 4) + 4 g + r % 4 of the sub-tile; its validity
     // bit in the sub-tile's word (two 16-bit page masks): (r % 4) + 8 ((r / 4) % 2) +
     // 16 (r / 8) after a shift by 4 g
-    uint32_t word = 0xFFFFFFFFu;
-    if (masked) word = vwords[2 * u + ((keyoff + 32 * H) >> 5)] >> (4 * g);
+    // (a select, not a product: the P of a padded key row may be inf)
     u32x4 ds[2];
+    if (masked) {
+      const uint32_t word = vwords[2 * u + ((keyoff + 32 * H) >> 5)] >> (4 * g);
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float pp[2];
+      for (int r = 0; r < 16; r += 2) {
+        float pp[2];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int bit = ((r + e) & 3) + 8 * (((r + e) >> 2) & 1) + 16 * ((r + e) >> 3);
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r + e], c2, nlse2));
-        pp[e] = ((word >> bit) & 1u) ? p * (dp_acc[r + e] - delta) : 0.f;
+        for (int e = 0; e < 2; ++e) {
+          const int bit = ((r + e) & 3) + 8 * (((r + e) >> 2) & 1) + 16 * ((r + e) >> 3);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r + e], c2, nlse2));
+          pp[e] = ((word >> bit) & 1u) ? p * dp_acc[r + e] : 0.f;
+        }
+        ds[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(pp[0], pp[1]));
       }
-      ds[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(pp[0], pp[1]));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c2, nlse2));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r + 1], c2, nlse2));
+        ds[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(p0 * dp_acc[r], p1 * dp_acc[r + 1]));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     constexpr int NOPS = 2 * ND;
