@@ -185,6 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
     }
   };
   float alpha = 1.f;  // exact kernel: rescale factor owed by the last softmax
+  float nm_fix = 0.f;  // fast kernel: -(fixed maximum) once the first sub-tile set it
   bool pending = false;
   // softmax of sc into p_out (the sequential form: exact kernel and peeled sub-iterations)
   auto softmax = [&](const f32x16 &sc, bf16x8 *p_out) __attribute__((always_inline)) {
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
                    __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
     constexpr int VOPS = 2 * ND, NM = DS + VOPS;
-    constexpr int PRE = 2, SLICES = 7;  // softmax slices 0, 1 (the maximum) run before the first MFMA
+    constexpr int SLICES = 4;  // probabilities of 4 scores each
     static_assert(DS == VOPS, "QK and PV products alternate one to one");
     const f32x16 &sc = sacc[P];
     f32x16 &sn = sacc[1 - P];
@@ -249,25 +250,16 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
       constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
       vop[J] = read_v_op(vbase + 16 * HH * D * 2 + ((4 * N + v_chunk_lane) ^ v_swz) * 16 + v_byte);
     };
-    float mx = kNegInf, nm = 0.f, rs0 = 0.f, rs1 = 0.f;
-    // slices 0, 1: maximum of 8 scores each; 2: column maximum and the fixed maximum;
-    // 3..6: probabilities of 4 scores (exp2, two partial row sums, bf16 packs)
+    float rs0 = 0.f, rs1 = 0.f;
+    // slice k: probabilities of scores 4 k .. 4 k + 3 (exp2, two partial row sums,
+    // bf16 packs) against the maximum fixed by the first sub-tile (nm_fix = -m2); no
+    // per-sub-tile maximum: a rise past the fixed maximum shows in the row sum, which
+    // the epilogue checks
     auto slice = [&](auto k_c) __attribute__((always_inline)) {
       constexpr int K = decltype(k_c)::value;
-      if constexpr (K < 2) {
-        constexpr int Q = 8 * K;
-        float m = max3(mx, sc[Q], sc[Q + 1]);
-        m = max3(m, sc[Q + 2], sc[Q + 3]);
-        m = max3(m, sc[Q + 4], sc[Q + 5]);
-        mx = max3(m, sc[Q + 6], sc[Q + 7]);
-      } else if constexpr (K == 2) {
-        const float m = half_max(mx) * c2;
-        const bool first = m2 == kNegInf;
-        over = over || (!first && m > m2 + kLimit);
-        m2 = first ? m : m2;
-        nm = m2 == kNegInf ? 0.f : -m2;
-      } else {
-        constexpr int R = 4 * (K - 3);
+      {
+        constexpr int R = 4 * K;
+        const float nm = nm_fix;
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = __builtin_fmaf(sc[R + e], c2, nm);
@@ -285,7 +277,6 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
     read_k(ic<1>{});
     read_v(ic<0>{});
     read_v(ic<1>{});
-    static_for<PRE>(slice);
     __builtin_amdgcn_sched_barrier(0);
     static_for<NM>([&](auto c_c) __attribute__((always_inline)) {
       constexpr int C = decltype(c_c)::value, KK = C / 2;
@@ -297,9 +288,9 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
         if constexpr (KK + 2 < VOPS) read_v(ic<KK + 2>{});
         oacc[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[KK], pp[HH], oacc[N], 0, 0, 0);
       }
-      static_for<SLICES - PRE>([&](auto k_c) __attribute__((always_inline)) {
+      static_for<SLICES>([&](auto k_c) __attribute__((always_inline)) {
         constexpr int K = decltype(k_c)::value;
-        if constexpr (K * NM / (SLICES - PRE) == C) slice(ic<K + PRE>{});
+        if constexpr (K * NM / SLICES == C) slice(ic<K>{});
       });
       if constexpr (C % 2 == 1) __builtin_amdgcn_sched_barrier(0);
     });
@@ -346,6 +337,7 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
       barrier();
       qk(K0, 0, sacc[0]);
       step(T, F, ic<0>{}, ic<kMaskCheck>{}, K0, V0, 0);  // S_1 comes from the same tile
+      nm_fix = m2 == kNegInf ? 0.f : -m2;
       // tile body t: sub-iterations 2t + 1 (softmax of tile t) and 2t + 2 (tile t + 1)
       auto tile = [&](auto par, auto masking, int t) __attribute__((always_inline)) {
         constexpr int PT = decltype(par)::value;
@@ -385,6 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
       load_page<D, kSwzTr>(vh, fwd_page(walk, 0, wave), (lds_char *)vbuf0, 16 * wave, lane);
       if (n_sub > 1) {
         step(T, F, ic<0>{}, ic<kMaskCheck>{}, K1, V1, 0);
+        nm_fix = m2 == kNegInf ? 0.f : -m2;
         auto sub = [&](auto par, auto masking, int i) __attribute__((always_inline)) {
           constexpr int PI = decltype(par)::value;
           const int32_t kp = fwd_page(walk, min(i + 2, n_sub - 1), wave);
@@ -419,6 +412,10 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
   wait_vmcnt<0>();
   wait_lgkm0();
   if (!EXACT && tid == 0) redo_any = 0;
+  // fast kernel: the fixed maximum is only safe if it existed before the row's first
+  // probability (else the sums ran against 0) and no score rose more than 2^kLimit
+  // above it (every probability is at most the row sum)
+  if (!EXACT) over = over || (m2 == kNegInf && l_run != 0.f) || !(l_run <= __builtin_exp2f(kLimit));
   barrier();
   if (!EXACT && __builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) redo_any = 1;
   {
