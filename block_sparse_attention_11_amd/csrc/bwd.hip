@@ -185,6 +185,10 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) nib &= ~((~(uint32_t)(adj >> (8 * (jbase + j) + 2 * wave)) & 0x3u) << (2 * j));
     const bool all_edges = nib == 0xFFu;
+    // the first two Q-row operands of the next query block's S chain
+    bf16x8 qpre[2];
+    qpre[0] = lds_read8(qt + xor_imm<0>(rd_base));
+    qpre[1] = lds_read8(qt + xor_imm<32>(rd_base));
     __builtin_amdgcn_sched_barrier(0);
     static_for<2>([&](auto qb_c) __attribute__((always_inline)) {
       constexpr int QB = decltype(qb_c)::value;
@@ -198,82 +202,67 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
       // P and dS as packed bf16 pairs (u32x4 [hh] = rows 16 hh .. + 15 of the block):
       // the A operands of the dV / dK products
       u32x4 pb[2], sb[2];
-      // (A) S = Q K^T, operand reads two k-steps ahead; then P = exp2(scale log2e S -
-      // lse2)
+      // Each phase's first two operand reads are issued before the element-wise work
+      // that precedes the phase, so that work hides their LDS latency.
+      auto rd_row = [&](const lds_char *t, auto s_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        return lds_read8(t + RB + xor_imm<32 * S>(rd_base));
+      };
+      // (A) S = Q K^T, operand reads two k-steps ahead
+      f32x16 sp;
       {
-        f32x16 sp;
         bf16x8 op[DS];
-        auto rd = [&](auto s_c) __attribute__((always_inline)) {
-          constexpr int S = decltype(s_c)::value;
-          op[S] = lds_read8(qt + RB + xor_imm<32 * S>(rd_base));
-        };
-        rd(ic<0>{});
-        rd(ic<1>{});
+        op[0] = qpre[0];
+        op[1] = qpre[1];
         static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
           constexpr int S = decltype(s_c)::value;
-          if constexpr (S + 2 < DS) rd(ic<S + 2>{});
+          if constexpr (S + 2 < DS) op[S + 2] = rd_row(qt, ic<S + 2>{});
           sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], kreg[S], S == 0 ? f32x16{} : sp, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         });
+      }
+      bf16x8 opb[DS];
+      opb[0] = rd_row(gt, ic<0>{});
+      opb[1] = rd_row(gt, ic<1>{});
+      const float nd = -*(const __attribute__((address_space(3))) float *)(stb + (((32 * QB + l32) >> 4) * 64 + 16 +
+                                                                               ((32 * QB + l32) & 15)) * 4);
+      // P = exp2(scale log2e S - lse2)
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          const f32x4 l4 = lse4(j4);
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const f32x4 l4 = lse4(j4);
 #pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            const int r = 4 * j4 + e;
-            pb[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sp[r], c2, -l4[e])),
-                                                        __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r + 1], c2, -l4[e + 1]))));
-          }
+        for (int e = 0; e < 4; e += 2) {
+          const int r = 4 * j4 + e;
+          pb[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sp[r], c2, -l4[e])),
+                                                      __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r + 1], c2, -l4[e + 1]))));
         }
-        // zero the P blocks of non-edge (query page, key slot) pairs: pb[hh] holds the
-        // rows of page 2 qb + hh of the half-step
-        if (!all_edges) {
+      }
+      // zero the P blocks of non-edge (query page, key slot) pairs: pb[hh] holds the
+      // rows of page 2 qb + hh of the half-step
+      if (!all_edges) {
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-            if (!((nib >> (2 * (2 * QB + hh) + khalf)) & 1u)) pb[hh] = u32x4{};
-        }
+        for (int hh = 0; hh < 2; ++hh)
+          if (!((nib >> (2 * (2 * QB + hh) + khalf)) & 1u)) pb[hh] = u32x4{};
       }
       __builtin_amdgcn_sched_barrier(0);
       // (B) dP - D = dO V^T - D, with D as one extra k-step (A = -D split into bf16
       // hi + lo in k = 0, 1 of lanes 0-31 for query row l32, B = ones), then (C)
       // dS = P (dP - D).  P enters dS as its bf16 value, an extra rounding of the order
       // of dS's own.
+      f32x16 dp;
       {
-        bf16x8 daug;
-        {
-          const int q = 32 * QB + l32;
-          const float nd = -*(const __attribute__((address_space(3))) float *)(stb + ((q >> 4) * 64 + 16 + (q & 15)) * 4);
-          const float hi = __builtin_bit_cast(float, pack_bf16(nd, 0.f) << 16);
-          const uint32_t w0 = g ? 0u : pack_bf16(hi, nd - hi);
-          daug = __builtin_bit_cast(bf16x8, u32x4{w0, 0u, 0u, 0u});
-        }
-        f32x16 dp;
-        bf16x8 op[DS];
-        auto rd = [&](auto s_c) __attribute__((always_inline)) {
-          constexpr int S = decltype(s_c)::value;
-          op[S] = lds_read8(gt + RB + xor_imm<32 * S>(rd_base));
-        };
-        rd(ic<0>{});
-        rd(ic<1>{});
+        const float hi = __builtin_bit_cast(float, pack_bf16(nd, 0.f) << 16);
+        const bf16x8 daug = __builtin_bit_cast(bf16x8, u32x4{g ? 0u : pack_bf16(hi, nd - hi), 0u, 0u, 0u});
         static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
           constexpr int S = decltype(s_c)::value;
-          if constexpr (S + 2 < DS) rd(ic<S + 2>{});
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], vreg[S], S == 0 ? f32x16{} : dp, 0, 0, 0);
+          if constexpr (S + 2 < DS) opb[S + 2] = rd_row(gt, ic<S + 2>{});
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb[S], vreg[S], S == 0 ? f32x16{} : dp, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         });
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(daug, __builtin_bit_cast(bf16x8, u32x4{ones_lo, 0u, 0u, 0u}), dp,
                                                      0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const uint32_t w = pb[r >> 3][(r & 7) >> 1];
-          sb[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(__builtin_bit_cast(float, w << 16) * dp[r],
-                                                      __builtin_bit_cast(float, w & 0xFFFF0000u) * dp[r + 1]));
-        }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // (D) dV += P^T dO and dK += dS^T Q over these 32 query rows (B operands: columns
-      // of dO and Q, transposed reads one product ahead)
+      // (D) operands: columns of dO and Q, transposed reads one product ahead
       constexpr int NOPS = 2 * ND;
       bf16x8 gt_op[NOPS], qt_op[NOPS];
       auto rdt = [&](auto j_c) __attribute__((always_inline)) {
@@ -285,9 +274,23 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
         qt_op[J] = tr_read8(qt + RH + oa, qt + RH + 8 * D * 2 + ob);
       };
       rdt(ic<0>{});
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const uint32_t w = pb[r >> 3][(r & 7) >> 1];
+        sb[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(__builtin_bit_cast(float, w << 16) * dp[r],
+                                                    __builtin_bit_cast(float, w & 0xFFFF0000u) * dp[r + 1]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // (D) dV += P^T dO and dK += dS^T Q over these 32 query rows; the next query
+      // block's first Q rows are read during the last products
       static_for<NOPS>([&](auto j_c) __attribute__((always_inline)) {
         constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
         if constexpr (J + 1 < NOPS) rdt(ic<J + 1>{});
+        if constexpr (QB == 0 && J == NOPS - 1) {
+          qpre[0] = lds_read8(qt + RB + 32 * D * 2 + xor_imm<0>(rd_base));
+          qpre[1] = lds_read8(qt + RB + 32 * D * 2 + xor_imm<32>(rd_base));
+        }
         dv[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pb[HH]), gt_op[J], dv[N], 0, 0, 0);
         dk[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sb[HH]), qt_op[J], dk[N], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
