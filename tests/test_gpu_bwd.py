@@ -104,6 +104,11 @@ def test_bwd_3d_padded_all_heads_two_checked():
     _run(make_workload(3, with_do=True), "21x30x52 all 40 heads", heads=[0, 37])
 
 
+def test_bwd_vsa_topk_all_heads_one_checked():
+    """The 21x45x80 top-87 workload at full size (40 heads, per-head graphs), one head checked."""
+    _run(make_workload(4, with_do=True), "21x45x80 top-87 all 40 heads", heads=[23])
+
+
 @pytest.mark.parametrize("name", list(EDGE_CASES))
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_edge_cases(name, d):
