@@ -32,7 +32,7 @@ TABLES = {
 }
 
 EXPORTED_SYMBOLS = (
-    "kpage_plan", "kpage_plan_upload", "kpage_attn_fwd", "kpage_bwd_workspace_size", "kpage_attn_bwd",
+    "kpage_plan", "kpage_plan_device", "kpage_plan_upload", "kpage_attn_fwd", "kpage_bwd_workspace_size", "kpage_attn_bwd",
     "kpage_plan_stats", "kpage_plan_export", "kpage_plan_destroy", "kpage_timing_enable", "kpage_timing_read",
     "kpage_last_error",
 )
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.kpage_plan.argtypes = [ctypes.POINTER(KpageProblem), ctypes.POINTER(KpagePlanOpts), ctypes.POINTER(vp)]
+        L.kpage_plan_device.argtypes = [ctypes.POINTER(KpageProblem), ctypes.c_int64, ctypes.POINTER(KpagePlanOpts), vp,
+                                        ctypes.POINTER(vp)]
         L.kpage_plan_upload.argtypes = [vp, vp]
         L.kpage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp]
         L.kpage_bwd_workspace_size.argtypes = [vp, ctypes.POINTER(sz)]
@@ -132,7 +134,7 @@ def kpage_plan(problem, align_q64: int = 0, align_q128: int = 0, q_group: int = 
     """Plan for ``problem`` (any object with the workloads.Workload descriptor attributes)."""
     qv = _arr(problem.q_valid, np.int32)
     kvv = _arr(problem.kv_valid, np.int32)
-    ko = _arr(problem.kv_offset, np.int64)
+    ko = None if problem.kv_offset is None else _arr(problem.kv_offset, np.int64)
     ptr = _arr(problem.q2k_ptr, np.int64)
     idx = _arr(problem.q2k_idx, np.int32)
     if idx.size == 0:
@@ -141,11 +143,45 @@ def kpage_plan(problem, align_q64: int = 0, align_q128: int = 0, q_group: int = 
         batch=problem.batch, heads=problem.heads, head_dim=problem.head_dim,
         n_q_blocks=problem.n_q, n_kv_blocks=problem.n_kv, seq_q=problem.seq_q, seq_kv=problem.seq_kv,
         per_head=1 if problem.per_head else 0,
-        q_valid=qv.ctypes.data, kv_valid=kvv.ctypes.data, kv_offset=ko.ctypes.data,
+        q_valid=qv.ctypes.data, kv_valid=kvv.ctypes.data, kv_offset=0 if ko is None else ko.ctypes.data,
         q2k_ptr=ptr.ctypes.data, q2k_idx=idx.ctypes.data)
     opts = KpagePlanOpts(q_group=q_group, align_q128=align_q128, align_q64=align_q64)
     h = ctypes.c_void_p()
     _check(lib().kpage_plan(ctypes.byref(p), ctypes.byref(opts), ctypes.byref(h)))
+    return Plan(h, problem.batch, problem.heads, problem.head_dim, problem.seq_q, problem.seq_kv)
+
+
+def kpage_plan_device(problem, align_q64: int = 0, align_q128: int = 0, q_group: int = 0, stream=None) -> Plan:
+    """Plan for ``problem`` built on the GPU from device copies of its descriptor arrays
+    (kpage_plan_device).  The arrays may be numpy arrays (copied to the current device
+    here) or CUDA tensors of the right dtypes."""
+    import torch
+
+    def dev(x, dtype):
+        if isinstance(x, torch.Tensor) and x.is_cuda:
+            t = x.contiguous()
+            if t.dtype != dtype:
+                raise KpageError(KPAGE_ERR_INVALID, f"descriptor array of dtype {t.dtype}, need {dtype}")
+            return t
+        return torch.from_numpy(np.ascontiguousarray(np.asarray(x))).to(dtype).cuda()
+
+    qv = dev(problem.q_valid, torch.int32)
+    kvv = dev(problem.kv_valid, torch.int32)
+    ko = None if problem.kv_offset is None else dev(problem.kv_offset, torch.int64)
+    ptr = dev(problem.q2k_ptr, torch.int64)
+    idx = dev(problem.q2k_idx, torch.int32)
+    nnz = int(idx.numel())
+    if nnz == 0:
+        idx = torch.zeros(1, dtype=torch.int32, device=qv.device)
+    p = KpageProblem(
+        batch=problem.batch, heads=problem.heads, head_dim=problem.head_dim,
+        n_q_blocks=problem.n_q, n_kv_blocks=problem.n_kv, seq_q=problem.seq_q, seq_kv=problem.seq_kv,
+        per_head=1 if problem.per_head else 0,
+        q_valid=qv.data_ptr(), kv_valid=kvv.data_ptr(), kv_offset=0 if ko is None else ko.data_ptr(),
+        q2k_ptr=ptr.data_ptr(), q2k_idx=idx.data_ptr())
+    opts = KpagePlanOpts(q_group=q_group, align_q128=align_q128, align_q64=align_q64)
+    h = ctypes.c_void_p()
+    _check(lib().kpage_plan_device(ctypes.byref(p), nnz, ctypes.byref(opts), _stream_ptr(stream), ctypes.byref(h)))
     return Plan(h, problem.batch, problem.heads, problem.head_dim, problem.seq_q, problem.seq_kv)
 
 

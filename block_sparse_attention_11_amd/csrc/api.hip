@@ -11,6 +11,7 @@
 #include "device.hpp"
 #include "kpage.h"
 #include "plan.hpp"
+#include "plan_dev.hpp"
 
 using namespace kpage;
 
@@ -78,6 +79,13 @@ struct kpage_plan {
   BwdTables B;
   PairStats S;
   bool fwd_on_device = false;
+  // built by kpage_plan_device: the descriptor and the forward tables live on the
+  // device; host copies are made on demand (backward planning, table export)
+  bool device_planned = false;
+  bool problem_on_host = true;
+  bool fwd_on_host = true;
+  DevProblem DP;
+  DevFwdTables DF;
   bool bwd_on_device = false;
   // forward device tables
   FwdItem *d_items128 = nullptr, *d_items64 = nullptr;
@@ -210,7 +218,45 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   return KPAGE_OK;
 }
 
+template <class T>
+void copy_down(std::vector<T> &dst, const T *src, int64_t n) {
+  dst.resize(size_t(std::max<int64_t>(n, 0)));
+  if (n > 0) (void)hipMemcpy(dst.data(), src, size_t(n) * sizeof(T), hipMemcpyDeviceToHost);
+}
+
+// device-planned plans: the descriptor's arrays, copied to the host problem
+void ensure_problem_on_host(PlanT *pl) {
+  if (pl->problem_on_host) return;
+  const DevProblem &D = pl->DP;
+  Problem &P = pl->P;
+  const int64_t G = P.slots, nq = P.n_q, nk = P.n_kv;
+  copy_down(P.q_valid, D.q_valid, G * nq);
+  copy_down(P.kv_valid, D.kv_valid, G * nk);
+  copy_down(P.kv_offset, D.kv_offset, G * nk);
+  copy_down(P.q2k_ptr, D.q2k_ptr, G * (nq + 1));
+  copy_down(P.q2k_idx, D.q2k_idx, D.nnz);
+  pl->problem_on_host = true;
+}
+
+// device-planned plans: the forward tables, copied for export
+void ensure_forward_on_host(PlanT *pl) {
+  if (pl->fwd_on_host) return;
+  const DevFwdTables &T = pl->DF;
+  FwdTables &F = pl->F;
+  const int64_t GQ = int64_t(pl->P.slots) * pl->P.n_q;
+  copy_down(F.route, T.route, GQ);
+  copy_down(F.walk_ptr, T.walk_ptr, int64_t(pl->P.slots) * (pl->P.n_q + 1));
+  copy_down(F.walk, T.walk, T.walk_total);
+  copy_down(F.nfull, T.nfull, GQ);
+  copy_down(F.valid, T.valid, T.walk_total / 2);
+  copy_down(F.q64_queue, T.q64_queue, 2 * int64_t(T.n_q64));
+  copy_down(F.q128_queue, T.q128_queue, 2 * int64_t(T.n_q128));
+  copy_down(F.unpadded, T.unpadded, GQ);
+  pl->fwd_on_host = true;
+}
+
 void ensure_backward_on_host(PlanT *pl) {
+  ensure_problem_on_host(pl);
   if (!pl->B.built) build_backward(pl->P, &pl->B, &pl->S);
 }
 
@@ -307,6 +353,86 @@ kpage_status kpage_plan(const kpage_problem *problem, const kpage_plan_opts *opt
     delete pl;
     return fail(KPAGE_ERR_OOM, "host allocation failed while planning");
   }
+  *out = pl;
+  g_last_error.clear();
+  return KPAGE_OK;
+}
+
+kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, const kpage_plan_opts *opts,
+                               void *stream, kpage_plan_t **out) {
+  if (!out) return fail(KPAGE_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!problem) return fail(KPAGE_ERR_INVALID, "problem is NULL");
+  // scalar checks of the host loader on a descriptor without arrays
+  kpage_problem shell = *problem;
+  if (!shell.q_valid || !shell.kv_valid || !shell.q2k_ptr || !shell.q2k_idx)
+    return fail(KPAGE_ERR_INVALID, "q_valid, kv_valid, q2k_ptr and q2k_idx are required");
+  if (q2k_nnz < 0) return fail(KPAGE_ERR_INVALID, "q2k_nnz must be >= 0");
+  PlanT *pl = new (std::nothrow) PlanT();
+  if (!pl) return fail(KPAGE_ERR_OOM, "host allocation failed");
+  std::string err;
+  int a64 = 16, a128 = 8;
+  kpage_status s = load_scalars(&shell, opts, &pl->P, &a64, &a128, &err);
+  if (s != KPAGE_OK) {
+    delete pl;
+    return fail(s, err);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Problem &P = pl->P;
+  const int64_t G = P.slots, nq = P.n_q, nk = P.n_kv;
+  auto alloc = [pl](size_t bytes) -> void * {
+    void *p = nullptr;
+    if (hipMalloc(&p, std::max<size_t>(bytes, 16)) != hipSuccess) return nullptr;
+    pl->allocations.push_back(p);
+    return p;
+  };
+  auto own = [&](const void *src, size_t bytes, const char *what) -> void * {
+    void *d = alloc(bytes);
+    if (d && bytes) {
+      if (hipMemcpyAsync(d, src, bytes, hipMemcpyDeviceToDevice, st) != hipSuccess) return nullptr;
+    }
+    (void)what;
+    return d;
+  };
+  DevProblem &D = pl->DP;
+  D.batch = P.batch; D.heads = P.heads; D.n_q = P.n_q; D.n_kv = P.n_kv; D.slots = P.slots;
+  D.seq_q = P.seq_q; D.seq_kv = P.seq_kv; D.per_head = P.per_head; D.nnz = q2k_nnz;
+  D.q_valid = static_cast<const int32_t *>(own(shell.q_valid, size_t(G * nq) * 4, "q_valid"));
+  D.kv_valid = static_cast<const int32_t *>(own(shell.kv_valid, size_t(G * nk) * 4, "kv_valid"));
+  D.q2k_ptr = static_cast<const int64_t *>(own(shell.q2k_ptr, size_t(G * (nq + 1)) * 8, "q2k_ptr"));
+  D.q2k_idx = static_cast<const int32_t *>(own(shell.q2k_idx, size_t(q2k_nnz) * 4, "q2k_idx"));
+  if (shell.kv_offset) {
+    D.kv_offset = static_cast<const int64_t *>(own(shell.kv_offset, size_t(G * nk) * 8, "kv_offset"));
+  } else {  // the plan keeps explicit offsets (host copies expect them)
+    std::vector<int64_t> off(size_t(G * nk));
+    for (int64_t i = 0; i < G * nk; ++i) off[size_t(i)] = int64_t(kBlockRows) * (i % nk);
+    int64_t *d = static_cast<int64_t *>(alloc(off.size() * 8));
+    if (d && hipMemcpy(d, off.data(), off.size() * 8, hipMemcpyHostToDevice) != hipSuccess) d = nullptr;
+    D.kv_offset = d;
+  }
+  if (!D.q_valid || !D.kv_valid || !D.q2k_ptr || !D.q2k_idx || !D.kv_offset) {
+    kpage_plan_destroy(pl);
+    return fail(KPAGE_ERR_OOM, "device allocation or copy failed while planning");
+  }
+  pl->F.align64 = a64;
+  pl->F.align128 = a128;
+  s = build_forward_device(D, a64, a128, st, alloc, &pl->DF, &err);
+  if (s != KPAGE_OK) {
+    kpage_plan_destroy(pl);
+    return fail(s, err);
+  }
+  pl->device_planned = true;
+  pl->problem_on_host = false;
+  pl->fwd_on_host = false;
+  pl->S = pl->DF.stats;
+  pl->d_pages = pl->DF.pages;
+  pl->d_valid = pl->DF.valid;
+  pl->d_items128 = pl->DF.items128;
+  pl->d_items64 = pl->DF.items64;
+  pl->d_redo = pl->DF.redo;
+  pl->n_items128 = pl->DF.n_q128;
+  pl->n_items64 = pl->DF.n_q64 + pl->DF.n_zero;
+  pl->fwd_on_device = true;
   *out = pl;
   g_last_error.clear();
   return KPAGE_OK;
@@ -421,6 +547,7 @@ kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf,
   if (!plan || !bytes) return fail(KPAGE_ERR_INVALID, "plan or bytes is NULL");
   if (table_id < 0 || table_id >= KPAGE_T_COUNT) return fail(KPAGE_ERR_INVALID, "unknown table id");
   if (table_id >= KPAGE_T_OWNER_PTR) ensure_backward_on_host(plan);
+  else ensure_forward_on_host(plan);
   const void *src = nullptr;
   size_t n = 0;
   switch (table_id) {

@@ -36,7 +36,7 @@ std::string str(const T &v) {
 
 }  // namespace
 
-kpage_status load_problem(const kpage_problem *p, const kpage_plan_opts *o, Problem *out, int *align64,
+kpage_status load_scalars(const kpage_problem *p, const kpage_plan_opts *o, Problem *out, int *align64,
                           int *align128, std::string *err) {
   if (!p) { *err = "problem is NULL"; return KPAGE_ERR_INVALID; }
   if (p->batch < 1 || p->heads < 1) { *err = "batch and heads must be >= 1"; return KPAGE_ERR_INVALID; }
@@ -70,6 +70,14 @@ kpage_status load_problem(const kpage_problem *p, const kpage_plan_opts *o, Prob
   P.seq_q = p->seq_q; P.seq_kv = p->seq_kv;
   P.per_head = p->per_head == 1;
   P.slots = P.per_head ? P.batch * P.heads : 1;
+  return KPAGE_OK;
+}
+
+kpage_status load_problem(const kpage_problem *p, const kpage_plan_opts *o, Problem *out, int *align64,
+                          int *align128, std::string *err) {
+  kpage_status s = load_scalars(p, o, out, align64, align128, err);
+  if (s != KPAGE_OK) return s;
+  Problem &P = *out;
   const size_t G = P.slots, nq = P.n_q, nk = P.n_kv;
   P.q_valid.assign(p->q_valid, p->q_valid + G * nq);
   P.kv_valid.assign(p->kv_valid, p->kv_valid + G * nk);

@@ -59,6 +59,9 @@ struct BwdTables {
   std::vector<int32_t> uncovered;
 };
 
+// Validates the scalar fields of the C descriptor and copies them (no array access).
+kpage_status load_scalars(const kpage_problem *p, const kpage_plan_opts *o, Problem *out, int *align64,
+                          int *align128, std::string *err);
 // Validates the C descriptor and copies it.  Returns KPAGE_OK or an error with `err` set.
 kpage_status load_problem(const kpage_problem *p, const kpage_plan_opts *o, Problem *out, int *align64,
                           int *align128, std::string *err);

@@ -107,6 +107,25 @@ typedef struct {
 kpage_status kpage_plan(const kpage_problem *problem, const kpage_plan_opts *opts,
                         kpage_plan_t **out);
 
+/*
+ * The same forward metadata as kpage_plan(), built on the GPU (section 3.4: the
+ * metadata depends only on the graph and the sizes, so a block selector that runs
+ * on the device can hand its graph to the planner without a host round trip).
+ * The descriptor struct is host memory; its arrays q_valid, kv_valid, kv_offset
+ * (or NULL), q2k_ptr and q2k_idx are DEVICE pointers to the same layouts as for
+ * kpage_plan(), and q2k_idx holds q2k_nnz entries (every q2k_ptr value must lie in
+ * [0, q2k_nnz]).  The plan keeps its own copies of the arrays, so the caller may
+ * reuse them once this returns.  Tables, queues and pair counts are identical to
+ * those of kpage_plan() on the same descriptor.  The descriptor is validated on
+ * the device with the same rules (KPAGE_ERR_INVALID, nothing left allocated).
+ * Work runs on `stream` (hipStream_t as void*), which is synchronised twice
+ * (table sizes, then queue lengths and pair counts).  Backward metadata is built
+ * lazily by the first kpage_attn_bwd() from a host copy of the descriptor;
+ * kpage_plan_export() copies device tables to the host on first use.
+ */
+kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, const kpage_plan_opts *opts,
+                               void *stream, kpage_plan_t **out);
+
 /* Copy the forward tables to the current HIP device on `stream` (idempotent). */
 kpage_status kpage_plan_upload(kpage_plan_t *plan, void *stream);
 

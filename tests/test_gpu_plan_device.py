@@ -1,0 +1,150 @@
+"""GPU-built plans (kpage_plan_device) against host-built plans (kpage_plan).
+
+The host planner is pinned bit for bit to the oracle planner by the CPU tests, so
+equality of every exported forward table, queue and pair count with the host plan is
+equality with the oracle.  Attention through both plans must then be bitwise equal
+(same kernels, same launch order), forward and backward (the device plan builds its
+backward metadata from a host copy of its descriptor).
+"""
+import copy
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_11_amd as K
+from tests.problems import make_problem, random_tensors
+from tests.test_gpu_fwd import EDGE_CASES
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+FWD_TABLES = ("fwd_route", "fwd_walk_ptr", "fwd_walk", "fwd_nfull", "fwd_valid", "q64_queue", "q128_queue")
+BWD_TABLES = ("owner_ptr", "owners", "owner_aligned", "revq_ptr", "revq", "qwalk_ptr", "qwalk", "adj", "bwd_queue")
+FWD_STATS = ("useful", "whole_block", "paged_m128", "nominal", "scheduled")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def same_plans(p, label, **opts):
+    h = K.kpage_plan(p, **opts)
+    d = K.kpage_plan_device(p, **opts)
+    for t in FWD_TABLES:
+        a, b = K.kpage_plan_export(h, t), K.kpage_plan_export(d, t)
+        assert a.dtype == b.dtype and np.array_equal(a, b), (label, t, a.shape, b.shape)
+    sh, sd = K.kpage_plan_stats(h), K.kpage_plan_stats(d)
+    for n in FWD_STATS:
+        assert sh[n] == sd[n], (label, n, sh[n], sd[n])
+    _say(f"  {label}: tables equal (walk {K.kpage_plan_export(d, 'fwd_walk').size} pages, useful {sd['useful']})")
+    return h, d
+
+
+CASES = {
+    "tiny 5x6x10 d=64": lambda: make_workload(1),
+    "16x32x32 two heads": lambda: make_workload(2, heads=[0, 1]),
+    "21x30x52 two heads": lambda: make_workload(3, heads=[0, 1]),
+    "21x45x80 top-87 two heads (per-head graphs)": lambda: make_workload(4, heads=[0, 1]),
+    "SVG2-like partitions two heads": lambda: make_workload(5, heads=[0, 1]),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_device_plan_tables_equal_host_plan(name):
+    _say(f"[plan] {name}")
+    same_plans(CASES[name](), name)
+
+
+@pytest.mark.parametrize("name", list(EDGE_CASES))
+@pytest.mark.parametrize("align", [(0, 0), (32, 16)])
+def test_device_plan_edge_cases(name, align):
+    cq, ck, rows = EDGE_CASES[name]
+    p = make_problem(cq, ck, rows, heads=3, head_dim=128, sort_rows=False)
+    same_plans(p, f"{name} align {align}", align_q64=align[0], align_q128=align[1])
+
+
+def test_device_plan_offsets_with_gaps_and_null_offsets():
+    ck = [50, 128, 3, 97, 16, 0, 33]
+    off = [448, 0, 160, 192, 128, 0, 320]
+    rows = [[0, 1, 2], [3, 4, 6], [6, 0], [1, 3, 5], [2]]
+    p = make_problem([128, 64, 90, 20, 128], ck, rows, heads=2, head_dim=128, kv_offset=off, seq_kv=512,
+                     sort_rows=False)
+    same_plans(p, "offsets with gaps")
+    q = make_problem([128, 64, 90], [128, 40, 7], [[0, 1], [2], [2, 1, 0]], heads=2, head_dim=128)
+    q.kv_offset = None  # NULL offsets: block k at row 128 k
+    same_plans(q, "null offsets")
+
+
+def test_device_plan_attention_is_bitwise_equal():
+    w = make_workload(3, heads=[0, 1], with_do=True)
+    h, d = same_plans(w, "21x30x52 two heads")
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
+    outs = []
+    for plan in (h, d):
+        o, lse = K.attn_fwd(plan, q, k, v, w.scale)
+        dq, dk, dv = K.attn_bwd(plan, q, k, v, o, lse, do, w.scale)
+        torch.cuda.synchronize()
+        outs.append([x.float().cpu().numpy() for x in (o, lse, dq, dk, dv)])
+    for n, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), *outs):
+        assert np.array_equal(a, b, equal_nan=True), n
+    for t in BWD_TABLES:
+        assert np.array_equal(K.kpage_plan_export(h, t), K.kpage_plan_export(d, t)), t
+    sh, sd = K.kpage_plan_stats(h), K.kpage_plan_stats(d)
+    assert sh["bwd_physical"] == sd["bwd_physical"] and sh["bwd_useful_check"] == sd["bwd_useful_check"]
+
+
+def _bad(p, what):
+    with pytest.raises(K.KpageError) as e:
+        K.kpage_plan_device(p)
+    assert e.value.status == K.KPAGE_ERR_INVALID, (what, e.value)
+    # the host planner agrees
+    with pytest.raises(K.KpageError) as e2:
+        K.kpage_plan(p)
+    assert e2.value.status == K.KPAGE_ERR_INVALID, what
+
+
+def test_device_plan_rejects_malformed_descriptors():
+    base = make_problem([128, 64], [128, 40, 7], [[0, 1], [2]], heads=1, head_dim=128)
+    p = copy.deepcopy(base)
+    p.q2k_idx = np.array([0, 0, 2], dtype=np.int32)
+    _bad(p, "duplicate block in a row")
+    p = copy.deepcopy(base)
+    p.q2k_idx = np.array([0, 5, 2], dtype=np.int32)
+    _bad(p, "block id out of range")
+    p = copy.deepcopy(base)
+    p.q_valid = np.array([[129, 64]], dtype=np.int32)
+    _bad(p, "q_valid out of range")
+    p = copy.deepcopy(base)
+    p.kv_valid = np.array([[128, -1, 7]], dtype=np.int32)
+    _bad(p, "kv_valid out of range")
+    p = copy.deepcopy(base)
+    p.kv_offset = np.array([[0, 64, 256]], dtype=np.int64)
+    _bad(p, "overlapping footprints")
+    p = copy.deepcopy(base)
+    p.kv_offset = np.array([[0, 136, 256]], dtype=np.int64)
+    _bad(p, "offset not a multiple of 16")
+    p = copy.deepcopy(base)
+    p.q2k_ptr = np.array([[0, 2, 9]], dtype=np.int64)
+    _bad(p, "row end past the index array")
+
+
+def test_device_plan_time_full_size():
+    """Not a speed assertion: prints host and device planning time on the full-size workloads."""
+    for cfg in (3, 4):
+        w = make_workload(cfg)
+        K.kpage_plan_device(w)  # warm up kernels and allocator
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h = K.kpage_plan(w)
+        th = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        d = K.kpage_plan_device(w)
+        td = time.perf_counter() - t0
+        assert np.array_equal(K.kpage_plan_export(h, "fwd_walk"), K.kpage_plan_export(d, "fwd_walk"))
+        assert np.array_equal(K.kpage_plan_export(h, "q128_queue"), K.kpage_plan_export(d, "q128_queue"))
+        _say(f"  workload {cfg}: forward plan host {th * 1e3:.2f} ms, device {td * 1e3:.2f} ms")
