@@ -28,7 +28,7 @@ TABLES = {
     "q128_queue": (6, np.int32), "owner_ptr": (7, np.int64), "owners": (8, np.int32),
     "owner_aligned": (9, np.uint8), "revq_ptr": (10, np.int64), "revq": (11, np.int32),
     "qwalk_ptr": (12, np.int64), "qwalk": (13, np.int32), "adj": (14, np.uint64),
-    "bwd_queue": (15, np.int32),
+    "bwd_queue": (15, np.int32), "uncovered_ptr": (16, np.int64), "uncovered": (17, np.int32),
 }
 
 EXPORTED_SYMBOLS = (

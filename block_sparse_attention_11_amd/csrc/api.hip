@@ -79,13 +79,14 @@ struct kpage_plan {
   BwdTables B;
   PairStats S;
   bool fwd_on_device = false;
-  // built by kpage_plan_device: the descriptor and the forward tables live on the
-  // device; host copies are made on demand (backward planning, table export)
+  // built by kpage_plan_device: the descriptor and every table live on the device
+  // (the host Problem holds the scalars only); host copies of the tables are made
+  // for export
   bool device_planned = false;
-  bool problem_on_host = true;
   bool fwd_on_host = true;
   DevProblem DP;
   DevFwdTables DF;
+  DevBwdTables DB;  // backward tables of a device-planned plan
   bool bwd_on_device = false;
   // forward device tables
   FwdItem *d_items128 = nullptr, *d_items64 = nullptr;
@@ -224,20 +225,6 @@ void copy_down(std::vector<T> &dst, const T *src, int64_t n) {
   if (n > 0) (void)hipMemcpy(dst.data(), src, size_t(n) * sizeof(T), hipMemcpyDeviceToHost);
 }
 
-// device-planned plans: the descriptor's arrays, copied to the host problem
-void ensure_problem_on_host(PlanT *pl) {
-  if (pl->problem_on_host) return;
-  const DevProblem &D = pl->DP;
-  Problem &P = pl->P;
-  const int64_t G = P.slots, nq = P.n_q, nk = P.n_kv;
-  copy_down(P.q_valid, D.q_valid, G * nq);
-  copy_down(P.kv_valid, D.kv_valid, G * nk);
-  copy_down(P.kv_offset, D.kv_offset, G * nk);
-  copy_down(P.q2k_ptr, D.q2k_ptr, G * (nq + 1));
-  copy_down(P.q2k_idx, D.q2k_idx, D.nnz);
-  pl->problem_on_host = true;
-}
-
 // device-planned plans: the forward tables, copied for export
 void ensure_forward_on_host(PlanT *pl) {
   if (pl->fwd_on_host) return;
@@ -255,14 +242,68 @@ void ensure_forward_on_host(PlanT *pl) {
   pl->fwd_on_host = true;
 }
 
-void ensure_backward_on_host(PlanT *pl) {
-  ensure_problem_on_host(pl);
-  if (!pl->B.built) build_backward(pl->P, &pl->B, &pl->S);
+void *plan_alloc(PlanT *pl, size_t bytes) {
+  void *p = nullptr;
+  if (hipMalloc(&p, std::max<size_t>(bytes, 16)) != hipSuccess) return nullptr;
+  pl->allocations.push_back(p);
+  return p;
+}
+
+// device-planned plans: the backward tables are built by kernels from the device
+// descriptor and the forward planner's page table
+kpage_status build_backward_on_device(PlanT *pl, hipStream_t stream) {
+  std::string err;
+  DevBwdTables &T = pl->DB;
+  kpage_status s = build_backward_device(
+      pl->DP, pl->DF.page_block, stream, [pl](size_t b) { return plan_alloc(pl, b); }, &T, &err);
+  if (s != KPAGE_OK) return fail(s, err);
+  pl->d_bitems = T.items;
+  pl->n_bitems = int(T.n_items);
+  pl->d_owners = T.owners;
+  pl->d_kmask = T.kmask;
+  pl->d_qpages = T.qpages;
+  pl->d_adj = T.adj;
+  pl->d_uncovered = T.uncovered;
+  pl->d_uncovered_ptr = T.uncovered_ptr;
+  pl->max_uncovered = T.max_uncovered;
+  pl->S.bwd_physical = T.bwd_physical;
+  pl->S.bwd_useful_check = T.bwd_useful_check;
+  pl->bwd_on_device = true;
+  return KPAGE_OK;
+}
+
+kpage_status ensure_backward_on_host(PlanT *pl) {
+  if (pl->B.built) return KPAGE_OK;
+  if (!pl->device_planned) {
+    build_backward(pl->P, &pl->B, &pl->S);
+    return KPAGE_OK;
+  }
+  if (!pl->bwd_on_device) {  // export before the first backward call
+    const kpage_status s = build_backward_on_device(pl, nullptr);
+    if (s != KPAGE_OK) return s;
+  }
+  const DevBwdTables &T = pl->DB;
+  BwdTables &B = pl->B;
+  const int64_t G = pl->P.slots;
+  copy_down(B.owner_ptr, T.owner_ptr, G + 1);
+  copy_down(B.owners, T.owners, T.n_own * kOwnerSlots);
+  copy_down(B.aligned, T.aligned, T.n_own);
+  copy_down(B.revq_ptr, T.revq_ptr, T.n_own + 1);
+  copy_down(B.revq, T.revq, T.revq_total);
+  copy_down(B.qwalk_ptr, T.qwalk_ptr, T.n_own + 1);
+  copy_down(B.qwalk, T.qwalk, T.qwalk_total);
+  copy_down(B.adj, T.adj, T.qwalk_total / kOwnerSlots);
+  copy_down(B.bwd_queue, T.bwd_queue, 2 * T.n_items);
+  copy_down(B.uncovered_ptr, T.uncovered_ptr, G + 1);
+  copy_down(B.uncovered, T.uncovered, T.uncovered_total);
+  B.built = true;
+  return KPAGE_OK;
 }
 
 kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
-  ensure_backward_on_host(pl);
   if (pl->bwd_on_device) return KPAGE_OK;
+  if (pl->device_planned) return build_backward_on_device(pl, stream);
+  ensure_backward_on_host(pl);
   const Problem &P = pl->P;
   const BwdTables &B = pl->B;
   const int nk = P.n_kv;
@@ -380,12 +421,7 @@ kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Problem &P = pl->P;
   const int64_t G = P.slots, nq = P.n_q, nk = P.n_kv;
-  auto alloc = [pl](size_t bytes) -> void * {
-    void *p = nullptr;
-    if (hipMalloc(&p, std::max<size_t>(bytes, 16)) != hipSuccess) return nullptr;
-    pl->allocations.push_back(p);
-    return p;
-  };
+  auto alloc = [pl](size_t bytes) { return plan_alloc(pl, bytes); };
   auto own = [&](const void *src, size_t bytes, const char *what) -> void * {
     void *d = alloc(bytes);
     if (d && bytes) {
@@ -422,7 +458,6 @@ kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, co
     return fail(s, err);
   }
   pl->device_planned = true;
-  pl->problem_on_host = false;
   pl->fwd_on_host = false;
   pl->S = pl->DF.stats;
   pl->d_pages = pl->DF.pages;
@@ -546,8 +581,12 @@ kpage_status kpage_plan_stats(const kpage_plan_t *plan, kpage_pair_stats *out) {
 kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf, size_t *bytes) {
   if (!plan || !bytes) return fail(KPAGE_ERR_INVALID, "plan or bytes is NULL");
   if (table_id < 0 || table_id >= KPAGE_T_COUNT) return fail(KPAGE_ERR_INVALID, "unknown table id");
-  if (table_id >= KPAGE_T_OWNER_PTR) ensure_backward_on_host(plan);
-  else ensure_forward_on_host(plan);
+  if (table_id >= KPAGE_T_OWNER_PTR) {
+    const kpage_status s = ensure_backward_on_host(plan);
+    if (s != KPAGE_OK) return s;
+  } else {
+    ensure_forward_on_host(plan);
+  }
   const void *src = nullptr;
   size_t n = 0;
   switch (table_id) {
@@ -572,6 +611,8 @@ kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf,
     KPAGE_TABLE(KPAGE_T_QWALK, plan->B.qwalk)
     KPAGE_TABLE(KPAGE_T_ADJ, plan->B.adj)
     KPAGE_TABLE(KPAGE_T_BWD_QUEUE, plan->B.bwd_queue)
+    KPAGE_TABLE(KPAGE_T_UNCOVERED_PTR, plan->B.uncovered_ptr)
+    KPAGE_TABLE(KPAGE_T_UNCOVERED, plan->B.uncovered)
 #undef KPAGE_TABLE
   }
   if (!host_buf) {

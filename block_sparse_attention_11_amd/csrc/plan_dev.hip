@@ -326,6 +326,7 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
   auto a64 = [&](int64_t n) { return static_cast<int64_t *>(alloc(size_t(std::max<int64_t>(n, 1)) * 8)); };
   Summary *d_sum = static_cast<Summary *>(alloc(sizeof(Summary)));
   int32_t *owner = a32(int64_t(p.slots) * n_pages);
+  t->page_block = owner;
   int64_t *len = a64(GQ);
   t->route = a32(GQ);
   t->nfull = a32(GQ);
@@ -421,6 +422,499 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
   t->stats.paged_m128 = h.paged_m128;
   t->stats.nominal = h.nominal;
   t->stats.scheduled = h.scheduled;
+  return KPAGE_OK;
+}
+
+
+// ---------------------------------------------------------------------------------
+// Backward tables (section 3.3).  Per graph slot: owners (3.3.1), the owner x Q-block
+// bitmap compacted into reverse-Q lists, Q-page walks with dummies to a multiple of 8
+// pages (3.3.2), one 64-bit adjacency word per step (3.3.3, eq. 6), the work order of
+// section 3.4 (descending step count, then (bh, owner)) and the pages outside every
+// block footprint.  Bitmaps: edge[slot][q][n_kv / 32] (a selected pair with c_q > 0
+// and c_k > 0), own_q[slot][owner][n_q / 32] (the owner holds a page of a block that q
+// selects).
+namespace {
+
+struct BwdSummary {
+  int64_t n_own, revq_total, qwalk_total, uncovered_total;
+  int32_t max_uncovered, pad;
+  unsigned long long useful_check;
+};
+
+__device__ __forceinline__ uint32_t page_mask(int c, int j) {
+  return (j + 1) * kPageRows <= c ? kFullMask : tail_mask(c);
+}
+
+// own_info packing: blocks in the owner | pages in the owner << 16
+__device__ __forceinline__ int32_t pack_info(int blocks, int pages) { return blocks | (pages << 16); }
+
+// Owners of slot blockIdx.x: every full block is an owner of its own, in block order;
+// the partial blocks then fill owners next-fit, in block order (a block opens a new
+// owner when its pages do not fit in the current one).  One thread runs the next-fit
+// over block sizes staged in LDS.
+constexpr int kStage = 4 * kScanThreads;
+
+__global__ __launch_bounds__(kScanThreads) void k_owners(DevProblem p, int32_t *owner_of, int32_t *pos_of,
+                                                         int32_t *own_info, int32_t *n_own) {
+  __shared__ int64_t lds[kScanThreads];
+  __shared__ int32_t s_ck[kStage];
+  const int g = blockIdx.x;
+  const int64_t gb = int64_t(g) * p.n_kv;
+  const int32_t *ck = p.kv_valid + gb;
+  int64_t carry = 0;
+  for (int base = 0; base < p.n_kv; base += kScanThreads) {
+    const int k = base + threadIdx.x;
+    const int c = k < p.n_kv ? ck[k] : 0;
+    int64_t total;
+    const int64_t pre = carry + block_scan(c == kBlockRows ? 1 : 0, lds, &total);
+    if (k < p.n_kv && c == kBlockRows) {
+      owner_of[gb + k] = int32_t(pre);
+      pos_of[gb + k] = 0;
+      own_info[gb + pre] = pack_info(1, kOwnerSlots);
+    } else if (k < p.n_kv && c == 0) {
+      owner_of[gb + k] = -1;
+      pos_of[gb + k] = 0;
+    }
+    carry += total;
+  }
+  int cur = -1, used = 0, blocks = 0, n = int(carry);
+  for (int base = 0; base < p.n_kv; base += kStage) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kStage; i += kScanThreads) s_ck[i] = base + i < p.n_kv ? ck[base + i] : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int m = min(kStage, p.n_kv - base);
+      for (int i = 0; i < m; ++i) {
+        const int c = s_ck[i];
+        if (c == 0 || c == kBlockRows) continue;
+        const int np = pages_of(c);
+        if (cur < 0 || kOwnerSlots - used < np) {
+          if (cur >= 0) own_info[gb + cur] = pack_info(blocks, used);
+          cur = n++;
+          used = 0;
+          blocks = 0;
+        }
+        owner_of[gb + base + i] = cur;
+        pos_of[gb + base + i] = used;
+        used += np;
+        ++blocks;
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (cur >= 0) own_info[gb + cur] = pack_info(blocks, used);
+    n_own[g] = n;
+  }
+}
+
+// pages of slot blockIdx.x outside every block footprint: count, or (unc != NULL)
+// write them in page order from unc_ptr[slot]
+__global__ __launch_bounds__(kScanThreads) void k_uncovered(DevProblem p, const int32_t *page_block, int32_t *count,
+                                                            const int64_t *unc_ptr, int32_t *unc) {
+  __shared__ int64_t lds[kScanThreads];
+  const int g = blockIdx.x;
+  const int64_t n_pages = p.seq_kv / kPageRows;
+  const int32_t *pb = page_block + int64_t(g) * n_pages;
+  int64_t carry = unc ? unc_ptr[g] : 0;
+  for (int64_t base = 0; base < n_pages; base += kScanThreads) {
+    const int64_t pg = base + threadIdx.x;
+    const int hole = pg < n_pages && pb[pg] < 0 ? 1 : 0;
+    int64_t total;
+    const int64_t pre = carry + block_scan(hole, lds, &total);
+    if (unc && hole) unc[pre] = int32_t(pg);
+    carry += total;
+  }
+  if (!unc && threadIdx.x == 0) count[g] = int32_t(carry);
+}
+
+// owner_ptr and uncovered_ptr over slots
+__global__ __launch_bounds__(kScanThreads) void k_slot_scans(int G, const int32_t *n_own, const int32_t *n_unc,
+                                                             int64_t *owner_ptr, int64_t *unc_ptr, BwdSummary *s) {
+  __shared__ int64_t lds[kScanThreads];
+  int64_t c1 = 0, c2 = 0;
+  int mx = 0;
+  for (int base = 0; base < G; base += kScanThreads) {
+    const int g = base + threadIdx.x;
+    const int64_t a = g < G ? n_own[g] : 0, b = g < G ? n_unc[g] : 0;
+    int64_t t1, t2;
+    const int64_t p1 = c1 + block_scan(a, lds, &t1);
+    const int64_t p2 = c2 + block_scan(b, lds, &t2);
+    if (g < G) {
+      owner_ptr[g] = p1;
+      unc_ptr[g] = p2;
+    }
+    mx = max(mx, int(b));
+    c1 += t1;
+    c2 += t2;
+  }
+  atomicMax(&s->max_uncovered, mx);
+  if (threadIdx.x == 0) {
+    owner_ptr[G] = c1;
+    unc_ptr[G] = c2;
+    s->n_own = c1;
+    s->uncovered_total = c2;
+  }
+}
+
+// per (slot, query block): edge bits of its row, its bit in the owner x Q bitmap of
+// every owner it reaches, and its bit in the slot's full-query-block mask
+__global__ void k_edges(DevProblem p, const int32_t *owner_of, int nkw, int nqw, uint32_t *edge, uint32_t *own_q,
+                        uint32_t *fullq) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(p.slots) * p.n_q) return;
+  const int g = int(i / p.n_q), q = int(i % p.n_q);
+  const int cq = p.q_valid[i];
+  const uint32_t qbit = 1u << (q & 31);
+  if (cq == kBlockRows) atomicOr(&fullq[int64_t(g) * nqw + (q >> 5)], qbit);
+  if (cq == 0) return;
+  const int64_t a = p.q2k_ptr[int64_t(g) * (p.n_q + 1) + q], b = p.q2k_ptr[int64_t(g) * (p.n_q + 1) + q + 1];
+  uint32_t *row = edge + i * nkw;  // written by this thread only
+  for (int64_t e = a; e < b; ++e) {
+    const int k = p.q2k_idx[e];
+    if (p.kv_valid[int64_t(g) * p.n_kv + k] == 0) continue;
+    row[k >> 5] |= 1u << (k & 31);
+    const int t = owner_of[int64_t(g) * p.n_kv + k];
+    atomicOr(&own_q[(int64_t(g) * p.n_kv + t) * nqw + (q >> 5)], qbit);
+  }
+}
+
+// per (slot, owner): reverse-Q count, Q-walk length (full query blocks first, 8 pages
+// each, then the pages of partial ones, padded to a multiple of 8), slot, alignment
+// flag and the empty page slots of the owner table
+__global__ void k_owner_counts(DevProblem p, const int64_t *owner_ptr, const int32_t *n_own, const int32_t *own_info,
+                               const uint32_t *own_q, const uint32_t *fullq, int nqw, int64_t *rcount, int64_t *qlen,
+                               int32_t *owner_slot, uint8_t *aligned, int32_t *owners, uint32_t *kmask) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(p.slots) * p.n_kv) return;
+  const int g = int(i / p.n_kv), t = int(i % p.n_kv);
+  if (t >= n_own[g]) return;
+  const int64_t tg = owner_ptr[g] + t;
+  const uint32_t *bm = own_q + i * nqw;
+  const uint32_t *fm = fullq + int64_t(g) * nqw;
+  int64_t r = 0, pages = 0;
+  for (int w = 0; w < nqw; ++w) {
+    const uint32_t bits = bm[w];
+    r += __popc(bits);
+    pages += int64_t(kOwnerSlots) * __popc(bits & fm[w]);
+    uint32_t part = bits & ~fm[w];
+    while (part) {
+      const int b = __ffs(part) - 1;
+      part &= part - 1;
+      pages += pages_of(p.q_valid[int64_t(g) * p.n_q + 32 * w + b]);
+    }
+  }
+  rcount[tg] = r;
+  qlen[tg] = (pages + kOwnerSlots - 1) / kOwnerSlots * kOwnerSlots;
+  owner_slot[tg] = g;
+  const int32_t info = own_info[i];
+  const int blocks = info & 0xFFFF, np = info >> 16;
+  aligned[tg] = (blocks == 1 && np == kOwnerSlots) ? 1 : 0;
+  for (int j = np; j < kOwnerSlots; ++j) {
+    owners[tg * kOwnerSlots + j] = -1;
+    kmask[tg * kOwnerSlots + j] = 0u;
+  }
+}
+
+// per (slot, block): the block's pages and row masks in its owner
+__global__ void k_owner_pages(DevProblem p, const int32_t *owner_of, const int32_t *pos_of, const int64_t *owner_ptr,
+                              int32_t *owners, uint32_t *kmask) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(p.slots) * p.n_kv) return;
+  const int t = owner_of[i];
+  if (t < 0) return;
+  const int g = int(i / p.n_kv), k = int(i % p.n_kv);
+  const int c = p.kv_valid[i];
+  const int64_t at = (owner_ptr[g] + t) * kOwnerSlots + pos_of[i];
+  const int32_t pg0 = int32_t(kv_off(p, g, k) / kPageRows);
+  for (int j = 0; j < pages_of(c); ++j) {
+    owners[at + j] = pg0 + j;
+    kmask[at + j] = page_mask(c, j);
+  }
+}
+
+// revq_ptr and qwalk_ptr over all owners
+__global__ __launch_bounds__(kScanThreads) void k_owner_scans(const BwdSummary *s, const int64_t *rcount,
+                                                              const int64_t *qlen, int64_t *revq_ptr,
+                                                              int64_t *qwalk_ptr, BwdSummary *out) {
+  __shared__ int64_t lds[kScanThreads];
+  const int64_t n = s->n_own;
+  int64_t c1 = 0, c2 = 0;
+  for (int64_t base = 0; base < n; base += kScanThreads) {
+    const int64_t t = base + threadIdx.x;
+    int64_t t1, t2;
+    const int64_t p1 = c1 + block_scan(t < n ? rcount[t] : 0, lds, &t1);
+    const int64_t p2 = c2 + block_scan(t < n ? qlen[t] : 0, lds, &t2);
+    if (t < n) {
+      revq_ptr[t] = p1;
+      qwalk_ptr[t] = p2;
+    }
+    c1 += t1;
+    c2 += t2;
+  }
+  if (threadIdx.x == 0) {
+    revq_ptr[n] = c1;
+    qwalk_ptr[n] = c2;
+    out->revq_total = c1;
+    out->qwalk_total = c2;
+  }
+}
+
+// per owner: reverse-Q list (ascending q) and Q-page walk
+__global__ void k_owner_fill(DevProblem p, int64_t n_own, const int64_t *owner_ptr, const int32_t *owner_slot,
+                             const uint32_t *own_q, const uint32_t *fullq, int nqw, const int64_t *revq_ptr,
+                             const int64_t *qwalk_ptr, int32_t *revq, int32_t *qwalk, int32_t *qpages) {
+  const int64_t tg = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (tg >= n_own) return;
+  const int g = owner_slot[tg];
+  const int64_t t = tg - owner_ptr[g];
+  const uint32_t *bm = own_q + (int64_t(g) * p.n_kv + t) * nqw;
+  const uint32_t *fm = fullq + int64_t(g) * nqw;
+  int64_t r = revq_ptr[tg];
+  for (int w = 0; w < nqw; ++w)
+    for (uint32_t bits = bm[w]; bits; bits &= bits - 1) revq[r++] = 32 * w + __ffs(bits) - 1;
+  int64_t pos = qwalk_ptr[tg];
+  const int64_t end = qwalk_ptr[tg + 1];
+  int32_t first = -1;
+  auto emit = [&](int32_t qp) {
+    if (first < 0) first = qp;
+    qwalk[pos] = qp;
+    qpages[pos] = qp >= 0 ? qp : first;
+    ++pos;
+  };
+  for (int w = 0; w < nqw; ++w)  // full query blocks: all 8 pages
+    for (uint32_t bits = bm[w] & fm[w]; bits; bits &= bits - 1) {
+      const int q = 32 * w + __ffs(bits) - 1;
+      for (int j = 0; j < kOwnerSlots; ++j) emit(kOwnerSlots * q + j);
+    }
+  for (int w = 0; w < nqw; ++w)  // partial query blocks: their valid pages
+    for (uint32_t bits = bm[w] & ~fm[w]; bits; bits &= bits - 1) {
+      const int q = 32 * w + __ffs(bits) - 1;
+      const int np = pages_of(p.q_valid[int64_t(g) * p.n_q + q]);
+      for (int j = 0; j < np; ++j) emit(kOwnerSlots * q + j);
+    }
+  while (pos < end) emit(-1);
+}
+
+// largest i in [0, n) with ptr[i] <= x (ptr non-decreasing, ptr[0] <= x)
+__device__ __forceinline__ int64_t upper_index(const int64_t *ptr, int64_t n, int64_t x) {
+  int64_t lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) / 2;
+    if (ptr[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// per 8-page step: adjacency word, bit 8 j + i = (Q page j of the step, owner page i)
+// belong to a selected block pair; pair count of the step for the visited-pair check
+__global__ void k_adj(DevProblem p, const int32_t *page_block, int64_t n_own, int64_t n_steps, unsigned long long mult,
+                      const int32_t *owner_slot, const int64_t *qwalk_ptr, const int32_t *owners, const int32_t *qwalk,
+                      const uint32_t *edge, int nkw, uint64_t *adj, BwdSummary *s) {
+  __shared__ unsigned long long acc;
+  if (threadIdx.x == 0) acc = 0;
+  __syncthreads();
+  const int64_t st = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (st < n_steps) {
+    const int64_t pos = int64_t(kOwnerSlots) * st;
+    const int64_t tg = upper_index(qwalk_ptr, n_own, pos);
+    const int g = owner_slot[tg];
+    const int64_t n_pages = p.seq_kv / kPageRows;
+    int kb[kOwnerSlots];
+    int kcount[kOwnerSlots];
+    for (int i = 0; i < kOwnerSlots; ++i) {
+      const int32_t kp = owners[tg * kOwnerSlots + i];
+      kb[i] = -1;
+      kcount[i] = 0;
+      if (kp < 0) continue;
+      const int k = page_block[int64_t(g) * n_pages + kp];
+      kb[i] = k;
+      kcount[i] = __popc(page_mask(p.kv_valid[int64_t(g) * p.n_kv + k], int(kp - kv_off(p, g, k) / kPageRows)));
+    }
+    uint64_t word = 0;
+    unsigned long long pairs = 0;
+    for (int j = 0; j < kOwnerSlots; ++j) {
+      const int32_t qp = qwalk[pos + j];
+      if (qp < 0) continue;
+      const int qb = qp / kOwnerSlots;
+      const int qcount = __popc(page_mask(p.q_valid[int64_t(g) * p.n_q + qb], qp % kOwnerSlots));
+      const uint32_t *row = edge + (int64_t(g) * p.n_q + qb) * nkw;
+      for (int i = 0; i < kOwnerSlots; ++i) {
+        if (kb[i] < 0 || !((row[kb[i] >> 5] >> (kb[i] & 31)) & 1u)) continue;
+        word |= uint64_t(1) << (kOwnerSlots * j + i);
+        pairs += (unsigned long long)qcount * (unsigned long long)kcount[i];
+      }
+    }
+    adj[st] = word;
+    if (pairs) atomicAdd(&acc, mult * pairs);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && acc) atomicAdd(&s->useful_check, acc);
+}
+
+// per (bh, owner within slot), f = that pair's index in (bh, owner) order: queue sort
+// key (steps descending, then f) and the launch item at its XCD position
+__global__ void k_bwd_items(DevProblem p, int64_t n_own, int64_t n_items, const int64_t *owner_ptr,
+                            const int64_t *qwalk_ptr, const uint8_t *aligned, unsigned long long *keys, BwdItem *items) {
+  const int64_t f = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (f >= n_items) return;
+  int bh;
+  int64_t tg;
+  if (p.per_head) {
+    bh = int(upper_index(owner_ptr, p.slots, f));
+    tg = f;
+  } else {
+    bh = int(f / n_own);
+    tg = f % n_own;
+  }
+  const int32_t steps = int32_t((qwalk_ptr[tg + 1] - qwalk_ptr[tg]) / kOwnerSlots);
+  keys[f] = ((unsigned long long)(0x7FFFFFFF - steps) << 32) | (unsigned long long)(uint32_t)f;
+  BwdItem x{};
+  x.qwalk_off = qwalk_ptr[tg];
+  x.bh = bh;
+  x.owner = int32_t(tg);
+  x.n_steps = steps;
+  x.aligned = aligned[tg];
+  items[xcd_position(f, n_items)] = x;
+}
+
+__global__ void k_bwd_queue_out(DevProblem p, int64_t n_own, int64_t n_items, const int64_t *owner_ptr,
+                                const unsigned long long *keys, int32_t *queue) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n_items) return;
+  const int64_t f = int64_t(keys[i] & 0xFFFFFFFFull);
+  int bh;
+  int64_t t;
+  if (p.per_head) {
+    bh = int(upper_index(owner_ptr, p.slots, f));
+    t = f - owner_ptr[bh];
+  } else {
+    bh = int(f / n_own);
+    t = f % n_own;
+  }
+  queue[2 * i] = bh;
+  queue[2 * i + 1] = int32_t(t);
+}
+
+}  // namespace
+
+kpage_status build_backward_device(const DevProblem &p, const int32_t *page_block, hipStream_t st,
+                                   const DevAlloc &alloc, DevBwdTables *t, std::string *err) {
+  const int G = p.slots;
+  const int64_t GK = int64_t(G) * p.n_kv, GQ = int64_t(G) * p.n_q;
+  const int64_t n_pages = p.seq_kv / kPageRows;
+  const int nkw = (p.n_kv + 31) / 32, nqw = (p.n_q + 31) / 32;
+  const unsigned long long mult = p.per_head ? 1ull : (unsigned long long)p.batch * p.heads;
+  bool oom = false;
+  auto A = [&](int64_t n, size_t elem) -> void * {
+    void *q = alloc(size_t(std::max<int64_t>(n, 1)) * elem);
+    if (!q) oom = true;
+    return q;
+  };
+  BwdSummary *d_sum = static_cast<BwdSummary *>(A(1, sizeof(BwdSummary)));
+  int32_t *owner_of = static_cast<int32_t *>(A(GK, 4));
+  int32_t *pos_of = static_cast<int32_t *>(A(GK, 4));
+  int32_t *own_info = static_cast<int32_t *>(A(GK, 4));
+  int32_t *n_own = static_cast<int32_t *>(A(G, 4));
+  int32_t *n_unc = static_cast<int32_t *>(A(G, 4));
+  uint32_t *edge = static_cast<uint32_t *>(A(GQ * nkw, 4));
+  uint32_t *own_q = static_cast<uint32_t *>(A(GK * nqw, 4));
+  uint32_t *fullq = static_cast<uint32_t *>(A(int64_t(G) * nqw, 4));
+  int64_t *rcount = static_cast<int64_t *>(A(GK, 8));
+  int64_t *qlen = static_cast<int64_t *>(A(GK, 8));
+  int32_t *owner_slot = static_cast<int32_t *>(A(GK, 4));
+  // owner-indexed tables at their upper bound (at most one owner per block)
+  t->owner_ptr = static_cast<int64_t *>(A(G + 1, 8));
+  t->owners = static_cast<int32_t *>(A(GK * kOwnerSlots, 4));
+  t->kmask = static_cast<uint32_t *>(A(GK * kOwnerSlots, 4));
+  t->aligned = static_cast<uint8_t *>(A(GK, 1));
+  t->revq_ptr = static_cast<int64_t *>(A(GK + 1, 8));
+  t->qwalk_ptr = static_cast<int64_t *>(A(GK + 1, 8));
+  t->uncovered_ptr = static_cast<int64_t *>(A(G + 1, 8));
+  t->uncovered = static_cast<int32_t *>(A(int64_t(G) * n_pages, 4));
+  if (oom) {
+    *err = "device allocation failed while planning the backward";
+    return KPAGE_ERR_OOM;
+  }
+  hipError_t e;
+#define KP_CHECK(call)                                                   \
+  do {                                                                   \
+    if ((e = (call)) != hipSuccess) {                                    \
+      *err = std::string(#call) + ": " + hipGetErrorString(e);           \
+      return KPAGE_ERR_HIP;                                              \
+    }                                                                    \
+  } while (0)
+  const int TB = 256;
+  KP_CHECK(hipMemsetAsync(d_sum, 0, sizeof(BwdSummary), st));
+  KP_CHECK(hipMemsetAsync(edge, 0, size_t(std::max<int64_t>(GQ * nkw, 1)) * 4, st));
+  KP_CHECK(hipMemsetAsync(own_q, 0, size_t(std::max<int64_t>(GK * nqw, 1)) * 4, st));
+  KP_CHECK(hipMemsetAsync(fullq, 0, size_t(std::max<int64_t>(int64_t(G) * nqw, 1)) * 4, st));
+  hipLaunchKernelGGL(k_owners, dim3(G), dim3(kScanThreads), 0, st, p, owner_of, pos_of, own_info, n_own);
+  hipLaunchKernelGGL(k_uncovered, dim3(G), dim3(kScanThreads), 0, st, p, page_block, n_unc, nullptr, nullptr);
+  hipLaunchKernelGGL(k_slot_scans, dim3(1), dim3(kScanThreads), 0, st, G, n_own, n_unc, t->owner_ptr,
+                     t->uncovered_ptr, d_sum);
+  hipLaunchKernelGGL(k_uncovered, dim3(G), dim3(kScanThreads), 0, st, p, page_block, n_unc, t->uncovered_ptr,
+                     t->uncovered);
+  hipLaunchKernelGGL(k_edges, dim3(blocks_for(GQ, TB)), dim3(TB), 0, st, p, owner_of, nkw, nqw, edge, own_q, fullq);
+  hipLaunchKernelGGL(k_owner_counts, dim3(blocks_for(GK, TB)), dim3(TB), 0, st, p, t->owner_ptr, n_own, own_info,
+                     own_q, fullq, nqw, rcount, qlen, owner_slot, t->aligned, t->owners, t->kmask);
+  hipLaunchKernelGGL(k_owner_pages, dim3(blocks_for(GK, TB)), dim3(TB), 0, st, p, owner_of, pos_of, t->owner_ptr,
+                     t->owners, t->kmask);
+  hipLaunchKernelGGL(k_owner_scans, dim3(1), dim3(kScanThreads), 0, st, d_sum, rcount, qlen, t->revq_ptr,
+                     t->qwalk_ptr, d_sum);
+  KP_CHECK(hipGetLastError());
+  BwdSummary h{};
+  KP_CHECK(hipMemcpyAsync(&h, d_sum, sizeof(BwdSummary), hipMemcpyDeviceToHost, st));
+  KP_CHECK(hipStreamSynchronize(st));
+  t->n_own = h.n_own;
+  t->revq_total = h.revq_total;
+  t->qwalk_total = h.qwalk_total;
+  t->uncovered_total = h.uncovered_total;
+  t->max_uncovered = h.max_uncovered;
+  t->n_items = int64_t(mult) * h.n_own;
+  if (t->n_items >= (int64_t(1) << 31)) {
+    *err = "more than 2^31 backward work items";
+    return KPAGE_ERR_UNSUPPORTED;
+  }
+  const int64_t n_steps = h.qwalk_total / kOwnerSlots;
+  t->revq = static_cast<int32_t *>(A(h.revq_total, 4));
+  t->qwalk = static_cast<int32_t *>(A(h.qwalk_total, 4));
+  t->qpages = static_cast<int32_t *>(A(h.qwalk_total, 4));
+  t->adj = static_cast<uint64_t *>(A(n_steps, 8));
+  t->items = static_cast<BwdItem *>(A(t->n_items, sizeof(BwdItem)));
+  t->bwd_queue = static_cast<int32_t *>(A(2 * t->n_items, 4));
+  unsigned long long *keys = static_cast<unsigned long long *>(A(2 * t->n_items, 8));
+  if (oom) {
+    *err = "device allocation failed while planning the backward";
+    return KPAGE_ERR_OOM;
+  }
+  if (h.n_own > 0) {
+    hipLaunchKernelGGL(k_owner_fill, dim3(blocks_for(h.n_own, TB)), dim3(TB), 0, st, p, h.n_own, t->owner_ptr,
+                       owner_slot, own_q, fullq, nqw, t->revq_ptr, t->qwalk_ptr, t->revq, t->qwalk, t->qpages);
+    if (n_steps > 0)
+      hipLaunchKernelGGL(k_adj, dim3(blocks_for(n_steps, TB)), dim3(TB), 0, st, p, page_block, h.n_own, n_steps, mult,
+                         owner_slot, t->qwalk_ptr, t->owners, t->qwalk, edge, nkw, t->adj, d_sum);
+    hipLaunchKernelGGL(k_bwd_items, dim3(blocks_for(t->n_items, TB)), dim3(TB), 0, st, p, h.n_own, t->n_items,
+                       t->owner_ptr, t->qwalk_ptr, t->aligned, keys, t->items);
+    size_t tmp_bytes = 0;
+    KP_CHECK(hipcub::DeviceRadixSort::SortKeys(nullptr, tmp_bytes, keys, keys + t->n_items, int(t->n_items), 0, 64,
+                                               st));
+    void *tmp = A(int64_t(std::max<size_t>(tmp_bytes, 16)), 1);
+    if (oom) {
+      *err = "device allocation failed while planning the backward";
+      return KPAGE_ERR_OOM;
+    }
+    KP_CHECK(hipcub::DeviceRadixSort::SortKeys(tmp, tmp_bytes, keys, keys + t->n_items, int(t->n_items), 0, 64, st));
+    hipLaunchKernelGGL(k_bwd_queue_out, dim3(blocks_for(t->n_items, TB)), dim3(TB), 0, st, p, h.n_own, t->n_items,
+                       t->owner_ptr, keys + t->n_items, t->bwd_queue);
+  }
+  KP_CHECK(hipGetLastError());
+  KP_CHECK(hipMemcpyAsync(&h, d_sum, sizeof(BwdSummary), hipMemcpyDeviceToHost, st));
+  KP_CHECK(hipStreamSynchronize(st));
+#undef KP_CHECK
+  t->bwd_physical = mult * (unsigned long long)kBlockRows * kBlockRows * (unsigned long long)n_steps;
+  t->bwd_useful_check = h.useful_check;
   return KPAGE_OK;
 }
 

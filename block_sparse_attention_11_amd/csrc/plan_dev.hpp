@@ -1,8 +1,8 @@
-// GPU-side construction of the forward page tables (KPage paper, sections 3.2.1-3.2.4
-// and 3.4): the same walks, routes, validity words, queues and pair statistics as the
-// host planner, built by kernels from a descriptor whose arrays live in device memory,
-// so that a block selector running on the GPU feeds the planner without a round trip
-// through host memory.
+// GPU-side construction of the page tables (KPage paper, sections 3.2.1-3.2.4, 3.3 and
+// 3.4): the same walks, routes, validity words, queues, owners, reverse-Q lists,
+// adjacency words and pair statistics as the host planner, built by kernels from a
+// descriptor whose arrays live in device memory, so that a block selector running on
+// the GPU feeds the planner without a round trip through host memory.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,9 +37,31 @@ struct DevFwdTables {
   int32_t *q64_queue = nullptr, *q128_queue = nullptr;  // (bh, q) pairs, queue order
   FwdItem *items128 = nullptr, *items64 = nullptr;      // launch order (see api.hip)
   int32_t *redo = nullptr;
+  int32_t *page_block = nullptr;  // [slots][seq_kv / 16] block whose footprint holds the page, -1 none
   int64_t walk_total = 0;
   int n_q64 = 0, n_q128 = 0, n_zero = 0;  // queue entries, empty query blocks
   PairStats stats;
+};
+
+// Device backward tables (section 3.3), same contents and order as BwdTables.
+struct DevBwdTables {
+  int64_t *owner_ptr = nullptr;      // [slots + 1]
+  int32_t *owners = nullptr;         // [n_own][8] page ids, -1 = empty slot
+  uint32_t *kmask = nullptr;         // [n_own][8] row masks of the owner pages
+  uint8_t *aligned = nullptr;        // [n_own]
+  int64_t *revq_ptr = nullptr;       // [n_own + 1]
+  int32_t *revq = nullptr;
+  int64_t *qwalk_ptr = nullptr;      // [n_own + 1]
+  int32_t *qwalk = nullptr;          // Q page ids (8 q + j), -1 = dummy
+  int32_t *qpages = nullptr;         // the same with dummies pointed at the walk's first page
+  uint64_t *adj = nullptr;           // one word per 8-page step
+  int32_t *bwd_queue = nullptr;      // (bh, owner within slot) pairs, queue order
+  BwdItem *items = nullptr;          // launch order (bh, owner), XCD-interleaved
+  int64_t *uncovered_ptr = nullptr;  // [slots + 1]
+  int32_t *uncovered = nullptr;
+  int64_t n_own = 0, revq_total = 0, qwalk_total = 0, n_items = 0, uncovered_total = 0;
+  int max_uncovered = 0;
+  uint64_t bwd_physical = 0, bwd_useful_check = 0;
 };
 
 using DevAlloc = std::function<void *(size_t)>;
@@ -49,5 +71,11 @@ using DevAlloc = std::function<void *(size_t)>;
 // once for the table sizes, once at the end for the queue lengths and pair counts.
 kpage_status build_forward_device(const DevProblem &p, int align64, int align128, hipStream_t stream,
                                   const DevAlloc &alloc, DevFwdTables *t, std::string *err);
+
+// Builds the backward tables on `stream` from a descriptor already validated by
+// build_forward_device and that call's page_block table.  Synchronises `stream` twice
+// (table sizes, then pair counts).
+kpage_status build_backward_device(const DevProblem &p, const int32_t *page_block, hipStream_t stream,
+                                   const DevAlloc &alloc, DevBwdTables *t, std::string *err);
 
 }  // namespace kpage

@@ -119,9 +119,13 @@ kpage_status kpage_plan(const kpage_problem *problem, const kpage_plan_opts *opt
  * those of kpage_plan() on the same descriptor.  The descriptor is validated on
  * the device with the same rules (KPAGE_ERR_INVALID, nothing left allocated).
  * Work runs on `stream` (hipStream_t as void*), which is synchronised twice
- * (table sizes, then queue lengths and pair counts).  Backward metadata is built
- * lazily by the first kpage_attn_bwd() from a host copy of the descriptor;
- * kpage_plan_export() copies device tables to the host on first use.
+ * (table sizes, then queue lengths and pair counts).  The backward metadata
+ * (section 3.3: owners, reverse-Q lists compacted from an owner x query-block
+ * bitmap, Q-page walks, adjacency words, work order) is built on the device too,
+ * lazily by the first kpage_attn_bwd() on that call's stream (synchronised twice),
+ * or by the first kpage_plan_export() of a backward table (on the null stream);
+ * it is identical to kpage_plan()'s.  kpage_plan_export() copies device tables to
+ * the host on first use; the descriptor itself never leaves the device.
  */
 kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, const kpage_plan_opts *opts,
                                void *stream, kpage_plan_t **out);
@@ -191,7 +195,9 @@ enum {
   KPAGE_T_QWALK = 13,         /* int32 Q page ids (8 q + j), -1 = dummy               */
   KPAGE_T_ADJ = 14,           /* uint64: step s of owner t at QWALK_PTR[t] / 8 + s    */
   KPAGE_T_BWD_QUEUE = 15,     /* int32 [n][2]: (b * heads + h, owner within its slot) */
-  KPAGE_T_COUNT = 16
+  KPAGE_T_UNCOVERED_PTR = 16, /* int64 [G + 1]: offsets into UNCOVERED                */
+  KPAGE_T_UNCOVERED = 17,     /* int32 K/V pages outside every block footprint, ascending */
+  KPAGE_T_COUNT = 18
 };
 
 /*

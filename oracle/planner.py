@@ -30,6 +30,9 @@ sections are missing from the text; the readings taken here:
                  real pages whose blocks form a graph edge
   backward order (b*H + h, owner) by descending step count, then ascending
                  b*H + h, then ascending owner
+  uncovered      K/V pages of [0, seq_kv / 16) inside no block's page footprint,
+                 ascending: no query reaches their rows, so their dK, dV rows are
+                 zero by definition and the backward writes them as such
 """
 from __future__ import annotations
 
@@ -72,6 +75,8 @@ class PlanTables:
     qwalk: np.ndarray              # int32 Q page ids (8 q + j), -1 = dummy
     adj: np.ndarray                # uint64, step s of owner t at qwalk_ptr[t] / 8 + s
     bwd_queue: np.ndarray          # int32 [n, 2] (bh, owner index within its slot)
+    uncovered_ptr: np.ndarray      # int64 [G + 1] offsets into uncovered
+    uncovered: np.ndarray          # int32 K/V page ids outside every block footprint
     stats: Dict[str, int] = field(default_factory=dict)
 
 
@@ -152,6 +157,7 @@ def oracle_plan(problem, align_q64: int = 16, align_q128: int = 8) -> PlanTables
     f_valid: List[int] = []
     o_ptr = np.zeros(G + 1, dtype=np.int64)
     owners_all, aligned_all, revq_ptr, revq, qw_ptr, qwalk, adj = [], [], [0], [], [0], [], []
+    unc_ptr, unc = [0], []
     steps_of: List[List[int]] = []
     stats = dict(useful=0, whole_block=0, paged_m128=0, nominal=0, scheduled=0,
                  bwd_physical=0, bwd_useful_check=0)
@@ -188,6 +194,8 @@ def oracle_plan(problem, align_q64: int = 16, align_q128: int = 8) -> PlanTables
         for k, t in owner_of.items():
             for j in range(_pages(int(c_k[k]))):
                 page_block[int(o_k[k]) // PAGE + j] = k
+        unc.extend(pg for pg in range(int(problem.seq_kv) // PAGE) if pg not in page_block)
+        unc_ptr.append(len(unc))
         kmask = {}
         for k in owner_of:
             ck = int(c_k[k])
@@ -264,5 +272,6 @@ def oracle_plan(problem, align_q64: int = 16, align_q128: int = 8) -> PlanTables
         qwalk_ptr=np.asarray(qw_ptr, dtype=np.int64), qwalk=np.asarray(qwalk, dtype=np.int32),
         adj=np.asarray(adj, dtype=np.uint64),
         bwd_queue=np.asarray([(bh, t) for _, bh, t in bq], dtype=np.int32).reshape(-1, 2),
+        uncovered_ptr=np.asarray(unc_ptr, dtype=np.int64), uncovered=np.asarray(unc, dtype=np.int32),
         stats=stats,
     )

@@ -1,10 +1,12 @@
 """GPU-built plans (kpage_plan_device) against host-built plans (kpage_plan).
 
 The host planner is pinned bit for bit to the oracle planner by the CPU tests, so
-equality of every exported forward table, queue and pair count with the host plan is
-equality with the oracle.  Attention through both plans must then be bitwise equal
-(same kernels, same launch order), forward and backward (the device plan builds its
-backward metadata from a host copy of its descriptor).
+equality of every exported table (forward walks, routes, masks, queues; backward
+owners, reverse-Q lists, Q-page walks, adjacency words, work order, uncovered pages)
+and pair count with the host plan is equality with the oracle.  Attention through
+both plans must then be bitwise equal (same kernels, same launch order), forward and
+backward; the device plan builds both table sets with kernels, without copying its
+descriptor to the host.
 """
 import copy
 import sys
@@ -22,8 +24,10 @@ from workloads import make_workload
 pytestmark = pytest.mark.gpu
 
 FWD_TABLES = ("fwd_route", "fwd_walk_ptr", "fwd_walk", "fwd_nfull", "fwd_valid", "q64_queue", "q128_queue")
-BWD_TABLES = ("owner_ptr", "owners", "owner_aligned", "revq_ptr", "revq", "qwalk_ptr", "qwalk", "adj", "bwd_queue")
+BWD_TABLES = ("owner_ptr", "owners", "owner_aligned", "revq_ptr", "revq", "qwalk_ptr", "qwalk", "adj", "bwd_queue",
+              "uncovered_ptr", "uncovered")
 FWD_STATS = ("useful", "whole_block", "paged_m128", "nominal", "scheduled")
+BWD_STATS = ("bwd_physical", "bwd_useful_check")
 
 
 def _say(msg):
@@ -31,7 +35,7 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def same_plans(p, label, **opts):
+def same_plans(p, label, bwd=True, **opts):
     h = K.kpage_plan(p, **opts)
     d = K.kpage_plan_device(p, **opts)
     for t in FWD_TABLES:
@@ -40,7 +44,15 @@ def same_plans(p, label, **opts):
     sh, sd = K.kpage_plan_stats(h), K.kpage_plan_stats(d)
     for n in FWD_STATS:
         assert sh[n] == sd[n], (label, n, sh[n], sd[n])
-    _say(f"  {label}: tables equal (walk {K.kpage_plan_export(d, 'fwd_walk').size} pages, useful {sd['useful']})")
+    if bwd:  # exporting a backward table builds the backward tables of both plans
+        for t in BWD_TABLES:
+            a, b = K.kpage_plan_export(h, t), K.kpage_plan_export(d, t)
+            assert a.dtype == b.dtype and np.array_equal(a, b), (label, t, a.shape, b.shape)
+        sh, sd = K.kpage_plan_stats(h), K.kpage_plan_stats(d)
+        for n in BWD_STATS:
+            assert sh[n] == sd[n], (label, n, sh[n], sd[n])
+    _say(f"  {label}: tables equal (walk {K.kpage_plan_export(d, 'fwd_walk').size} pages, useful {sd['useful']}"
+         + (f", {K.kpage_plan_export(d, 'adj').size} backward steps)" if bwd else ")"))
     return h, d
 
 
@@ -81,7 +93,7 @@ def test_device_plan_offsets_with_gaps_and_null_offsets():
 
 def test_device_plan_attention_is_bitwise_equal():
     w = make_workload(3, heads=[0, 1], with_do=True)
-    h, d = same_plans(w, "21x30x52 two heads")
+    h, d = same_plans(w, "21x30x52 two heads", bwd=False)  # backward tables built by the first backward call
     dev = torch.device("cuda", 0)
     q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
     outs = []
@@ -133,18 +145,27 @@ def test_device_plan_rejects_malformed_descriptors():
     _bad(p, "row end past the index array")
 
 
-def test_device_plan_time_full_size():
-    """Not a speed assertion: prints host and device planning time on the full-size workloads."""
-    for cfg in (3, 4):
-        w = make_workload(cfg)
-        K.kpage_plan_device(w)  # warm up kernels and allocator
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        h = K.kpage_plan(w)
-        th = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        d = K.kpage_plan_device(w)
-        td = time.perf_counter() - t0
-        assert np.array_equal(K.kpage_plan_export(h, "fwd_walk"), K.kpage_plan_export(d, "fwd_walk"))
-        assert np.array_equal(K.kpage_plan_export(h, "q128_queue"), K.kpage_plan_export(d, "q128_queue"))
-        _say(f"  workload {cfg}: forward plan host {th * 1e3:.2f} ms, device {td * 1e3:.2f} ms")
+def _plan_and_backward_tables(plan_fn, w):
+    t0 = time.perf_counter()
+    pl = plan_fn(w)
+    t1 = time.perf_counter()
+    K.kpage_plan_export(pl, "owner_ptr")  # builds the backward tables (device: kernels, then a copy down)
+    t2 = time.perf_counter()
+    return pl, t1 - t0, t2 - t1
+
+
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_device_plan_full_size(cfg):
+    """Bit-exact on the full-size workloads (all heads); prints host and device planning time
+    (not a speed assertion; the device's backward time includes copying its tables down)."""
+    w = make_workload(cfg)
+    K.kpage_plan_device(w)  # warm up kernels and allocator
+    torch.cuda.synchronize()
+    h, hf, hb = _plan_and_backward_tables(K.kpage_plan, w)
+    d, df, db = _plan_and_backward_tables(K.kpage_plan_device, w)
+    for t in FWD_TABLES + BWD_TABLES:
+        assert np.array_equal(K.kpage_plan_export(h, t), K.kpage_plan_export(d, t)), (cfg, t)
+    sh, sd = K.kpage_plan_stats(h), K.kpage_plan_stats(d)
+    assert sh == sd, (cfg, sh, sd)
+    _say(f"  workload {cfg}: forward plan host {hf * 1e3:.2f} ms, device {df * 1e3:.2f} ms; "
+         f"backward tables host {hb * 1e3:.2f} ms, device {db * 1e3:.2f} ms")

@@ -231,3 +231,25 @@ def test_adjacency_marks_only_graph_edges():
             for i in range(8):
                 want = i < 4 and ((qb == 0 and i < 2) or (qb == 1 and 2 <= i < 4))
                 assert bool(word >> (8 * j + i) & 1) == want
+
+
+def test_uncovered_pages_worked_by_hand():
+    """Pages outside every footprint of a layout with gaps, worked by hand: footprints are
+    pages 28-31 (c=50 at row 448), 0-7 (c=128 at 0), 10 (c=3 at 160), 12-18 (c=97 at 192),
+    8 (c=16 at 128), none (c=0), 20-22 (c=33 at 320) of 32 pages."""
+    ck = [50, 128, 3, 97, 16, 0, 33]
+    off = [448, 0, 160, 192, 128, 0, 320]
+    p = make_problem([128, 64], ck, [[0, 1], [2, 3]], heads=2, kv_offset=off, seq_kv=512, sort_rows=False)
+    t = oracle_plan(p)
+    assert t.uncovered.tolist() == [9, 11, 19, 23, 24, 25, 26, 27]
+    assert t.uncovered_ptr.tolist() == [0, 8]
+
+
+@pytest.mark.parametrize("cfg,heads", [(1, None), (2, None), (5, [3, 7])])
+def test_uncovered_pages_complement_the_footprints(cfg, heads):
+    """Per slot: uncovered count = seq_kv / 16 - sum of ceil(c_k / 16) (footprints are disjoint)."""
+    w = make_workload(cfg, heads=heads)
+    t = oracle_plan(w)
+    for g in range(w.kv_valid.shape[0]):
+        n = int(t.uncovered_ptr[g + 1] - t.uncovered_ptr[g])
+        assert n == w.seq_kv // 16 - sum(-(-int(c) // 16) for c in w.kv_valid[g])
