@@ -139,6 +139,17 @@ def main():
     torch.cuda.synchronize()
     bwd_plan_ms = (time.perf_counter() - t0) * 1e3
     stats = K.kpage_plan_stats(plan)
+    # the same plan built on the GPU (identical tables; the timed steps use the host-built one)
+    K.kpage_plan_device(w).close()  # first use: kernel and allocator warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dplan = K.kpage_plan_device(w)
+    dev_plan_ms = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    K.kpage_attn_bwd(dplan, q, k, v, o, lse, do, dq, dk, dv, ws, w.scale)
+    torch.cuda.synchronize()
+    dev_bwd_plan_ms = (time.perf_counter() - t0) * 1e3
+    dplan.close()
 
     def step():
         K.kpage_attn_fwd(plan, q, k, v, o, lse, w.scale)
@@ -203,7 +214,9 @@ def main():
         "kernel_ms_per_step": {n: round(kern[n][0] / args.steps, 4) for n in K.KERNELS},
         "pairs": {kk: stats[kk] for kk in ("useful", "whole_block", "paged_m128", "nominal", "scheduled",
                                              "bwd_physical")},
-        "plan_ms": {"forward": round(plan_ms, 2), "backward_lazy_incl_first_call": round(bwd_plan_ms, 2)},
+        "plan_ms": {"forward": round(plan_ms, 2), "backward_lazy_incl_first_call": round(bwd_plan_ms, 2),
+                    "device_forward_incl_descriptor_upload": round(dev_plan_ms, 2),
+                    "device_backward_lazy_incl_first_call": round(dev_bwd_plan_ms, 2)},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
