@@ -37,7 +37,7 @@ EXPORTED_SYMBOLS = (
     "kpage_last_error",
 )
 
-KERNELS = {"fwd_q128": 0, "fwd_q64": 1, "bwd_pre": 2, "bwd_zero": 3, "bwd_kv": 4, "bwd_dq": 5}
+KERNELS = {"fwd_q128": 0, "fwd_q64": 1, "bwd_pre": 2, "bwd_zero": 3, "bwd_kv": 4, "bwd_dq": 5, "bwd_reduce": 6}
 
 
 class KpageError(RuntimeError):

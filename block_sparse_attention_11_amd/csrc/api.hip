@@ -102,6 +102,10 @@ struct kpage_plan {
   uint64_t *d_adj = nullptr;
   int64_t *d_uncovered_ptr = nullptr;
   int max_uncovered = 0;
+  // owners split over several Q groups: fp32 partial slots in the workspace, reduce list
+  BwdReduce *d_reduce = nullptr;
+  int n_reduce = 0;
+  int64_t n_partials = -1;  // -1: not counted yet
   std::vector<void *> allocations;
   EventTimer *timer = nullptr;
 };
@@ -300,6 +304,48 @@ kpage_status ensure_backward_on_host(PlanT *pl) {
   return KPAGE_OK;
 }
 
+// Backward launch items from the exported work order: one per (owner, Q group) entry,
+// launched in (bh, owner, group) order.  Owners with more than one item accumulate
+// fp32 partials (one slot per item, consecutive in group order) that the reduce pass
+// sums; an owner with a single item writes bf16 directly.
+void make_bwd_items(const Problem &P, const BwdTables &B, std::vector<BwdItem> *items, std::vector<BwdReduce> *reduce,
+                    int64_t *n_partials) {
+  const int ng = B.n_groups;
+  items->clear();
+  reduce->clear();
+  for (size_t i = 0; i < B.bwd_queue.size(); i += 2) {
+    const int bh = B.bwd_queue[i], tg_local = B.bwd_queue[i + 1];
+    const int64_t t = B.owner_ptr[P.slot_of(bh)] + tg_local / ng;
+    const int64_t w = t * ng + tg_local % ng;
+    BwdItem x{};
+    x.qwalk_off = B.qwalk_ptr[w];
+    x.n_steps = int32_t((B.qwalk_ptr[w + 1] - B.qwalk_ptr[w]) / 8);
+    x.bh = bh;
+    x.owner = int32_t(t);
+    x.aligned = B.aligned[t];
+    x.partial = tg_local % ng;  // group, until the slots are assigned below
+    items->push_back(x);
+  }
+  std::stable_sort(items->begin(), items->end(), [](const BwdItem &a, const BwdItem &b) {
+    if (a.bh != b.bh) return a.bh < b.bh;
+    if (a.owner != b.owner) return a.owner < b.owner;
+    return a.partial < b.partial;
+  });
+  int64_t n_part = 0;
+  for (size_t i = 0; i < items->size();) {
+    size_t j = i;
+    while (j < items->size() && (*items)[j].bh == (*items)[i].bh && (*items)[j].owner == (*items)[i].owner) ++j;
+    if (j - i > 1) {
+      reduce->push_back(BwdReduce{(*items)[i].bh, (*items)[i].owner, int32_t(n_part), int32_t(j - i)});
+      for (size_t k = i; k < j; ++k) (*items)[k].partial = int32_t(n_part++);
+    } else {
+      (*items)[i].partial = -1;
+    }
+    i = j;
+  }
+  *n_partials = n_part;
+}
+
 kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
   if (pl->bwd_on_device) return KPAGE_OK;
   if (pl->device_planned) return build_backward_on_device(pl, stream);
@@ -333,21 +379,8 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
   std::vector<int32_t> qpages = redirect_dummies(B.qwalk, B.qwalk_ptr);
   std::vector<int32_t> owners(B.owners);
   std::vector<BwdItem> items;
-  for (size_t i = 0; i < B.bwd_queue.size(); i += 2) {
-    const int bh = B.bwd_queue[i], t_local = B.bwd_queue[i + 1];
-    const int g = P.slot_of(bh);
-    const int64_t t = B.owner_ptr[g] + t_local;
-    BwdItem x{};
-    x.qwalk_off = B.qwalk_ptr[t];
-    x.n_steps = int32_t((B.qwalk_ptr[t + 1] - B.qwalk_ptr[t]) / 8);
-    x.bh = bh;
-    x.owner = int32_t(t);
-    x.aligned = B.aligned[t];
-    items.push_back(x);
-  }
-  std::stable_sort(items.begin(), items.end(), [](const BwdItem &a, const BwdItem &b) {
-    return a.bh != b.bh ? a.bh < b.bh : a.owner < b.owner;
-  });
+  std::vector<BwdReduce> reduce;
+  make_bwd_items(P, B, &items, &reduce, &pl->n_partials);
   items = xcd_interleave(items);
   kpage_status s;
   if ((s = upload(pl, items, &pl->d_bitems, stream)) != KPAGE_OK) return s;
@@ -357,6 +390,8 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
   if ((s = upload(pl, B.adj, &pl->d_adj, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, B.uncovered, &pl->d_uncovered, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, B.uncovered_ptr, &pl->d_uncovered_ptr, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, reduce, &pl->d_reduce, stream)) != KPAGE_OK) return s;
+  pl->n_reduce = int(reduce.size());
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   pl->n_bitems = int(items.size());
@@ -367,6 +402,19 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
 }
 
 bool bad_scale(float s) { return !(s > 0.f) || !std::isfinite(s); }
+
+// byte offset of the partial slots in the backward workspace
+size_t partials_offset(size_t rows) { return (2 * rows * 4 + 255) / 256 * 256; }
+
+kpage_status count_partials(PlanT *pl) {
+  if (pl->n_partials >= 0) return KPAGE_OK;
+  const kpage_status s = ensure_backward_on_host(pl);
+  if (s != KPAGE_OK) return s;
+  std::vector<BwdItem> items;
+  std::vector<BwdReduce> reduce;
+  make_bwd_items(pl->P, pl->B, &items, &reduce, &pl->n_partials);
+  return KPAGE_OK;
+}
 
 }  // namespace
 
@@ -417,6 +465,10 @@ kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, co
   if (s != KPAGE_OK) {
     delete pl;
     return fail(s, err);
+  }
+  if (pl->P.q_group != 0) {
+    delete pl;
+    return fail(KPAGE_ERR_UNSUPPORTED, "kpage_plan_device builds one Q group only (q_group = 0)");
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Problem &P = pl->P;
@@ -509,8 +561,14 @@ kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, co
 kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes) {
   if (!plan || !bytes) return fail(KPAGE_ERR_INVALID, "plan or bytes is NULL");
   const size_t rows = size_t(plan->P.batch) * plan->P.heads * size_t(plan->P.seq_q);
-  // fp32 LSE * log2(e), then fp32 D = rowsum(dO * O), each [BH, seq_q]
+  // fp32 LSE * log2(e), then fp32 D = rowsum(dO * O), each [BH, seq_q]; with Q groups,
+  // then the fp32 dK/dV partials of owners split over several groups
   *bytes = 2 * rows * 4;
+  if (plan->P.q_group > 0) {
+    const kpage_status s = count_partials(plan);
+    if (s != KPAGE_OK) return s;
+    *bytes = partials_offset(rows) + size_t(plan->n_partials) * 2 * 128 * size_t(plan->P.head_dim) * 4;
+  }
   return KPAGE_OK;
 }
 
@@ -546,6 +604,12 @@ kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, co
   a.adj = plan->d_adj;
   a.uncovered = plan->d_uncovered;
   a.uncovered_ptr = plan->d_uncovered_ptr;
+  if (plan->n_reduce > 0 && reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(KPAGE_ERR_INVALID, "workspace must be 16-byte aligned when q_group > 0");
+  a.reduce = plan->d_reduce;
+  a.n_reduce = plan->n_reduce;
+  a.part = plan->n_reduce > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + partials_offset(rows))
+                              : nullptr;
   a.fitems128 = plan->d_items128;
   a.fitems64 = plan->d_items64;
   a.n_fitems128 = plan->n_items128;

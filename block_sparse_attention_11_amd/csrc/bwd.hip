@@ -315,6 +315,19 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
 
   // ---- write dK (scaled) and dV by page id ----
   // lane = head-dim column, register r = key row acc_row(r, g) of the wave's 32 keys
+  if (it.partial >= 0) {  // one of several Q groups of this owner: unscaled fp32 partials
+    float *pk = a.part + (int64_t)it.partial * 2 * 128 * D + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * wave + acc_row(r, g);
+#pragma unroll
+      for (int n = 0; n < ND; ++n) {
+        pk[key * D + 32 * n] = dk[n][r];
+        pk[(128 + key) * D + 32 * n] = dv[n][r];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = 32 * wave + acc_row(r, g);
@@ -561,6 +574,47 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a, cons
   }
 }
 
+// ---------------------------------------------------------------------------
+// Owners split over several Q groups: sum their fp32 partials in group order (so the
+// result does not depend on scheduling), scale dK, and write both by page id with the
+// owner's row masks (rows past c_k as zeros, empty slots untouched).  HBM-bound: one
+// workgroup per owner, 8 consecutive columns per thread.
+template <int D>
+__global__ __launch_bounds__(256) void kpage_bwd_kv_reduce(BwdArgs a) {
+  constexpr int CH = D / 8;
+  const BwdReduce r = a.reduce[blockIdx.x];
+  const int32_t *own = a.owners + (int64_t)r.owner * 8;
+  const uint32_t *kmk = a.owner_kmask + (int64_t)r.owner * 8;
+  for (int e = threadIdx.x; e < 128 * CH; e += 256) {
+    const int key = e / CH, c8 = (e % CH) * 8;
+    const int slot = key >> 4, rin = key & 15;
+    const uint32_t km = kmk[slot];
+    if (km == 0u) continue;
+    f32x4 sk0{}, sk1{}, sv0{}, sv1{};
+    if ((km >> rin) & 1u) {
+      for (int p = 0; p < r.count; ++p) {
+        const float *pk = a.part + (int64_t)(r.part0 + p) * 2 * 128 * D + key * D + c8;
+        const float *pv = pk + 128 * D;
+        sk0 += *(const f32x4 *)pk;
+        sk1 += *(const f32x4 *)(pk + 4);
+        sv0 += *(const f32x4 *)pv;
+        sv1 += *(const f32x4 *)(pv + 4);
+      }
+    }
+    bf16x8 ok, ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ok[i] = (__bf16)(sk0[i] * a.scale);
+      ok[4 + i] = (__bf16)(sk1[i] * a.scale);
+      ov[i] = (__bf16)sv0[i];
+      ov[4 + i] = (__bf16)sv1[i];
+    }
+    const int64_t row = (int64_t)r.bh * a.seq_kv + (int64_t)own[slot] * 16 + rin;
+    *(bf16x8 *)((__bf16 *)a.dk + row * D + c8) = ok;
+    *(bf16x8 *)((__bf16 *)a.dv + row * D + c8) = ov;
+  }
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
   const int64_t rows = (int64_t)a.bh_count * a.seq_q;
@@ -578,6 +632,11 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
     if (t) t->before(4, stream);
     hipLaunchKernelGGL(kpage_bwd_kv<D>, dim3(a.n_items), dim3(64 * kKvWaves), 0, stream, a);
     if (t) t->after(4, stream);
+  }
+  if (a.n_reduce > 0) {
+    if (t) t->before(6, stream);
+    hipLaunchKernelGGL(kpage_bwd_kv_reduce<D>, dim3(a.n_reduce), dim3(256), 0, stream, a);
+    if (t) t->after(6, stream);
   }
   if (t) t->before(5, stream);
   if (a.n_fitems128 > 0)

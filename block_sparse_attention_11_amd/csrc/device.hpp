@@ -38,6 +38,15 @@ struct BwdItem {
   int32_t owner;       // global owner index (row of the owner table)
   int32_t n_steps;
   int32_t aligned;     // 1: the owner is one block of 8 contiguous pages
+  int32_t partial;     // -1: write dK/dV (bf16) directly; >= 0: fp32 partial slot of
+                       // an owner split over several Q groups (summed by the reduce pass)
+  int32_t pad;
+};
+
+// One owner whose Q groups were split over `count` work items: partial slots
+// [part0, part0 + count) are summed in group order and written as bf16.
+struct BwdReduce {
+  int32_t bh, owner, part0, count;
 };
 
 struct BwdArgs {
@@ -54,6 +63,9 @@ struct BwdArgs {
   const uint64_t *adj;        // adjacency word per step
   const int32_t *uncovered;   // K/V pages outside every footprint, per slot
   const int64_t *uncovered_ptr;
+  float *part;                // fp32 [n_partials][2][128][d]: unscaled dK, then dV, per owner row
+  const BwdReduce *reduce;
+  int32_t n_reduce;
   // Q-owned pass (dQ): the forward work items and page walks of both routes
   const FwdItem *fitems128, *fitems64;
   const int32_t *pages;

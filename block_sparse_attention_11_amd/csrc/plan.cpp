@@ -54,7 +54,7 @@ kpage_status load_scalars(const kpage_problem *p, const kpage_plan_opts *o, Prob
   }
   int a64 = 16, a128 = 8;
   if (o) {
-    if (o->q_group != 0) { *err = "only q_group = 0 (one Q group) is implemented"; return KPAGE_ERR_UNSUPPORTED; }
+    if (o->q_group < 0) { *err = "q_group must be >= 0"; return KPAGE_ERR_INVALID; }
     if (o->align_q64) a64 = o->align_q64;
     if (o->align_q128) a128 = o->align_q128;
     if (a64 < 16 || a64 % 16 || a128 < 8 || a128 % 8) {
@@ -70,6 +70,7 @@ kpage_status load_scalars(const kpage_problem *p, const kpage_plan_opts *o, Prob
   P.seq_q = p->seq_q; P.seq_kv = p->seq_kv;
   P.per_head = p->per_head == 1;
   P.slots = P.per_head ? P.batch * P.heads : 1;
+  P.q_group = o ? o->q_group : 0;
   return KPAGE_OK;
 }
 
@@ -223,7 +224,10 @@ void build_backward(const Problem &P, BwdTables *T, PairStats *S) {
   T->uncovered_ptr.push_back(0);
   S->bwd_physical = 0;
   S->bwd_useful_check = 0;
-  std::vector<std::vector<int>> steps_of(G);
+  const int gsz = P.q_group > 0 ? std::min(P.q_group, nq) : nq;
+  const int n_groups = (nq + gsz - 1) / gsz;
+  T->n_groups = n_groups;
+  std::vector<std::vector<std::vector<int>>> steps_of(G);  // [slot][owner][group]
   const int64_t n_pages = P.seq_kv / kPageRows;
   for (int g = 0; g < G; ++g) {
     const int32_t *cq = &P.q_valid[size_t(g) * nq];
@@ -279,56 +283,72 @@ void build_backward(const Problem &P, BwdTables *T, PairStats *S) {
       auto &pages = own[t];
       const uint8_t al = (own_blocks[t].size() == 1 && pages.size() == size_t(kOwnerSlots)) ? 1 : 0;
       while (pages.size() < size_t(kOwnerSlots)) pages.push_back(-1);
-      std::vector<int32_t> R;
-      for (int q = 0; q < nq; ++q)
-        if (bitmap[size_t(t) * nq + q]) R.push_back(q);
-      T->revq.insert(T->revq.end(), R.begin(), R.end());
-      T->revq_ptr.push_back(int64_t(T->revq.size()));
-      const size_t w0 = T->qwalk.size();
-      for (int q : R)
-        if (cq[q] == kBlockRows)
-          for (int j = 0; j < 8; ++j) T->qwalk.push_back(8 * q + j);
-      for (int q : R)
-        if (cq[q] > 0 && cq[q] < kBlockRows)
-          for (int j = 0; j < pages_of(cq[q]); ++j) T->qwalk.push_back(8 * q + j);
-      while ((T->qwalk.size() - w0) % 8) T->qwalk.push_back(-1);
-      T->qwalk_ptr.push_back(int64_t(T->qwalk.size()));
-      const int n_steps = int((T->qwalk.size() - w0) / 8);
-      for (int s = 0; s < n_steps; ++s) {
-        uint64_t word = 0;
-        for (int j = 0; j < 8; ++j) {
-          const int32_t qp = T->qwalk[w0 + 8 * s + j];
-          if (qp < 0) continue;
-          const int qb = qp / 8;
-          const uint32_t qm = page_mask(cq[qb], qp % 8);
-          for (int i = 0; i < 8; ++i) {
-            const int32_t kp = pages[i];
-            if (kp < 0) continue;
-            const int kb = page_block[kp];
-            if (!edge[size_t(qb) * nk + kb]) continue;
-            word |= uint64_t(1) << (8 * j + i);
-            const uint32_t km = page_mask(ck[kb], int(kp - ok[kb] / kPageRows));
-            S->bwd_useful_check += mult * uint64_t(__builtin_popcount(qm)) * uint64_t(__builtin_popcount(km));
+      std::vector<int> owner_steps;
+      for (int grp = 0; grp < n_groups; ++grp) {
+        // reverse neighbourhood of owner t inside Q group grp, ascending q
+        std::vector<int32_t> R;
+        for (int q = grp * gsz; q < std::min(nq, (grp + 1) * gsz); ++q)
+          if (bitmap[size_t(t) * nq + q]) R.push_back(q);
+        T->revq.insert(T->revq.end(), R.begin(), R.end());
+        T->revq_ptr.push_back(int64_t(T->revq.size()));
+        const size_t w0 = T->qwalk.size();
+        for (int q : R)
+          if (cq[q] == kBlockRows)
+            for (int j = 0; j < 8; ++j) T->qwalk.push_back(8 * q + j);
+        for (int q : R)
+          if (cq[q] > 0 && cq[q] < kBlockRows)
+            for (int j = 0; j < pages_of(cq[q]); ++j) T->qwalk.push_back(8 * q + j);
+        while ((T->qwalk.size() - w0) % 8) T->qwalk.push_back(-1);
+        T->qwalk_ptr.push_back(int64_t(T->qwalk.size()));
+        const int n_steps = int((T->qwalk.size() - w0) / 8);
+        for (int s = 0; s < n_steps; ++s) {
+          uint64_t word = 0;
+          for (int j = 0; j < 8; ++j) {
+            const int32_t qp = T->qwalk[w0 + 8 * s + j];
+            if (qp < 0) continue;
+            const int qb = qp / 8;
+            const uint32_t qm = page_mask(cq[qb], qp % 8);
+            for (int i = 0; i < 8; ++i) {
+              const int32_t kp = pages[i];
+              if (kp < 0) continue;
+              const int kb = page_block[kp];
+              if (!edge[size_t(qb) * nk + kb]) continue;
+              word |= uint64_t(1) << (8 * j + i);
+              const uint32_t km = page_mask(ck[kb], int(kp - ok[kb] / kPageRows));
+              S->bwd_useful_check += mult * uint64_t(__builtin_popcount(qm)) * uint64_t(__builtin_popcount(km));
+            }
           }
+          T->adj.push_back(word);
         }
-        T->adj.push_back(word);
+        S->bwd_physical += mult * uint64_t(kBlockRows) * kBlockRows * uint64_t(n_steps);
+        owner_steps.push_back(n_steps);
       }
-      S->bwd_physical += mult * uint64_t(kBlockRows) * kBlockRows * uint64_t(n_steps);
       T->owners.insert(T->owners.end(), pages.begin(), pages.end());
       T->aligned.push_back(al);
-      steps_of[g].push_back(n_steps);
+      steps_of[g].push_back(owner_steps);
     }
     T->owner_ptr.push_back(T->owner_ptr.back() + n_own);
   }
-  std::vector<std::tuple<int, int, int>> ent;
+  // work items: every (owner, group) with a non-empty neighbourhood (n_steps > 0); an owner
+  // without any keeps one item for group 0, which writes its zero gradients
+  std::vector<std::tuple<int, int, int, int>> ent;
   for (int bh = 0; bh < BH; ++bh) {
     const int g = P.slot_of(bh);
-    for (size_t t = 0; t < steps_of[g].size(); ++t) ent.emplace_back(-steps_of[g][t], bh, int(t));
+    for (size_t t = 0; t < steps_of[g].size(); ++t) {
+      const auto &st = steps_of[g][t];
+      bool any = false;
+      for (int grp = 0; grp < n_groups; ++grp)
+        if (st[grp] > 0) {
+          ent.emplace_back(-st[grp], bh, int(t), grp);
+          any = true;
+        }
+      if (!any) ent.emplace_back(0, bh, int(t), 0);
+    }
   }
   std::sort(ent.begin(), ent.end());
   for (auto &x : ent) {
     T->bwd_queue.push_back(std::get<1>(x));
-    T->bwd_queue.push_back(std::get<2>(x));
+    T->bwd_queue.push_back(std::get<2>(x) * n_groups + std::get<3>(x));
   }
   T->built = true;
 }

@@ -18,6 +18,7 @@ struct Problem {
   int batch = 0, heads = 0, head_dim = 0, n_q = 0, n_kv = 0, slots = 0;
   int64_t seq_q = 0, seq_kv = 0;
   bool per_head = false;
+  int q_group = 0;  // Q blocks per backward Q group; 0 = one group
   std::vector<int32_t> q_valid, kv_valid;   // [slots][n]
   std::vector<int64_t> kv_offset;           // [slots][n_kv]
   std::vector<int64_t> q2k_ptr;             // [slots][n_q + 1]
@@ -46,15 +47,16 @@ struct FwdTables {
 // Backward tables, concatenated over graph slots.
 struct BwdTables {
   bool built = false;
+  int n_groups = 1;                 // Q groups (section 3.3.2)
   std::vector<int64_t> owner_ptr;   // [slots + 1]
   std::vector<int32_t> owners;      // [n_own][8]
   std::vector<uint8_t> aligned;     // [n_own]
-  std::vector<int64_t> revq_ptr;    // [n_own + 1]
+  std::vector<int64_t> revq_ptr;    // [n_own * n_groups + 1], per (owner, group), owner-major
   std::vector<int32_t> revq;
-  std::vector<int64_t> qwalk_ptr;   // [n_own + 1]
+  std::vector<int64_t> qwalk_ptr;   // [n_own * n_groups + 1]
   std::vector<int32_t> qwalk;
   std::vector<uint64_t> adj;        // one word per step
-  std::vector<int32_t> bwd_queue;   // pairs (bh, owner within slot)
+  std::vector<int32_t> bwd_queue;   // pairs (bh, owner within slot * n_groups + group)
   std::vector<int64_t> uncovered_ptr;  // [slots + 1] K/V pages outside every block footprint
   std::vector<int32_t> uncovered;
 };

@@ -776,6 +776,7 @@ __global__ void k_bwd_items(DevProblem p, int64_t n_own, int64_t n_items, const 
   x.owner = int32_t(tg);
   x.n_steps = steps;
   x.aligned = aligned[tg];
+  x.partial = -1;
   items[xcd_position(f, n_items)] = x;
 }
 

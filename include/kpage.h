@@ -71,8 +71,12 @@ typedef struct {
  * Planner options (NULL = defaults).  Section 3.2.2: the Q64 path consumes 16
  * pages per iteration and the Q128 path 8, so walks are padded with dummy pages
  * to a multiple of align_q64 / align_q128 (defaults 16 / 8; multiples of those
- * values are accepted).  q_group is the Q-group size of section 3.3.2; only 0
- * (one group) is implemented.
+ * values are accepted).  q_group is the Q-group size of section 3.3.2, in Q
+ * blocks: 0 = one group; n > 0 splits every owner's reverse neighbourhood into
+ * the groups [g n, (g + 1) n) of Q blocks, one backward work item per non-empty
+ * (owner, group), which bounds the serial Q work of an item.  An owner split over
+ * several items sums fp32 partials of dK/dV (in group order, deterministic) in
+ * the backward workspace.  Negative values are KPAGE_ERR_INVALID.
  */
 typedef struct {
   int32_t q_group;
@@ -101,7 +105,7 @@ typedef struct {
  * Host-only: no device memory is touched here; tables are copied to the device
  * on first use (kpage_plan_upload or the first attention call).
  * Returns KPAGE_ERR_INVALID for a malformed descriptor, KPAGE_ERR_UNSUPPORTED
- * for head_dim not in {64,128} or q_group != 0.  *out is owned by the caller
+ * for head_dim not in {64,128}.  *out is owned by the caller
  * and released with kpage_plan_destroy().
  */
 kpage_status kpage_plan(const kpage_problem *problem, const kpage_plan_opts *opts,
@@ -146,7 +150,10 @@ kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, co
                             void *o, float *lse, float softmax_scale, void *stream);
 
 /* Bytes of device workspace kpage_attn_bwd needs: two fp32 values per query row
- * (LSE * log2(e) and rowsum(dO * O)), i.e. 8 * batch * heads * seq_q. */
+ * (LSE * log2(e) and rowsum(dO * O)), i.e. 8 * batch * heads * seq_q; with
+ * q_group > 0, rounded up to 256 and followed by 2 * 128 * head_dim fp32 values
+ * per work item of an owner split over several Q groups (this call then builds
+ * the backward metadata, on the host). */
 kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes);
 
 /*
@@ -163,7 +170,8 @@ kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes);
  * query-block sizes reach the kernels.  Every row of Q and dO must hold finite
  * values, padded rows included (they meet zero weights inside the products).
  * workspace is a caller-owned device buffer of at least
- * kpage_bwd_workspace_size() bytes, 4-byte aligned; at most 2^29 query rows
+ * kpage_bwd_workspace_size() bytes, 4-byte aligned (16-byte aligned when
+ * q_group > 0); at most 2^29 query rows
  * (batch * heads * seq_q) per call.
  * Invalid rows of dQ (by Q sizes) and of dK/dV (by K/V sizes), and rows of
  * blocks with no edge, are written as 0.
@@ -227,7 +235,8 @@ enum {
   KPAGE_K_BWD_ZERO = 3,  /* dK/dV pages outside every block footprint              */
   KPAGE_K_BWD_KV = 4,    /* K/V-owned pass: dK, dV                                  */
   KPAGE_K_BWD_DQ = 5,    /* Q-owned pass over the forward walks (both routes): dQ  */
-  KPAGE_K_COUNT = 6
+  KPAGE_K_BWD_REDUCE = 6,/* sum of the fp32 dK/dV partials of owners split over Q groups */
+  KPAGE_K_COUNT = 7
 };
 kpage_status kpage_timing_enable(kpage_plan_t *plan, int enable);
 kpage_status kpage_timing_read(kpage_plan_t *plan, int kernel_id, double *total_ms, int64_t *launches);

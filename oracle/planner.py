@@ -23,13 +23,21 @@ sections are missing from the text; the readings taken here:
                  next-fit in ascending order, never crossing an owner; the
                  aligned flag is set when one block with 8 pages fills the owner
   reverse Q      bitmap[owner(k)][q] over the graph edges with c_q, c_k > 0;
-                 each owner's list is its set bits in ascending q (one Q group)
-  Q-page walk    pages 8q + j of full Q blocks in the list, then the pages of
-                 partial Q blocks, then dummies up to a multiple of 8
+                 each owner's list is its set bits in ascending q
+  Q groups       q_group = 0: one group; q_group = n > 0: G_g = the Q blocks
+                 [g n, (g + 1) n); the reverse neighbourhood of owner t in group
+                 g is its list restricted to G_g (section 3.3.2).  Tables are kept
+                 per (owner, group) pair, owner-major, empty pairs included
+  Q-page walk    per (owner, group): pages 8q + j of full Q blocks in the list,
+                 then the pages of partial Q blocks, then dummies up to a
+                 multiple of 8
   adjacency      per 8-page step, bit 8 j + i set when Q slot j and K slot i are
                  real pages whose blocks form a graph edge
-  backward order (b*H + h, owner) by descending step count, then ascending
-                 b*H + h, then ascending owner
+  backward order work items (b*H + h, owner, group) for every pair with a
+                 non-empty group list, plus (b*H + h, owner, 0) for an owner whose
+                 lists are all empty (it still writes its zero gradients); by
+                 descending step count, then ascending b*H + h, owner, group;
+                 exported as (b*H + h, owner * n_groups + group)
   uncovered      K/V pages of [0, seq_kv / 16) inside no block's page footprint,
                  ascending: no query reaches their rows, so their dK, dV rows are
                  zero by definition and the backward writes them as such
@@ -69,12 +77,12 @@ class PlanTables:
     owner_ptr: np.ndarray          # int64 [G + 1] offsets into owners
     owners: np.ndarray             # int32 [n_own, 8] page ids, -1 = empty slot
     owner_aligned: np.ndarray      # uint8 [n_own]
-    revq_ptr: np.ndarray           # int64 [n_own + 1]
+    revq_ptr: np.ndarray           # int64 [n_own * n_groups + 1] per (owner, group)
     revq: np.ndarray               # int32 Q block ids
-    qwalk_ptr: np.ndarray          # int64 [n_own + 1] offsets into qwalk (multiples of 8)
+    qwalk_ptr: np.ndarray          # int64 [n_own * n_groups + 1] offsets into qwalk (multiples of 8)
     qwalk: np.ndarray              # int32 Q page ids (8 q + j), -1 = dummy
     adj: np.ndarray                # uint64, step s of owner t at qwalk_ptr[t] / 8 + s
-    bwd_queue: np.ndarray          # int32 [n, 2] (bh, owner index within its slot)
+    bwd_queue: np.ndarray          # int32 [n, 2] (bh, owner index within its slot * n_groups + group)
     uncovered_ptr: np.ndarray      # int64 [G + 1] offsets into uncovered
     uncovered: np.ndarray          # int32 K/V page ids outside every block footprint
     stats: Dict[str, int] = field(default_factory=dict)
@@ -141,9 +149,11 @@ def _owners_slot(c_k, o_k):
     return owners, aligned, owner_of
 
 
-def oracle_plan(problem, align_q64: int = 16, align_q128: int = 8) -> PlanTables:
+def oracle_plan(problem, align_q64: int = 16, align_q128: int = 8, q_group: int = 0) -> PlanTables:
     """Build every forward and backward table of ``problem`` (a workloads.Workload-like object)."""
     G, n_q = problem.q_valid.shape
+    group_size = q_group if q_group > 0 else n_q
+    n_groups = -(-n_q // group_size)
     H = problem.heads
     BH = problem.batch * H
     slots_bh = {}
@@ -211,36 +221,40 @@ def oracle_plan(problem, align_q64: int = 16, align_q128: int = 8) -> PlanTables
                     continue
                 edges.add((q, int(k)))
                 bitmap[owner_of[int(k)], q] = True
-        slot_steps = []
+        slot_steps = []  # [owner][group]
         for t, pages in enumerate(owners):
-            R = [int(x) for x in np.nonzero(bitmap[t])[0]]
-            revq.extend(R)
-            revq_ptr.append(len(revq))
-            qp = [8 * q + j for q in R if int(c_q[q]) == BLOCK for j in range(8)]
-            qp += [8 * q + j for q in R if 0 < int(c_q[q]) < BLOCK for j in range(_pages(int(c_q[q])))]
-            qp += [-1] * ((-len(qp)) % 8)
-            qwalk.extend(qp)
-            qw_ptr.append(len(qwalk))
-            n_steps = len(qp) // 8
-            slot_steps.append(n_steps)
-            for s in range(n_steps):
-                word = 0
-                for j in range(8):
-                    qpg = qp[8 * s + j]
-                    if qpg < 0:
-                        continue
-                    qb = qpg // 8
-                    cq = int(c_q[qb])
-                    qm = FULL_MASK if ((qpg % 8) + 1) * PAGE <= cq else _tail_mask(cq)
-                    for i in range(8):
-                        kpg = pages[i]
-                        if kpg < 0:
+            R_all = [int(x) for x in np.nonzero(bitmap[t])[0]]
+            owner_steps = []
+            for grp in range(n_groups):
+                R = [q for q in R_all if q // group_size == grp]
+                revq.extend(R)
+                revq_ptr.append(len(revq))
+                qp = [8 * q + j for q in R if int(c_q[q]) == BLOCK for j in range(8)]
+                qp += [8 * q + j for q in R if 0 < int(c_q[q]) < BLOCK for j in range(_pages(int(c_q[q])))]
+                qp += [-1] * ((-len(qp)) % 8)
+                qwalk.extend(qp)
+                qw_ptr.append(len(qwalk))
+                n_steps = len(qp) // 8
+                owner_steps.append(n_steps)
+                for s in range(n_steps):
+                    word = 0
+                    for j in range(8):
+                        qpg = qp[8 * s + j]
+                        if qpg < 0:
                             continue
-                        if (qb, page_block[kpg]) in edges:
-                            word |= 1 << (8 * j + i)
-                            stats["bwd_useful_check"] += nbh * bin(qm).count("1") * bin(kmask[kpg]).count("1")
-                adj.append(word)
-            stats["bwd_physical"] += nbh * BLOCK * BLOCK * n_steps
+                        qb = qpg // 8
+                        cq = int(c_q[qb])
+                        qm = FULL_MASK if ((qpg % 8) + 1) * PAGE <= cq else _tail_mask(cq)
+                        for i in range(8):
+                            kpg = pages[i]
+                            if kpg < 0:
+                                continue
+                            if (qb, page_block[kpg]) in edges:
+                                word |= 1 << (8 * j + i)
+                                stats["bwd_useful_check"] += nbh * bin(qm).count("1") * bin(kmask[kpg]).count("1")
+                    adj.append(word)
+                stats["bwd_physical"] += nbh * BLOCK * BLOCK * n_steps
+            slot_steps.append(owner_steps)
             owners_all.append(pages)
             aligned_all.append(aligned[t])
         steps_of.append(slot_steps)
@@ -255,11 +269,19 @@ def oracle_plan(problem, align_q64: int = 16, align_q128: int = 8) -> PlanTables
         ent.sort()
         return np.asarray([(bh, q) for _, bh, q in ent], dtype=np.int32).reshape(-1, 2)
 
+    def revq_len(g, t, grp):
+        i = (int(o_ptr[g]) + t) * n_groups + grp
+        return revq_ptr[i + 1] - revq_ptr[i]
+
     bq = []
     for bh in range(BH):
         g = bh if problem.per_head else 0
-        for t, st in enumerate(steps_of[g]):
-            bq.append((-st, bh, t))
+        for t, owner_steps in enumerate(steps_of[g]):
+            # a group with no Q block of the owner's neighbourhood has no work; an owner with none
+            # at all keeps one item for group 0
+            groups = [grp for grp in range(n_groups) if revq_len(g, t, grp) > 0] or [0]
+            for grp in groups:
+                bq.append((-owner_steps[grp], bh, t, grp))
     bq.sort()
 
     return PlanTables(
@@ -271,7 +293,7 @@ def oracle_plan(problem, align_q64: int = 16, align_q128: int = 8) -> PlanTables
         revq_ptr=np.asarray(revq_ptr, dtype=np.int64), revq=np.asarray(revq, dtype=np.int32),
         qwalk_ptr=np.asarray(qw_ptr, dtype=np.int64), qwalk=np.asarray(qwalk, dtype=np.int32),
         adj=np.asarray(adj, dtype=np.uint64),
-        bwd_queue=np.asarray([(bh, t) for _, bh, t in bq], dtype=np.int32).reshape(-1, 2),
+        bwd_queue=np.asarray([(bh, t * n_groups + grp) for _, bh, t, grp in bq], dtype=np.int32).reshape(-1, 2),
         uncovered_ptr=np.asarray(unc_ptr, dtype=np.int64), uncovered=np.asarray(unc, dtype=np.int32),
         stats=stats,
     )

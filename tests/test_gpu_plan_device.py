@@ -120,6 +120,13 @@ def _bad(p, what):
     assert e2.value.status == K.KPAGE_ERR_INVALID, what
 
 
+def test_device_plan_builds_one_q_group_only():
+    p = make_problem([128, 64], [128, 40, 7], [[0, 1], [2]], heads=1, head_dim=128)
+    with pytest.raises(K.KpageError) as e:
+        K.kpage_plan_device(p, q_group=2)
+    assert e.value.status == K.KPAGE_ERR_UNSUPPORTED
+
+
 def test_device_plan_rejects_malformed_descriptors():
     base = make_problem([128, 64], [128, 40, 7], [[0, 1], [2]], heads=1, head_dim=128)
     p = copy.deepcopy(base)

@@ -253,3 +253,69 @@ def test_uncovered_pages_complement_the_footprints(cfg, heads):
     for g in range(w.kv_valid.shape[0]):
         n = int(t.uncovered_ptr[g + 1] - t.uncovered_ptr[g])
         assert n == w.seq_kv // 16 - sum(-(-int(c) // 16) for c in w.kv_valid[g])
+
+
+def _group_lists(t, n_groups):
+    """revq lists per (owner, group), owner-major."""
+    return [t.revq[t.revq_ptr[i]:t.revq_ptr[i + 1]].tolist() for i in range(len(t.revq_ptr) - 1)]
+
+
+@pytest.mark.parametrize("q_group", [1, 3, 8])
+def test_q_groups_partition_each_reverse_neighbourhood(q_group):
+    """Section 3.3.2: the group lists of an owner are its one-group list cut at multiples of
+    q_group; every edge's token pairs are still visited once (bwd_useful_check == useful);
+    the work items are the non-empty (owner, group) pairs, and an owner without any keeps
+    one item for group 0."""
+    for w in (make_workload(1), make_workload(3, heads=[0]), make_workload(5, heads=[1])):
+        one = oracle_plan(w)
+        t = oracle_plan(w, q_group=q_group)
+        n_groups = -(-w.n_q // q_group)
+        R1 = _group_lists(one, 1)
+        Rg = _group_lists(t, n_groups)
+        assert len(Rg) == len(R1) * n_groups
+        for o, r in enumerate(R1):
+            parts = Rg[o * n_groups:(o + 1) * n_groups]
+            assert sum(parts, []) == r
+            for grp, part in enumerate(parts):
+                assert all(grp * q_group <= q < (grp + 1) * q_group for q in part)
+        assert t.stats["bwd_useful_check"] == t.stats["useful"] == one.stats["useful"]
+        assert np.array_equal(t.owners, one.owners)
+        # work items
+        BH = w.batch * w.heads
+        want = set()
+        for bh in range(BH):
+            g = bh if w.per_head else 0
+            for o in range(int(t.owner_ptr[g + 1] - t.owner_ptr[g])):
+                oo = int(t.owner_ptr[g]) + o
+                grps = [grp for grp in range(n_groups) if Rg[oo * n_groups + grp]] or [0]
+                want |= {(bh, o * n_groups + grp) for grp in grps}
+        got = [tuple(x) for x in t.bwd_queue.tolist()]
+        assert len(got) == len(set(got)) and set(got) == want
+
+
+def test_q_group_not_below_n_q_is_one_group():
+    w = make_workload(3, heads=[0])
+    a, b = oracle_plan(w), oracle_plan(w, q_group=w.n_q)
+    for f in ("revq_ptr", "revq", "qwalk_ptr", "qwalk", "adj", "bwd_queue"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+    assert a.stats == b.stats
+
+
+def test_q_groups_worked_by_hand():
+    """Two K blocks in one owner (c = 32 each), Q blocks 0..3 full: q0 -> k0, q1 -> k1, q3 -> k0.
+    With q_group = 2 the owner's list [0, 1, 3] splits into [0, 1] and [3]."""
+    p = make_problem([128, 128, 128, 128], [32, 32], [[0], [1], [], [0]])
+    t = oracle_plan(p, q_group=2)
+    assert t.owners.tolist() == [[0, 1, 8, 9, -1, -1, -1, -1]]
+    assert t.revq_ptr.tolist() == [0, 2, 3]
+    assert t.revq.tolist() == [0, 1, 3]
+    assert t.qwalk_ptr.tolist() == [0, 16, 24]
+    assert t.qwalk.tolist() == list(range(0, 16)) + list(range(24, 32))
+    # group 0 (2 steps) before group 1 (1 step)
+    assert t.bwd_queue.tolist() == [[0, 0], [0, 1]]
+    full = (1 << 64) - 1
+    k0 = sum(1 << (8 * j + i) for j in range(8) for i in (0, 1))
+    k1 = sum(1 << (8 * j + i) for j in range(8) for i in (2, 3))
+    assert t.adj.tolist() == [k0, k1, k0]
+    assert t.stats["bwd_physical"] == 3 * 128 * 128
+    assert full != k0

@@ -70,8 +70,25 @@ def test_invalid_descriptors_are_rejected_before_device_work(mutate, status):
     assert K.kpage_last_error()
 
 
-def test_q_groups_other_than_one_are_unsupported():
+def test_negative_q_group_is_invalid():
     p = make_problem([128], [128], [[0]], head_dim=128)
     with pytest.raises(K.KpageError) as e:
-        K.kpage_plan(p, q_group=4)
-    assert e.value.status == K.KPAGE_ERR_UNSUPPORTED
+        K.kpage_plan(p, q_group=-1)
+    assert e.value.status == K.KPAGE_ERR_INVALID
+
+
+@pytest.mark.parametrize("q_group", [1, 2, 5, 64])
+@pytest.mark.parametrize("cfg,heads", [(1, None), (3, [0]), (5, [3])])
+def test_q_groups_bit_exact(cfg, heads, q_group):
+    _assert_same(make_workload(cfg, heads=heads), q_group=q_group)
+
+
+def test_q_groups_random_small_layouts_bit_exact():
+    rng = np.random.default_rng(11)
+    sizes = [0, 1, 16, 17, 64, 65, 127, 128]
+    for _ in range(40):
+        n_q, n_kv = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        rows = [rng.permutation(n_kv)[:int(rng.integers(0, n_kv + 1))].tolist() for _ in range(n_q)]
+        p = make_problem(rng.choice(sizes, size=n_q), rng.choice(sizes, size=n_kv), rows, heads=2, head_dim=64,
+                         sort_rows=False)
+        _assert_same(p, q_group=int(rng.integers(1, n_q + 2)))
