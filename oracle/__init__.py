@@ -13,6 +13,8 @@ Attention" (arXiv 2610.28096), sections 3.2-3.4.
 * ``planner``: the page-table, route, validity, owner, reverse-Q, Q-page and
   adjacency construction, step by step, in integers, plus the pair statistics
   of section 4.4.
+* ``selection``: block mean pooling, block scores and top-k selection in a fixed
+  fp64 operation order (the selector in front of KPage that produces its graph).
 * ``layout``: the oracle's own reading of how a T x H x W token grid is
   flattened into 128-row blocks, used to check block-sparse results against
   dense attention over the original tokens.
@@ -27,3 +29,4 @@ from .attention import (  # noqa: F401
     brute_force_fwd,
 )
 from .planner import oracle_plan, PlanTables  # noqa: F401
+from .selection import block_means, block_scores, select_topk, topk_rows  # noqa: F401
