@@ -34,7 +34,7 @@ TABLES = {
 EXPORTED_SYMBOLS = (
     "kpage_plan", "kpage_plan_device", "kpage_plan_upload", "kpage_attn_fwd", "kpage_bwd_workspace_size", "kpage_attn_bwd",
     "kpage_plan_stats", "kpage_plan_export", "kpage_plan_destroy", "kpage_timing_enable", "kpage_timing_read",
-    "kpage_last_error",
+    "kpage_last_error", "kpage_select_workspace_size", "kpage_select_topk",
 )
 
 KERNELS = {"fwd_q128": 0, "fwd_q64": 1, "bwd_pre": 2, "bwd_zero": 3, "bwd_kv": 4, "bwd_dq": 5, "bwd_reduce": 6}
@@ -58,6 +58,15 @@ class KpageProblem(ctypes.Structure):
 
 class KpagePlanOpts(ctypes.Structure):
     _fields_ = [("q_group", ctypes.c_int32), ("align_q128", ctypes.c_int32), ("align_q64", ctypes.c_int32)]
+
+
+class KpageSelectLayout(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("n_q_blocks", ctypes.c_int32), ("n_kv_blocks", ctypes.c_int32),
+        ("seq_q", ctypes.c_int64), ("seq_kv", ctypes.c_int64),
+        ("q_valid", ctypes.c_void_p), ("kv_valid", ctypes.c_void_p), ("kv_offset", ctypes.c_void_p),
+    ]
 
 
 class KpagePairStats(ctypes.Structure):
@@ -87,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.kpage_plan_export.argtypes = [vp, i32, vp, ctypes.POINTER(sz)]
         L.kpage_timing_enable.argtypes = [vp, i32]
         L.kpage_timing_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.kpage_select_workspace_size.argtypes = [ctypes.POINTER(KpageSelectLayout), ctypes.POINTER(sz)]
+        L.kpage_select_topk.argtypes = [ctypes.POINTER(KpageSelectLayout), vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]
         L.kpage_plan_destroy.argtypes = [vp]
         L.kpage_plan_destroy.restype = None
         L.kpage_last_error.restype = ctypes.c_char_p
@@ -278,3 +289,76 @@ def attn_bwd(plan: Plan, q, k, v, o, lse, do, softmax_scale: float, stream=None,
         workspace = torch.empty(kpage_bwd_workspace_size(plan), dtype=torch.uint8, device=q.device)
     kpage_attn_bwd(plan, q, k, v, o, lse, do, dq, dk, dv, workspace, softmax_scale, stream)
     return dq, dk, dv
+
+
+# ---- block selection prelude (device graph for kpage_plan_device) ----
+
+def _select_layout(q, k, q_valid, kv_valid, kv_offset):
+    import torch
+    for name, t, dt in (("q_valid", q_valid, torch.int32), ("kv_valid", kv_valid, torch.int32)):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dt and t.is_contiguous() and t.dim() == 1):
+            raise KpageError(KPAGE_ERR_INVALID, f"{name}: need a contiguous 1-D int32 CUDA tensor")
+    if kv_offset is not None and not (isinstance(kv_offset, torch.Tensor) and kv_offset.is_cuda
+                                      and kv_offset.dtype == torch.int64 and kv_offset.is_contiguous()):
+        raise KpageError(KPAGE_ERR_INVALID, "kv_offset: need a contiguous int64 CUDA tensor or None")
+    for name, t in (("q", q), ("k", k)):
+        if not (t.is_cuda and t.dtype == torch.bfloat16 and t.is_contiguous() and t.dim() == 4):
+            raise KpageError(KPAGE_ERR_INVALID, f"{name}: need a contiguous bf16 CUDA tensor [B, H, S, d]")
+    B, H, Sq, d = q.shape
+    if tuple(k.shape[:2]) != (B, H) or k.shape[3] != d:
+        raise KpageError(KPAGE_ERR_INVALID, "q and k must agree in batch, heads and head_dim")
+    return KpageSelectLayout(batch=B, heads=H, head_dim=d, n_q_blocks=int(q_valid.numel()),
+                             n_kv_blocks=int(kv_valid.numel()), seq_q=Sq, seq_kv=k.shape[2],
+                             q_valid=q_valid.data_ptr(), kv_valid=kv_valid.data_ptr(),
+                             kv_offset=0 if kv_offset is None else kv_offset.data_ptr())
+
+
+def kpage_select_workspace_size(q, k, q_valid, kv_valid, kv_offset=None) -> int:
+    lay = _select_layout(q, k, q_valid, kv_valid, kv_offset)
+    n = ctypes.c_size_t(0)
+    _check(lib().kpage_select_workspace_size(ctypes.byref(lay), ctypes.byref(n)))
+    return int(n.value)
+
+
+def select_topk(q, k, q_valid, kv_valid, kv_offset, top_k: int, stream=None, workspace=None):
+    """Top-k block selection on the GPU (kpage_select_topk): returns the device CSR graph
+    (q2k_ptr int64 [B*H, n_q + 1], q2k_idx int32 [B*H*n_q*top_k] capacity)."""
+    import torch
+    lay = _select_layout(q, k, q_valid, kv_valid, kv_offset)
+    BH, n_q = lay.batch * lay.heads, lay.n_q_blocks
+    ptr = torch.empty((BH, n_q + 1), dtype=torch.int64, device=q.device)
+    idx = torch.empty(max(BH * n_q * top_k, 1), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check(lib().kpage_select_workspace_size(ctypes.byref(lay), ctypes.byref(n)))
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=q.device)
+    _check(lib().kpage_select_topk(ctypes.byref(lay), q.data_ptr(), k.data_ptr(), int(top_k), ptr.data_ptr(),
+                                   idx.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream_ptr(stream)))
+    return ptr, idx
+
+
+class SelectedProblem:
+    """A kpage problem whose descriptor arrays are device tensors: one block layout
+    shared by all heads (repeated per slot) and a per-(b, h) selected graph."""
+
+    def __init__(self, q, k, q_valid, kv_valid, kv_offset, q2k_ptr, q2k_idx):
+        import torch
+        B, H, Sq, d = q.shape
+        G = B * H
+        self.batch, self.heads, self.head_dim = B, H, d
+        self.n_q, self.n_kv = int(q_valid.numel()), int(kv_valid.numel())
+        self.seq_q, self.seq_kv = Sq, k.shape[2]
+        self.per_head = True
+        self.q_valid = q_valid.repeat(G).view(G, -1)
+        self.kv_valid = kv_valid.repeat(G).view(G, -1)
+        off = kv_offset if kv_offset is not None else \
+            torch.arange(self.n_kv, dtype=torch.int64, device=q.device) * 128
+        self.kv_offset = off.repeat(G).view(G, -1)
+        self.q2k_ptr, self.q2k_idx = q2k_ptr, q2k_idx
+
+
+def plan_topk(q, k, q_valid, kv_valid, kv_offset, top_k: int, stream=None, **opts) -> Plan:
+    """Selection, then planning, both on the GPU: the plan of the top-k graph of (q, k)."""
+    ptr, idx = select_topk(q, k, q_valid, kv_valid, kv_offset, top_k, stream)
+    return kpage_plan_device(SelectedProblem(q, k, q_valid, kv_valid, kv_offset, ptr, idx), stream=stream, **opts)

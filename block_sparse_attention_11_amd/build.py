@@ -10,7 +10,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/plan.cpp", "csrc/api.hip", "csrc/plan_dev.hip", "csrc/fwd.hip", "csrc/bwd.hip"]
+SOURCES = ["csrc/plan.cpp", "csrc/api.hip", "csrc/plan_dev.hip", "csrc/fwd.hip", "csrc/bwd.hip", "csrc/select.hip"]
 OUT = os.path.join(HERE, "libkpage.so")
 
 FLAGS = [

@@ -12,6 +12,7 @@
 #include "kpage.h"
 #include "plan.hpp"
 #include "plan_dev.hpp"
+#include "select.hpp"
 
 using namespace kpage;
 
@@ -421,6 +422,55 @@ kpage_status count_partials(PlanT *pl) {
 extern "C" {
 
 const char *kpage_last_error(void) { return g_last_error.c_str(); }
+
+static kpage_status select_args(const kpage_select_layout *l, SelectArgs *a) {
+  if (!l) return fail(KPAGE_ERR_INVALID, "layout is NULL");
+  if (l->head_dim != 64 && l->head_dim != 128) return fail(KPAGE_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (l->batch < 1 || l->heads < 1) return fail(KPAGE_ERR_INVALID, "batch and heads must be >= 1");
+  if (int64_t(l->batch) * l->heads > 65535) return fail(KPAGE_ERR_UNSUPPORTED, "batch * heads above 65535");
+  if (l->n_q_blocks < 1 || l->n_kv_blocks < 1) return fail(KPAGE_ERR_INVALID, "n_q_blocks and n_kv_blocks must be >= 1");
+  if (l->n_kv_blocks > kSelectMaxKv) return fail(KPAGE_ERR_UNSUPPORTED, "more than 4096 key blocks");
+  if (l->seq_q != int64_t(128) * l->n_q_blocks) return fail(KPAGE_ERR_INVALID, "seq_q must equal 128 * n_q_blocks");
+  if (l->seq_kv < 1) return fail(KPAGE_ERR_INVALID, "seq_kv must be >= 1");
+  if (!l->q_valid || !l->kv_valid) return fail(KPAGE_ERR_INVALID, "q_valid and kv_valid are required");
+  a->q_valid = l->q_valid;
+  a->kv_valid = l->kv_valid;
+  a->kv_offset = l->kv_offset;
+  a->seq_q = l->seq_q;
+  a->seq_kv = l->seq_kv;
+  a->n_q = l->n_q_blocks;
+  a->n_kv = l->n_kv_blocks;
+  a->bh_count = l->batch * l->heads;
+  return KPAGE_OK;
+}
+
+kpage_status kpage_select_workspace_size(const kpage_select_layout *layout, size_t *bytes) {
+  if (!bytes) return fail(KPAGE_ERR_INVALID, "bytes is NULL");
+  SelectArgs a{};
+  const kpage_status s = select_args(layout, &a);
+  if (s != KPAGE_OK) return s;
+  *bytes = select_workspace(a, layout->head_dim).total;
+  return KPAGE_OK;
+}
+
+kpage_status kpage_select_topk(const kpage_select_layout *layout, const void *q, const void *k, int32_t top_k,
+                               int64_t *q2k_ptr, int32_t *q2k_idx, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+  SelectArgs a{};
+  kpage_status s = select_args(layout, &a);
+  if (s != KPAGE_OK) return s;
+  if (!q || !k || !q2k_ptr || !q2k_idx || !workspace) return fail(KPAGE_ERR_INVALID, "tensor or output pointer is NULL");
+  if (top_k < 1) return fail(KPAGE_ERR_INVALID, "top_k must be >= 1");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k)) % 16)
+    return fail(KPAGE_ERR_INVALID, "q and k must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(KPAGE_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < select_workspace(a, layout->head_dim).total)
+    return fail(KPAGE_ERR_INVALID, "workspace smaller than kpage_select_workspace_size()");
+  const hipError_t e = launch_select(a, layout->head_dim, top_k, q, k, workspace, q2k_ptr, q2k_idx,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "selection launch");
+  return KPAGE_OK;
+}
 
 kpage_status kpage_plan(const kpage_problem *problem, const kpage_plan_opts *opts, kpage_plan_t **out) {
   if (!out) return fail(KPAGE_ERR_INVALID, "out is NULL");

@@ -244,6 +244,52 @@ kpage_status kpage_timing_read(kpage_plan_t *plan, int kernel_id, double *total_
 /* Message of the last non-OK status on this thread ("" if none). */
 const char *kpage_last_error(void);
 
+/*
+ * Block selection prelude (the selector in front of KPage; KPage paper, sections 1
+ * and 2: VSA-style dynamic selection over 3D video blocks, SSTA's top-k selection).
+ * It produces the per-(b, h) sparse graph that kpage_plan_device() consumes, on the
+ * GPU, so that selection, planning and attention need no host round trip.
+ *
+ * One block layout shared by all (b, h): Q block q holds rows [128 q, 128 q + c_q)
+ * of Q, K block k rows [kv_offset_k, kv_offset_k + c_k) of K (kv_offset NULL: 128 k).
+ * q_valid, kv_valid and kv_offset are DEVICE arrays with the rules of kpage_problem;
+ * the kernels clamp rows to the tensors, and a layout that breaks the rules gives
+ * unspecified lists (kpage_plan_device rejects it).  n_kv_blocks <= 4096;
+ * batch * heads <= 65535.
+ */
+typedef struct {
+  int32_t batch, heads, head_dim;  /* head_dim in {64, 128} */
+  int32_t n_q_blocks, n_kv_blocks;
+  int64_t seq_q, seq_kv;           /* seq_q = 128 * n_q_blocks */
+  const int32_t *q_valid;          /* DEVICE [n_q_blocks] in [0, 128] */
+  const int32_t *kv_valid;         /* DEVICE [n_kv_blocks] in [0, 128] */
+  const int64_t *kv_offset;        /* DEVICE [n_kv_blocks] or NULL */
+} kpage_select_layout;
+
+/* Device workspace of kpage_select_topk(): the fp64 block means,
+ * 8 * batch * heads * head_dim * (n_q + n_kv) bytes plus a few KiB. */
+kpage_status kpage_select_workspace_size(const kpage_select_layout *layout, size_t *bytes);
+
+/*
+ * Top-k block selection: for every (b, h) and query block q with c_q > 0,
+ *   qbar_q, kbar_k = fp64 means of the valid rows (rows added in ascending order),
+ *   s_qk = qbar_q . kbar_k (fp64 products added over ascending columns, each
+ *          operation rounded on its own),
+ *   K_q  = the min(top_k, n_live) key blocks with c_k > 0 of largest s_qk (ties to
+ *          the lower block), in ascending block order; n_live = blocks with c_k > 0.
+ * A query block with c_q = 0 selects nothing.  q, k: bf16 [batch, heads, seq, d]
+ * contiguous, 16-byte aligned, DEVICE.  Outputs, DEVICE, caller-owned:
+ *   q2k_ptr  int64 [batch * heads][n_q + 1], absolute offsets into q2k_idx
+ *            (the per_head = 1 layout of kpage_problem, slot = b * heads + h);
+ *   q2k_idx  int32, capacity batch * heads * n_q * top_k.
+ * The fixed operation order makes the lists a function of the inputs alone.
+ * Asynchronous on `stream`; workspace >= kpage_select_workspace_size(), 256-byte
+ * aligned.  KPAGE_ERR_INVALID / UNSUPPORTED for bad arguments before any GPU work.
+ */
+kpage_status kpage_select_topk(const kpage_select_layout *layout, const void *q, const void *k, int32_t top_k,
+                               int64_t *q2k_ptr, int32_t *q2k_idx, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif
