@@ -29,4 +29,4 @@ from .attention import (  # noqa: F401
     brute_force_fwd,
 )
 from .planner import oracle_plan, PlanTables  # noqa: F401
-from .selection import block_means, block_scores, select_topk, topk_rows  # noqa: F401
+from .selection import block_means, block_scores, select_top_p, select_topk, top_p_clusters, topk_rows  # noqa: F401

@@ -17,6 +17,22 @@ blocks" taken here, for one block layout shared by all heads:
 The fixed operation order makes the scores, and so the selected sets, a function of the
 inputs alone, so a GPU implementation that follows the same order must select exactly
 the same blocks.
+
+Cluster selection (SVG2-style: Q and K tokens clustered and permuted into independent
+partitions, KPage paper sections 3.4.1 and 4.6; the selection rule is SVG2's, read as):
+
+  cluster score  s_ck = scale * (qcent_c . kcent_k), the dot product as above over the
+                 fp32 centroids widened to fp64, then one rounded product with scale
+  kept clusters  for each Q cluster with tokens, the K clusters with tokens ordered by
+                 score descending (ties to the lower cluster); softmax probabilities
+                 p = exp(s - s_max) / sum; keep the shortest prefix whose cumulative
+                 probability reaches top_p (all of them if rounding never reaches it)
+  block lists    a Q block of cluster c selects every K block of a kept cluster, in
+                 ascending block order; a Q block without a cluster selects nothing
+
+The exponential and the probability sums are where two correct implementations may
+round differently: a cut can only move where the cumulative probability lies within
+rounding of top_p.
 """
 from __future__ import annotations
 
@@ -77,3 +93,34 @@ def select_topk(q: np.ndarray, k: np.ndarray, q_valid, kv_valid, kv_offset, top_
             kbar = block_means(k[b, h], kv_valid, kv_offset)
             out[(b, h)] = topk_rows(block_scores(qbar, kbar), q_valid, kv_valid, top_k)
     return out
+
+
+def top_p_clusters(scores: np.ndarray, live: Sequence[int], top_p: float) -> List[int]:
+    """Kept K clusters of one Q cluster (ascending), by the rule in the module header."""
+    live = np.asarray(list(live), dtype=np.int64)
+    if len(live) == 0:
+        return []
+    x = scores[live]
+    order = np.lexsort((live, -x))
+    z = x[order] - x[order[0]]
+    e = np.exp(z)
+    csum = np.cumsum(e / e.sum())
+    m = int(np.searchsorted(csum, top_p)) + 1  # first index whose cumulative probability >= top_p
+    return sorted(int(c) for c in live[order[:min(m, len(order))]])
+
+
+def select_top_p(q_cent, k_cent, q_size, k_size, q_block_cluster, k_block_cluster, top_p: float, scale: float):
+    """Block lists of one (b, h) from its clustering (every argument as in the module header)."""
+    qc = np.asarray(q_cent, dtype=np.float64)
+    kc = np.asarray(k_cent, dtype=np.float64)
+    s = block_scores(qc, kc) * float(scale)
+    live = [k for k in range(kc.shape[0]) if int(k_size[k]) > 0]
+    kept = {c: set(top_p_clusters(s[c], live, top_p)) for c in range(qc.shape[0]) if int(q_size[c]) > 0}
+    rows = []
+    for c in q_block_cluster:
+        c = int(c)
+        if c < 0 or c not in kept:
+            rows.append([])
+            continue
+        rows.append([k for k, kc_ in enumerate(k_block_cluster) if int(kc_) in kept[c]])
+    return rows

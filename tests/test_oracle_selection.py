@@ -114,3 +114,44 @@ def test_invariants(seed):
             if r:
                 rest = [k for k in live if k not in r]
                 assert all(s[a, x] >= s[a, y] for x in r for y in rest)
+
+
+def test_top_p_worked_by_hand():
+    """Scores log 6, log 3, 0 give softmax 0.6, 0.3, 0.1 (cumulative 0.6, 0.9, 1.0)."""
+    from oracle.selection import top_p_clusters
+    s = np.array([np.log(3.0), 0.0, np.log(6.0), -50.0])
+    live = [0, 1, 2]  # cluster 3 has no tokens
+    assert top_p_clusters(s, live, 0.5) == [2]
+    assert top_p_clusters(s, live, 0.85) == [0, 2]
+    assert top_p_clusters(s, live, 0.95) == [0, 1, 2]
+    assert top_p_clusters(s, [], 0.9) == []
+    # equal scores: the lower cluster comes first
+    t = np.array([1.0, 1.0, 1.0, 1.0])
+    assert top_p_clusters(t, [0, 1, 2, 3], 0.3) == [0, 1]   # 0.25 < 0.3 <= 0.5
+    assert top_p_clusters(t, [3, 1, 2], 0.3) == [1]         # 1/3 >= 0.3
+
+
+def test_top_p_block_lists_worked_by_hand():
+    """Two Q clusters, three K clusters (cluster 1 empty); centroids make cluster 0 prefer K
+    cluster 2 strongly and cluster 1 split evenly; K blocks 0..4 belong to clusters 0,2,2,0,-1."""
+    from oracle.selection import select_top_p
+    qc = np.array([[10.0, 0.0], [0.0, 0.0]])
+    kc = np.array([[0.0, 1.0], [5.0, 5.0], [1.0, 0.0]])
+    rows = select_top_p(qc, kc, q_size=[3, 1], k_size=[4, 0, 7], q_block_cluster=[1, 0, -1, 0],
+                        k_block_cluster=[0, 2, 2, 0, -1], top_p=0.9, scale=1.0)
+    # cluster 0: scores 0 (k0), 10 (k2): p(k2) = 1 / (1 + e^-10) > 0.9 -> {2}
+    # cluster 1: scores 0, 0: p = 0.5 each -> both needed for 0.9 -> {0, 2}
+    assert rows == [[0, 1, 2, 3], [1, 2], [], [1, 2]]
+
+
+def test_top_p_matches_the_workload_generator():
+    """The SVG2-like workload's graph comes from an independent implementation of the same rule
+    (numpy product, division by sqrt(d)); every row agrees on two heads."""
+    from oracle.selection import select_top_p
+    w = make_workload(5, heads=[0, 1])
+    for g in range(2):
+        c = w.clusters[g]
+        rows = select_top_p(c["q_cent"], c["k_cent"], c["q_size"], c["k_size"], c["q_block_cluster"],
+                            c["k_block_cluster"], 0.9, 1.0 / np.sqrt(w.head_dim))
+        for q in range(w.n_q):
+            assert rows[q] == w.q2k_idx[w.q2k_ptr[g, q]:w.q2k_ptr[g, q + 1]].tolist(), (g, q)

@@ -90,6 +90,10 @@ class Workload:
     do: Optional[torch.Tensor] = None   # bf16 [B, H, seq_q, d]
     head_ids: List[int] = field(default_factory=list)
     layout: Optional[dict] = None
+    # independent partitions only: per slot, the clustering the graph was selected from
+    # (q_cent / k_cent fp32 [n_clusters, d], q_size / k_size tokens per cluster,
+    # q_block_cluster [n_q] / k_block_cluster [n_kv] cluster of each block, -1 none)
+    clusters: Optional[list] = None
 
     @property
     def n_slots(self) -> int:
@@ -349,7 +353,8 @@ def _make_svg2(cfg: int, head_ids, batch, with_do, n_qc=200, n_kc=600, top_p=0.9
             for i, c in enumerate(kvalid):
                 koff[i] = acc
                 acc += PAGE_ROWS * (-(-int(c) // PAGE_ROWS))
-            per.append(dict(qt=qt[pq], kt=kt[pk], vt=vt[pk], qblocks=qblocks, kblocks=kblocks,
+            per.append(dict(cq=cq, ck=ck, nq_sz=nq_sz, nk_sz=nk_sz, qcl=qcl, kcl=kcl,
+                            qt=qt[pq], kt=kt[pk], vt=vt[pk], qblocks=qblocks, kblocks=kblocks,
                             qvalid=np.asarray([c for _, c in qblocks], dtype=np.int32),
                             kvalid=kvalid, koff=koff, kfoot=acc, rows=rows, b=b, h=h))
     n_q = max(len(p["qblocks"]) for p in per)
@@ -365,9 +370,17 @@ def _make_svg2(cfg: int, head_ids, batch, with_do, n_qc=200, n_kc=600, top_p=0.9
     out = {nm: torch.zeros(batch, len(head_ids), (S_q if nm in ("q", "do") else S_kv), d,
                            dtype=torch.bfloat16) for nm in names}
     ptrs, idxs, base = [], [], 0
+    clusters = []
     for g, p in enumerate(per):
         b, hi = g // len(head_ids), g % len(head_ids)
         nq, nk = len(p["qblocks"]), len(p["kblocks"])
+        qbc = np.full(n_q, -1, dtype=np.int32)
+        kbc = np.full(n_kv, -1, dtype=np.int32)
+        qbc[:nq] = p["qcl"]
+        kbc[:nk] = p["kcl"]
+        clusters.append(dict(q_cent=np.asarray(p["cq"], dtype=np.float32), k_cent=np.asarray(p["ck"], dtype=np.float32),
+                             q_size=np.asarray(p["nq_sz"], dtype=np.int32), k_size=np.asarray(p["nk_sz"], dtype=np.int32),
+                             q_block_cluster=qbc, k_block_cluster=kbc))
         q_valid[g, :nq] = p["qvalid"]
         kv_valid[g, :nk] = p["kvalid"]
         kv_offset[g, :nk] = p["koff"]
@@ -393,7 +406,7 @@ def _make_svg2(cfg: int, head_ids, batch, with_do, n_qc=200, n_kc=600, top_p=0.9
         q_valid=q_valid, kv_valid=kv_valid, kv_offset=kv_offset,
         q2k_ptr=np.stack(ptrs), q2k_idx=np.concatenate(idxs),
         q=out["q"], k=out["k"], v=out["v"], do=out.get("do"), head_ids=list(head_ids),
-        layout=dict(T=spec["T"], H=spec["H"], W=spec["W"], tile=TILE, grid=grid),
+        layout=dict(T=spec["T"], H=spec["H"], W=spec["W"], tile=TILE, grid=grid), clusters=clusters,
     )
 
 
