@@ -74,6 +74,39 @@ def _prelude(K, w, q, k, top_k=87, reps=5):
                          "algorithmic": "Q and K valid rows read once + CSR graph written"}}
 
 
+def _prelude_top_p(K, w, top_p=0.9, reps=5):
+    """GPU cluster top-p selection (SVG2-style) from the workload's own clustering, then the
+    GPU planner on its graph.  Timed with events on torch's current stream."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda", 0)
+    st = lambda key, dt: torch.as_tensor(np.stack([c[key] for c in w.clusters]), device=dev).to(dt).contiguous()
+    args = [st("q_cent", torch.float32), st("k_cent", torch.float32), st("q_size", torch.int32),
+            st("k_size", torch.int32), st("q_block_cluster", torch.int32), st("k_block_cluster", torch.int32)]
+    scale = 1.0 / np.sqrt(w.head_dim)
+    ptr, idx = K.select_top_p(w.batch, w.heads, *args, top_p=top_p, scale=scale)  # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        ptr, idx = K.select_top_p(w.batch, w.heads, *args, top_p=top_p, scale=scale)
+    e1.record()
+    torch.cuda.synchronize()
+    sel_ms = e0.elapsed_time(e1) / reps
+    p = type("SelectedGraph", (), {})()
+    for a in ("batch", "heads", "head_dim", "n_q", "n_kv", "seq_q", "seq_kv", "per_head", "q_valid", "kv_valid",
+              "kv_offset"):
+        setattr(p, a, getattr(w, a))
+    p.q2k_ptr, p.q2k_idx = ptr, idx
+    t0 = time.perf_counter()
+    plan = K.kpage_plan_device(p)
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    plan.close()
+    return {"select_top_p_ms": round(sel_ms, 4), "plan_device_ms_incl_sync": round(plan_ms, 2), "top_p": top_p,
+            "clusters": [int(args[0].shape[1]), int(args[1].shape[1])]}
+
+
 def _cpu_baseline(workload, heads):
     """The fp64 CPU oracle on a bounded sample: forward + backward of a few heads."""
     import numpy as np  # noqa: F401
@@ -256,6 +289,8 @@ def main():
     }
     if args.workload == 4:
         out["prelude"] = _prelude(K, w, q, k)
+    if args.workload == 5:
+        out["prelude"] = _prelude_top_p(K, w)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(args.workload, cpu_heads)
     print(json.dumps(out), flush=True)

@@ -34,7 +34,8 @@ TABLES = {
 EXPORTED_SYMBOLS = (
     "kpage_plan", "kpage_plan_device", "kpage_plan_upload", "kpage_attn_fwd", "kpage_bwd_workspace_size", "kpage_attn_bwd",
     "kpage_plan_stats", "kpage_plan_export", "kpage_plan_destroy", "kpage_timing_enable", "kpage_timing_read",
-    "kpage_last_error", "kpage_select_workspace_size", "kpage_select_topk",
+    "kpage_last_error", "kpage_select_workspace_size", "kpage_select_topk", "kpage_select_top_p_workspace_size",
+    "kpage_select_top_p",
 )
 
 KERNELS = {"fwd_q128": 0, "fwd_q64": 1, "bwd_pre": 2, "bwd_zero": 3, "bwd_kv": 4, "bwd_dq": 5, "bwd_reduce": 6}
@@ -69,6 +70,17 @@ class KpageSelectLayout(ctypes.Structure):
     ]
 
 
+class KpageSelectClusters(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("n_q_clusters", ctypes.c_int32), ("n_kv_clusters", ctypes.c_int32),
+        ("n_q_blocks", ctypes.c_int32), ("n_kv_blocks", ctypes.c_int32),
+        ("q_centroids", ctypes.c_void_p), ("kv_centroids", ctypes.c_void_p),
+        ("q_cluster_size", ctypes.c_void_p), ("kv_cluster_size", ctypes.c_void_p),
+        ("q_block_cluster", ctypes.c_void_p), ("kv_block_cluster", ctypes.c_void_p),
+    ]
+
+
 class KpagePairStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in
                 ("useful", "whole_block", "paged_m128", "nominal", "scheduled", "bwd_physical", "bwd_useful_check")]
@@ -98,6 +110,9 @@ def lib() -> ctypes.CDLL:
         L.kpage_timing_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.kpage_select_workspace_size.argtypes = [ctypes.POINTER(KpageSelectLayout), ctypes.POINTER(sz)]
         L.kpage_select_topk.argtypes = [ctypes.POINTER(KpageSelectLayout), vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp]
+        L.kpage_select_top_p_workspace_size.argtypes = [ctypes.POINTER(KpageSelectClusters), ctypes.POINTER(sz)]
+        L.kpage_select_top_p.argtypes = [ctypes.POINTER(KpageSelectClusters), ctypes.c_double, ctypes.c_double, vp, vp,
+                                         vp, sz, vp]
         L.kpage_plan_destroy.argtypes = [vp]
         L.kpage_plan_destroy.restype = None
         L.kpage_last_error.restype = ctypes.c_char_p
@@ -362,3 +377,38 @@ def plan_topk(q, k, q_valid, kv_valid, kv_offset, top_k: int, stream=None, **opt
     """Selection, then planning, both on the GPU: the plan of the top-k graph of (q, k)."""
     ptr, idx = select_topk(q, k, q_valid, kv_valid, kv_offset, top_k, stream)
     return kpage_plan_device(SelectedProblem(q, k, q_valid, kv_valid, kv_offset, ptr, idx), stream=stream, **opts)
+
+
+def select_top_p(batch: int, heads: int, q_cent, k_cent, q_size, k_size, q_block_cluster, k_block_cluster,
+                 top_p: float, scale: float, stream=None, workspace=None):
+    """Cluster top-p selection on the GPU (kpage_select_top_p).  Arrays are CUDA tensors:
+    q_cent / k_cent fp32 [B*H, n_clusters, d]; q_size / k_size int32 [B*H, n_clusters];
+    q_block_cluster / k_block_cluster int32 [B*H, n_blocks].  Returns the device CSR graph
+    (q2k_ptr int64 [B*H, n_q + 1], q2k_idx int32 with capacity B*H*n_q*n_kv)."""
+    import torch
+    arrs = dict(q_cent=(q_cent, torch.float32, 3), k_cent=(k_cent, torch.float32, 3),
+                q_size=(q_size, torch.int32, 2), k_size=(k_size, torch.int32, 2),
+                q_block_cluster=(q_block_cluster, torch.int32, 2), k_block_cluster=(k_block_cluster, torch.int32, 2))
+    for name, (t, dt, nd) in arrs.items():
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dt and t.is_contiguous() and t.dim() == nd
+                and t.shape[0] == batch * heads):
+            raise KpageError(KPAGE_ERR_INVALID, f"{name}: need a contiguous {dt} CUDA tensor of rank {nd}, "
+                                                f"first dimension batch * heads")
+    G, n_qc, d = q_cent.shape
+    n_kc = k_cent.shape[1]
+    n_q, n_kv = q_block_cluster.shape[1], k_block_cluster.shape[1]
+    desc = KpageSelectClusters(batch=batch, heads=heads, head_dim=d, n_q_clusters=n_qc, n_kv_clusters=n_kc,
+                               n_q_blocks=n_q, n_kv_blocks=n_kv, q_centroids=q_cent.data_ptr(),
+                               kv_centroids=k_cent.data_ptr(), q_cluster_size=q_size.data_ptr(),
+                               kv_cluster_size=k_size.data_ptr(), q_block_cluster=q_block_cluster.data_ptr(),
+                               kv_block_cluster=k_block_cluster.data_ptr())
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check(lib().kpage_select_top_p_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+        workspace = torch.empty(n.value, dtype=torch.uint8, device=q_cent.device)
+    ptr = torch.empty((G, n_q + 1), dtype=torch.int64, device=q_cent.device)
+    idx = torch.empty(max(G * n_q * n_kv, 1), dtype=torch.int32, device=q_cent.device)
+    _check(lib().kpage_select_top_p(ctypes.byref(desc), float(top_p), float(scale), ptr.data_ptr(), idx.data_ptr(),
+                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                    _stream_ptr(stream)))
+    return ptr, idx

@@ -472,6 +472,58 @@ kpage_status kpage_select_topk(const kpage_select_layout *layout, const void *q,
   return KPAGE_OK;
 }
 
+static kpage_status cluster_args(const kpage_select_clusters *c, ClusterArgs *a) {
+  if (!c) return fail(KPAGE_ERR_INVALID, "clusters descriptor is NULL");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(KPAGE_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->batch < 1 || c->heads < 1) return fail(KPAGE_ERR_INVALID, "batch and heads must be >= 1");
+  if (int64_t(c->batch) * c->heads > 65535) return fail(KPAGE_ERR_UNSUPPORTED, "batch * heads above 65535");
+  if (c->n_q_clusters < 1 || c->n_kv_clusters < 1 || c->n_q_blocks < 1 || c->n_kv_blocks < 1)
+    return fail(KPAGE_ERR_INVALID, "cluster and block counts must be >= 1");
+  if (c->n_kv_clusters > kSelectMaxKv) return fail(KPAGE_ERR_UNSUPPORTED, "more than 4096 K clusters");
+  if (!c->q_centroids || !c->kv_centroids || !c->q_cluster_size || !c->kv_cluster_size || !c->q_block_cluster ||
+      !c->kv_block_cluster)
+    return fail(KPAGE_ERR_INVALID, "a clusters array is NULL");
+  a->q_cent = c->q_centroids;
+  a->k_cent = c->kv_centroids;
+  a->q_size = c->q_cluster_size;
+  a->k_size = c->kv_cluster_size;
+  a->q_block_cluster = c->q_block_cluster;
+  a->k_block_cluster = c->kv_block_cluster;
+  a->n_qc = c->n_q_clusters;
+  a->n_kc = c->n_kv_clusters;
+  a->n_q = c->n_q_blocks;
+  a->n_kv = c->n_kv_blocks;
+  a->bh_count = c->batch * c->heads;
+  return KPAGE_OK;
+}
+
+kpage_status kpage_select_top_p_workspace_size(const kpage_select_clusters *c, size_t *bytes) {
+  if (!bytes) return fail(KPAGE_ERR_INVALID, "bytes is NULL");
+  ClusterArgs a{};
+  const kpage_status s = cluster_args(c, &a);
+  if (s != KPAGE_OK) return s;
+  *bytes = cluster_workspace(a, c->head_dim).total;
+  return KPAGE_OK;
+}
+
+kpage_status kpage_select_top_p(const kpage_select_clusters *c, double top_p, double scale, int64_t *q2k_ptr,
+                                int32_t *q2k_idx, void *workspace, size_t workspace_bytes, void *stream) {
+  ClusterArgs a{};
+  kpage_status s = cluster_args(c, &a);
+  if (s != KPAGE_OK) return s;
+  if (!(top_p > 0.0 && top_p <= 1.0)) return fail(KPAGE_ERR_INVALID, "top_p must lie in (0, 1]");
+  if (!(scale > 0.0) || !std::isfinite(scale)) return fail(KPAGE_ERR_INVALID, "scale must be positive and finite");
+  if (!q2k_ptr || !q2k_idx || !workspace) return fail(KPAGE_ERR_INVALID, "output or workspace pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(KPAGE_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < cluster_workspace(a, c->head_dim).total)
+    return fail(KPAGE_ERR_INVALID, "workspace smaller than kpage_select_top_p_workspace_size()");
+  a.top_p = top_p;
+  a.scale = scale;
+  const hipError_t e = launch_select_top_p(a, c->head_dim, workspace, q2k_ptr, q2k_idx, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cluster selection launch");
+  return KPAGE_OK;
+}
+
 kpage_status kpage_plan(const kpage_problem *problem, const kpage_plan_opts *opts, kpage_plan_t **out) {
   if (!out) return fail(KPAGE_ERR_INVALID, "out is NULL");
   *out = nullptr;

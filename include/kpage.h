@@ -266,8 +266,8 @@ typedef struct {
   const int64_t *kv_offset;        /* DEVICE [n_kv_blocks] or NULL */
 } kpage_select_layout;
 
-/* Device workspace of kpage_select_topk(): the fp64 block means,
- * 8 * batch * heads * head_dim * (n_q + n_kv) bytes plus a few KiB. */
+/* Device workspace of kpage_select_topk(): the fp64 block means and block scores,
+ * 8 * batch * heads * (head_dim * (n_q + n_kv) + n_q * n_kv) bytes plus a few KiB. */
 kpage_status kpage_select_workspace_size(const kpage_select_layout *layout, size_t *bytes);
 
 /*
@@ -289,6 +289,45 @@ kpage_status kpage_select_workspace_size(const kpage_select_layout *layout, size
 kpage_status kpage_select_topk(const kpage_select_layout *layout, const void *q, const void *k, int32_t top_k,
                                int64_t *q2k_ptr, int32_t *q2k_idx, void *workspace, size_t workspace_bytes,
                                void *stream);
+
+/*
+ * Cluster selection for independent Q/K partitions (SVG2-style: Q and K tokens
+ * clustered and permuted so each cluster occupies contiguous blocks; KPage paper,
+ * sections 3.4.1 and 4.6).  Per (b, h) slot g = b * heads + h, DEVICE arrays:
+ *   q_centroids  fp32 [G][n_q_clusters][head_dim], kv_centroids fp32 [G][n_kv_clusters][head_dim]
+ *   q_cluster_size, kv_cluster_size  int32 [G][n_clusters]: tokens per cluster
+ *   q_block_cluster int32 [G][n_q_blocks], kv_block_cluster int32 [G][n_kv_blocks]:
+ *                the cluster each block belongs to, -1 for none (out-of-range ids count as none)
+ * n_kv_clusters <= 4096; batch * heads <= 65535.
+ */
+typedef struct {
+  int32_t batch, heads, head_dim;  /* head_dim in {64, 128} */
+  int32_t n_q_clusters, n_kv_clusters, n_q_blocks, n_kv_blocks;
+  const float *q_centroids, *kv_centroids;
+  const int32_t *q_cluster_size, *kv_cluster_size;
+  const int32_t *q_block_cluster, *kv_block_cluster;
+} kpage_select_clusters;
+
+/* Device workspace of kpage_select_top_p(): fp64 centroids and cluster scores,
+ * a keep mask and per-row counts, about 8 * G * (head_dim * (n_qc + n_kc) + n_qc * n_kc
+ * + n_q_blocks) bytes. */
+kpage_status kpage_select_top_p_workspace_size(const kpage_select_clusters *c, size_t *bytes);
+
+/*
+ * Top-p cluster selection: for every slot and Q cluster with tokens,
+ *   s_k   = scale * (qcent . kcent_k) for every K cluster with tokens (fp64; the dot
+ *           product over ascending columns, each operation rounded on its own),
+ *   order = s descending, ties to the lower cluster; softmax p = exp(s - s_max) / sum,
+ *   keep  = the shortest prefix of that order whose cumulative p reaches top_p (all of
+ *           them if rounding never reaches it);
+ * a Q block of that cluster selects every K block of a kept cluster, in ascending block
+ * order; a Q block without a cluster selects nothing.  Outputs, DEVICE, caller-owned:
+ *   q2k_ptr int64 [G][n_q_blocks + 1], absolute offsets into q2k_idx;
+ *   q2k_idx int32, capacity G * n_q_blocks * n_kv_blocks.
+ * 0 < top_p <= 1, scale > 0.  Asynchronous on `stream`; workspace 256-byte aligned.
+ */
+kpage_status kpage_select_top_p(const kpage_select_clusters *c, double top_p, double scale, int64_t *q2k_ptr,
+                                int32_t *q2k_idx, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -129,3 +129,79 @@ def test_select_time_full_size():
     K.plan_topk(q, k, qv, kvv, ko, 87)
     torch.cuda.synchronize()
     _say(f"  select + GPU plan: {(time.perf_counter() - t0) * 1e3:.2f} ms")
+
+
+# ---- cluster top-p selection (independent partitions) ----
+
+def _stack(dicts, key, dtype):
+    return torch.as_tensor(np.stack([c[key] for c in dicts]), device=DEV).to(dtype).contiguous()
+
+
+def _top_p_rows_gpu(clusters, B, H, top_p, scale):
+    args = [_stack(clusters, k, t) for k, t in (("q_cent", torch.float32), ("k_cent", torch.float32),
+                                                ("q_size", torch.int32), ("k_size", torch.int32),
+                                                ("q_block_cluster", torch.int32), ("k_block_cluster", torch.int32))]
+    ptr, idx = K.select_top_p(B, H, *args, top_p=top_p, scale=scale)
+    torch.cuda.synchronize()
+    n_q = clusters[0]["q_block_cluster"].shape[0]
+    return _gpu_rows(ptr, idx, B, H, n_q), (ptr, idx)
+
+
+def _check_top_p(clusters, B, H, top_p, scale, label):
+    from oracle.selection import block_scores, select_top_p
+    got, dev = _top_p_rows_gpu(clusters, B, H, top_p, scale)
+    for g, c in enumerate(clusters):
+        ref = select_top_p(c["q_cent"], c["k_cent"], c["q_size"], c["k_size"], c["q_block_cluster"],
+                           c["k_block_cluster"], top_p, scale)
+        rows = got[(g // H, g % H)]
+        for q, (a, b) in enumerate(zip(rows, ref)):
+            if a == b:
+                continue
+            # a different cut is only allowed where the cumulative probability sits within rounding of top_p
+            cl = int(c["q_block_cluster"][q])
+            s = block_scores(np.asarray(c["q_cent"], np.float64), np.asarray(c["k_cent"], np.float64))[cl] * scale
+            live = np.nonzero(np.asarray(c["k_size"]) > 0)[0]
+            x = np.sort(s[live])[::-1]
+            e = np.exp(x - x[0])
+            csum = np.cumsum(e / e.sum())
+            assert np.min(np.abs(csum - top_p)) <= 1e-12, (label, g, q)
+    _say(f"  {label}: {len(clusters)} slots equal")
+    return dev
+
+
+def test_select_top_p_svg2_like_two_heads():
+    w = make_workload(5, heads=[0, 1])
+    _check_top_p(w.clusters, 1, 2, 0.9, 1.0 / np.sqrt(w.head_dim), "SVG2-like clusters two heads")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("top_p", [0.3, 0.9, 1.0])
+def test_select_top_p_small(d, top_p):
+    rng = np.random.default_rng(d + int(10 * top_p))
+    n_qc, n_kc, n_q, n_kv = 5, 9, 8, 14
+    clusters = []
+    for _ in range(3):
+        k_cent = rng.standard_normal((n_kc, d)).astype(np.float32)
+        k_cent[4] = k_cent[1]  # equal scores: the lower cluster first
+        clusters.append(dict(
+            q_cent=rng.standard_normal((n_qc, d)).astype(np.float32), k_cent=k_cent,
+            q_size=np.array([3, 0, 7, 1, 2], dtype=np.int32), k_size=np.array([1, 4, 0, 2, 9, 3, 0, 5, 1], np.int32),
+            q_block_cluster=np.array([0, 2, 2, -1, 3, 4, 1, 0], dtype=np.int32),
+            k_block_cluster=rng.integers(-1, n_kc, size=n_kv).astype(np.int32)))
+    _check_top_p(clusters, 1, 3, top_p, 0.25, f"small clusters d={d} top_p={top_p}")
+
+
+def test_select_top_p_then_plan():
+    """GPU cluster selection feeds the GPU planner: the plan equals the host plan of the
+    workload's own graph (the same rule, pinned against the oracle)."""
+    w = make_workload(5, heads=[0, 1])
+    _, (ptr, idx) = _top_p_rows_gpu(w.clusters, 1, 2, 0.9, 1.0 / np.sqrt(w.head_dim))
+    p = type("P", (), {})()
+    for a in ("batch", "heads", "head_dim", "n_q", "n_kv", "seq_q", "seq_kv", "per_head", "q_valid", "kv_valid",
+              "kv_offset"):
+        setattr(p, a, getattr(w, a))
+    p.q2k_ptr, p.q2k_idx = ptr, idx
+    d = K.kpage_plan_device(p)
+    h = K.kpage_plan(w)
+    for t in ("fwd_walk", "fwd_walk_ptr", "q128_queue", "q64_queue", "owners", "qwalk", "adj"):
+        assert np.array_equal(K.kpage_plan_export(d, t), K.kpage_plan_export(h, t)), t
