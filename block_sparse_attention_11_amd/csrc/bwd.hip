@@ -19,7 +19,10 @@
 //   kpage_bwd_pre   D_i = sum_d dO_id O_id and LSE_i * log2(e) (+inf for rows
 //                   without keys), 16 threads per row.
 //   kpage_bwd_zero  zero dK/dV pages that lie outside every block footprint.
-//   kpage_bwd_kv    one workgroup per (batch*head, owner): dK, dV.
+//   kpage_bwd_kv    one workgroup per (batch*head, owner), or per (batch*head,
+//                   owner, Q group) when the plan splits reverse neighbourhoods
+//                   into Q groups (section 3.3.2): dK, dV, or fp32 partials of them.
+//   kpage_bwd_kv_reduce  sums the partials of owners split over Q groups.
 //   kpage_bwd_dq    one workgroup per forward work item (query block): dQ.
 #include <hip/hip_runtime.h>
 

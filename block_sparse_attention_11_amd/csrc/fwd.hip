@@ -1,23 +1,24 @@
 // Forward KPage attention for gfx950 (MI355X, CDNA4).
 //
 // KPage paper, section 3.2: every work item is one query block of one
-// (batch, head).  Its K/V page walk is consumed in tiles of 8 Page16 regions
-// (128 key rows).  Each page is a contiguous 16-row run of the original K/V
-// tensors and is copied straight from global memory into LDS with 16-byte
-// direct-to-LDS loads (section 3.2.3); no compacted copy exists in HBM.  The
-// consumer is a flash-attention step on the assembled tile: bf16 MFMA for
-// Q K^T and P V with fp32 accumulation, and an online softmax (section 3.2.4:
-// invalid rows are set to -inf before the row maximum, and only on tiles at or
-// past the end of the fully valid prefix).
+// (batch, head).  Its K/V page walk (8 Page16 regions per step for M128 x N128,
+// 16 for M64 x N256) is consumed in tiles of 4 pages (64 key rows).  Each page is
+// a contiguous 16-row run of the original K/V tensors and is copied straight from
+// global memory into LDS with 16-byte direct-to-LDS loads (section 3.2.3); no
+// compacted copy exists in HBM.  The consumer is a flash-attention step on the
+// assembled tile: bf16 MFMA for Q K^T and P V with fp32 accumulation, and an
+// online softmax (section 3.2.4: invalid rows are set to -inf before the row
+// maximum, and only on tiles at or past the end of the fully valid prefix).
 //
-// Work split.  A workgroup has 8 waves, two per SIMD, so that one wave's
-// vector work can issue while the other's matrix work runs.  Every wave owns 32
-// query rows of the item and a fixed key range of every tile, walked as
-// sub-tiles of 32 keys.  Route M128 x N128 (section 3.2.2): 4 query groups x 2
-// key halves, 2 sub-tiles per wave per tile.  Route M64 x N256: 2 query groups
-// x 4 key quarters, 1 sub-tile per wave per tile, so the route's 16-page
-// iteration is two tiles.  Each wave keeps its own running maximum, sum and
-// output; the waves that share query rows are merged once at the end.
+// Work split.  A workgroup has 4 waves and two workgroups share a CU, so every
+// SIMD runs two waves of different items that drift apart: one wave's vector
+// work issues while the other's matrix work runs.  Each wave copies one K and one
+// V page of every tile, owns 32 query rows of the item and a fixed key range of
+// every tile, walked as sub-tiles of 32 keys.  Route M128 x N128 (section 3.2.2):
+// 4 query groups, every wave takes all 64 keys of a tile (2 sub-tiles).  Route
+// M64 x N256: 2 query groups x 2 key halves, 1 sub-tile per wave per tile.  Each
+// wave keeps its own running maximum, sum and output; waves that share query
+// rows are merged once at the end.
 //
 // Matrix layout per wave (v_mfma_f32_32x32x16_bf16, 32 cycles each):
 //   S^T (key x query) = K . Q^T : A = K rows from LDS, B = Q rows kept in VGPRs.
