@@ -224,27 +224,29 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   return KPAGE_OK;
 }
 
+// device table -> host vector; false when the copy fails
 template <class T>
-void copy_down(std::vector<T> &dst, const T *src, int64_t n) {
+bool copy_down(std::vector<T> &dst, const T *src, int64_t n) {
   dst.resize(size_t(std::max<int64_t>(n, 0)));
-  if (n > 0) (void)hipMemcpy(dst.data(), src, size_t(n) * sizeof(T), hipMemcpyDeviceToHost);
+  return n <= 0 || hipMemcpy(dst.data(), src, size_t(n) * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
 }
 
 // device-planned plans: the forward tables, copied for export
-void ensure_forward_on_host(PlanT *pl) {
-  if (pl->fwd_on_host) return;
+kpage_status ensure_forward_on_host(PlanT *pl) {
+  if (pl->fwd_on_host) return KPAGE_OK;
   const DevFwdTables &T = pl->DF;
   FwdTables &F = pl->F;
   const int64_t GQ = int64_t(pl->P.slots) * pl->P.n_q;
-  copy_down(F.route, T.route, GQ);
-  copy_down(F.walk_ptr, T.walk_ptr, int64_t(pl->P.slots) * (pl->P.n_q + 1));
-  copy_down(F.walk, T.walk, T.walk_total);
-  copy_down(F.nfull, T.nfull, GQ);
-  copy_down(F.valid, T.valid, T.walk_total / 2);
-  copy_down(F.q64_queue, T.q64_queue, 2 * int64_t(T.n_q64));
-  copy_down(F.q128_queue, T.q128_queue, 2 * int64_t(T.n_q128));
-  copy_down(F.unpadded, T.unpadded, GQ);
+  const bool ok = copy_down(F.route, T.route, GQ) &&
+                  copy_down(F.walk_ptr, T.walk_ptr, int64_t(pl->P.slots) * (pl->P.n_q + 1)) &&
+                  copy_down(F.walk, T.walk, T.walk_total) && copy_down(F.nfull, T.nfull, GQ) &&
+                  copy_down(F.valid, T.valid, T.walk_total / 2) &&
+                  copy_down(F.q64_queue, T.q64_queue, 2 * int64_t(T.n_q64)) &&
+                  copy_down(F.q128_queue, T.q128_queue, 2 * int64_t(T.n_q128)) &&
+                  copy_down(F.unpadded, T.unpadded, GQ);
+  if (!ok) return fail(KPAGE_ERR_HIP, "copying the forward tables to the host failed");
   pl->fwd_on_host = true;
+  return KPAGE_OK;
 }
 
 void *plan_alloc(PlanT *pl, size_t bytes) {
@@ -290,17 +292,15 @@ kpage_status ensure_backward_on_host(PlanT *pl) {
   const DevBwdTables &T = pl->DB;
   BwdTables &B = pl->B;
   const int64_t G = pl->P.slots;
-  copy_down(B.owner_ptr, T.owner_ptr, G + 1);
-  copy_down(B.owners, T.owners, T.n_own * kOwnerSlots);
-  copy_down(B.aligned, T.aligned, T.n_own);
-  copy_down(B.revq_ptr, T.revq_ptr, T.n_own + 1);
-  copy_down(B.revq, T.revq, T.revq_total);
-  copy_down(B.qwalk_ptr, T.qwalk_ptr, T.n_own + 1);
-  copy_down(B.qwalk, T.qwalk, T.qwalk_total);
-  copy_down(B.adj, T.adj, T.qwalk_total / kOwnerSlots);
-  copy_down(B.bwd_queue, T.bwd_queue, 2 * T.n_items);
-  copy_down(B.uncovered_ptr, T.uncovered_ptr, G + 1);
-  copy_down(B.uncovered, T.uncovered, T.uncovered_total);
+  const bool ok = copy_down(B.owner_ptr, T.owner_ptr, G + 1) &&
+                  copy_down(B.owners, T.owners, T.n_own * kOwnerSlots) && copy_down(B.aligned, T.aligned, T.n_own) &&
+                  copy_down(B.revq_ptr, T.revq_ptr, T.n_own + 1) && copy_down(B.revq, T.revq, T.revq_total) &&
+                  copy_down(B.qwalk_ptr, T.qwalk_ptr, T.n_own + 1) && copy_down(B.qwalk, T.qwalk, T.qwalk_total) &&
+                  copy_down(B.adj, T.adj, T.qwalk_total / kOwnerSlots) &&
+                  copy_down(B.bwd_queue, T.bwd_queue, 2 * T.n_items) &&
+                  copy_down(B.uncovered_ptr, T.uncovered_ptr, G + 1) &&
+                  copy_down(B.uncovered, T.uncovered, T.uncovered_total);
+  if (!ok) return fail(KPAGE_ERR_HIP, "copying the backward tables to the host failed");
   B.built = true;
   return KPAGE_OK;
 }
@@ -576,23 +576,20 @@ kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, co
   const Problem &P = pl->P;
   const int64_t G = P.slots, nq = P.n_q, nk = P.n_kv;
   auto alloc = [pl](size_t bytes) { return plan_alloc(pl, bytes); };
-  auto own = [&](const void *src, size_t bytes, const char *what) -> void * {
+  auto own = [&](const void *src, size_t bytes) -> void * {  // plan-owned copy of a descriptor array
     void *d = alloc(bytes);
-    if (d && bytes) {
-      if (hipMemcpyAsync(d, src, bytes, hipMemcpyDeviceToDevice, st) != hipSuccess) return nullptr;
-    }
-    (void)what;
+    if (d && bytes && hipMemcpyAsync(d, src, bytes, hipMemcpyDeviceToDevice, st) != hipSuccess) return nullptr;
     return d;
   };
   DevProblem &D = pl->DP;
   D.batch = P.batch; D.heads = P.heads; D.n_q = P.n_q; D.n_kv = P.n_kv; D.slots = P.slots;
   D.seq_q = P.seq_q; D.seq_kv = P.seq_kv; D.per_head = P.per_head; D.nnz = q2k_nnz;
-  D.q_valid = static_cast<const int32_t *>(own(shell.q_valid, size_t(G * nq) * 4, "q_valid"));
-  D.kv_valid = static_cast<const int32_t *>(own(shell.kv_valid, size_t(G * nk) * 4, "kv_valid"));
-  D.q2k_ptr = static_cast<const int64_t *>(own(shell.q2k_ptr, size_t(G * (nq + 1)) * 8, "q2k_ptr"));
-  D.q2k_idx = static_cast<const int32_t *>(own(shell.q2k_idx, size_t(q2k_nnz) * 4, "q2k_idx"));
+  D.q_valid = static_cast<const int32_t *>(own(shell.q_valid, size_t(G * nq) * 4));
+  D.kv_valid = static_cast<const int32_t *>(own(shell.kv_valid, size_t(G * nk) * 4));
+  D.q2k_ptr = static_cast<const int64_t *>(own(shell.q2k_ptr, size_t(G * (nq + 1)) * 8));
+  D.q2k_idx = static_cast<const int32_t *>(own(shell.q2k_idx, size_t(q2k_nnz) * 4));
   if (shell.kv_offset) {
-    D.kv_offset = static_cast<const int64_t *>(own(shell.kv_offset, size_t(G * nk) * 8, "kv_offset"));
+    D.kv_offset = static_cast<const int64_t *>(own(shell.kv_offset, size_t(G * nk) * 8));
   } else {  // the plan keeps explicit offsets (host copies expect them)
     std::vector<int64_t> off(size_t(G * nk));
     for (int64_t i = 0; i < G * nk; ++i) off[size_t(i)] = int64_t(kBlockRows) * (i % nk);
@@ -751,7 +748,8 @@ kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf,
     const kpage_status s = ensure_backward_on_host(plan);
     if (s != KPAGE_OK) return s;
   } else {
-    ensure_forward_on_host(plan);
+    const kpage_status s = ensure_forward_on_host(plan);
+    if (s != KPAGE_OK) return s;
   }
   const void *src = nullptr;
   size_t n = 0;

@@ -198,8 +198,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_walks(DevProblem p, const
 }
 
 // walk, redirected page table and validity words of (slot, query block)
-__global__ void k_fill_walks(DevProblem p, const int32_t *route, const int32_t *nfull, const int64_t *walk_ptr,
-                             int32_t *walk, int32_t *pages, uint32_t *valid) {
+__global__ void k_fill_walks(DevProblem p, const int32_t *route, const int64_t *walk_ptr, int32_t *walk,
+                             int32_t *pages, uint32_t *valid) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= int64_t(p.slots) * p.n_q || route[i] == 0) return;
   const int g = int(i / p.n_q), q = int(i % p.n_q);
@@ -229,7 +229,6 @@ __global__ void k_fill_walks(DevProblem p, const int32_t *route, const int32_t *
     if (ck % kPageRows) emit(int32_t(kv_off(p, g, k) / kPageRows) + ck / kPageRows, tail_mask(ck));
   }
   while (pos < end) emit(-1, 0u);  // dummies (a walk that has any page starts with a real one)
-  (void)nfull;
 }
 
 // queue sort keys: (unpadded descending, bh * n_q + q ascending); other routes sort last
@@ -387,8 +386,8 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
     *err = "device allocation failed while planning";
     return KPAGE_ERR_OOM;
   }
-  hipLaunchKernelGGL(k_fill_walks, dim3(blocks_for(GQ, TB)), dim3(TB), 0, st, p, t->route, t->nfull, t->walk_ptr,
-                     t->walk, t->pages, t->valid);
+  hipLaunchKernelGGL(k_fill_walks, dim3(blocks_for(GQ, TB)), dim3(TB), 0, st, p, t->route, t->walk_ptr, t->walk,
+                     t->pages, t->valid);
   hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(n_redo, TB)), dim3(TB), 0, st, t->redo, int64_t(n_redo), 0);
   // queues: one radix sort per route over all (bh, q) keys
   unsigned long long *k64 = keys, *k128 = keys + BHQ, *ksorted = keys + 2 * BHQ;
