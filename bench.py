@@ -171,6 +171,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=WORKLOAD, choices=sorted(WORKLOADS),
                     help="configuration to time (default: the metric's 3D-padded fwd+bwd workload)")
+    ap.add_argument("--q-group", type=int, default=0, metavar="N",
+                    help="backward Q-group size in Q blocks (0: one group, the default)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the known-size kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -194,7 +196,7 @@ def main():
     w = make_workload(args.workload, with_do=True)
     d = w.head_dim
     t0 = time.perf_counter()
-    plan = K.kpage_plan(w)
+    plan = K.kpage_plan(w, q_group=args.q_group)
     plan_ms = (time.perf_counter() - t0) * 1e3
     q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
     o = torch.empty_like(q)
@@ -242,7 +244,7 @@ def main():
     ms_step = total_ms / args.steps
     pairs = stats["useful"]
     fwd_ms = sum(kern[n][0] for n in ("fwd_q128", "fwd_q64")) / args.steps
-    bwd_ms = sum(kern[n][0] for n in ("bwd_pre", "bwd_zero", "bwd_kv", "bwd_dq")) / args.steps
+    bwd_ms = sum(kern[n][0] for n in ("bwd_pre", "bwd_zero", "bwd_kv", "bwd_reduce", "bwd_dq")) / args.steps
     value = 14 * d * pairs / (ms_step * 1e-3) / 1e12
     fwd_tflops = 4 * d * pairs / (fwd_ms * 1e-3) / 1e12
 
@@ -273,7 +275,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": desc, "batch": 1, "heads": w.heads, "head_dim": d, "tokens": tokens,
+        "config": {"workload": desc + (f", backward Q groups of {args.q_group} blocks" if args.q_group else ""),
+                   "batch": 1, "heads": w.heads, "head_dim": d, "tokens": tokens,
                    "seq_physical": w.seq_q},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(fwd_ms, 4), "useful_tflops": round(fwd_tflops, 2),
