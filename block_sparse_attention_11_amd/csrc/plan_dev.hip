@@ -79,8 +79,10 @@ __global__ void k_check_kv(DevProblem p, int32_t *page_owner, Summary *sum) {
 }
 
 // per (slot, query block): validation, route, walk lengths and pair counts
+// `seen` (optional): one bit per K/V block for every (slot, query block), so the
+// duplicate check of a selection list is linear; without it the check is quadratic.
 __global__ void k_count(DevProblem p, int align64, int align128, int32_t *route, int32_t *nfull, int32_t *unpadded,
-                        int64_t *len, Summary *sum) {
+                        int64_t *len, Summary *sum, uint32_t *seen) {
   __shared__ unsigned long long st[5];
   __shared__ int cnt[3];
   if (threadIdx.x < 5) st[threadIdx.x] = 0;
@@ -103,6 +105,12 @@ __global__ void k_count(DevProblem p, int align64, int align128, int32_t *route,
       atomicOr(&sum->err, kErrPtr);
       ok = false;
     }
+    uint32_t *row = nullptr;
+    if (seen) {
+      const int nkw = (p.n_kv + 31) / 32;
+      row = seen + i * nkw;
+      for (int w = 0; w < nkw; ++w) row[w] = 0u;
+    }
     if (ok) {
       unsigned long long useful = 0, psum = 0;
       int tails = 0;
@@ -113,11 +121,20 @@ __global__ void k_count(DevProblem p, int align64, int align128, int32_t *route,
           ok = false;
           continue;
         }
-        for (int64_t e2 = a; e2 < e; ++e2)
-          if (p.q2k_idx[e2] == k) {
+        if (row) {  // this thread's own row: plain read-modify-write
+          const uint32_t bit = 1u << (k & 31);
+          if (row[k >> 5] & bit) {
             atomicOr(&sum->err, kErrDup);
             ok = false;
           }
+          row[k >> 5] |= bit;
+        } else {
+          for (int64_t e2 = a; e2 < e; ++e2)
+            if (p.q2k_idx[e2] == k) {
+              atomicOr(&sum->err, kErrDup);
+              ok = false;
+            }
+        }
         const int ck = min(max(p.kv_valid[int64_t(g) * p.n_kv + k], 0), kBlockRows);
         nf += ck / kPageRows;
         tails += (ck % kPageRows) ? 1 : 0;
@@ -348,8 +365,11 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
   hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(int64_t(p.slots) * n_pages, TB)), dim3(TB), 0, st, owner,
                      int64_t(p.slots) * n_pages, -1);
   hipLaunchKernelGGL(k_check_kv, dim3(blocks_for(GK, TB)), dim3(TB), 0, st, p, owner, d_sum);
+  // duplicate-check bitmap, when it fits in 256 MiB (else the quadratic check)
+  const int64_t seen_words = GQ * ((p.n_kv + 31) / 32);
+  uint32_t *seen = seen_words * 4 <= (int64_t(256) << 20) ? static_cast<uint32_t *>(alloc(size_t(seen_words) * 4)) : nullptr;
   hipLaunchKernelGGL(k_count, dim3(blocks_for(GQ, TB)), dim3(TB), 0, st, p, align64, align128, t->route, t->nfull,
-                     t->unpadded, len, d_sum);
+                     t->unpadded, len, d_sum, seen);
   hipLaunchKernelGGL(k_scan_walks, dim3(1), dim3(kScanThreads), 0, st, p, len, t->walk_ptr, d_sum);
   KP_CHECK(hipGetLastError());
   Summary h{};
