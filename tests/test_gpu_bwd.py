@@ -109,6 +109,11 @@ def test_bwd_vsa_topk_all_heads_one_checked():
     _run(make_workload(4, with_do=True), "21x45x80 top-87 all 40 heads", heads=[23])
 
 
+def test_bwd_independent_partitions_all_heads_one_checked():
+    """The SVG2-like workload at full size (40 heads, per-head partitions), one head checked."""
+    _run(make_workload(5, with_do=True), "SVG2-like partitions all 40 heads", heads=[17])
+
+
 @pytest.mark.parametrize("name", list(EDGE_CASES))
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_edge_cases(name, d):

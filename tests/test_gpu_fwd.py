@@ -114,6 +114,16 @@ def test_fwd_3d_padded_full_heads_sampled():
     _sampled(make_workload(3), "21x30x52 all 40 heads", per_head=6)
 
 
+def test_fwd_vsa_topk_full_heads_sampled():
+    """The 21x45x80 top-87 workload at full size (40 heads, per-head graphs), as the benchmark launches it."""
+    _sampled(make_workload(4), "21x45x80 top-87 all 40 heads", per_head=4)
+
+
+def test_fwd_independent_partitions_full_heads_sampled():
+    """The SVG2-like workload at full size (40 heads, per-head partitions), as the benchmark launches it."""
+    _sampled(make_workload(5), "SVG2-like partitions all 40 heads", per_head=4)
+
+
 def test_fwd_padding_free_full_heads_sampled():
     _sampled(make_workload(2), "16x32x32 all 24 heads", per_head=8)
 
