@@ -94,9 +94,14 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
   constexpr int TILE = 64 * D * 2;        // one half-step tile (4 pages) of Q or dO
   constexpr int STATS = kKvWaves * 256;   // per half-step: 64 floats per page (lse2, delta, spare)
 
-  // half-step buffers [Q 0][dO 0][Q 1][dO 1] (every offset fits a ds_read immediate)
+  // half-step buffers [Q 0][dO 0][Q 1][dO 1] (every offset fits a ds_read immediate).
+  // The two stats buffers are separate objects: their direct-to-LDS writes use a
+  // per-wave offset, and only distinct objects let the compiler see that the copy
+  // into one buffer does not alias the reads of the other (else it waits for the
+  // copy to land before the half-step's first LDS read).
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
-  __shared__ __attribute__((aligned(256))) char stats[2 * STATS];
+  __shared__ __attribute__((aligned(256))) char stats0[STATS];
+  __shared__ __attribute__((aligned(256))) char stats1[STATS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,16 +130,18 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
 
   // half-step u (pages 4 (u & 1) .. + 3 of step u / 2): one Q and one dO page per wave,
   // and the page's lse2 and delta
-  auto load_half = [&](int32_t page, int buf) __attribute__((always_inline)) {
+  auto load_half = [&](int32_t page, auto buf_c) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
     lds_char *qt = (lds_char *)smem + (2 * buf) * TILE;
     lds_char *gt = (lds_char *)smem + (2 * buf + 1) * TILE;
+    char *stats = buf == 0 ? stats0 : stats1;
     load_page<D, kSwzBoth>(qgl, page, qt, 16 * wave, lane);
     load_page<D, kSwzBoth>(ggl, page, gt, 16 * wave, lane);
     // lanes 0-15: lse2 of the page's rows, 16-31: delta, 32-63: the same again
     // (delta = lse2 + rows: one scalar base and a 32-bit lane offset)
     const char *src = (const char *)(l2h + (int64_t)page * 16);
     const uint32_t off = (uint32_t)xor_imm<0x40000000>(stat_off) ^ 0x40000000u;  // recomputed, not kept
-    __builtin_amdgcn_global_load_lds((const void *)(src + off), (lds_char *)(stats + buf * STATS + wave * 256), 4, 0, 0);
+    lds_dma<4>(src, off, (lds_char *)(stats + wave * 256));
   };
 
   // this wave's 32 key rows as MFMA B operands (k = head dim, n = key).  Empty owner
@@ -151,7 +158,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
       vreg[s] = vr[2 * s + g];
     }
   }
-  if (n_half > 0) load_half(qpages[wave], 0);
+  if (n_half > 0) load_half(qpages[wave], ic<0>{});
 
   f32x16 dk[ND], dv[ND];
 #pragma unroll
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
     constexpr int BUF = decltype(buf_c)::value;
     const lds_char *qt = (const lds_char *)smem + (2 * BUF) * TILE;
     const lds_char *gt = (const lds_char *)smem + (2 * BUF + 1) * TILE;
-    const lds_char *stb = (const lds_char *)stats + BUF * STATS;
+    const lds_char *stb = (const lds_char *)(BUF == 0 ? stats0 : stats1);
     // Pair mask.  Query rows without a valid key (invalid rows included) have
     // lse2 = +inf, so their P is 0 by itself.  Key validity needs no mask here: the P
     // and dS of an invalid key reach only that key's own dK / dV rows, which are
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
     wait_lgkm0();
     wait_vmcnt<0>();
     barrier();  // half-step u resident for every wave; nobody reads buffer 1 - BUF any more
-    if (u + 1 < n_half) load_half(pn, 1 - BUF);
+    if (u + 1 < n_half) load_half(pn, ic<1 - BUF>{});
     half_step(buf_c, u, adj);
   };
   for_range(ic<0>{}, 0, n_half, iter);

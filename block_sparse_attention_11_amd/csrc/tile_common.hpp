@@ -104,6 +104,27 @@ __device__ __forceinline__ int xor_imm(int x) {
   }
 }
 
+// Direct-to-LDS copy of SIZE (4 or 16) bytes per lane from sbase + voff to the LDS
+// address `lds` + lane * SIZE (sbase and lds wave-uniform), written as inline assembly.
+// The compiler's own waits for such copies cannot tell which LDS buffer a copy writes,
+// so with the builtin it holds the first LDS read issued after a copy until that copy
+// has landed, even when the read is of the other buffer of a double-buffered pair: the
+// prefetch of the next step would then serialise with the current one.  Every caller
+// orders copies and reads itself: wait_vmcnt, then a workgroup barrier, before a buffer
+// written by copies is read.  M0 (the copy's LDS base) is written here; the kernels
+// that use these copies issue no other instruction that reads M0.
+template <int SIZE>
+__device__ __forceinline__ void lds_dma(const char *sbase, uint32_t voff, lds_char *lds) {
+  static_assert(SIZE == 4 || SIZE == 16, "direct-to-LDS copies of 4 or 16 bytes per lane");
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds;
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" : : "s"(m0), "v"(voff), "s"(sbase)
+                 : "memory");
+}
+
 template <int SWZ, int CH>
 constexpr bool swizzle_flip_is_uniform(int base, int n, int flip) {
   for (int r = 0; r < n; ++r)
@@ -135,8 +156,7 @@ __device__ __forceinline__ void load_page(const char *src, int32_t page, lds_cha
     const char *pi = pbase + I * ROWS_PER_INST * D * 2;
     asm volatile("" : "+s"(pi));  // keep the base scalar: saddr + 32-bit lane offset
     const uint32_t off = (uint32_t)xor_imm<16 * FLIP>(off0);
-    __builtin_amdgcn_global_load_lds((const void *)(pi + off), (lds_char *)(tile + (r0 + I * ROWS_PER_INST) * D * 2),
-                                     16, 0, 0);
+    lds_dma<16>(pi, off, (lds_char *)(tile + (r0 + I * ROWS_PER_INST) * D * 2));
   });
 }
 
