@@ -94,14 +94,9 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
   constexpr int TILE = 64 * D * 2;        // one half-step tile (4 pages) of Q or dO
   constexpr int STATS = kKvWaves * 256;   // per half-step: 64 floats per page (lse2, delta, spare)
 
-  // half-step buffers [Q 0][dO 0][Q 1][dO 1] (every offset fits a ds_read immediate).
-  // The two stats buffers are separate objects: their direct-to-LDS writes use a
-  // per-wave offset, and only distinct objects let the compiler see that the copy
-  // into one buffer does not alias the reads of the other (else it waits for the
-  // copy to land before the half-step's first LDS read).
+  // half-step buffers [Q 0][dO 0][Q 1][dO 1] (every offset fits a ds_read immediate)
   __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];
-  __shared__ __attribute__((aligned(256))) char stats0[STATS];
-  __shared__ __attribute__((aligned(256))) char stats1[STATS];
+  __shared__ __attribute__((aligned(256))) char stats[2 * STATS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,14 +129,13 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
     constexpr int buf = decltype(buf_c)::value;
     lds_char *qt = (lds_char *)smem + (2 * buf) * TILE;
     lds_char *gt = (lds_char *)smem + (2 * buf + 1) * TILE;
-    char *stats = buf == 0 ? stats0 : stats1;
     load_page<D, kSwzBoth>(qgl, page, qt, 16 * wave, lane);
     load_page<D, kSwzBoth>(ggl, page, gt, 16 * wave, lane);
     // lanes 0-15: lse2 of the page's rows, 16-31: delta, 32-63: the same again
     // (delta = lse2 + rows: one scalar base and a 32-bit lane offset)
     const char *src = (const char *)(l2h + (int64_t)page * 16);
     const uint32_t off = (uint32_t)xor_imm<0x40000000>(stat_off) ^ 0x40000000u;  // recomputed, not kept
-    lds_dma<4>(src, off, (lds_char *)(stats + wave * 256));
+    lds_dma<4>(src, off, (lds_char *)(stats + buf * STATS + wave * 256));
   };
 
   // this wave's 32 key rows as MFMA B operands (k = head dim, n = key).  Empty owner
@@ -182,7 +176,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
     constexpr int BUF = decltype(buf_c)::value;
     const lds_char *qt = (const lds_char *)smem + (2 * BUF) * TILE;
     const lds_char *gt = (const lds_char *)smem + (2 * BUF + 1) * TILE;
-    const lds_char *stb = (const lds_char *)(BUF == 0 ? stats0 : stats1);
+    const lds_char *stb = (const lds_char *)stats + BUF * STATS;
     // Pair mask.  Query rows without a valid key (invalid rows included) have
     // lse2 = +inf, so their P is 0 by itself.  Key validity needs no mask here: the P
     // and dS of an invalid key reach only that key's own dK / dV rows, which are
