@@ -186,7 +186,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by head with no exchange, and multi-GPU runs are not part of this build.",
+              "the attention shards by head with no exchange between GPUs, and this benchmark times one GPU's share.",
               file=sys.stderr)
         sys.exit(2)
 
