@@ -33,3 +33,61 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(K, "_lib_handle", None)
     with pytest.raises(K.KpageError):
         K.lib()
+
+
+def _layout(**kw):
+    base = dict(batch=1, heads=2, head_dim=128, n_q_blocks=4, n_kv_blocks=6, seq_q=512, seq_kv=768,
+                q_valid=0x1000, kv_valid=0x2000, kv_offset=0)
+    base.update(kw)
+    return K.KpageSelectLayout(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), K.KPAGE_ERR_UNSUPPORTED),
+    (dict(n_kv_blocks=5000), K.KPAGE_ERR_UNSUPPORTED),
+    (dict(seq_q=500), K.KPAGE_ERR_INVALID),
+    (dict(n_q_blocks=0, seq_q=0), K.KPAGE_ERR_INVALID),
+    (dict(q_valid=0), K.KPAGE_ERR_INVALID),
+    (dict(batch=300, heads=300), K.KPAGE_ERR_UNSUPPORTED),
+])
+def test_select_layout_checks_run_before_any_device_work(kw, status):
+    """Argument checks of the selection entry points (host only: no device pointer is touched)."""
+    n = ctypes.c_size_t(0)
+    assert K.lib().kpage_select_workspace_size(ctypes.byref(_layout(**kw)), ctypes.byref(n)) == status
+    assert K.lib().kpage_select_topk(ctypes.byref(_layout(**kw)), 0x3000, 0x4000, 8, 0x5000, 0x6000, 0x7000,
+                                     1 << 30, None) == status
+
+
+def test_select_topk_argument_checks():
+    lay = _layout()
+    n = ctypes.c_size_t(0)
+    assert K.lib().kpage_select_workspace_size(ctypes.byref(lay), ctypes.byref(n)) == K.KPAGE_OK and n.value > 0
+    # top_k < 1, workspace too small, misaligned workspace: rejected before any launch
+    assert K.lib().kpage_select_topk(ctypes.byref(lay), 0x3000, 0x4000, 0, 0x5000, 0x6000, 0x7000, n.value,
+                                     None) == K.KPAGE_ERR_INVALID
+    assert K.lib().kpage_select_topk(ctypes.byref(lay), 0x3000, 0x4000, 8, 0x5000, 0x6000, 0x7000, n.value - 1,
+                                     None) == K.KPAGE_ERR_INVALID
+    assert K.lib().kpage_select_topk(ctypes.byref(lay), 0x3000, 0x4000, 8, 0x5000, 0x6000, 0x7010, n.value,
+                                     None) == K.KPAGE_ERR_INVALID
+
+
+def _clusters(**kw):
+    base = dict(batch=1, heads=2, head_dim=64, n_q_clusters=5, n_kv_clusters=9, n_q_blocks=8, n_kv_blocks=14,
+                q_centroids=0x1000, kv_centroids=0x2000, q_cluster_size=0x3000, kv_cluster_size=0x4000,
+                q_block_cluster=0x5000, kv_block_cluster=0x6000)
+    base.update(kw)
+    return K.KpageSelectClusters(**base)
+
+
+@pytest.mark.parametrize("kw,top_p,scale,status", [
+    (dict(), 0.0, 0.25, K.KPAGE_ERR_INVALID),
+    (dict(), 1.5, 0.25, K.KPAGE_ERR_INVALID),
+    (dict(), 0.9, 0.0, K.KPAGE_ERR_INVALID),
+    (dict(n_kv_clusters=5000), 0.9, 0.25, K.KPAGE_ERR_UNSUPPORTED),
+    (dict(head_dim=80), 0.9, 0.25, K.KPAGE_ERR_UNSUPPORTED),
+    (dict(kv_block_cluster=0), 0.9, 0.25, K.KPAGE_ERR_INVALID),
+])
+def test_select_top_p_argument_checks(kw, top_p, scale, status):
+    c = _clusters(**kw)
+    assert K.lib().kpage_select_top_p(ctypes.byref(c), top_p, scale, 0x7000, 0x8000, 0x9000, 1 << 40, None) == status
+    assert K.kpage_last_error()
