@@ -176,3 +176,39 @@ def test_device_plan_full_size(cfg):
     assert sh == sd, (cfg, sh, sd)
     _say(f"  workload {cfg}: forward plan host {hf * 1e3:.2f} ms, device {df * 1e3:.2f} ms; "
          f"backward tables host {hb * 1e3:.2f} ms, device {db * 1e3:.2f} ms")
+
+
+def test_device_plan_random_layouts():
+    """Random small layouts (sizes 0..128 with tails, shuffled offsets with gaps, empty rows,
+    shared and per-head graphs, both alignments): every table equal to the host plan's."""
+    from tests.problems import Problem
+    rng = np.random.default_rng(23)
+    sizes = [0, 1, 2, 15, 16, 17, 31, 48, 63, 64, 65, 100, 112, 113, 127, 128]
+    for trial in range(30):
+        G = int(rng.integers(1, 4))
+        n_q, n_kv = int(rng.integers(1, 12)), int(rng.integers(1, 12))
+        qv = rng.choice(sizes, size=(G, n_q)).astype(np.int32)
+        kv = rng.choice(sizes, size=(G, n_kv)).astype(np.int32)
+        off = np.zeros((G, n_kv), dtype=np.int64)
+        seq_kv = 16
+        for g in range(G):
+            acc = 0
+            for k in rng.permutation(n_kv):
+                off[g, k] = acc
+                acc += 16 * ((int(kv[g, k]) + 15) // 16) + 16 * int(rng.integers(0, 2))
+            seq_kv = max(seq_kv, acc)
+        ptr = np.zeros((G, n_q + 1), dtype=np.int64)
+        idx = []
+        for g in range(G):
+            for q in range(n_q):
+                row = rng.permutation(n_kv)[:int(rng.integers(0, n_kv + 1))].tolist()
+                idx.extend(row)
+                ptr[g, q + 1] = len(idx)
+            if g + 1 < G:
+                ptr[g + 1, 0] = len(idx)
+        per_head = G > 1
+        p = Problem(batch=1, heads=G if per_head else int(rng.integers(1, 3)), head_dim=64, n_q=n_q, n_kv=n_kv,
+                    seq_q=128 * n_q, seq_kv=seq_kv, per_head=per_head, q_valid=qv, kv_valid=kv, kv_offset=off,
+                    q2k_ptr=ptr, q2k_idx=np.asarray(idx, dtype=np.int32))
+        align = [(0, 0), (32, 16)][trial % 2]
+        same_plans(p, f"random layout {trial}", align_q64=align[0], align_q128=align[1])
