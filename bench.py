@@ -167,6 +167,51 @@ def _copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "reads": n, "writes": n}), flush=True)
 
 
+def _dense_reference():
+    """Context for the roofline fraction: what this GPU sustains on dense bf16 MFMA work
+    with random data, through the vendor libraries behind PyTorch (hipBLASLt GEMMs and
+    the flash-attention backend of scaled_dot_product_attention, forced so that no math
+    fallback runs).  The kernels of this package are not involved."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    def timed(fn, iters, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    torch.manual_seed(0)
+    out = {"peak_bf16_tflops": PEAK_BF16_TFLOPS}
+    for n in (8192, 16384):
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        ms = timed(lambda: torch.matmul(a, b), 20, 5)
+        out[f"gemm_bf16_{n}^3"] = {"ms": round(ms, 4), "tflops": round(2 * n ** 3 / ms / 1e9, 1)}
+        del a, b
+    h, s, d = 40, 16384, 128
+    q, k, v, do = (torch.randn(1, h, s, d, device="cuda", dtype=torch.bfloat16) for _ in range(4))
+    with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+        ms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v), 10, 3)
+        out["flash_attention_fwd"] = {"shape": [1, h, s, d], "ms": round(ms, 4),
+                                      "tflops": round(4 * s * s * d * h / ms / 1e9, 1)}
+        qg, kg, vg = (t.clone().requires_grad_(True) for t in (q, k, v))
+
+        def fwd_bwd():
+            torch.nn.functional.scaled_dot_product_attention(qg, kg, vg).backward(do)
+
+        ms = timed(fwd_bwd, 5, 2)
+        out["flash_attention_fwd_bwd"] = {"shape": [1, h, s, d], "ms": round(ms, 4),
+                                          "tflops": round(14 * s * s * d * h / ms / 1e9, 1)}
+    print(json.dumps({"dense_reference": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,9 +225,15 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the known-size kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="only time dense bf16 GEMMs and dense flash attention through PyTorch's vendor "
+                         "libraries (what this GPU sustains on dense MFMA work) and exit")
     args = ap.parse_args()
     if args.copy_calibration:
         _copy_calibration(args.copy_calibration)
+        return
+    if args.dense_reference:
+        _dense_reference()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
