@@ -403,6 +403,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a, cons
   // this wave's 32 query rows: Q and dO as MFMA B operands, lse2 and delta per lane
   const int64_t qrow = bh * a.seq_q + 128 * it.q + 32 * qg + l32;
   const bool qok = 32 * qg + l32 < cq;
+  const bool idle = 32 * qg >= cq;  // wave-uniform: no valid row in this query group
   bf16x8 qreg[DS], greg[DS];
   {
     const bf16x8 *qp = (const bf16x8 *)((const char *)a.q + qrow * D * 2);
@@ -530,7 +531,9 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a, cons
     barrier();  // half-tile u resident; buffer 1 - BUF free
     if (u + 1 < n_half) load_half(pnext, 1 - BUF);
     const bool masked = u >= full_half;
-    static_for<NH>([&](auto h_c) __attribute__((always_inline)) { sub_tile(buf_c, h_c, u, masked); });
+    // a query group without valid rows computes nothing (its dQ rows are written as 0);
+    // the wave still copies its pages and meets every barrier
+    if (!idle) static_for<NH>([&](auto h_c) __attribute__((always_inline)) { sub_tile(buf_c, h_c, u, masked); });
   };
   for_range(ic<0>{}, 0, n_half, iter);
 

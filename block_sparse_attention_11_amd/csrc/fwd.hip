@@ -100,6 +100,10 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
   const int full_tiles = it.n_full / kTilePages;  // tiles inside the fully valid prefix
   const int qg = wave % NQG;
   const int keyoff = (wave / NQG) * KW;  // first key of this wave in a tile
+  // a query group without valid rows (c_q <= 32 qg) computes nothing: the wave still
+  // copies its pages and meets every barrier (none sits inside the compute below),
+  // and its rows are written as O = 0, LSE = -inf like every row past c_q
+  const bool idle = 32 * qg >= cq;
 
   const char *kh = (const char *)args.k + (int64_t)bh * args.seq_kv * D * 2;
   const char *vh = (const char *)args.v + (int64_t)bh * args.seq_kv * D * 2;
@@ -156,6 +160,7 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
   // S^T of one sub-tile (32 keys x 32 queries) from the K tile in `kt`
   auto qk = [&](const lds_char *kt, int half, f32x16 &acc) __attribute__((always_inline)) {
     acc = f32x16{};
+    if (idle) return;
     const lds_char *base = kt + k_row_off + half * 32 * D * 2;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
@@ -165,6 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
   };
   // O^T += V^T P^T for one sub-tile from the V tile in `vt`
   auto pv = [&](const lds_char *vt, int half, const bf16x8 *p) __attribute__((always_inline)) {
+    if (idle) return;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const lds_char *vrow = vt + v_row_off + (32 * half + 16 * hh) * D * 2;
@@ -308,6 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
     constexpr bool HAS_PV = decltype(has_pv)::value;
     constexpr int P = decltype(par)::value;
     constexpr int MASK = decltype(masking)::value;
+    if (idle) return;
     rescale();
     if (MASK == kMaskAlways || (MASK == kMaskCheck && i / NH >= full_tiles)) mask(i, sacc[P]);
     __builtin_amdgcn_sched_barrier(0);
