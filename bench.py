@@ -43,6 +43,22 @@ WORKLOADS = {
 }
 
 
+def _device_plan_ms(K, problem, reps=3):
+    """Host wall time of kpage_plan_device on a selected graph, synchronised: one untimed
+    call first (first-use allocations), then the median of `reps` calls."""
+    import torch
+    K.kpage_plan_device(problem).close()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        plan = K.kpage_plan_device(problem)
+        torch.cuda.synchronize()
+        times.append((time.perf_counter() - t0) * 1e3)
+        plan.close()
+    return sorted(times)[len(times) // 2]
+
+
 def _prelude(K, w, q, k, top_k=87, reps=5):
     """GPU block selection (mean pooling + top-k) on the workload's own layout, then the GPU
     planner on its graph: the selector and planner a dynamic-sparsity step would run before
@@ -62,17 +78,13 @@ def _prelude(K, w, q, k, top_k=87, reps=5):
     e1.record()
     torch.cuda.synchronize()
     sel_ms = e0.elapsed_time(e1) / reps
-    t0 = time.perf_counter()
-    plan = K.kpage_plan_device(K.SelectedProblem(q, k, qv, kvv, ko, ptr, idx))
-    torch.cuda.synchronize()
-    plan_ms = (time.perf_counter() - t0) * 1e3
-    plan.close()
+    plan_ms = _device_plan_ms(K, K.SelectedProblem(q, k, qv, kvv, ko, ptr, idx))
     BH = w.batch * w.heads
     rows_q, rows_k = int(w.q_valid[0].sum()), int(w.kv_valid[0].sum())
     # algorithmic bytes: the valid rows of Q and K read once, the graph written once
     nbytes = BH * (rows_q + rows_k) * w.head_dim * 2 + BH * (w.n_q * top_k * 4 + (w.n_q + 1) * 8)
     gbs = nbytes / (sel_ms * 1e-3) / 1e9
-    return {"select_ms": round(sel_ms, 4), "plan_device_ms_incl_sync": round(plan_ms, 2), "top_k": top_k,
+    return {"select_ms": round(sel_ms, 4), "plan_device_ms_median_incl_sync": round(plan_ms, 2), "top_k": top_k,
             "roofline": {"kernel": "kpage_select_topk (all kernels of one call)", "bound": "hbm",
                          "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(gbs / 8000.0, 4),
                          "algorithmic": "Q and K valid rows read once + CSR graph written"}}
@@ -102,12 +114,8 @@ def _prelude_top_p(K, w, top_p=0.9, reps=5):
               "kv_offset"):
         setattr(p, a, getattr(w, a))
     p.q2k_ptr, p.q2k_idx = ptr, idx
-    t0 = time.perf_counter()
-    plan = K.kpage_plan_device(p)
-    torch.cuda.synchronize()
-    plan_ms = (time.perf_counter() - t0) * 1e3
-    plan.close()
-    return {"select_top_p_ms": round(sel_ms, 4), "plan_device_ms_incl_sync": round(plan_ms, 2), "top_p": top_p,
+    plan_ms = _device_plan_ms(K, p)
+    return {"select_top_p_ms": round(sel_ms, 4), "plan_device_ms_median_incl_sync": round(plan_ms, 2), "top_p": top_p,
             "clusters": [int(args[0].shape[1]), int(args[1].shape[1])]}
 
 
@@ -139,15 +147,18 @@ def _cpu_baseline(workload, heads):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bwd_3d_padded_h40.json")
 
 
-def _measured_traffic(kernel):
+def _measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE counter
-    summary (already scaled by the copy calibration), or None when the kernel's sources
-    changed since the counters were taken."""
+    summary (already scaled by the copy calibration), or None when the counters were taken
+    on another workload or the kernel's sources changed since they were taken."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)["kernels"][kernel]
-    except (OSError, KeyError, ValueError):
+            full = json.load(f)
+        rec = full["kernels"][kernel]
+        if int(full["workload_id"]) != workload:
+            return None
+    except (OSError, KeyError, ValueError, TypeError):
         return None
     h = hashlib.sha256()
     for name in rec["sources"]:
@@ -314,7 +325,7 @@ def main():
     achieved = per_pair * d * pairs / (dom_avg * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": _measured_traffic(dom), "traffic_unit": "HBM bytes per launch (counters)", "avg_ms": round(dom_avg, 4), "launches": dom_n,
+                "traffic": _measured_traffic(dom, args.workload), "traffic_unit": "HBM bytes per launch (counters)", "avg_ms": round(dom_avg, 4), "launches": dom_n,
                 "algorithmic": f"{per_pair}*d*useful_pairs per launch"}
 
     out = {
