@@ -309,7 +309,7 @@ def main():
     K.kpage_timing_enable(plan, False)
     ms_step = total_ms / args.steps
     pairs = stats["useful"]
-    fwd_ms = sum(kern[n][0] for n in ("fwd_q128", "fwd_q64")) / args.steps
+    fwd_ms = sum(kern[n][0] for n in ("fwd", "fwd_exact")) / args.steps
     bwd_ms = sum(kern[n][0] for n in ("bwd_pre", "bwd_zero", "bwd_kv", "bwd_reduce", "bwd_dq")) / args.steps
     value = 14 * d * pairs / (ms_step * 1e-3) / 1e12
     fwd_tflops = 4 * d * pairs / (fwd_ms * 1e-3) / 1e12
@@ -318,7 +318,7 @@ def main():
     # K/V-owned pass 4 GEMMs (S, dP, dV, dK) = 8 d; Q-owned dQ pass 3 GEMMs (S, dP, dQ) = 6 d;
     # forward (both routes) 2 GEMMs = 4 d
     cands = {"kpage_bwd_kv": (8, kern["bwd_kv"]), "kpage_bwd_dq": (6, kern["bwd_dq"]),
-             "kpage_fwd": (4, (sum(kern[n][0] for n in ("fwd_q128", "fwd_q64")), kern["fwd_q128"][1]))}
+             "kpage_fwd": (4, (sum(kern[n][0] for n in ("fwd", "fwd_exact")), kern["fwd"][1]))}
     dom = max(cands, key=lambda n: cands[n][1][0])
     per_pair, (dom_ms, dom_n) = cands[dom]
     dom_avg = dom_ms / max(dom_n, 1)

@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "kpage_select_top_p",
 )
 
-KERNELS = {"fwd_q128": 0, "fwd_q64": 1, "bwd_pre": 2, "bwd_zero": 3, "bwd_kv": 4, "bwd_dq": 5, "bwd_reduce": 6}
+KERNELS = {"fwd": 0, "fwd_exact": 1, "bwd_pre": 2, "bwd_zero": 3, "bwd_kv": 4, "bwd_dq": 5, "bwd_reduce": 6}
 
 
 class KpageError(RuntimeError):

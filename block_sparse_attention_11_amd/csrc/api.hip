@@ -94,7 +94,7 @@ struct kpage_plan {
   int n_items128 = 0, n_items64 = 0;
   int32_t *d_pages = nullptr;
   uint32_t *d_valid = nullptr;
-  int32_t *d_redo = nullptr;  // per launch position of either route: item needs the exact pass
+  int32_t *d_redo = nullptr;  // per workgroup of the forward launch (both routes): item needs the exact pass
   // backward device tables
   BwdItem *d_bitems = nullptr;
   int n_bitems = 0;
@@ -213,8 +213,8 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   if ((s = upload(pl, F.valid, &pl->d_valid, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, it128, &pl->d_items128, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, it64, &pl->d_items64, stream)) != KPAGE_OK) return s;
-  // the routes run one after the other on the stream, so they share one flag array
-  if ((s = upload(pl, std::vector<int32_t>(std::max(it128.size(), it64.size()), 0), &pl->d_redo, stream)) != KPAGE_OK)
+  // one exact-pass flag per workgroup of the forward launch (both routes)
+  if ((s = upload(pl, std::vector<int32_t>(std::max<size_t>(it128.size() + it64.size(), 1), 0), &pl->d_redo, stream)) != KPAGE_OK)
     return s;
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -646,14 +646,13 @@ kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, co
   a.seq_kv = plan->P.seq_kv;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  FwdArgs a64 = a;
   a.items = plan->d_items128;
   a.n_items = plan->n_items128;
-  hipError_t e = launch_fwd(a, plan->P.head_dim, 128, st, plan->timer);
-  if (e != hipSuccess) return hip_fail(e, "forward launch (M128 route)");
-  a.items = plan->d_items64;
-  a.n_items = plan->n_items64;
-  e = launch_fwd(a, plan->P.head_dim, 64, st, plan->timer);
-  if (e != hipSuccess) return hip_fail(e, "forward launch (M64 route)");
+  a64.items = plan->d_items64;
+  a64.n_items = plan->n_items64;
+  const hipError_t e = launch_fwd(a, a64, plan->P.head_dim, st, plan->timer);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
   return KPAGE_OK;
 }
 

@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
 constexpr int kDqWaves = 4;
 
 template <int D, int ROUTE>
-__global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a, const FwdItem *items) {
+__device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, int item, char *smem) {
   constexpr int DS = D / 16;
   constexpr int ND = D / 32;
   constexpr int M = ROUTE;
@@ -376,8 +376,6 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a, cons
   constexpr int PART_BYTES = 32 * D * 4;
   static_assert(kDqWaves * PART_BYTES <= 4 * HTILE, "dQ partials reuse the tile buffers");
 
-  // K half-tiles 0/1, V half-tiles 0/1; at the end the per-wave dQ partials
-  __shared__ __attribute__((aligned(1024))) char smem[4 * HTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -387,7 +385,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a, cons
   const int sl = lane & 15;
   const int mgrp = lane >> 4;
 
-  const FwdItem it = items[blockIdx.x];
+  const FwdItem it = items[item];
   const int64_t bh = it.bh;
   const int cq = it.c_q;
   const int n_half = it.walk_len / 4;
@@ -622,6 +620,18 @@ __global__ __launch_bounds__(256) void kpage_bwd_kv_reduce(BwdArgs a) {
   }
 }
 
+// dQ over both routes in one launch: workgroups [0, n128) take the M128 items, the rest
+// the M64 items (and cleanup items), so the shorter M64 items fill the end of the M128
+// work.  K half-tiles 0/1 and V half-tiles 0/1 in LDS; at the end the per-wave dQ
+// partials.
+template <int D>
+__global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * 64 * D * 2];
+  const int b = blockIdx.x;
+  if (b < a.n_fitems128) dq_item<D, 128>(a, a.fitems128, b, smem);
+  else dq_item<D, 64>(a, a.fitems64, b - a.n_fitems128, smem);
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
   const int64_t rows = (int64_t)a.bh_count * a.seq_q;
@@ -645,12 +655,11 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
     hipLaunchKernelGGL(kpage_bwd_kv_reduce<D>, dim3(a.n_reduce), dim3(256), 0, stream, a);
     if (t) t->after(6, stream);
   }
-  if (t) t->before(5, stream);
-  if (a.n_fitems128 > 0)
-    hipLaunchKernelGGL((kpage_bwd_dq<D, 128>), dim3(a.n_fitems128), dim3(64 * kDqWaves), 0, stream, a, a.fitems128);
-  if (a.n_fitems64 > 0)
-    hipLaunchKernelGGL((kpage_bwd_dq<D, 64>), dim3(a.n_fitems64), dim3(64 * kDqWaves), 0, stream, a, a.fitems64);
-  if (t) t->after(5, stream);
+  if (a.n_fitems128 + a.n_fitems64 > 0) {
+    if (t) t->before(5, stream);
+    hipLaunchKernelGGL(kpage_bwd_dq<D>, dim3(a.n_fitems128 + a.n_fitems64), dim3(64 * kDqWaves), 0, stream, a);
+    if (t) t->after(5, stream);
+  }
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ struct FwdArgs {
   const int32_t *pages;     // walk entries; dummy slots point at a real page of the same walk
   const uint32_t *valid;    // two 16-bit row masks per word, indexed by walk position / 2
   int64_t seq_q, seq_kv;
-  int32_t *redo;            // per launch position: 1 when the item needs the exact rescaling pass
+  int32_t *redo;            // per workgroup of the launch: 1 when its item needs the exact rescaling pass
   int32_t n_items;
   float scale;              // softmax scale
   float scale_log2;         // softmax scale * log2(e)
@@ -84,7 +84,9 @@ struct LaunchTimer {
   virtual ~LaunchTimer() = default;
 };
 
-hipError_t launch_fwd(const FwdArgs &a, int head_dim, int route, hipStream_t stream, LaunchTimer *timer);
+// Forward over both routes in one launch (M128 items first, then M64 items), then the
+// exact re-run launch; timer ids 0 and 1.  The redo flags hold n128 + n64 entries.
+hipError_t launch_fwd(const FwdArgs &a128, const FwdArgs &a64, int head_dim, hipStream_t stream, LaunchTimer *timer);
 hipError_t launch_bwd(const BwdArgs &a, int head_dim, hipStream_t stream, LaunchTimer *timer);
 
 }  // namespace kpage

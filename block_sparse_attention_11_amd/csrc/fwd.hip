@@ -64,8 +64,20 @@ __device__ __forceinline__ int32_t fwd_page(c_i32 *walk, int t, int j) { return 
 // MASK values of a sub-iteration: no masking, a runtime check, or masking always.
 constexpr int kMaskNone = 0, kMaskCheck = 1, kMaskAlways = 2;
 
+// LDS of one workgroup, the same for both routes: K tiles 0/1, then V tiles 0/1 (at the
+// end the per-wave partial outputs), and the per-wave row statistics of the merge.
+template <int D>
+struct FwdLds {
+  __attribute__((aligned(1024))) char tiles[4 * 16 * kTilePages * D * 2];
+  float stat_m[kWaves][32];
+  float stat_l[kWaves][32];
+  int redo_any;
+};
+
+// One work item of route ROUTE: `item` indexes the route's item array, `slot` is the
+// workgroup's position in the launch (its entry of the redo flags).
 template <int D, int ROUTE, bool EXACT>
-__global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
+__device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, int slot, FwdLds<D> &lds) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int DS = D / 16;         // MFMA k-steps over the head dimension
   constexpr int ND = D / 32;         // 32-wide output blocks over the head dimension
@@ -77,13 +89,13 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
   constexpr int TILE_BYTES = 16 * kTilePages * D * 2;
   constexpr int LOADS = 16 * CH / 64;  // direct loads per wave per tile and tensor
 
-  // K tiles 0/1, then V tiles 0/1; at the end the per-wave partial outputs
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];
-  __shared__ float stat_m[kWaves][32];
-  __shared__ float stat_l[kWaves][32];
-  __shared__ int redo_any;
+  static_assert(sizeof(FwdLds<D>::tiles) == 4 * TILE_BYTES, "two K and two V tiles");
+  char *smem = lds.tiles;
+  float(&stat_m)[kWaves][32] = lds.stat_m;
+  float(&stat_l)[kWaves][32] = lds.stat_l;
+  int &redo_any = lds.redo_any;
 
-  if (EXACT && args.redo[blockIdx.x] == 0) return;
+  if (EXACT && args.redo[slot] == 0) return;
 
   char *kbuf0 = smem, *kbuf1 = smem + TILE_BYTES, *vbuf0 = smem + 2 * TILE_BYTES, *vbuf1 = smem + 3 * TILE_BYTES;
   const int tid = threadIdx.x;
@@ -92,7 +104,7 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
   const int g = lane >> 5;           // lane half: selects 8 of the 16 k values of an MFMA operand
   const int l32 = lane & 31;
 
-  const FwdItem it = args.items[blockIdx.x];
+  const FwdItem it = args.items[item];
   const int bh = it.bh;
   const int cq = it.c_q;
   const int n_tiles = it.walk_len / kTilePages;
@@ -437,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
   barrier();
   if (!EXACT) {
     const int redo = redo_any;
-    if (tid == 0) args.redo[blockIdx.x] = redo;
+    if (tid == 0) args.redo[slot] = redo;
     if (redo) return;  // the exact kernel writes this item
   }
   // merged maximum and sum of query row qr (0..31) of query group q_g
@@ -513,25 +525,37 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs args) {
   }
 }
 
-template <int D, int ROUTE>
-void launch_route(const FwdArgs &a, hipStream_t stream) {
-  dim3 grid(a.n_items), block(kThreads);
-  hipLaunchKernelGGL((kpage_fwd_kernel<D, ROUTE, false>), grid, block, 0, stream, a);
-  hipLaunchKernelGGL((kpage_fwd_kernel<D, ROUTE, true>), grid, block, 0, stream, a);
+// Both routes in one launch: workgroups [0, n128) take the M128 x N128 items, the rest
+// the M64 x N256 items (and the cleanup items of empty blocks), so the shorter M64 items
+// fill the end of the M128 work instead of starting after its last workgroup.
+template <int D, bool EXACT>
+__global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs a128, FwdArgs a64) {
+  __shared__ FwdLds<D> lds;
+  const int b = blockIdx.x;
+  if (b < a128.n_items) fwd_item<D, 128, EXACT>(a128, b, b, lds);
+  else fwd_item<D, 64, EXACT>(a64, b - a128.n_items, b, lds);
+}
+
+template <int D>
+void launch_d(const FwdArgs &a128, const FwdArgs &a64, hipStream_t stream, LaunchTimer *timer) {
+  dim3 grid(a128.n_items + a64.n_items), block(kThreads);
+  if (timer) timer->before(0, stream);
+  hipLaunchKernelGGL((kpage_fwd_kernel<D, false>), grid, block, 0, stream, a128, a64);
+  if (timer) timer->after(0, stream);
+  if (timer) timer->before(1, stream);
+  hipLaunchKernelGGL((kpage_fwd_kernel<D, true>), grid, block, 0, stream, a128, a64);
+  if (timer) timer->after(1, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs &a, int head_dim, int route, hipStream_t stream, LaunchTimer *timer) {
-  if (a.n_items <= 0) return hipSuccess;
-  const int kid = route == 128 ? 0 : 1;
-  if (timer) timer->before(kid, stream);
-  if (head_dim == 128 && route == 128) launch_route<128, 128>(a, stream);
-  else if (head_dim == 128 && route == 64) launch_route<128, 64>(a, stream);
-  else if (head_dim == 64 && route == 128) launch_route<64, 128>(a, stream);
-  else if (head_dim == 64 && route == 64) launch_route<64, 64>(a, stream);
+hipError_t launch_fwd(const FwdArgs &a128, const FwdArgs &a64, int head_dim, hipStream_t stream,
+                      LaunchTimer *timer) {
+  if (a128.n_items < 0 || a64.n_items < 0) return hipErrorInvalidValue;
+  if (a128.n_items + a64.n_items == 0) return hipSuccess;
+  if (head_dim == 128) launch_d<128>(a128, a64, stream, timer);
+  else if (head_dim == 64) launch_d<64>(a128, a64, stream, timer);
   else return hipErrorInvalidValue;
-  if (timer) timer->after(kid, stream);
   return hipGetLastError();
 }
 

@@ -398,7 +398,7 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
   t->q128_queue = a32(2 * int64_t(h.n_q128));
   t->items128 = static_cast<FwdItem *>(alloc(size_t(std::max(h.n_q128, 1)) * sizeof(FwdItem)));
   t->items64 = static_cast<FwdItem *>(alloc(size_t(std::max(h.n_q64 + h.n_zero, 1)) * sizeof(FwdItem)));
-  const int n_redo = std::max(std::max(h.n_q128, h.n_q64 + h.n_zero), 1);
+  const int n_redo = std::max(h.n_q128 + h.n_q64 + h.n_zero, 1);  // one flag per workgroup of the forward launch
   t->redo = a32(n_redo);
   unsigned long long *keys = static_cast<unsigned long long *>(alloc(size_t(std::max<int64_t>(BHQ, 1)) * 8 * 3));
   if (!t->walk || !t->pages || !t->valid || !t->q64_queue || !t->q128_queue || !t->items128 || !t->items64 ||

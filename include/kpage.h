@@ -229,8 +229,10 @@ void kpage_plan_destroy(kpage_plan_t *plan);
  * event records per launch and nothing else.
  */
 enum {
-  KPAGE_K_FWD_Q128 = 0,  /* forward, M128 x N128 route                            */
-  KPAGE_K_FWD_Q64 = 1,   /* forward, M64 x N256 route and empty-block cleanup      */
+  KPAGE_K_FWD = 0,       /* forward, both routes in one launch (M128 x N128 items, */
+                         /* then M64 x N256 items and empty-block cleanup)         */
+  KPAGE_K_FWD_EXACT = 1, /* forward re-run with online rescaling of the items the  */
+                         /* fixed-maximum pass flagged (one launch, both routes)   */
   KPAGE_K_BWD_PRE = 2,   /* rowsum(dO * O) and LSE * log2(e) per query row         */
   KPAGE_K_BWD_ZERO = 3,  /* dK/dV pages outside every block footprint              */
   KPAGE_K_BWD_KV = 4,    /* K/V-owned pass: dK, dV                                  */
