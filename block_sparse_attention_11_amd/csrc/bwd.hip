@@ -313,7 +313,12 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
     wait_vmcnt<0>();
     barrier();  // half-step u resident for every wave; nobody reads buffer 1 - BUF any more
     if (u + 1 < n_half) load_half(pn, ic<1 - BUF>{});
-    half_step(buf_c, u, adj);
+    // A half-step with no edge between its 4 query pages and this wave's 2 key slots
+    // (dummy query pages, or pages of blocks outside each other's selection) has P = 0
+    // and dS = 0 everywhere and adds nothing to dK and dV: the wave skips its compute
+    // (wave-uniform; the copies above and the barriers are unchanged).
+    const uint64_t wave_bits = (0x03030303ull << (32 * (u & 1))) << (2 * wave);
+    if ((adj & wave_bits) != 0) half_step(buf_c, u, adj);
   };
   for_range(ic<0>{}, 0, n_half, iter);
 
