@@ -23,7 +23,8 @@
 //                   owner, Q group) when the plan splits reverse neighbourhoods
 //                   into Q groups (section 3.3.2): dK, dV, or fp32 partials of them.
 //   kpage_bwd_kv_reduce  sums the partials of owners split over Q groups.
-//   kpage_bwd_dq    one workgroup per forward work item (query block): dQ.
+//   kpage_bwd_dq    one workgroup per forward work item (query block), both routes
+//                   in one launch: dQ.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"

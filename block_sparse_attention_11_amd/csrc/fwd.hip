@@ -18,7 +18,8 @@
 // 4 query groups, every wave takes all 64 keys of a tile (2 sub-tiles).  Route
 // M64 x N256: 2 query groups x 2 key halves, 1 sub-tile per wave per tile.  Each
 // wave keeps its own running maximum, sum and output; waves that share query
-// rows are merged once at the end.
+// rows are merged once at the end.  One launch covers both routes: the first
+// workgroups take the M128 items, the rest the M64 items.
 //
 // Matrix layout per wave (v_mfma_f32_32x32x16_bf16, 32 cycles each):
 //   S^T (key x query) = K . Q^T : A = K rows from LDS, B = Q rows kept in VGPRs.
