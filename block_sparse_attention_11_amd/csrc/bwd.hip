@@ -382,7 +382,6 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
   constexpr int PART_BYTES = 32 * D * 4;
   static_assert(kDqWaves * PART_BYTES <= 4 * HTILE, "dQ partials reuse the tile buffers");
 
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
