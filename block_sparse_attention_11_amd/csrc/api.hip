@@ -155,27 +155,13 @@ std::vector<int32_t> redirect_dummies(const std::vector<int32_t> &walk, const st
   return out;
 }
 
-// Launch order for MI355X's 8 XCDs.  The dispatcher hands workgroup i to XCD i % 8
-// and each XCD has its own 4 MB L2, so position 8 j + x holds the j-th item of XCD
-// x's share, and the share of XCD x is the x-th contiguous eighth of `seq`.  With
-// `seq` in head-major, spatially ordered form, the workgroups resident on one XCD
-// work on one head and on neighbouring blocks at a time: their page gathers reuse
-// that XCD's L2, and the chip as a whole keeps about 8 heads' K/V live in the
-// memory-side cache instead of all of them.  The plan's queues (longest walk
-// first) keep their order for export; this permutation only decides which
-// workgroup runs which item.
-constexpr int kXcds = 8;
-
+// Launch order (launch_position): the plan's queues (longest walk first) keep their
+// order for export; this permutation only decides which workgroup runs which item.
 template <class T>
-std::vector<T> xcd_interleave(const std::vector<T> &seq) {
-  const size_t n = seq.size(), m = n / kXcds, r = n % kXcds;
-  std::vector<T> out(n);
-  size_t start = 0;
-  for (int x = 0; x < kXcds; ++x) {
-    const size_t cnt = m + (size_t(x) < r ? 1 : 0);
-    for (size_t j = 0; j < cnt; ++j) out[j * kXcds + x] = seq[start + j];
-    start += cnt;
-  }
+std::vector<T> xcd_interleave(const std::vector<T> &seq, int64_t chunk) {
+  const int64_t n = int64_t(seq.size());
+  std::vector<T> out(seq.size());
+  for (int64_t p = 0; p < n; ++p) out[size_t(launch_position(p, n, chunk))] = seq[size_t(p)];
   return out;
 }
 
@@ -206,8 +192,9 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   for (int bh = 0; bh < P.batch * P.heads; ++bh)
     for (int q = 0; q < nq; ++q)
       if (P.q_valid[size_t(P.slot_of(bh)) * nq + q] == 0) it64.push_back(make(bh, q));
-  it128 = xcd_interleave(it128);
-  it64 = xcd_interleave(it64);
+  const int64_t chunk = xcd_chunk_for(P.seq_q, P.seq_kv, P.head_dim);
+  it128 = xcd_interleave(it128, chunk);
+  it64 = xcd_interleave(it64, chunk);
   kpage_status s;
   if ((s = upload(pl, pages, &pl->d_pages, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, F.valid, &pl->d_valid, stream)) != KPAGE_OK) return s;
@@ -382,7 +369,7 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
   std::vector<BwdItem> items;
   std::vector<BwdReduce> reduce;
   make_bwd_items(P, B, &items, &reduce, &pl->n_partials);
-  items = xcd_interleave(items);
+  items = xcd_interleave(items, xcd_chunk_for(P.seq_q, P.seq_kv, P.head_dim));
   kpage_status s;
   if ((s = upload(pl, items, &pl->d_bitems, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, owners, &pl->d_owners, stream)) != KPAGE_OK) return s;
@@ -584,6 +571,7 @@ kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, co
   DevProblem &D = pl->DP;
   D.batch = P.batch; D.heads = P.heads; D.n_q = P.n_q; D.n_kv = P.n_kv; D.slots = P.slots;
   D.seq_q = P.seq_q; D.seq_kv = P.seq_kv; D.per_head = P.per_head; D.nnz = q2k_nnz;
+  D.xcd_chunk = xcd_chunk_for(P.seq_q, P.seq_kv, P.head_dim);
   D.q_valid = static_cast<const int32_t *>(own(shell.q_valid, size_t(G * nq) * 4));
   D.kv_valid = static_cast<const int32_t *>(own(shell.kv_valid, size_t(G * nk) * 4));
   D.q2k_ptr = static_cast<const int64_t *>(own(shell.q2k_ptr, size_t(G * (nq + 1)) * 8));

@@ -77,6 +77,50 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
+// Launch order for MI355X's 8 XCDs.  The dispatcher hands workgroup i to XCD i % 8, and
+// each XCD has its own 4 MB L2.  Entry p of a work list (head-major, spatially ordered)
+// goes to launch position launch_position(p, n, chunk), a bijection onto [0, n) in which
+// XCD x receives exactly the positions with p % 8 == x:
+//  - chunk <= 0: XCD x takes the x-th contiguous eighth of the list, so each XCD works
+//    through its own run of heads and its workgroups gather neighbouring blocks' pages
+//    from its L2; 8 heads (one per XCD) are live at a time.
+//  - chunk > 0: the list is dealt to the XCDs in chunks of `chunk` consecutive entries
+//    (the entries after the last full round of 8 chunks are split into 8 contiguous
+//    shares), so all XCDs stay within the same one or two heads.
+// The first keeps more L2 locality, the second keeps the live K/V small enough for the
+// memory-side cache when 8 heads of it would not fit (xcd_chunk_for).
+constexpr int kXcds = 8;
+constexpr int64_t kMemCacheBytes = int64_t(256) << 20;  // MI355X Infinity Cache
+
+__host__ __device__ inline int64_t launch_position(int64_t p, int64_t n, int64_t chunk) {
+  const int64_t round = kXcds * chunk;
+  const int64_t full = chunk > 0 ? n / round : 0;
+  if (p < full * round) {
+    const int64_t k = p / chunk, o = p % chunk;
+    return ((k / kXcds) * chunk + o) * kXcds + k % kXcds;
+  }
+  const int64_t m = n - full * round, q = p - full * round;
+  const int64_t per = m / kXcds, extra = m % kXcds;
+  int64_t x, j;
+  if (q < extra * (per + 1)) {
+    x = q / (per + 1);
+    j = q % (per + 1);
+  } else {
+    x = extra + (q - extra * (per + 1)) / per;
+    j = (q - extra * (per + 1)) % per;
+  }
+  return (full * chunk + j) * kXcds + x;
+}
+
+// Chunk length of a plan's launch order: whole-head runs per XCD (0) while one head's
+// pair of gathered tensors (K and V, or Q and dO) times 8 fits the memory-side cache,
+// else 64 entries (one XCD's two workgroups per CU).
+inline int64_t xcd_chunk_for(int64_t seq_q, int64_t seq_kv, int head_dim) {
+  const int64_t rows = seq_q > seq_kv ? seq_q : seq_kv;
+  const int64_t head_bytes = rows * head_dim * 2 * 2;
+  return kXcds * head_bytes > kMemCacheBytes ? 64 : 0;
+}
+
 // Optional per-launch timing: called right before and right after each kernel launch.
 struct LaunchTimer {
   virtual void before(int kernel_id, hipStream_t stream) = 0;

@@ -270,21 +270,6 @@ __global__ void k_queue_out(const unsigned long long *keys, int n, int n_q, int3
   queue[2 * i + 1] = int32_t(f % uint32_t(n_q));
 }
 
-// Launch position of entry p of a list of n: workgroup i goes to XCD i % 8, so XCD x
-// takes the x-th contiguous eighth of the list in order (see the host planner glue).
-__device__ __forceinline__ int64_t xcd_position(int64_t pidx, int64_t n) {
-  const int64_t m = n / 8, r = n % 8;
-  int64_t x, j;
-  if (pidx < r * (m + 1)) {
-    x = pidx / (m + 1);
-    j = pidx % (m + 1);
-  } else {
-    x = r + (pidx - r * (m + 1)) / m;
-    j = (pidx - r * (m + 1)) % m;
-  }
-  return j * 8 + x;
-}
-
 // launch items in (bh, q) order per route; the Q64 list also carries the cleanup items
 // of empty query blocks after its own items
 __global__ __launch_bounds__(kScanThreads) void k_items(DevProblem p, const int32_t *route, const int32_t *nfull,
@@ -319,9 +304,9 @@ __global__ __launch_bounds__(kScanThreads) void k_items(DevProblem p, const int3
       x.q = q;
       x.n_full = nfull[i];
       x.c_q = cq;
-      if (r == 128) items128[xcd_position(p128, n128)] = x;
-      else if (r == 64) items64[xcd_position(p64, nall64)] = x;
-      else items64[xcd_position(n64 + pz, nall64)] = x;
+      if (r == 128) items128[launch_position(p128, n128, p.xcd_chunk)] = x;
+      else if (r == 64) items64[launch_position(p64, nall64, p.xcd_chunk)] = x;
+      else items64[launch_position(n64 + pz, nall64, p.xcd_chunk)] = x;
     }
     c128 += t128;
     c64 += t64;
@@ -796,7 +781,7 @@ __global__ void k_bwd_items(DevProblem p, int64_t n_own, int64_t n_items, const 
   x.n_steps = steps;
   x.aligned = aligned[tg];
   x.partial = -1;
-  items[xcd_position(f, n_items)] = x;
+  items[launch_position(f, n_items, p.xcd_chunk)] = x;
 }
 
 __global__ void k_bwd_queue_out(DevProblem p, int64_t n_own, int64_t n_items, const int64_t *owner_ptr,

@@ -25,6 +25,7 @@ struct DevProblem {
   const int32_t *q_valid = nullptr, *kv_valid = nullptr, *q2k_idx = nullptr;
   const int64_t *kv_offset = nullptr, *q2k_ptr = nullptr;
   int64_t nnz = 0;  // entries of q2k_idx
+  int64_t xcd_chunk = 0;  // launch-order chunk (launch_position)
 };
 
 // Device forward tables (every array allocated through the caller's allocator).
