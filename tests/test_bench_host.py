@@ -1,0 +1,34 @@
+"""Host logic of bench.py (no GPU): when the committed counter traffic is reported, and the
+one-GPU guard."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_traffic_reported_only_for_its_workload_and_sources(tmp_path, monkeypatch):
+    with open(bench.TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    wl = int(rec["workload_id"])
+    for kernel, entry in rec["kernels"].items():
+        assert bench._measured_traffic(kernel, wl) == entry["bytes_per_launch"], kernel
+        assert bench._measured_traffic(kernel, wl + 1) is None, kernel
+    assert bench._measured_traffic("no_such_kernel", wl) is None
+    # a record whose source hash no longer matches the sources is not used
+    stale = dict(rec, kernels={k: dict(v, sources_sha256="0" * 64) for k, v in rec["kernels"].items()})
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(stale))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    for kernel in rec["kernels"]:
+        assert bench._measured_traffic(kernel, wl) is None, kernel
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
