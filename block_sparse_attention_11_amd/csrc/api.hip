@@ -165,6 +165,21 @@ std::vector<T> xcd_interleave(const std::vector<T> &seq, int64_t chunk) {
   return out;
 }
 
+// The last tail_len(count) items of each XCD's launch sequence (positions 8 j + x) in
+// descending step count (ties keep their order), so that an XCD ends on its shortest
+// owners instead of whichever came last in spatial order.
+void sort_xcd_tails(std::vector<BwdItem> &items) {
+  const int64_t n = int64_t(items.size());
+  for (int x = 0; x < kXcds; ++x) {
+    const int64_t cnt = n > x ? (n - x + kXcds - 1) / kXcds : 0;
+    const int64_t t = bwd_tail_len(cnt);
+    std::vector<BwdItem> tail;
+    for (int64_t j = cnt - t; j < cnt; ++j) tail.push_back(items[size_t(j * kXcds + x)]);
+    std::stable_sort(tail.begin(), tail.end(), [](const BwdItem &a, const BwdItem &b) { return a.n_steps > b.n_steps; });
+    for (int64_t j = cnt - t; j < cnt; ++j) items[size_t(j * kXcds + x)] = tail[size_t(j - (cnt - t))];
+  }
+}
+
 kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   if (pl->fwd_on_device) return KPAGE_OK;
   const Problem &P = pl->P;
@@ -370,6 +385,7 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
   std::vector<BwdReduce> reduce;
   make_bwd_items(P, B, &items, &reduce, &pl->n_partials);
   items = xcd_interleave(items, xcd_chunk_for(P.seq_q, P.seq_kv, P.head_dim));
+  sort_xcd_tails(items);
   kpage_status s;
   if ((s = upload(pl, items, &pl->d_bitems, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, owners, &pl->d_owners, stream)) != KPAGE_OK) return s;

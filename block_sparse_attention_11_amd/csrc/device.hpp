@@ -112,6 +112,15 @@ __host__ __device__ inline int64_t launch_position(int64_t p, int64_t n, int64_t
   return (full * chunk + j) * kXcds + x;
 }
 
+// Entries at the end of each XCD's backward launch sequence that run longest-first
+// (5%, at most kMaxBwdTail): owners differ in step count by up to 4x, and an XCD that
+// ends on a long one idles the rest of its CUs.
+constexpr int64_t kMaxBwdTail = 1024;
+__host__ __device__ inline int64_t bwd_tail_len(int64_t count) {
+  const int64_t t = count / 20;
+  return t < kMaxBwdTail ? t : kMaxBwdTail;
+}
+
 // Chunk length of a plan's launch order: whole-head runs per XCD (0) while one head's
 // pair of gathered tensors (K and V, or Q and dO) times 8 fits the memory-side cache,
 // else 64 entries (one XCD's two workgroups per CU).

@@ -784,6 +784,43 @@ __global__ void k_bwd_items(DevProblem p, int64_t n_own, int64_t n_items, const 
   items[launch_position(f, n_items, p.xcd_chunk)] = x;
 }
 
+// The last bwd_tail_len(count) items of each XCD's launch sequence (positions 8 j + x)
+// in descending step count, ties in their order: one workgroup per XCD sorts its tail
+// in LDS (bitonic, over kMaxBwdTail keys), the same order as the host planner's.
+__global__ __launch_bounds__(1024) void k_bwd_tails(BwdItem *items, int64_t n) {
+  __shared__ unsigned long long key[kMaxBwdTail];
+  __shared__ BwdItem buf[kMaxBwdTail];
+  const int x = int(blockIdx.x);
+  const int64_t cnt = n > x ? (n - x + kXcds - 1) / kXcds : 0;
+  const int64_t t = bwd_tail_len(cnt);
+  const int64_t j0 = cnt - t;
+  for (int i = int(threadIdx.x); i < kMaxBwdTail; i += int(blockDim.x)) {
+    if (i < t) {
+      const BwdItem it = items[(j0 + i) * kXcds + x];
+      buf[i] = it;
+      key[i] = ((unsigned long long)(uint32_t)(0x7FFFFFFF - it.n_steps) << 32) | (unsigned long long)(uint32_t)i;
+    } else {
+      key[i] = ~0ull;
+    }
+  }
+  __syncthreads();
+  for (int k = 2; k <= kMaxBwdTail; k <<= 1)
+    for (int h = k >> 1; h > 0; h >>= 1) {
+      for (int i = int(threadIdx.x); i < kMaxBwdTail; i += int(blockDim.x)) {
+        const int l = i ^ h;
+        if (l > i) {
+          const unsigned long long a = key[i], b = key[l];
+          if ((a > b) == ((i & k) == 0)) {
+            key[i] = b;
+            key[l] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = int(threadIdx.x); i < t; i += int(blockDim.x)) items[(j0 + i) * kXcds + x] = buf[uint32_t(key[i])];
+}
+
 __global__ void k_bwd_queue_out(DevProblem p, int64_t n_own, int64_t n_items, const int64_t *owner_ptr,
                                 const unsigned long long *keys, int32_t *queue) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -902,6 +939,7 @@ kpage_status build_backward_device(const DevProblem &p, const int32_t *page_bloc
                          owner_slot, t->qwalk_ptr, t->owners, t->qwalk, edge, nkw, t->adj, d_sum);
     hipLaunchKernelGGL(k_bwd_items, dim3(blocks_for(t->n_items, TB)), dim3(TB), 0, st, p, h.n_own, t->n_items,
                        t->owner_ptr, t->qwalk_ptr, t->aligned, keys, t->items);
+    hipLaunchKernelGGL(k_bwd_tails, dim3(kXcds), dim3(1024), 0, st, t->items, t->n_items);
     size_t tmp_bytes = 0;
     KP_CHECK(hipcub::DeviceRadixSort::SortKeys(nullptr, tmp_bytes, keys, keys + t->n_items, int(t->n_items), 0, 64,
                                                st));

@@ -110,6 +110,27 @@ def test_device_plan_attention_is_bitwise_equal():
     assert sh["bwd_physical"] == sd["bwd_physical"] and sh["bwd_useful_check"] == sd["bwd_useful_check"]
 
 
+def test_device_plan_full_size_attention_is_bitwise_equal():
+    """All 40 heads of the 21x30x52 workload (10,320 backward items, so every XCD's
+    longest-first tail holds 64 owners): outputs of the GPU-built plan equal the host
+    plan's bit for bit."""
+    w = make_workload(3, with_do=True)
+    _say(f"[device plan] full-size 21x30x52, {w.heads} heads")
+    h, d = K.kpage_plan(w), K.kpage_plan_device(w)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
+    outs = []
+    for plan in (h, d):
+        o, lse = K.attn_fwd(plan, q, k, v, w.scale)
+        dq, dk, dv = K.attn_bwd(plan, q, k, v, o, lse, do, w.scale)
+        torch.cuda.synchronize()
+        outs.append([x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+                     for x in (o, lse, dq, dk, dv)])
+        del o, lse, dq, dk, dv
+    for n, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), *outs):
+        assert np.array_equal(a, b), n
+
+
 def _bad(p, what):
     with pytest.raises(K.KpageError) as e:
         K.kpage_plan_device(p)
