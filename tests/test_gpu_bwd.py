@@ -15,13 +15,14 @@ import torch
 
 import block_sparse_attention_11_amd as K
 from oracle import oracle_bwd
+from tests import parity_log
 from tests.problems import make_problem, random_tensors
+from tests.tolerances import GRAD_RTOL
 from tests.test_gpu_fwd import EDGE_CASES
 from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
 
-GRAD_RTOL = 2e-2
 
 
 def _say(msg):
@@ -68,6 +69,7 @@ def check_grads(got, ref, label, problem, heads=None):
         scale = np.abs(r).max()
         err = np.abs(g - r).max() / max(scale, 1e-2)
         _say(f"  {label} {name}: max-norm-rel {err:.3e} (max |ref| {scale:.3e})")
+        parity_log.record(label, name, err, GRAD_RTOL, "max|g - g*| / max(max|g*|, 1e-2)")
         assert err <= GRAD_RTOL, (label, name, err)
         assert np.all(g[z] == 0), f"{label} {name}: rows without any valid pair must be exactly 0"
 

@@ -1,13 +1,21 @@
 """Forward parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
 
-Tolerances (bf16 inputs, fp32 accumulation): O max-abs <= 1e-2; LSE relative error
-<= 1e-3, taken against max(1, |LSE|) so rows with LSE near 0 are not ill-conditioned;
-rows the oracle marks empty (LSE = -inf) must be exactly O = 0 and LSE = -inf.
-
-O is stored in bf16, whose spacing is 2^-6 = 0.0156 for |O| in [2, 4): there the output
-format alone cannot meet 1e-2, so the bound per element is max(1e-2, one bf16 ulp of the
-reference value).  This only matters for rows that attend to a handful of keys (the edge
-cases); the five workloads keep |O| well below 2.
+Tolerances, for bf16 inputs with fp32 accumulation:
+  * LSE: relative error <= 1e-3, |L - L*| <= 1e-3 |L*| + 1e-5.  The 1e-5 absolute floor
+    only matters where |L*| < 1e-2; the fp32 evaluation of m + log(l) has an absolute
+    rounding error of order 2^-23 (|m| + |log l|), far below it.
+  * O on the five benchmark configurations: max-abs <= 1e-2, flat.
+  * O on the synthetic edge cases (rows that attend to one or a few keys of N(0,1)
+    values, so |O| reaches 2-4): per element max(1e-2, E) with E the rounding bound of
+    the computation (output rounded to bf16, half a bf16 ulp of the result; each
+    probability rounded to bf16 before the P.V product, relative 2^-8, so at most
+    2^-8 sum_j P_ij |V_jc|; 2^-12 of the same sum for fp32 accumulation).  For |O| >= 4
+    no bf16 output can be within 1e-2 of every real value (half an ulp there is
+    2^-6 = 0.0156), and between 2 and 4 half an ulp already takes 0.0078 of it.
+    E is computed with the oracle: sum_j P_ij |V_jc| is the oracle's attention output
+    for the values |V|.
+  * Rows the oracle marks empty (LSE = -inf) must be exactly O = 0 and LSE = -inf.
+The worst error of every check, against its bound, is printed after the run.
 """
 import math
 import sys
@@ -18,14 +26,12 @@ import torch
 
 import block_sparse_attention_11_amd as K
 from oracle import oracle_fwd
+from tests import parity_log
+from tests.tolerances import LSE_ATOL, LSE_RTOL, O_ATOL, rounding_bound
 from tests.problems import make_problem, random_tensors
 from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
-
-O_ATOL = 1e-2
-LSE_RTOL = 1e-3
-
 
 def _say(msg):
     print(msg, flush=True)
@@ -41,26 +47,42 @@ def gpu_fwd(problem, q, k, v, plan=None):
     return o.float().cpu().numpy(), lse.cpu().numpy()
 
 
-def bf16_ulp(x):
-    """Spacing of bf16 numbers at |x| (8 significant bits)."""
-    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
-    return 2.0 ** (e - 7)
-
-
-def check(O, L, Oref, Lref, label):
+def check(O, L, Oref, Lref, label, Aabs=None):
+    """O against the flat 1e-2 when Aabs is None, else against max(1e-2, rounding bound)."""
     done = ~np.isnan(Lref)
     empty = done & np.isneginf(Lref)
     live = done & ~empty
     assert np.all(np.isneginf(L[empty])), f"{label}: rows without keys must have LSE = -inf"
     assert np.all(O[empty] == 0), f"{label}: rows without keys must have O = 0"
     assert np.all(np.isfinite(L[live])), f"{label}: non-finite LSE on a live row"
-    err_o = np.abs(O[live] - Oref[live]).max() if live.any() else 0.0
-    excess = (np.abs(O[live] - Oref[live]) - np.maximum(O_ATOL, bf16_ulp(Oref[live]))).max() if live.any() else -1.0
-    err_l = (np.abs(L[live] - Lref[live]) / np.maximum(1.0, np.abs(Lref[live]))).max() if live.any() else 0.0
+    if not live.any():
+        return
+    err = np.abs(O[live] - Oref[live])
+    err_o = float(err.max())
+    if Aabs is None:
+        bound = np.full_like(err, O_ATOL)
+        note = "flat 1e-2"
+    else:
+        bound = np.maximum(O_ATOL, rounding_bound(Oref[live], Aabs[live]))
+        note = f"max(1e-2, rounding bound); {int((err > O_ATOL).sum())} elements above 1e-2"
+    i = int(np.argmax(err / bound))
+    ratio = float(err.flat[i] / bound.flat[i])
+    lerr = np.abs(L[live] - Lref[live])
+    lbound = LSE_RTOL * np.abs(Lref[live]) + LSE_ATOL
+    j = int(np.argmax(lerr / lbound))
+    lratio = float(lerr[j] / lbound[j])
+    err_l = float((lerr / np.maximum(np.abs(Lref[live]), LSE_ATOL)).max())
     _say(f"  {label}: rows={int(live.sum())} empty={int(empty.sum())} O max-abs={err_o:.3e} "
-         f"(max |O| {np.abs(Oref[live]).max() if live.any() else 0:.2f}) LSE rel={err_l:.3e}")
-    assert excess <= 0, (label, err_o)
-    assert err_l <= LSE_RTOL, (label, err_l)
+         f"(max |O| {np.abs(Oref[live]).max():.2f}, worst error/bound {ratio:.3f}) LSE rel={err_l:.3e}")
+    parity_log.record(label, "O", float(err.flat[i]), float(bound.flat[i]), f"{note}; max-abs {err_o:.3e}")
+    parity_log.record(label, "LSE", float(lerr[j]), float(lbound[j]), f"1e-3 |L*| + 1e-5; max rel {err_l:.3e}")
+    assert ratio <= 1.0, (label, err_o, ratio)
+    assert lratio <= 1.0, (label, err_l)
+
+
+def abs_values_attention(problem, q, k, v, items=None):
+    """sum_j P_ij |V_jc| from the oracle: its attention output for the values |V|."""
+    return oracle_fwd(problem, q, k, v.abs(), items=items)[0]
 
 
 def padded_rows(w, side):
@@ -149,7 +171,7 @@ def test_fwd_edge_cases(name, d):
     _say(f"[fwd] edge case {name} d={d}")
     O, L = gpu_fwd(p, t["q"], t["k"], t["v"])
     Oref, Lref = oracle_fwd(p, t["q"], t["k"], t["v"])
-    check(O, L, Oref, Lref, f"{name} d={d}")
+    check(O, L, Oref, Lref, f"{name} d={d}", Aabs=abs_values_attention(p, t["q"], t["k"], t["v"]))
 
 
 def rising_scores_problem(d):
@@ -182,7 +204,7 @@ def test_fwd_large_score_rise_uses_exact_pass(d):
     _say(f"[fwd] large score rise d={d}")
     O, L = gpu_fwd(p, q, k, v)
     Oref, Lref = oracle_fwd(p, q, k, v)
-    check(O, L, Oref, Lref, f"large score rise d={d}")
+    check(O, L, Oref, Lref, f"large score rise d={d}", Aabs=abs_values_attention(p, q, k, v))
 
 
 def test_fwd_independent_offsets_with_gaps():
@@ -196,7 +218,7 @@ def test_fwd_independent_offsets_with_gaps():
     _say("[fwd] shuffled offsets with gaps")
     O, L = gpu_fwd(p, t["q"], t["k"], t["v"])
     Oref, Lref = oracle_fwd(p, t["q"], t["k"], t["v"])
-    check(O, L, Oref, Lref, "offsets with gaps")
+    check(O, L, Oref, Lref, "offsets with gaps", Aabs=abs_values_attention(p, t["q"], t["k"], t["v"]))
 
 
 def test_fwd_padding_contents_do_not_matter():
@@ -227,7 +249,7 @@ def test_fwd_selection_order_does_not_matter():
     assert np.abs(O1 - O2).max() <= O_ATOL
     fin = np.isfinite(L1)
     assert np.array_equal(fin, np.isfinite(L2))
-    assert (np.abs(L1[fin] - L2[fin]) / np.maximum(1, np.abs(L1[fin]))).max() <= LSE_RTOL
+    assert (np.abs(L1[fin] - L2[fin]) <= 2 * (LSE_RTOL * np.abs(L1[fin]) + LSE_ATOL)).all()
 
 
 def test_fwd_is_deterministic_and_plan_is_reusable():

@@ -319,3 +319,48 @@ def test_q_groups_worked_by_hand():
     assert t.adj.tolist() == [k0, k1, k0]
     assert t.stats["bwd_physical"] == 3 * 128 * 128
     assert full != k0
+
+
+def _order_case(key):
+    g = _gold("order_conventions.json")[key]
+    return g
+
+
+def test_walk_section_order_worked_by_hand():
+    """Reading R12/R13: full pages in K_q order (not page order), then each partial block's
+    tail page in K_q order, then dummies; masks two per word, even position low."""
+    g = _order_case("walk_order")
+    p = make_problem(g["q_valid"], g["kv_valid"], g["rows"], sort_rows=False)
+    t = oracle_plan(p)
+    for q, (walk, nf, words) in enumerate(zip(g["walks"], g["n_full"], g["valid_words"])):
+        a, b = int(t.fwd_walk_ptr[0, q]), int(t.fwd_walk_ptr[0, q + 1])
+        assert t.fwd_walk[a:b].tolist() == walk, q
+        assert int(t.fwd_nfull[0, q]) == nf
+        assert t.fwd_valid[a // 2:b // 2].tolist() == words, q
+
+
+def test_queue_and_backward_order_ties_worked_by_hand():
+    """Reading R14 (queue ties: unpadded pages, then b*H + h, then q) and R26 (backward
+    work order: steps, then b*H + h, then owner) on a layout with ties in both."""
+    g = _order_case("queue_ties")
+    p = make_problem(g["q_valid"], g["kv_valid"], g["rows"], heads=g["heads"], sort_rows=False)
+    t = oracle_plan(p)
+    assert t.q128_queue.tolist() == g["q128_queue"]
+    assert t.q64_queue.tolist() == g["q64_queue"]
+    assert t.owners.tolist() == g["owners"]
+    assert t.revq.tolist() == g["revq"]
+    assert t.qwalk.tolist() == g["qwalk"]
+    assert [int(x) for x in t.adj] == [int(x, 16) for x in g["adj"]]
+    assert t.bwd_queue.tolist() == g["bwd_queue"]
+    assert t.stats["useful"] == g["useful"] and t.stats["bwd_physical"] == g["bwd_physical"]
+
+
+def test_q_group_work_order_worked_by_hand():
+    """Reading R30: (owner, group) lists owner-major, items by steps, then b*H + h, owner,
+    group, exported as (b*H + h, owner * n_groups + group)."""
+    g0 = _order_case("queue_ties")
+    g = _order_case("q_group_order")
+    p = make_problem(g0["q_valid"], g0["kv_valid"], g0["rows"], heads=g0["heads"], sort_rows=False)
+    t = oracle_plan(p, q_group=g["q_group"])
+    assert t.revq_ptr.tolist() == g["revq_ptr"]
+    assert t.bwd_queue.tolist() == g["bwd_queue"]

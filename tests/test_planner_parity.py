@@ -92,3 +92,14 @@ def test_q_groups_random_small_layouts_bit_exact():
         p = make_problem(rng.choice(sizes, size=n_q), rng.choice(sizes, size=n_kv), rows, heads=2, head_dim=64,
                          sort_rows=False)
         _assert_same(p, q_group=int(rng.integers(1, n_q + 2)))
+
+
+@pytest.mark.parametrize("key,q_group", [("walk_order", 0), ("queue_ties", 0), ("queue_ties", 2)])
+def test_order_convention_layouts_bit_exact(key, q_group):
+    """The hand-worked layouts that pin the walk, queue and work-order readings in the oracle."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "order_conventions.json")) as f:
+        g = json.load(f)[key]
+    p = make_problem(g["q_valid"], g["kv_valid"], g["rows"], heads=g.get("heads", 1), head_dim=64, sort_rows=False)
+    _assert_same(p, q_group=q_group)
