@@ -94,7 +94,6 @@ struct kpage_plan {
   int n_items128 = 0, n_items64 = 0;
   int32_t *d_pages = nullptr;
   uint32_t *d_valid = nullptr;
-  int32_t *d_redo = nullptr;  // per workgroup of the forward launch (both routes): item needs the exact pass
   // backward device tables
   BwdItem *d_bitems = nullptr;
   int n_bitems = 0;
@@ -105,6 +104,7 @@ struct kpage_plan {
   int max_uncovered = 0;
   // owners split over several Q groups: fp32 partial slots in the workspace, reduce list
   BwdReduce *d_reduce = nullptr;
+  const int32_t *d_qvalid = nullptr;  // [slots][n_q] query sizes for the backward's row masks
   int n_reduce = 0;
   int64_t n_partials = -1;  // -1: not counted yet
   std::vector<void *> allocations;
@@ -123,6 +123,17 @@ kpage_status fail(kpage_status s, const std::string &msg) {
 
 kpage_status hip_fail(hipError_t e, const char *what) {
   return fail(KPAGE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Runs an entry point's body; a failed host allocation inside it (lazy table builds)
+// becomes KPAGE_ERR_OOM instead of an exception crossing the C ABI.
+template <class F>
+kpage_status guarded(F &&body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc &) {
+    return fail(KPAGE_ERR_OOM, "host allocation failed");
+  }
 }
 
 template <class T>
@@ -195,6 +206,7 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
     x.bh = bh;
     x.q = q;
     x.n_full = F.nfull[size_t(g) * nq + q];
+    x.n_pages = F.unpadded[size_t(g) * nq + q];
     x.c_q = P.q_valid[size_t(g) * nq + q];
     return x;
   };
@@ -215,9 +227,6 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   if ((s = upload(pl, F.valid, &pl->d_valid, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, it128, &pl->d_items128, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, it64, &pl->d_items64, stream)) != KPAGE_OK) return s;
-  // one exact-pass flag per workgroup of the forward launch (both routes)
-  if ((s = upload(pl, std::vector<int32_t>(std::max<size_t>(it128.size() + it64.size(), 1), 0), &pl->d_redo, stream)) != KPAGE_OK)
-    return s;
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   pl->n_items128 = int(it128.size());
@@ -275,6 +284,7 @@ kpage_status build_backward_on_device(PlanT *pl, hipStream_t stream) {
   pl->d_uncovered = T.uncovered;
   pl->d_uncovered_ptr = T.uncovered_ptr;
   pl->max_uncovered = T.max_uncovered;
+  pl->d_qvalid = pl->DP.q_valid;
   pl->S.bwd_physical = T.bwd_physical;
   pl->S.bwd_useful_check = T.bwd_useful_check;
   pl->bwd_on_device = true;
@@ -395,6 +405,9 @@ kpage_status ensure_backward_on_device(PlanT *pl, hipStream_t stream) {
   if ((s = upload(pl, B.uncovered, &pl->d_uncovered, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, B.uncovered_ptr, &pl->d_uncovered_ptr, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, reduce, &pl->d_reduce, stream)) != KPAGE_OK) return s;
+  int32_t *qv = nullptr;
+  if ((s = upload(pl, P.q_valid, &qv, stream)) != KPAGE_OK) return s;
+  pl->d_qvalid = qv;
   pl->n_reduce = int(reduce.size());
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -552,8 +565,16 @@ kpage_status kpage_plan(const kpage_problem *problem, const kpage_plan_opts *opt
   return KPAGE_OK;
 }
 
+static kpage_status plan_device_body(const kpage_problem *problem, int64_t q2k_nnz, const kpage_plan_opts *opts,
+                                     void *stream, kpage_plan_t **out);
+
 kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, const kpage_plan_opts *opts,
                                void *stream, kpage_plan_t **out) {
+  return guarded([&] { return plan_device_body(problem, q2k_nnz, opts, stream, out); });
+}
+
+static kpage_status plan_device_body(const kpage_problem *problem, int64_t q2k_nnz, const kpage_plan_opts *opts,
+                                     void *stream, kpage_plan_t **out) {
   if (!out) return fail(KPAGE_ERR_INVALID, "out is NULL");
   *out = nullptr;
   if (!problem) return fail(KPAGE_ERR_INVALID, "problem is NULL");
@@ -619,7 +640,6 @@ kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, co
   pl->d_valid = pl->DF.valid;
   pl->d_items128 = pl->DF.items128;
   pl->d_items64 = pl->DF.items64;
-  pl->d_redo = pl->DF.redo;
   pl->n_items128 = pl->DF.n_q128;
   pl->n_items64 = pl->DF.n_q64 + pl->DF.n_zero;
   pl->fwd_on_device = true;
@@ -630,7 +650,7 @@ kpage_status kpage_plan_device(const kpage_problem *problem, int64_t q2k_nnz, co
 
 kpage_status kpage_plan_upload(kpage_plan_t *plan, void *stream) {
   if (!plan) return fail(KPAGE_ERR_INVALID, "plan is NULL");
-  return ensure_forward_on_device(plan, static_cast<hipStream_t>(stream));
+  return guarded([&] { return ensure_forward_on_device(plan, static_cast<hipStream_t>(stream)); });
 }
 
 kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, const void *v, void *o, float *lse,
@@ -639,13 +659,12 @@ kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, co
   if (!q || !k || !v || !o || !lse) return fail(KPAGE_ERR_INVALID, "tensor pointer is NULL");
   if (bad_scale(softmax_scale)) return fail(KPAGE_ERR_INVALID, "softmax_scale must be positive and finite");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  kpage_status s = ensure_forward_on_device(plan, st);
+  kpage_status s = guarded([&] { return ensure_forward_on_device(plan, st); });
   if (s != KPAGE_OK) return s;
   FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.pages = plan->d_pages;
   a.valid = plan->d_valid;
-  a.redo = plan->d_redo;
   a.seq_q = plan->P.seq_q;
   a.seq_kv = plan->P.seq_kv;
   a.scale = softmax_scale;
@@ -667,7 +686,7 @@ kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes) {
   // then the fp32 dK/dV partials of owners split over several groups
   *bytes = 2 * rows * 4;
   if (plan->P.q_group > 0) {
-    const kpage_status s = count_partials(plan);
+    const kpage_status s = guarded([&] { return count_partials(plan); });
     if (s != KPAGE_OK) return s;
     *bytes = partials_offset(rows) + size_t(plan->n_partials) * 2 * 128 * size_t(plan->P.head_dim) * 4;
   }
@@ -682,12 +701,13 @@ kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, co
     return fail(KPAGE_ERR_INVALID, "tensor or workspace pointer is NULL");
   if (bad_scale(softmax_scale)) return fail(KPAGE_ERR_INVALID, "softmax_scale must be positive and finite");
   size_t need = 0;
-  kpage_bwd_workspace_size(plan, &need);
+  kpage_status s = kpage_bwd_workspace_size(plan, &need);
+  if (s != KPAGE_OK) return s;
   if (workspace_bytes < need) return fail(KPAGE_ERR_INVALID, "workspace smaller than kpage_bwd_workspace_size()");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  kpage_status s = ensure_forward_on_device(plan, st);  // the dQ pass walks the forward tables
+  s = guarded([&] { return ensure_forward_on_device(plan, st); });  // the dQ pass walks the forward tables
   if (s != KPAGE_OK) return s;
-  s = ensure_backward_on_device(plan, st);
+  s = guarded([&] { return ensure_backward_on_device(plan, st); });
   if (s != KPAGE_OK) return s;
   const Problem &P = plan->P;
   const size_t rows = size_t(P.batch) * P.heads * size_t(P.seq_q);
@@ -696,6 +716,7 @@ kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, co
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dO; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
+  a.q_valid = plan->d_qvalid;
   a.lse2 = static_cast<float *>(workspace);
   a.delta = static_cast<float *>(workspace) + rows;
   a.items = plan->d_bitems;
@@ -748,10 +769,10 @@ kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf,
   if (!plan || !bytes) return fail(KPAGE_ERR_INVALID, "plan or bytes is NULL");
   if (table_id < 0 || table_id >= KPAGE_T_COUNT) return fail(KPAGE_ERR_INVALID, "unknown table id");
   if (table_id >= KPAGE_T_OWNER_PTR) {
-    const kpage_status s = ensure_backward_on_host(plan);
+    const kpage_status s = guarded([&] { return ensure_backward_on_host(plan); });
     if (s != KPAGE_OK) return s;
   } else {
-    const kpage_status s = ensure_forward_on_host(plan);
+    const kpage_status s = guarded([&] { return ensure_forward_on_host(plan); });
     if (s != KPAGE_OK) return s;
   }
   const void *src = nullptr;

@@ -17,7 +17,7 @@
 //
 // Kernels:
 //   kpage_bwd_pre   D_i = sum_d dO_id O_id and LSE_i * log2(e) (+inf for rows
-//                   without keys), 16 threads per row.
+//                   without keys and rows past c_q), 16 threads per row.
 //   kpage_bwd_zero  zero dK/dV pages that lie outside every block footprint.
 //   kpage_bwd_kv    one workgroup per (batch*head, owner), or per (batch*head,
 //                   owner, Q group) when the plan splits reverse neighbourhoods
@@ -34,13 +34,18 @@ namespace kpage {
 namespace {
 
 // ---------------------------------------------------------------------------
-// pre: 16 threads per query row
+// pre: 16 threads per query row.  Rows past c_q of their block (the plan's query sizes)
+// get lse2 = +inf and D = 0 whatever the caller's LSE and O hold there, so padded rows
+// never reach the gradients.
 template <int D>
 __global__ __launch_bounds__(256) void kpage_bwd_pre(BwdArgs a) {
   const int64_t rows = (int64_t)a.bh_count * a.seq_q;
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   if (row >= rows) return;
+  const int64_t bh = row / a.seq_q, r = row - bh * a.seq_q;
+  const int slot = a.per_head ? (int)bh : 0;
+  const bool valid = (int)(r & 127) < a.q_valid[(int64_t)slot * a.n_q + (r >> 7)];
   constexpr int PER = D / 16;  // elements per thread
   typedef __bf16 row_t __attribute__((ext_vector_type(PER)));
   const row_t o = *(const row_t *)((const __bf16 *)a.o + row * D + sub * PER);
@@ -51,10 +56,10 @@ __global__ __launch_bounds__(256) void kpage_bwd_pre(BwdArgs a) {
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
   if (sub == 0) {
-    a.delta[row] = s;
+    a.delta[row] = valid ? s : 0.f;
     const float l = a.lse[row];
-    // rows without a valid key (and invalid rows) get +inf: exp2(x - lse2) = 0
-    a.lse2[row] = l == kNegInf ? __builtin_inff() : l * kLog2e;
+    // rows without a valid key (and rows past c_q) get +inf: exp2(x - lse2) = 0
+    a.lse2[row] = (!valid || l == kNegInf) ? __builtin_inff() : l * kLog2e;
   }
 }
 
@@ -393,7 +398,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
   const FwdItem it = items[item];
   const int64_t bh = it.bh;
   const int cq = it.c_q;
-  const int n_half = it.walk_len / 4;
+  const int n_half = (it.n_pages + 3) / 4;  // all-dummy half-tiles of the padding skipped
   const int full_half = it.n_full / 4;
   const int qg = wave % NQG;
   const int keyoff = (wave / NQG) * KW;

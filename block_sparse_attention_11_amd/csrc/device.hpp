@@ -14,7 +14,8 @@ struct FwdItem {
   int32_t walk_len;  // pages, a multiple of the pages per step (0: nothing selected)
   int32_t n_full;    // pages of the fully valid prefix
   int32_t c_q;       // valid query rows (0 only for cleanup items of empty blocks)
-  int32_t pad;
+  int32_t n_pages;   // real pages of the walk (the rest are dummies, which the kernels skip
+                     // past the last 4-page tile holding a real page)
 };
 
 struct FwdArgs {
@@ -25,7 +26,6 @@ struct FwdArgs {
   const int32_t *pages;     // walk entries; dummy slots point at a real page of the same walk
   const uint32_t *valid;    // two 16-bit row masks per word, indexed by walk position / 2
   int64_t seq_q, seq_kv;
-  int32_t *redo;            // per workgroup of the launch: 1 when its item needs the exact rescaling pass
   int32_t n_items;
   float scale;              // softmax scale
   float scale_log2;         // softmax scale * log2(e)
@@ -53,7 +53,9 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float *lse;
   void *dq, *dk, *dv;
-  float *lse2;                // fp32 [BH, seq_q]: LSE * log2(e), 0 for rows without keys
+  const int32_t *q_valid;     // [slots][n_q] valid rows per query block (rows past them are padding)
+  float *lse2;                // fp32 [BH, seq_q]: LSE * log2(e); +inf for rows without keys and rows
+                              // past c_q, so that exp2(x - lse2) = 0 there
   float *delta;               // fp32 [BH, seq_q]: rowsum(dO * O)
   // K/V-owned pass (dK, dV)
   const BwdItem *items;
@@ -138,7 +140,7 @@ struct LaunchTimer {
 };
 
 // Forward over both routes in one launch (M128 items first, then M64 items), then the
-// exact re-run launch; timer ids 0 and 1.  The redo flags hold n128 + n64 entries.
+// exact re-run launch over the items the first marked in their LSE; timer ids 0 and 1.
 hipError_t launch_fwd(const FwdArgs &a128, const FwdArgs &a64, int head_dim, hipStream_t stream, LaunchTimer *timer);
 hipError_t launch_bwd(const BwdArgs &a, int head_dim, hipStream_t stream, LaunchTimer *timer);
 

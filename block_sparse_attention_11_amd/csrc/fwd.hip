@@ -40,10 +40,12 @@
 // exp2(s - m) with a stale m, so the output accumulators are never rescaled
 // inside the loop (which keeps them in the matrix-core registers).  This is
 // exact as long as later scores exceed m by less than 2^64 (no overflow of P,
-// O or l in fp32); an item where some score rises further sets a flag and is
-// recomputed by the second kernel, which raises the maximum whenever a
+// O or l in fp32); an item where some score rises further is marked in its first
+// LSE row and recomputed by the second kernel, which raises the maximum whenever a
 // sub-tile exceeds it by more than 2^8 and rescales O and l then.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "device.hpp"
 #include "tile_common.hpp"
@@ -58,6 +60,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTilePages = 4;
 constexpr float kLimit = 64.0f;  // fast kernel: largest rise of a score over the fixed maximum (base 2)
 constexpr float kRaise = 8.0f;   // exact kernel: raise the maximum only past this margin (base 2)
+// First LSE row of an item the fast kernel leaves to the exact kernel: a quiet NaN no
+// real result produces (LSE is finite or -inf).
+constexpr uint32_t kRedoMark = 0x7FC0DA0Au;
+constexpr int kExactBlocks = 512;  // exact re-run grid cap: 2 workgroups per CU
 
 // Page of wave j in tile t of a walk (one scalar load).
 __device__ __forceinline__ int32_t fwd_page(c_i32 *walk, int t, int j) { return walk[kTilePages * t + j]; }
@@ -75,10 +81,9 @@ struct FwdLds {
   int redo_any;
 };
 
-// One work item of route ROUTE: `item` indexes the route's item array, `slot` is the
-// workgroup's position in the launch (its entry of the redo flags).
+// One work item of route ROUTE: `item` indexes the route's item array.
 template <int D, int ROUTE, bool EXACT>
-__device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, int slot, FwdLds<D> &lds) {
+__device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D> &lds) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int DS = D / 16;         // MFMA k-steps over the head dimension
   constexpr int ND = D / 32;         // 32-wide output blocks over the head dimension
@@ -96,8 +101,6 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, int slot
   float(&stat_l)[kWaves][32] = lds.stat_l;
   int &redo_any = lds.redo_any;
 
-  if (EXACT && args.redo[slot] == 0) return;
-
   char *kbuf0 = smem, *kbuf1 = smem + TILE_BYTES, *vbuf0 = smem + 2 * TILE_BYTES, *vbuf1 = smem + 3 * TILE_BYTES;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,7 +111,9 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, int slot
   const FwdItem it = args.items[item];
   const int bh = it.bh;
   const int cq = it.c_q;
-  const int n_tiles = it.walk_len / kTilePages;
+  // 4-page tiles up to the last one holding a real page; the all-dummy tiles of the
+  // walk's step padding are neither copied nor computed
+  const int n_tiles = (it.n_pages + kTilePages - 1) / kTilePages;
   const int n_sub = n_tiles * NH;
   const int full_tiles = it.n_full / kTilePages;  // tiles inside the fully valid prefix
   const int qg = wave % NQG;
@@ -448,10 +453,12 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, int slot
   }
   wait_lgkm0();
   barrier();
-  if (!EXACT) {
-    const int redo = redo_any;
-    if (tid == 0) args.redo[slot] = redo;
-    if (redo) return;  // the exact kernel writes this item
+  const int64_t orow0 = (int64_t)bh * args.seq_q + 128 * it.q;
+  if (!EXACT && redo_any) {
+    // the exact kernel writes this item; the mark lives in the caller's own LSE row,
+    // so concurrent calls on one plan (different outputs) never see each other's
+    if (tid == 0) args.lse[orow0] = __builtin_bit_cast(float, kRedoMark);
+    return;
   }
   // merged maximum and sum of query row qr (0..31) of query group q_g
   auto merged = [&](int q_g, int qr, float *mt_out) __attribute__((always_inline)) -> float {
@@ -487,7 +494,6 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, int slot
   wait_lgkm0();
   barrier();
 
-  const int64_t orow0 = (int64_t)bh * args.seq_q + 128 * it.q;
   const int vrows = cq < M ? cq : M;
   constexpr int GROUPS = D / 8;
   for (int u = tid; u < 128 * GROUPS; u += kThreads) {
@@ -529,22 +535,59 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, int slot
 // Both routes in one launch: workgroups [0, n128) take the M128 x N128 items, the rest
 // the M64 x N256 items (and the cleanup items of empty blocks), so the shorter M64 items
 // fill the end of the M128 work instead of starting after its last workgroup.
-template <int D, bool EXACT>
+template <int D>
 __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs a128, FwdArgs a64) {
   __shared__ FwdLds<D> lds;
   const int b = blockIdx.x;
-  if (b < a128.n_items) fwd_item<D, 128, EXACT>(a128, b, b, lds);
-  else fwd_item<D, 64, EXACT>(a64, b - a128.n_items, b, lds);
+  if (b < a128.n_items) fwd_item<D, 128, false>(a128, b, lds);
+  else fwd_item<D, 64, false>(a64, b - a128.n_items, lds);
+}
+
+// Exact re-run over the items the fast kernel marked (first LSE row = kRedoMark): a small
+// grid whose workgroups check 256 items at a time (one per thread) and run the marked
+// ones, so a launch with nothing marked costs a few microseconds.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void kpage_fwd_exact_kernel(FwdArgs a128, FwdArgs a64) {
+  __shared__ FwdLds<D> lds;
+  __shared__ uint64_t marked[kWaves];
+  const int n = a128.n_items + a64.n_items;
+  const int tid = threadIdx.x;
+  for (int base = blockIdx.x * kThreads; base < n; base += gridDim.x * kThreads) {
+    const int i = base + tid;
+    bool mark = false;
+    if (i < n) {
+      const FwdItem it = i < a128.n_items ? a128.items[i] : a64.items[i - a128.n_items];
+      mark = __builtin_bit_cast(uint32_t, a128.lse[(int64_t)it.bh * a128.seq_q + 128 * it.q]) == kRedoMark;
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(mark);
+    if ((tid & 63) == 0) marked[tid >> 6] = m;
+    __syncthreads();
+    for (int w = 0; w < kWaves; ++w) {
+      const uint64_t mw = marked[w];
+      uint64_t left = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(mw >> 32)) << 32) |
+                      __builtin_amdgcn_readfirstlane((uint32_t)mw);
+      while (left) {
+        const int j = base + 64 * w + __builtin_ctzll(left);
+        left &= left - 1;
+        if (j < a128.n_items) fwd_item<D, 128, true>(a128, j, lds);
+        else fwd_item<D, 64, true>(a64, j - a128.n_items, lds);
+        __syncthreads();  // the next item reuses the LDS
+      }
+    }
+    __syncthreads();  // `marked` is rewritten by the next round
+  }
 }
 
 template <int D>
 void launch_d(const FwdArgs &a128, const FwdArgs &a64, hipStream_t stream, LaunchTimer *timer) {
   dim3 grid(a128.n_items + a64.n_items), block(kThreads);
   if (timer) timer->before(0, stream);
-  hipLaunchKernelGGL((kpage_fwd_kernel<D, false>), grid, block, 0, stream, a128, a64);
+  hipLaunchKernelGGL((kpage_fwd_kernel<D>), grid, block, 0, stream, a128, a64);
   if (timer) timer->after(0, stream);
+  const int n = a128.n_items + a64.n_items;
+  const int exact_blocks = std::min((n + kThreads - 1) / kThreads, kExactBlocks);
   if (timer) timer->before(1, stream);
-  hipLaunchKernelGGL((kpage_fwd_kernel<D, true>), grid, block, 0, stream, a128, a64);
+  hipLaunchKernelGGL((kpage_fwd_exact_kernel<D>), dim3(exact_blocks), block, 0, stream, a128, a64);
   if (timer) timer->after(1, stream);
 }
 

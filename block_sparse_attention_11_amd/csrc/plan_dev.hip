@@ -273,8 +273,8 @@ __global__ void k_queue_out(const unsigned long long *keys, int n, int n_q, int3
 // launch items in (bh, q) order per route; the Q64 list also carries the cleanup items
 // of empty query blocks after its own items
 __global__ __launch_bounds__(kScanThreads) void k_items(DevProblem p, const int32_t *route, const int32_t *nfull,
-                                                        const int64_t *walk_ptr, const Summary *sum, FwdItem *items128,
-                                                        FwdItem *items64) {
+                                                        const int32_t *unpadded, const int64_t *walk_ptr,
+                                                        const Summary *sum, FwdItem *items128, FwdItem *items64) {
   __shared__ int64_t lds[kScanThreads];
   const int64_t n = int64_t(p.batch) * p.heads * p.n_q;
   const int64_t n128 = sum->n_q128, n64 = sum->n_q64, nall64 = sum->n_q64 + sum->n_zero;
@@ -303,6 +303,7 @@ __global__ __launch_bounds__(kScanThreads) void k_items(DevProblem p, const int3
       x.bh = bh;
       x.q = q;
       x.n_full = nfull[i];
+      x.n_pages = unpadded[i];
       x.c_q = cq;
       if (r == 128) items128[launch_position(p128, n128, p.xcd_chunk)] = x;
       else if (r == 64) items64[launch_position(p64, nall64, p.xcd_chunk)] = x;
@@ -383,17 +384,14 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
   t->q128_queue = a32(2 * int64_t(h.n_q128));
   t->items128 = static_cast<FwdItem *>(alloc(size_t(std::max(h.n_q128, 1)) * sizeof(FwdItem)));
   t->items64 = static_cast<FwdItem *>(alloc(size_t(std::max(h.n_q64 + h.n_zero, 1)) * sizeof(FwdItem)));
-  const int n_redo = std::max(h.n_q128 + h.n_q64 + h.n_zero, 1);  // one flag per workgroup of the forward launch
-  t->redo = a32(n_redo);
   unsigned long long *keys = static_cast<unsigned long long *>(alloc(size_t(std::max<int64_t>(BHQ, 1)) * 8 * 3));
   if (!t->walk || !t->pages || !t->valid || !t->q64_queue || !t->q128_queue || !t->items128 || !t->items64 ||
-      !t->redo || !keys) {
+      !keys) {
     *err = "device allocation failed while planning";
     return KPAGE_ERR_OOM;
   }
   hipLaunchKernelGGL(k_fill_walks, dim3(blocks_for(GQ, TB)), dim3(TB), 0, st, p, t->route, t->walk_ptr, t->walk,
                      t->pages, t->valid);
-  hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(n_redo, TB)), dim3(TB), 0, st, t->redo, int64_t(n_redo), 0);
   // queues: one radix sort per route over all (bh, q) keys
   unsigned long long *k64 = keys, *k128 = keys + BHQ, *ksorted = keys + 2 * BHQ;
   hipLaunchKernelGGL(k_queue_keys, dim3(blocks_for(BHQ, TB)), dim3(TB), 0, st, p, t->route, t->unpadded, k64, k128);
@@ -414,7 +412,7 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
     hipLaunchKernelGGL(k_queue_out, dim3(blocks_for(h.n_q128, TB)), dim3(TB), 0, st, ksorted, h.n_q128, p.n_q,
                        t->q128_queue);
   }
-  hipLaunchKernelGGL(k_items, dim3(1), dim3(kScanThreads), 0, st, p, t->route, t->nfull, t->walk_ptr, d_sum,
+  hipLaunchKernelGGL(k_items, dim3(1), dim3(kScanThreads), 0, st, p, t->route, t->nfull, t->unpadded, t->walk_ptr, d_sum,
                      t->items128, t->items64);
   KP_CHECK(hipGetLastError());
   KP_CHECK(hipMemcpyAsync(&h, d_sum, sizeof(Summary), hipMemcpyDeviceToHost, st));

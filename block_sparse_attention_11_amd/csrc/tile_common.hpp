@@ -111,18 +111,17 @@ __device__ __forceinline__ int xor_imm(int x) {
 // has landed, even when the read is of the other buffer of a double-buffered pair: the
 // prefetch of the next step would then serialise with the current one.  Every caller
 // orders copies and reads itself: wait_vmcnt, then a workgroup barrier, before a buffer
-// written by copies is read.  M0 (the copy's LDS base) is written here; the kernels
-// that use these copies issue no other instruction that reads M0.
+// written by copies is read.  M0 (the copy's LDS base) is an input operand of the asm,
+// so the compiler writes it and knows it is in use; the s_nop covers the wait state
+// between that write and the copy reading M0.
 template <int SIZE>
 __device__ __forceinline__ void lds_dma(const char *sbase, uint32_t voff, lds_char *lds) {
   static_assert(SIZE == 4 || SIZE == 16, "direct-to-LDS copies of 4 or 16 bytes per lane");
   const uint32_t m0 = (uint32_t)(uintptr_t)lds;
   if constexpr (SIZE == 16)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(m0), "v"(voff), "s"(sbase)
-                 : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" : : "s"(m0), "v"(voff), "s"(sbase)
-                 : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
 
 template <int SWZ, int CH>

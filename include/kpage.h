@@ -145,6 +145,11 @@ kpage_status kpage_plan_upload(kpage_plan_t *plan, void *stream);
  * compacted copy is written to device memory.  Rows outside the valid prefix
  * of a block, blocks with c_q = 0 and rows with no valid key get O = 0 and
  * LSE = -inf.  q, k, v, o: bf16 device pointers; lse: fp32 device pointer.
+ * Two launches on `stream`: the fixed-maximum pass, then an exact re-run of the
+ * items it marked, the mark being a NaN written into the item's first LSE row
+ * (overwritten by the re-run).  A plan holds no per-call state, so calls on one
+ * plan may run concurrently on several streams as long as their o and lse
+ * buffers differ.
  */
 kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, const void *v,
                             void *o, float *lse, float softmax_scale, void *stream);
@@ -165,10 +170,11 @@ kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes);
  * forward page walks (each query block recomputes its scores), so every output
  * row is written by exactly one workgroup and all three gradients are
  * deterministic.  The backward metadata is built on the first call (lazily,
- * section 3.4).  o and lse are the forward outputs: a query row with
- * LSE = -inf (invalid, or without a valid key) contributes nothing, which is how
- * query-block sizes reach the kernels.  Every row of Q and dO must hold finite
- * values, padded rows included (they meet zero weights inside the products).
+ * section 3.4).  o and lse are the forward outputs; query rows past c_q of
+ * their block (the plan's query sizes, section 3.4.1) are ignored whatever o,
+ * lse and dO hold there, and a valid row with LSE = -inf (no valid key)
+ * contributes nothing.  Every row of Q and dO must hold finite values, padded
+ * rows included (they meet zero weights inside the products).
  * workspace is a caller-owned device buffer of at least
  * kpage_bwd_workspace_size() bytes, 4-byte aligned (16-byte aligned when
  * q_group > 0); at most 2^29 query rows
@@ -232,7 +238,7 @@ enum {
   KPAGE_K_FWD = 0,       /* forward, both routes in one launch (M128 x N128 items, */
                          /* then M64 x N256 items and empty-block cleanup)         */
   KPAGE_K_FWD_EXACT = 1, /* forward re-run with online rescaling of the items the  */
-                         /* fixed-maximum pass flagged (one launch, both routes)   */
+                         /* fixed-maximum pass marked (one launch, both routes)    */
   KPAGE_K_BWD_PRE = 2,   /* rowsum(dO * O) and LSE * log2(e) per query row         */
   KPAGE_K_BWD_ZERO = 3,  /* dK/dV pages outside every block footprint              */
   KPAGE_K_BWD_KV = 4,    /* K/V-owned pass: dK, dV                                  */

@@ -10,19 +10,34 @@ import bench
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "block_sparse_attention_11_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def test_traffic_reported_only_for_its_workload_and_sources(tmp_path, monkeypatch):
+    """A counter record is used only for its own workload and while the kernel's sources
+    hash to the value stored with it (the committed record itself may predate the
+    current sources; then bench reports traffic as null)."""
     with open(bench.TRAFFIC_FILE) as f:
         rec = json.load(f)
     wl = int(rec["workload_id"])
+    fresh = dict(rec, kernels={k: dict(v, sources_sha256=_sources_sha256(v["sources"]))
+                               for k, v in rec["kernels"].items()})
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(fresh))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
     for kernel, entry in rec["kernels"].items():
         assert bench._measured_traffic(kernel, wl) == entry["bytes_per_launch"], kernel
         assert bench._measured_traffic(kernel, wl + 1) is None, kernel
     assert bench._measured_traffic("no_such_kernel", wl) is None
     # a record whose source hash no longer matches the sources is not used
     stale = dict(rec, kernels={k: dict(v, sources_sha256="0" * 64) for k, v in rec["kernels"].items()})
-    path = tmp_path / "traffic.json"
     path.write_text(json.dumps(stale))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
     for kernel in rec["kernels"]:
         assert bench._measured_traffic(kernel, wl) is None, kernel
 

@@ -150,3 +150,27 @@ def test_bwd_gradients_are_deterministic():
     b = gpu_fwd_bwd(w, w.q, w.k, w.v, w.do, plan=plan)
     for name, x, y in zip(("dQ", "dK", "dV"), a, b):
         assert np.array_equal(x, y), name
+
+
+def test_bwd_ignores_padded_lse_o_and_do_rows():
+    """Finite garbage in the padded query rows of LSE, O and dO (rows past c_q of a block)
+    leaves every gradient bit-identical: the backward takes query validity from the plan's
+    query sizes, not from the caller's LSE."""
+    w = make_workload(3, heads=[0, 1], with_do=True)
+    dev = torch.device("cuda", 0)
+    plan = K.kpage_plan(w)
+    q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
+    o, lse = K.attn_fwd(plan, q, k, v, w.scale)
+    _say("[bwd] garbage in padded LSE / O / dO rows")
+    clean = [x.clone() for x in K.attn_bwd(plan, q, k, v, o, lse, do, w.scale)]
+    rows = torch.cat([torch.arange(128 * b + int(c), 128 * b + 128) for b, c in enumerate(w.q_valid[0]) if c < 128])
+    assert rows.numel() > 0
+    g = torch.Generator().manual_seed(9)
+    o2, lse2, do2 = o.clone(), lse.clone(), do.clone()
+    lse2[:, :, rows] = (10 * torch.randn(lse2[:, :, rows].shape, generator=g)).to(dev)
+    o2[:, :, rows] = (100 * torch.randn(o2[:, :, rows].shape, generator=g)).to(torch.bfloat16).to(dev)
+    do2[:, :, rows] = (100 * torch.randn(do2[:, :, rows].shape, generator=g)).to(torch.bfloat16).to(dev)
+    dirty = K.attn_bwd(plan, q, k, v, o2, lse2, do2, w.scale)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), clean, dirty):
+        assert torch.equal(a, b), name

@@ -270,3 +270,29 @@ def test_fwd_rejects_bad_arguments_before_launch():
         K.attn_fwd(plan, q, k, v, -1.0)
     with pytest.raises(K.KpageError):
         K.attn_fwd(plan, q[:, :1].contiguous(), k, v, w.scale)
+
+
+def test_fwd_two_streams_share_one_plan():
+    """Two forward calls on one plan, on two streams with different outputs, overlap safely:
+    the exact re-run's marks live in each call's own LSE rows.  Uses the score-rise
+    problem, where every item goes through the exact re-run."""
+    p, q, k, v, _ = rising_scores_problem(128)
+    dev = torch.device("cuda", 0)
+    plan = K.kpage_plan(p)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    ref_o, ref_l = K.attn_fwd(plan, qd, kd, vd, p.scale)
+    torch.cuda.synchronize()
+    _say("[fwd] two streams, one plan")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for s in (s1, s2):
+        with torch.cuda.stream(s):
+            o = torch.empty_like(qd)
+            lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+            outs.append((o, lse))
+    for _ in range(4):
+        for s, (o, lse) in zip((s1, s2), outs):
+            K.kpage_attn_fwd(plan, qd, kd, vd, o, lse, p.scale, stream=s)
+    torch.cuda.synchronize()
+    for o, lse in outs:
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
