@@ -33,6 +33,7 @@ TABLES = {
 
 EXPORTED_SYMBOLS = (
     "kpage_plan", "kpage_plan_device", "kpage_plan_upload", "kpage_attn_fwd", "kpage_bwd_workspace_size", "kpage_attn_bwd",
+    "kpage_attn_bwd_noalloc",
     "kpage_plan_stats", "kpage_plan_export", "kpage_plan_destroy", "kpage_timing_enable", "kpage_timing_read",
     "kpage_last_error", "kpage_select_workspace_size", "kpage_select_topk", "kpage_select_top_p_workspace_size",
     "kpage_select_top_p",
@@ -104,6 +105,7 @@ def lib() -> ctypes.CDLL:
         L.kpage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp]
         L.kpage_bwd_workspace_size.argtypes = [vp, ctypes.POINTER(sz)]
         L.kpage_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, f32, vp]
+        L.kpage_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp]
         L.kpage_plan_stats.argtypes = [vp, ctypes.POINTER(KpagePairStats)]
         L.kpage_plan_export.argtypes = [vp, i32, vp, ctypes.POINTER(sz)]
         L.kpage_timing_enable.argtypes = [vp, i32]
@@ -285,6 +287,22 @@ def kpage_attn_bwd(plan: Plan, q, k, v, o, lse, do, dq, dk, dv, workspace, softm
             _dev(dv, plan.seq_kv, plan, "dv", bf))
     _check(lib().kpage_attn_bwd(plan.handle, *args, workspace.data_ptr(), ctypes.c_size_t(ws_bytes),
                                 ctypes.c_float(softmax_scale), _stream_ptr(stream)))
+
+
+# the static scratch of kpage_attn_bwd_noalloc (KPAGE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def kpage_attn_bwd_noalloc(plan: Plan, q, k, v, o, lse, do, dq, dk, dv, softmax_scale: float, stream=None):
+    """kpage_attn_bwd with the library's static device scratch as workspace: no allocation."""
+    import torch
+    bf = torch.bfloat16
+    args = (_dev(q, plan.seq_q, plan, "q", bf), _dev(k, plan.seq_kv, plan, "k", bf),
+            _dev(v, plan.seq_kv, plan, "v", bf), _dev(o, plan.seq_q, plan, "o", bf),
+            _dev(lse, plan.seq_q, plan, "lse", torch.float32), _dev(do, plan.seq_q, plan, "do", bf),
+            _dev(dq, plan.seq_q, plan, "dq", bf), _dev(dk, plan.seq_kv, plan, "dk", bf),
+            _dev(dv, plan.seq_kv, plan, "dv", bf))
+    _check(lib().kpage_attn_bwd_noalloc(plan.handle, *args, ctypes.c_float(softmax_scale), _stream_ptr(stream)))
 
 
 # ---- convenience wrappers (allocation of outputs only) ----

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -693,22 +694,11 @@ kpage_status kpage_bwd_workspace_size(kpage_plan_t *plan, size_t *bytes) {
   return KPAGE_OK;
 }
 
-kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, const void *v, const void *o,
-                            const float *lse, const void *dO, void *dq, void *dk, void *dv, void *workspace,
-                            size_t workspace_bytes, float softmax_scale, void *stream) {
-  if (!plan) return fail(KPAGE_ERR_INVALID, "plan is NULL");
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
-    return fail(KPAGE_ERR_INVALID, "tensor or workspace pointer is NULL");
-  if (bad_scale(softmax_scale)) return fail(KPAGE_ERR_INVALID, "softmax_scale must be positive and finite");
-  size_t need = 0;
-  kpage_status s = kpage_bwd_workspace_size(plan, &need);
-  if (s != KPAGE_OK) return s;
-  if (workspace_bytes < need) return fail(KPAGE_ERR_INVALID, "workspace smaller than kpage_bwd_workspace_size()");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  s = guarded([&] { return ensure_forward_on_device(plan, st); });  // the dQ pass walks the forward tables
-  if (s != KPAGE_OK) return s;
-  s = guarded([&] { return ensure_backward_on_device(plan, st); });
-  if (s != KPAGE_OK) return s;
+// Backward launches on device tables that already exist, with `workspace` (device
+// memory of at least the workspace size) holding lse2, D and the Q-group partials.
+static kpage_status launch_backward(kpage_plan_t *plan, const void *q, const void *k, const void *v, const void *o,
+                                    const float *lse, const void *dO, void *dq, void *dk, void *dv, void *workspace,
+                                    float softmax_scale, hipStream_t st) {
   const Problem &P = plan->P;
   const size_t rows = size_t(P.batch) * P.heads * size_t(P.seq_q);
   // the K/V pass addresses delta as lse2 plus a 32-bit byte offset
@@ -751,6 +741,76 @@ kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, co
   hipError_t e = launch_bwd(a, P.head_dim, st, plan->timer);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return KPAGE_OK;
+}
+
+kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, const void *v, const void *o,
+                            const float *lse, const void *dO, void *dq, void *dk, void *dv, void *workspace,
+                            size_t workspace_bytes, float softmax_scale, void *stream) {
+  if (!plan) return fail(KPAGE_ERR_INVALID, "plan is NULL");
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv || !workspace)
+    return fail(KPAGE_ERR_INVALID, "tensor or workspace pointer is NULL");
+  if (bad_scale(softmax_scale)) return fail(KPAGE_ERR_INVALID, "softmax_scale must be positive and finite");
+  size_t need = 0;
+  kpage_status s = kpage_bwd_workspace_size(plan, &need);
+  if (s != KPAGE_OK) return s;
+  if (workspace_bytes < need) return fail(KPAGE_ERR_INVALID, "workspace smaller than kpage_bwd_workspace_size()");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s = guarded([&] { return ensure_forward_on_device(plan, st); });  // the dQ pass walks the forward tables
+  if (s != KPAGE_OK) return s;
+  s = guarded([&] { return ensure_backward_on_device(plan, st); });
+  if (s != KPAGE_OK) return s;
+  return launch_backward(plan, q, k, v, o, lse, dO, dq, dk, dv, workspace, softmax_scale, st);
+}
+
+// ---- backward without allocation: the workspace is a static device array ----
+//
+// `scratch` is a file-scope device array; host code never passes its name to a kernel
+// (on the host the name is only a stand-in for the symbol).  Its device address is
+// looked up once per device with that device current and kept in g_scratch_ptr.
+static __device__ __align__(256) char scratch[KPAGE_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices];
+
+static kpage_status scratch_on_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KPAGE_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KPAGE_OK;
+}
+
+kpage_status kpage_attn_bwd_noalloc(kpage_plan_t *plan, const void *q, const void *k, const void *v, const void *o,
+                                    const float *lse, const void *dO, void *dq, void *dk, void *dv,
+                                    float softmax_scale, void *stream) {
+  if (!plan) return fail(KPAGE_ERR_INVALID, "plan is NULL");
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return fail(KPAGE_ERR_INVALID, "tensor pointer is NULL");
+  if (bad_scale(softmax_scale)) return fail(KPAGE_ERR_INVALID, "softmax_scale must be positive and finite");
+  const Problem &P = plan->P;
+  const size_t rows = size_t(P.batch) * P.heads * size_t(P.seq_q);
+  size_t need = 2 * rows * 4;
+  if (need > KPAGE_NOALLOC_SCRATCH_BYTES)
+    return fail(KPAGE_ERR_INVALID, "the backward needs " + std::to_string(need) + " bytes of workspace, more than the " +
+                                       std::to_string(KPAGE_NOALLOC_SCRATCH_BYTES) + "-byte static scratch");
+  if (!plan->fwd_on_device || !plan->bwd_on_device)
+    return fail(KPAGE_ERR_INVALID, "the plan's device tables are not built yet: run kpage_attn_bwd once on this plan");
+  if (plan->n_reduce > 0)
+    need = partials_offset(rows) + size_t(plan->n_partials) * 2 * 128 * size_t(P.head_dim) * 4;
+  if (need > KPAGE_NOALLOC_SCRATCH_BYTES)
+    return fail(KPAGE_ERR_INVALID, "the backward needs " + std::to_string(need) + " bytes of workspace, more than the " +
+                                       std::to_string(KPAGE_NOALLOC_SCRATCH_BYTES) + "-byte static scratch");
+  void *ws = nullptr;
+  const kpage_status s = scratch_on_current_device(&ws);
+  if (s != KPAGE_OK) return s;
+  return launch_backward(plan, q, k, v, o, lse, dO, dq, dk, dv, ws, softmax_scale, static_cast<hipStream_t>(stream));
 }
 
 kpage_status kpage_plan_stats(const kpage_plan_t *plan, kpage_pair_stats *out) {

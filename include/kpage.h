@@ -187,6 +187,29 @@ kpage_status kpage_attn_bwd(kpage_plan_t *plan, const void *q, const void *k, co
                             void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
                             float softmax_scale, void *stream);
 
+/*
+ * kpage_attn_bwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same kernels and results
+ * (bit for bit) as kpage_attn_bwd; the workspace is a static device array of
+ * KPAGE_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library, one per device the
+ * library runs on, held until the process ends.  Its device address is looked
+ * up on the first call on each device (the current device must be the
+ * stream's); later calls make no allocation of any kind.
+ * Preconditions: the plan's device tables exist, i.e. kpage_attn_bwd has run
+ * once on this plan (it builds and uploads them); otherwise KPAGE_ERR_INVALID.
+ * A problem whose workspace (kpage_bwd_workspace_size) exceeds 32 MiB, e.g.
+ * more than 4,194,304 query rows (batch * heads * seq_q) with one Q group, is
+ * rejected with KPAGE_ERR_INVALID before any device work.
+ * Every call on one device shares the array and leaves its contents behind
+ * (every byte a call reads it first writes): calls that overlap on one device,
+ * on any streams, race and must be serialised by the caller.
+ */
+#define KPAGE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+kpage_status kpage_attn_bwd_noalloc(kpage_plan_t *plan, const void *q, const void *k, const void *v,
+                                    const void *o, const float *lse, const void *dO,
+                                    void *dq, void *dk, void *dv, float softmax_scale, void *stream);
+
 /* Pair statistics (host memory).  Backward fields are filled once the backward
  * metadata exists (after kpage_attn_bwd or an export of a backward table). */
 kpage_status kpage_plan_stats(const kpage_plan_t *plan, kpage_pair_stats *out);
