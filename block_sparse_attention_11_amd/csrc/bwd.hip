@@ -209,43 +209,78 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
         const int q = 32 * QB + 8 * j4 + 4 * g;
         return *(const __attribute__((address_space(3))) f32x4 *)(stb + ((q >> 4) * 64 + (q & 15)) * 4);
       };
-      // P and dS as packed bf16 pairs (u32x4 [hh] = rows 16 hh .. + 15 of the block):
-      // the A operands of the dV / dK products
-      u32x4 pb[2], sb[2];
-      // Each phase's first two operand reads are issued before the element-wise work
-      // that precedes the phase, so that work hides their LDS latency.
       auto rd_row = [&](const lds_char *t, auto s_c) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
         return lds_read8(t + RB + xor_imm<32 * S>(rd_base));
       };
-      // (A) S = Q K^T, operand reads two k-steps ahead
-      f32x16 sp;
-      {
-        bf16x8 op[DS];
-        op[0] = qpre[0];
-        op[1] = qpre[1];
-        static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
-          constexpr int S = decltype(s_c)::value;
-          if constexpr (S + 2 < DS) op[S + 2] = rd_row(qt, ic<S + 2>{});
-          sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], kreg[S], S == 0 ? f32x16{} : sp, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      }
-      bf16x8 opb[DS];
-      opb[0] = rd_row(gt, ic<0>{});
-      opb[1] = rd_row(gt, ic<1>{});
-      const float nd = -*(const __attribute__((address_space(3))) float *)(stb + (((32 * QB + l32) >> 4) * 64 + 16 +
-                                                                               ((32 * QB + l32) & 15)) * 4);
-      // P = exp2(scale log2e S - lse2)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const f32x4 l4 = lse4(j4);
+      // The block is one stream of MFMAs: S = Q K^T (DS), dP - D = dO V^T - D (DS + 1),
+      // dV += P^T dO and dK += dS^T Q (2 ND each half).  The element-wise work sits
+      // between them where its inputs are ready and its outputs are not yet needed, so a
+      // wave's VALU and MFMA work overlap: the probabilities of group j4 (4 scores per
+      // lane) between the dP MFMAs, the dS of the first 16 queries between the first dV
+      // MFMAs, that of the other 16 between the first dK MFMAs.  Row operands are read
+      // from LDS two MFMAs ahead across the S -> dP boundary, each lse2 group two MFMAs
+      // before its use.
+      // P slice j4 sits after dP MFMA p_at(j4) (-1: right after the S chain, which frees
+      // half of the score registers before the dP chain: the register file has no room
+      // for all of S and dP at once)
+      constexpr int p_at[4] = {-1, -1, DS == 8 ? 2 : 1, DS == 8 ? 5 : 3};
+      f32x16 sp, dp;
+      f32x4 l4[4];
+      float nd = 0.f;
+      u32x4 pb[2], sb[2];  // P and dS as packed bf16 pairs (u32x4 [hh] = rows 16 hh .. + 15)
+      bf16x8 op[2 * DS];   // S chain operands (Q rows), then dP chain operands (dO rows)
+      op[0] = qpre[0];
+      op[1] = qpre[1];
+      auto read_op = [&](auto i_c) __attribute__((always_inline)) {
+        constexpr int I = decltype(i_c)::value;
+        if constexpr (I < DS) op[I] = rd_row(qt, ic<I>{});
+        else if constexpr (I < 2 * DS) op[I] = rd_row(gt, ic<I - DS>{});
+      };
+      // (A) S = Q K^T
+      static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        read_op(ic<S + 2>{});
+        if constexpr (S == DS - 2) nd = -*(const __attribute__((address_space(3))) float *)(
+                                        stb + (((32 * QB + l32) >> 4) * 64 + 16 + ((32 * QB + l32) & 15)) * 4);
+        if constexpr (S == DS - 4) l4[0] = lse4(0);
+        if constexpr (S == DS - 3) l4[1] = lse4(1);
+        sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], kreg[S], S == 0 ? f32x16{} : sp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // P = exp2(scale log2e S - lse2) for score group j4
+      auto p_slice = [&](auto j_c) __attribute__((always_inline)) {
+        constexpr int J4 = decltype(j_c)::value;
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
-          const int r = 4 * j4 + e;
-          pb[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sp[r], c2, -l4[e])),
-                                                      __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r + 1], c2, -l4[e + 1]))));
+          const int r = 4 * J4 + e;
+          pb[r >> 3][(r & 7) >> 1] =
+              pinned(pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sp[r], c2, -l4[J4][e])),
+                               __builtin_amdgcn_exp2f(__builtin_fmaf(sp[r + 1], c2, -l4[J4][e + 1]))));
         }
+      };
+      p_slice(ic<0>{});
+      p_slice(ic<1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      // (B) dP - D = dO V^T - D, with D as one extra k-step (A = -D split into bf16 hi +
+      // lo in k = 0, 1 of lanes 0-31 for query row l32, B = ones), then dS = P (dP - D)
+      // with P as its bf16 value (an extra rounding of the order of dS's own)
+      static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_c)::value;
+        read_op(ic<DS + S + 2>{});
+        if constexpr (S == 0) l4[2] = lse4(2);
+        if constexpr (S == p_at[3] - 2) l4[3] = lse4(3);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[DS + S], vreg[S], S == 0 ? f32x16{} : dp, 0, 0, 0);
+        static_for<4>([&](auto j_c) __attribute__((always_inline)) {
+          if constexpr (p_at[decltype(j_c)::value] == S) p_slice(j_c);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      {
+        const float hi = __builtin_bit_cast(float, pack_bf16(nd, 0.f) << 16);
+        const bf16x8 daug = __builtin_bit_cast(bf16x8, u32x4{g ? 0u : pack_bf16(hi, nd - hi), 0u, 0u, 0u});
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(daug, __builtin_bit_cast(bf16x8, u32x4{ones_lo, 0u, 0u, 0u}), dp,
+                                                     0, 0, 0);
       }
       // zero the P blocks of non-edge (query page, key slot) pairs: pb[hh] holds the
       // rows of page 2 qb + hh of the half-step
@@ -255,54 +290,50 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
           if (!((nib >> (2 * (2 * QB + hh) + khalf)) & 1u)) pb[hh] = u32x4{};
       }
       __builtin_amdgcn_sched_barrier(0);
-      // (B) dP - D = dO V^T - D, with D as one extra k-step (A = -D split into bf16
-      // hi + lo in k = 0, 1 of lanes 0-31 for query row l32, B = ones), then (C)
-      // dS = P (dP - D).  P enters dS as its bf16 value, an extra rounding of the order
-      // of dS's own.
-      f32x16 dp;
-      {
-        const float hi = __builtin_bit_cast(float, pack_bf16(nd, 0.f) << 16);
-        const bf16x8 daug = __builtin_bit_cast(bf16x8, u32x4{g ? 0u : pack_bf16(hi, nd - hi), 0u, 0u, 0u});
-        static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
-          constexpr int S = decltype(s_c)::value;
-          if constexpr (S + 2 < DS) opb[S + 2] = rd_row(gt, ic<S + 2>{});
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opb[S], vreg[S], S == 0 ? f32x16{} : dp, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(daug, __builtin_bit_cast(bf16x8, u32x4{ones_lo, 0u, 0u, 0u}), dp,
-                                                     0, 0, 0);
-      }
-      // (D) operands: columns of dO and Q, transposed reads one product ahead
-      constexpr int NOPS = 2 * ND;
-      bf16x8 gt_op[NOPS], qt_op[NOPS];
-      auto rdt = [&](auto j_c) __attribute__((always_inline)) {
-        constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
-        constexpr int RH = RB + 16 * HH * D * 2;
-        const int oa = xor_imm<64 * N>(tr_base);
-        const int ob = xor_imm<64 * (N ^ 1)>(tr_base);
-        gt_op[J] = tr_read8(gt + RH + oa, gt + RH + 8 * D * 2 + ob);
-        qt_op[J] = tr_read8(qt + RH + oa, qt + RH + 8 * D * 2 + ob);
+      // (C) dV += P^T dO and dK += dS^T Q over these 32 query rows, in the operand order
+      // dV (hh 0), dK (hh 0), dV (hh 1), dK (hh 1); B operands = columns of dO and Q,
+      // transposed reads one product ahead.  The next query block's first Q rows are
+      // read during the last products.
+      constexpr int NOPS = 4 * ND;
+      bf16x8 top[NOPS];
+      // operand i: tile (dO for even phase, Q for odd), hh = i / (2 ND), n = i % ND
+      auto rdt = [&](auto i_c) __attribute__((always_inline)) {
+        constexpr int I = decltype(i_c)::value;
+        if constexpr (I < NOPS) {
+          constexpr int PH = I / ND, N = I % ND, HH = PH / 2;
+          constexpr int RH = RB + 16 * HH * D * 2;
+          const lds_char *t = (PH & 1) ? qt : gt;
+          top[I] = tr_read8(t + RH + xor_imm<64 * N>(tr_base), t + RH + 8 * D * 2 + xor_imm<64 * (N ^ 1)>(tr_base));
+        }
+      };
+      auto ds_pair = [&](auto r_c) __attribute__((always_inline)) {
+        constexpr int R = decltype(r_c)::value;
+        const uint32_t w = pb[R >> 3][(R & 7) >> 1];
+        sb[R >> 3][(R & 7) >> 1] = pinned(pack_bf16(__builtin_bit_cast(float, w << 16) * dp[R],
+                                                    __builtin_bit_cast(float, w & 0xFFFF0000u) * dp[R + 1]));
       };
       rdt(ic<0>{});
+      rdt(ic<1>{});
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const uint32_t w = pb[r >> 3][(r & 7) >> 1];
-        sb[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(__builtin_bit_cast(float, w << 16) * dp[r],
-                                                    __builtin_bit_cast(float, w & 0xFFFF0000u) * dp[r + 1]));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // (D) dV += P^T dO and dK += dS^T Q over these 32 query rows; the next query
-      // block's first Q rows are read during the last products
-      static_for<NOPS>([&](auto j_c) __attribute__((always_inline)) {
-        constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
-        if constexpr (J + 1 < NOPS) rdt(ic<J + 1>{});
-        if constexpr (QB == 0 && J == NOPS - 1) {
+      static_for<NOPS>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int I = decltype(i_c)::value;
+        constexpr int PH = I / ND, N = I % ND, HH = PH / 2;
+        rdt(ic<I + 2>{});
+        if constexpr (QB == 0 && I == NOPS - 2) {
           qpre[0] = lds_read8(qt + RB + 32 * D * 2 + xor_imm<0>(rd_base));
           qpre[1] = lds_read8(qt + RB + 32 * D * 2 + xor_imm<32>(rd_base));
         }
-        dv[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pb[HH]), gt_op[J], dv[N], 0, 0, 0);
-        dk[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sb[HH]), qt_op[J], dk[N], 0, 0, 0);
+        if constexpr ((PH & 1) == 0)
+          dv[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pb[HH]), top[I], dv[N], 0, 0, 0);
+        else
+          dk[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sb[HH]), top[I], dk[N], 0, 0, 0);
+        // dS of rows 16 hh .. + 15 (4 pairs) during the phase before its first use:
+        // hh 0 during dV (hh 0), hh 1 during dK (hh 0)
+        if constexpr (PH < 2) {
+          constexpr int HHS = PH;  // rows being computed
+          if constexpr (ND == 4) ds_pair(ic<8 * HHS + 2 * N>{});
+          else { ds_pair(ic<8 * HHS + 4 * N>{}); ds_pair(ic<8 * HHS + 4 * N + 2>{}); }
+        }
         __builtin_amdgcn_sched_barrier(0);
       });
     });
