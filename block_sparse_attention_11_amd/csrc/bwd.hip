@@ -483,98 +483,112 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
   const int trk = keyoff * D * 2 + chunk_off<kSwzBoth, D>(4 * g + (sl >> 2), 2 * (mgrp & 1) + ((sl & 3) >> 1)) +
                   (sl & 1) * 8;
 
-  auto sub_tile = [&](auto buf_c, auto h_c, int u, bool masked) __attribute__((always_inline)) {
+  // One 32-key sub-tile as one MFMA stream: S^T = K Q^T (DS), dP^T - D (DS + 1),
+  // dQ^T += K^T dS^T (2 ND).  The probabilities of score group j4 (4 per lane) are
+  // computed between the dP MFMAs (S is complete by then), dS of the first 16 keys
+  // before the dQ MFMAs and that of the other 16 between the first half of them, so a
+  // wave's VALU work overlaps its own MFMAs.  K and V row operands stream two MFMAs
+  // ahead across the S -> dP boundary, the transposed K operands one ahead.
+  // MASKED: invalid key rows (validity word of the sub-tile) get P = 0 (a select, not a
+  // product: the P of a padded key row may be inf).
+  auto sub_tile = [&](auto buf_c, auto h_c, auto masked_c, int u) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_c)::value, H = decltype(h_c)::value;
+    constexpr bool MASKED = decltype(masked_c)::value;
     constexpr int RB = 32 * H * D * 2;  // byte offset of the sub-tile in the wave's key range
     const lds_char *kt = (const lds_char *)smem + BUF * HTILE + RB;
     const lds_char *vt = (const lds_char *)smem + (2 + BUF) * HTILE + RB;
+    // P slice j4 after dP MFMA p_at[j4]
+    constexpr int p_at[4] = {DS == 8 ? 1 : 0, DS == 8 ? 3 : 1, DS == 8 ? 5 : 2, DS == 8 ? 7 : 3};
     f32x16 s_acc, dp_acc;
-    {
-      bf16x8 op[DS];
-      auto rd = [&](auto s_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_c)::value;
-        op[S] = lds_read8(kt + xor_imm<32 * S>(rdk));
-      };
-      rd(ic<0>{});
-      rd(ic<1>{});
-      static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_c)::value;
-        if constexpr (S + 2 < DS) rd(ic<S + 2>{});
-        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], qreg[S], S == 0 ? f32x16{} : s_acc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    }
-    {
-      bf16x8 op[DS];
-      auto rd = [&](auto s_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_c)::value;
-        op[S] = lds_read8(vt + xor_imm<32 * S>(rdv));
-      };
-      rd(ic<0>{});
-      rd(ic<1>{});
-      static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
-        constexpr int S = decltype(s_c)::value;
-        if constexpr (S + 2 < DS) rd(ic<S + 2>{});
-        dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], greg[S], S == 0 ? f32x16{} : dp_acc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(one_aug, nd_aug, dp_acc, 0, 0, 0);
-    }
-    // key row of register r: 8 (r / 4) + 4 g + r % 4 of the sub-tile; its validity
-    // bit in the sub-tile's word (two 16-bit page masks): (r % 4) + 8 ((r / 4) % 2) +
-    // 16 (r / 8) after a shift by 4 g
-    // (a select, not a product: the P of a padded key row may be inf)
-    u32x4 ds[2];
-    if (masked) {
-      const uint32_t word = vwords[2 * u + ((keyoff + 32 * H) >> 5)] >> (4 * g);
+    bf16x8 op[2 * DS];
+    auto read_op = [&](auto i_c) __attribute__((always_inline)) {
+      constexpr int I = decltype(i_c)::value;
+      if constexpr (I < DS) op[I] = lds_read8(kt + xor_imm<32 * I>(rdk));
+      else if constexpr (I < 2 * DS) op[I] = lds_read8(vt + xor_imm<32 * (I - DS)>(rdv));
+    };
+    uint32_t word = 0;
+    if constexpr (MASKED) word = vwords[2 * u + ((keyoff + 32 * H) >> 5)] >> (4 * g);
+    read_op(ic<0>{});
+    read_op(ic<1>{});
+    static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_c)::value;
+      read_op(ic<S + 2>{});
+      s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], qreg[S], S == 0 ? f32x16{} : s_acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // probabilities in place of the scores; key row of register r: 8 (r / 4) + 4 g +
+    // r % 4 of the sub-tile, its validity bit in the sub-tile's word (two 16-bit page
+    // masks): (r % 4) + 8 ((r / 4) % 2) + 16 (r / 8) after the shift by 4 g
+    auto p_slice = [&](auto j_c) __attribute__((always_inline)) {
+      constexpr int J4 = decltype(j_c)::value;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float pp[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int bit = ((r + e) & 3) + 8 * (((r + e) >> 2) & 1) + 16 * ((r + e) >> 3);
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r + e], c2, nlse2));
-          pp[e] = ((word >> bit) & 1u) ? p * dp_acc[r + e] : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * J4 + e;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c2, nlse2));
+        if constexpr (MASKED) {
+          const int bit = (r & 3) + 8 * ((r >> 2) & 1) + 16 * (r >> 3);
+          s_acc[r] = ((word >> bit) & 1u) ? p : 0.f;
+        } else {
+          s_acc[r] = p;
         }
-        ds[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(pp[0], pp[1]));
       }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c2, nlse2));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r + 1], c2, nlse2));
-        ds[r >> 3][(r & 7) >> 1] = pinned(pack_bf16(p0 * dp_acc[r], p1 * dp_acc[r + 1]));
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    };
+    static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_c)::value;
+      read_op(ic<DS + S + 2>{});
+      dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[DS + S], greg[S], S == 0 ? f32x16{} : dp_acc, 0, 0, 0);
+      static_for<4>([&](auto j_c) __attribute__((always_inline)) {
+        if constexpr (p_at[decltype(j_c)::value] == S) p_slice(j_c);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(one_aug, nd_aug, dp_acc, 0, 0, 0);
     constexpr int NOPS = 2 * ND;
     bf16x8 kop[NOPS];
     auto rdt = [&](auto j_c) __attribute__((always_inline)) {
       constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
-      const lds_char *p = kt + 16 * HH * D * 2;
-      kop[J] = tr_read8(p + xor_imm<64 * N>(trk), p + 8 * D * 2 + xor_imm<64 * (N ^ 1)>(trk));
+      if constexpr (J < NOPS) {
+        const lds_char *p = kt + 16 * HH * D * 2;
+        kop[J] = tr_read8(p + xor_imm<64 * N>(trk), p + 8 * D * 2 + xor_imm<64 * (N ^ 1)>(trk));
+      }
+    };
+    u32x4 ds[2];
+    auto ds_pair = [&](auto r_c) __attribute__((always_inline)) {
+      constexpr int R = decltype(r_c)::value;
+      ds[R >> 3][(R & 7) >> 1] = pinned(pack_bf16(s_acc[R] * dp_acc[R], s_acc[R + 1] * dp_acc[R + 1]));
     };
     rdt(ic<0>{});
+    rdt(ic<1>{});
+    static_for<4>([&](auto i_c) __attribute__((always_inline)) { ds_pair(ic<2 * decltype(i_c)::value>{}); });
+    __builtin_amdgcn_sched_barrier(0);
     static_for<NOPS>([&](auto j_c) __attribute__((always_inline)) {
       constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
-      if constexpr (J + 1 < NOPS) rdt(ic<J + 1>{});
+      rdt(ic<J + 2>{});
       dq[N] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[J], __builtin_bit_cast(bf16x8, ds[HH]), dq[N], 0, 0, 0);
+      // dS of keys 16 .. 31 during the products of keys 0 .. 15
+      if constexpr (HH == 0) {
+        if constexpr (ND == 4) ds_pair(ic<8 + 2 * N>{});
+        else { ds_pair(ic<8 + 4 * N>{}); ds_pair(ic<8 + 4 * N + 2>{}); }
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  auto iter = [&](auto buf_c, auto, int u) __attribute__((always_inline)) {
+  auto iter = [&](auto buf_c, auto masked_c, int u) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_c)::value;
     const int32_t pnext = walk[4 * min(u + 1, n_half - 1) + wave];
     wait_lgkm0();
     wait_vmcnt<0>();
     barrier();  // half-tile u resident; buffer 1 - BUF free
     if (u + 1 < n_half) load_half(pnext, 1 - BUF);
-    const bool masked = u >= full_half;
     // a query group without valid rows computes nothing (its dQ rows are written as 0);
     // the wave still copies its pages and meets every barrier
-    if (!idle) static_for<NH>([&](auto h_c) __attribute__((always_inline)) { sub_tile(buf_c, h_c, u, masked); });
+    if (!idle)
+      static_for<NH>([&](auto h_c) __attribute__((always_inline)) { sub_tile(buf_c, h_c, masked_c, u); });
   };
-  for_range(ic<0>{}, 0, n_half, iter);
+  // half-tiles of the fully valid prefix, then the ones that may hold invalid key rows
+  const int split = min(full_half, n_half);
+  for_range(ic<false>{}, 0, split, iter);
+  for_range(ic<true>{}, split, n_half, iter);
 
   // ---- sum the waves that share query rows, then write dQ = scale * acc (bf16) ----
   wait_vmcnt<0>();
