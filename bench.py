@@ -171,6 +171,44 @@ def _measured_traffic(kernel, workload):
     return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
+def _route_pairs(w):
+    """Useful pairs of the M128 x N128 and M64 x N256 routes (c_q > 64 and 1 <= c_q <= 64)."""
+    import numpy as np
+    BH = w.batch * w.heads
+    slots = range(BH) if w.per_head else [0]
+    out = {"q128": 0, "q64": 0}
+    for g in slots:
+        for q in range(w.n_q):
+            cq = int(w.q_valid[g, q])
+            if cq == 0:
+                continue
+            ks = w.q2k_idx[w.q2k_ptr[g, q]:w.q2k_ptr[g, q + 1]]
+            pairs = cq * int(np.asarray(w.kv_valid[g])[ks].sum())
+            out["q128" if cq > 64 else "q64"] += pairs
+    if not w.per_head:
+        out = {k: v * BH for k, v in out.items()}
+    return out
+
+
+def _route_split(K, plan, step, w, steps=5):
+    """Forward and dQ launches split by route (timing mode 2), after the timed region: per-route
+    time and useful TFLOP/s (4 d per pair for the forward, 6 d for the dQ pass)."""
+    K.kpage_timing_enable(plan, 2)
+    for _ in range(steps):
+        step()
+    kern = {n: K.kpage_timing_read(plan, n) for n in K.KERNELS}
+    K.kpage_timing_enable(plan, False)
+    pairs = _route_pairs(w)
+    d = w.head_dim
+    out = {}
+    for name, key, route, per in (("fwd_q128", "fwd", "q128", 4), ("fwd_q64", "fwd_q64", "q64", 4),
+                                  ("dq_q128", "bwd_dq", "q128", 6), ("dq_q64", "bwd_dq_q64", "q64", 6)):
+        ms = kern[key][0] / max(kern[key][1], 1)
+        out[name] = {"ms": round(ms, 4), "useful_pairs": pairs[route],
+                     "useful_tflops": round(per * d * pairs[route] / (ms * 1e-3) / 1e12, 1) if ms > 0 else None}
+    return out
+
+
 def _copy_calibration(mib):
     import torch
     n = mib << 20
@@ -233,6 +271,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-route-split", action="store_true",
+                    help="skip the extra steps that time the forward and dQ launches per route (profiling runs)")
     ap.add_argument("--workload", type=int, default=WORKLOAD, choices=sorted(WORKLOADS),
                     help="configuration to time (default: the metric's 3D-padded fwd+bwd workload)")
     ap.add_argument("--q-group", type=int, default=0, metavar="N",
@@ -368,6 +408,8 @@ def main():
                     "device_backward_lazy_incl_first_call": round(dev_bwd_plan_ms, 2)},
         "roofline": roofline,
     }
+    if not args.no_route_split:
+        out["routes"] = _route_split(K, plan, step, w)
     if args.workload == 4:
         out["prelude"] = _prelude(K, w, q, k)
     if args.workload == 5:

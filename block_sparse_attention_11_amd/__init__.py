@@ -39,7 +39,8 @@ EXPORTED_SYMBOLS = (
     "kpage_select_top_p",
 )
 
-KERNELS = {"fwd": 0, "fwd_exact": 1, "bwd_pre": 2, "bwd_zero": 3, "bwd_kv": 4, "bwd_dq": 5, "bwd_reduce": 6}
+KERNELS = {"fwd": 0, "fwd_exact": 1, "bwd_pre": 2, "bwd_zero": 3, "bwd_kv": 4, "bwd_dq": 5, "bwd_reduce": 6,
+           "fwd_q64": 7, "bwd_dq_q64": 8}
 
 
 class KpageError(RuntimeError):
@@ -229,8 +230,9 @@ def kpage_plan_export(plan: Plan, table: str) -> np.ndarray:
     return out
 
 
-def kpage_timing_enable(plan: Plan, enable: bool = True):
-    _check(lib().kpage_timing_enable(plan.handle, 1 if enable else 0))
+def kpage_timing_enable(plan: Plan, enable=True):
+    """enable: False/0 off, True/1 on, 2 on with the forward and dQ launches split by route."""
+    _check(lib().kpage_timing_enable(plan.handle, int(enable)))
 
 
 def kpage_timing_read(plan: Plan, kernel: str):

@@ -22,6 +22,8 @@ namespace {
 // HIP event pairs around every launch, pooled and kept per kernel id until read.
 class EventTimer final : public LaunchTimer {
  public:
+  explicit EventTimer(bool split) : split_(split) {}
+  bool split_routes() const override { return split_; }
   ~EventTimer() override {
     for (auto &k : pending_)
       for (auto &p : k) {
@@ -68,6 +70,7 @@ class EventTimer final : public LaunchTimer {
     pool_.pop_back();
     return e;
   }
+  bool split_;
   std::vector<hipEvent_t> pool_;
   hipEvent_t open_[KPAGE_K_COUNT] = {};
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending_[KPAGE_K_COUNT];
@@ -875,7 +878,12 @@ kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf,
 
 kpage_status kpage_timing_enable(kpage_plan_t *plan, int enable) {
   if (!plan) return fail(KPAGE_ERR_INVALID, "plan is NULL");
-  if (enable && !plan->timer) plan->timer = new (std::nothrow) EventTimer();
+  if (enable < 0 || enable > 2) return fail(KPAGE_ERR_INVALID, "enable must be 0, 1 or 2");
+  if (plan->timer && plan->timer->split_routes() != (enable == 2)) {  // switching modes drops the record
+    delete plan->timer;
+    plan->timer = nullptr;
+  }
+  if (enable && !plan->timer) plan->timer = new (std::nothrow) EventTimer(enable == 2);
   if (enable && !plan->timer) return fail(KPAGE_ERR_OOM, "host allocation failed");
   if (!enable && plan->timer) {
     delete plan->timer;

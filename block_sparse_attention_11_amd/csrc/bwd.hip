@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
+#include "kpage.h"
 #include "tile_common.hpp"
 
 namespace kpage {
@@ -710,10 +711,25 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
     hipLaunchKernelGGL(kpage_bwd_kv_reduce<D>, dim3(a.n_reduce), dim3(256), 0, stream, a);
     if (t) t->after(6, stream);
   }
-  if (a.n_fitems128 + a.n_fitems64 > 0) {
-    if (t) t->before(5, stream);
+  if (t && t->split_routes()) {  // profiling: one dQ launch per route
+    BwdArgs only128 = a, only64 = a;
+    only128.n_fitems64 = 0;
+    only64.n_fitems128 = 0;
+    only64.fitems128 = nullptr;
+    if (a.n_fitems128 > 0) {
+      t->before(KPAGE_K_BWD_DQ, stream);
+      hipLaunchKernelGGL(kpage_bwd_dq<D>, dim3(a.n_fitems128), dim3(64 * kDqWaves), 0, stream, only128);
+      t->after(KPAGE_K_BWD_DQ, stream);
+    }
+    if (a.n_fitems64 > 0) {
+      t->before(KPAGE_K_BWD_DQ_Q64, stream);
+      hipLaunchKernelGGL(kpage_bwd_dq<D>, dim3(a.n_fitems64), dim3(64 * kDqWaves), 0, stream, only64);
+      t->after(KPAGE_K_BWD_DQ_Q64, stream);
+    }
+  } else if (a.n_fitems128 + a.n_fitems64 > 0) {
+    if (t) t->before(KPAGE_K_BWD_DQ, stream);
     hipLaunchKernelGGL(kpage_bwd_dq<D>, dim3(a.n_fitems128 + a.n_fitems64), dim3(64 * kDqWaves), 0, stream, a);
-    if (t) t->after(5, stream);
+    if (t) t->after(KPAGE_K_BWD_DQ, stream);
   }
   return hipGetLastError();
 }

@@ -136,6 +136,9 @@ inline int64_t xcd_chunk_for(int64_t seq_q, int64_t seq_kv, int head_dim) {
 struct LaunchTimer {
   virtual void before(int kernel_id, hipStream_t stream) = 0;
   virtual void after(int kernel_id, hipStream_t stream) = 0;
+  // profiling mode: the forward and dQ passes launch their two routes separately
+  // (M128 items under the pass's own id, M64 items under KPAGE_K_FWD_Q64 / KPAGE_K_BWD_DQ_Q64)
+  virtual bool split_routes() const { return false; }
   virtual ~LaunchTimer() = default;
 };
 

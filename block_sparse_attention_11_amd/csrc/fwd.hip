@@ -48,6 +48,7 @@
 #include <algorithm>
 
 #include "device.hpp"
+#include "kpage.h"
 #include "tile_common.hpp"
 
 namespace kpage {
@@ -581,14 +582,30 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_exact_kernel(FwdArgs a1
 template <int D>
 void launch_d(const FwdArgs &a128, const FwdArgs &a64, hipStream_t stream, LaunchTimer *timer) {
   dim3 grid(a128.n_items + a64.n_items), block(kThreads);
-  if (timer) timer->before(0, stream);
-  hipLaunchKernelGGL((kpage_fwd_kernel<D>), grid, block, 0, stream, a128, a64);
-  if (timer) timer->after(0, stream);
+  if (timer && timer->split_routes()) {  // profiling: one launch per route
+    FwdArgs none128 = a128, none64 = a64;
+    none128.n_items = 0;
+    none64.n_items = 0;
+    if (a128.n_items > 0) {
+      timer->before(KPAGE_K_FWD, stream);
+      hipLaunchKernelGGL((kpage_fwd_kernel<D>), dim3(a128.n_items), block, 0, stream, a128, none64);
+      timer->after(KPAGE_K_FWD, stream);
+    }
+    if (a64.n_items > 0) {
+      timer->before(KPAGE_K_FWD_Q64, stream);
+      hipLaunchKernelGGL((kpage_fwd_kernel<D>), dim3(a64.n_items), block, 0, stream, none128, a64);
+      timer->after(KPAGE_K_FWD_Q64, stream);
+    }
+  } else {
+    if (timer) timer->before(KPAGE_K_FWD, stream);
+    hipLaunchKernelGGL((kpage_fwd_kernel<D>), grid, block, 0, stream, a128, a64);
+    if (timer) timer->after(KPAGE_K_FWD, stream);
+  }
   const int n = a128.n_items + a64.n_items;
   const int exact_blocks = std::min((n + kThreads - 1) / kThreads, kExactBlocks);
-  if (timer) timer->before(1, stream);
+  if (timer) timer->before(KPAGE_K_FWD_EXACT, stream);
   hipLaunchKernelGGL((kpage_fwd_exact_kernel<D>), dim3(exact_blocks), block, 0, stream, a128, a64);
-  if (timer) timer->after(1, stream);
+  if (timer) timer->after(KPAGE_K_FWD_EXACT, stream);
 }
 
 }  // namespace

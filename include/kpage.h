@@ -254,8 +254,12 @@ void kpage_plan_destroy(kpage_plan_t *plan);
  * makes is bracketed by a pair of HIP events recorded on the launch stream.
  * kpage_timing_read() waits for those events, returns the summed milliseconds
  * and the number of launches of one kernel since the last read, and resets that
- * kernel's record.  Kernel ids below.  Disabled by default; enabling it adds two
- * event records per launch and nothing else.
+ * kernel's record.  Kernel ids below.  Disabled by default; enable = 1 adds two
+ * event records per launch and nothing else.  enable = 2 is a profiling mode that
+ * also splits the forward and dQ launches by route: the M128 x N128 items keep
+ * the pass's own id and the M64 x N256 items (with the empty-block cleanup) are
+ * timed as KPAGE_K_FWD_Q64 / KPAGE_K_BWD_DQ_Q64 (two launches per pass instead of
+ * one, so the pass itself may run slightly slower).
  */
 enum {
   KPAGE_K_FWD = 0,       /* forward, both routes in one launch (M128 x N128 items, */
@@ -267,7 +271,9 @@ enum {
   KPAGE_K_BWD_KV = 4,    /* K/V-owned pass: dK, dV                                  */
   KPAGE_K_BWD_DQ = 5,    /* Q-owned pass over the forward walks (both routes): dQ  */
   KPAGE_K_BWD_REDUCE = 6,/* sum of the fp32 dK/dV partials of owners split over Q groups */
-  KPAGE_K_COUNT = 7
+  KPAGE_K_FWD_Q64 = 7,   /* timing mode 2 only: the forward's M64 x N256 launch      */
+  KPAGE_K_BWD_DQ_Q64 = 8,/* timing mode 2 only: the dQ pass's M64 x N256 launch      */
+  KPAGE_K_COUNT = 9
 };
 kpage_status kpage_timing_enable(kpage_plan_t *plan, int enable);
 kpage_status kpage_timing_read(kpage_plan_t *plan, int kernel_id, double *total_ms, int64_t *launches);
