@@ -17,7 +17,8 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkpage.so")
+# KPAGE_LIB names another build of the same library (the host-sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("KPAGE_LIB") or os.path.join(_HERE, "libkpage.so")
 
 KPAGE_OK, KPAGE_ERR_INVALID, KPAGE_ERR_UNSUPPORTED, KPAGE_ERR_OOM, KPAGE_ERR_HIP = range(5)
 STATUS_NAMES = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "OOM", 4: "HIP"}
