@@ -38,8 +38,9 @@ def _run(cmd, verbose):
 # UndefinedBehaviorSanitizer for the CPU tests (GPU code is never sanitized: each
 # -fsanitize= applies to the host pass only).
 SANITIZED = ["csrc/plan.cpp", "csrc/api.hip"]
-SAN_FLAGS = [f for opt in ("-fsanitize=address", "-fsanitize=undefined", "-fno-omit-frame-pointer",
-                           "-fno-sanitize-recover=all", "-shared-libasan") for f in ("-Xarch_host", opt)]
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all",
+             "-Xarch_host", "-shared-libasan"]
 SAN_OUT = os.path.join(HERE, "_build", "libkpage_san.so")
 
 
