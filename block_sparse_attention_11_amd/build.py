@@ -36,7 +36,7 @@ def _run(cmd, verbose):
 
 # Host code of the planner and the C ABI, built again with AddressSanitizer and
 # UndefinedBehaviorSanitizer for the CPU tests (GPU code is never sanitized: each
-# -fsanitize= applies to the host pass only).
+# sanitizer option applies to the host pass only).
 SANITIZED = ["csrc/plan.cpp", "csrc/api.hip"]
 SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all",
