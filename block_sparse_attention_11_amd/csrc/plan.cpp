@@ -7,7 +7,7 @@
 // route, longer walks first; walks padded to whole iterations of 16 or 8 pages),
 // 3.2.4 (two 16-bit page masks per 32-bit word), 3.3.1 (owners of eight page
 // slots, full blocks aligned to their own owner, partial blocks packed without
-// crossing an owner), 3.3.2 (reverse-Q lists from an owner x Q bitmap; full Q
+// crossing an owner, by least growth of the owner's reverse neighbourhood), 3.3.2 (reverse-Q lists from an owner x Q bitmap; full Q
 // blocks first, then pages of partial Q blocks), 3.3.3 (one 64-bit adjacency
 // word per 8 x 8 page step), 3.4 (metadata depends only on the graph and the
 // valid-row counts) and 4.4 (pair-capacity accounting).
@@ -234,7 +234,11 @@ void build_backward(const Problem &P, BwdTables *T, PairStats *S) {
     const int32_t *ck = &P.kv_valid[size_t(g) * nk];
     const int64_t *ok = &P.kv_offset[size_t(g) * nk];
     const uint64_t mult = uint64_t(bh_per_slot[g]);
-    // owners: full blocks first (each its own aligned owner), then partial blocks next-fit
+    // owners (reading of section 3.3.1's packing): every full block is an owner of its
+    // own, in block order; the partial blocks then fill owners one at a time: the
+    // smallest unplaced one opens an owner, and while one fits, the fitting block that
+    // adds the fewest query blocks to the owner's reverse neighbourhood joins (ties to
+    // the smaller index).  Reverse neighbourhoods as bitsets over query blocks.
     std::vector<std::vector<int32_t>> own;
     std::vector<std::vector<int32_t>> own_blocks;
     std::vector<int32_t> owner_of(nk, -1);
@@ -245,18 +249,55 @@ void build_backward(const Problem &P, BwdTables *T, PairStats *S) {
       own_blocks.push_back({k});
       for (int j = 0; j < kOwnerSlots; ++j) own.back().push_back(int32_t(ok[k] / kPageRows) + j);
     }
-    int cur = -1;
-    for (int k = 0; k < nk; ++k) {
-      if (ck[k] == 0 || ck[k] == kBlockRows) continue;
-      const int p = pages_of(ck[k]);
-      if (cur < 0 || kOwnerSlots - int(own[cur].size()) < p) {
+    {
+      const int qw = (nq + 63) / 64;
+      std::vector<int32_t> partial;
+      for (int k = 0; k < nk; ++k)
+        if (ck[k] > 0 && ck[k] < kBlockRows) partial.push_back(k);
+      std::vector<uint64_t> rq(size_t(nk) * qw, 0);  // reverse neighbourhood of each block
+      for (int q = 0; q < nq; ++q) {
+        if (cq[q] == 0) continue;
+        const int64_t a = P.q2k_ptr[size_t(g) * (nq + 1) + q], b = P.q2k_ptr[size_t(g) * (nq + 1) + q + 1];
+        for (int64_t e = a; e < b; ++e) {
+          const int k = P.q2k_idx[e];
+          if (ck[k] > 0) rq[size_t(k) * qw + q / 64] |= uint64_t(1) << (q % 64);
+        }
+      }
+      std::vector<uint8_t> placed(nk, 0);
+      std::vector<uint64_t> covered(qw);
+      for (size_t s0 = 0; s0 < partial.size(); ++s0) {
+        const int seed = partial[s0];
+        if (placed[seed]) continue;
+        const int cur = int(own.size());
         own.emplace_back();
         own_blocks.emplace_back();
-        cur = int(own.size()) - 1;
+        std::fill(covered.begin(), covered.end(), 0);
+        auto place = [&](int k) {
+          placed[k] = 1;
+          owner_of[k] = cur;
+          own_blocks[cur].push_back(k);
+          for (int j = 0; j < pages_of(ck[k]); ++j) own[cur].push_back(int32_t(ok[k] / kPageRows) + j);
+          for (int w = 0; w < qw; ++w) covered[w] |= rq[size_t(k) * qw + w];
+        };
+        place(seed);
+        for (;;) {
+          const int free_slots = kOwnerSlots - int(own[cur].size());
+          int best = -1, best_new = 0;
+          for (size_t i = s0 + 1; i < partial.size() && free_slots > 0; ++i) {
+            const int k = partial[i];
+            if (placed[k] || pages_of(ck[k]) > free_slots) continue;
+            int new_q = 0;
+            for (int w = 0; w < qw; ++w) new_q += __builtin_popcountll(rq[size_t(k) * qw + w] & ~covered[w]);
+            if (best < 0 || new_q < best_new) {
+              best = k;
+              best_new = new_q;
+              if (new_q == 0) break;  // the smallest index adding nothing
+            }
+          }
+          if (best < 0) break;
+          place(best);
+        }
       }
-      owner_of[k] = cur;
-      own_blocks[cur].push_back(k);
-      for (int j = 0; j < p; ++j) own[cur].push_back(int32_t(ok[k] / kPageRows) + j);
     }
     const int n_own = int(own.size());
     // per-page block and row mask, for adjacency and the visited-pair check

@@ -38,6 +38,7 @@ struct Summary {
 };
 
 constexpr int kScanThreads = 1024;
+constexpr int kOwnersLdsMax = 48 * 1024;  // dynamic LDS of the owner packing (about 390,000 blocks)
 
 __device__ __forceinline__ int pages_of(int c) { return (c + kPageRows - 1) / kPageRows; }
 __device__ __forceinline__ uint32_t tail_mask(int c) { return (1u << (c % kPageRows)) - 1u; }
@@ -451,22 +452,55 @@ __device__ __forceinline__ uint32_t page_mask(int c, int j) {
 // own_info packing: blocks in the owner | pages in the owner << 16
 __device__ __forceinline__ int32_t pack_info(int blocks, int pages) { return blocks | (pages << 16); }
 
-// Owners of slot blockIdx.x: every full block is an owner of its own, in block order;
-// the partial blocks then fill owners next-fit, in block order (a block opens a new
-// owner when its pages do not fit in the current one).  One thread runs the next-fit
-// over block sizes staged in LDS.
-constexpr int kStage = 4 * kScanThreads;
+// Reverse neighbourhood of every K/V block: the query blocks with c_q > 0 that select it,
+// as a bitset of nqw words per (slot, block); one thread per (slot, query block).
+__global__ void k_block_revq(DevProblem p, int nqw, uint32_t *rev_k) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= int64_t(p.slots) * p.n_q) return;
+  const int g = int(i / p.n_q), q = int(i % p.n_q);
+  if (p.q_valid[i] == 0) return;
+  const int64_t a = p.q2k_ptr[int64_t(g) * (p.n_q + 1) + q], b = p.q2k_ptr[int64_t(g) * (p.n_q + 1) + q + 1];
+  for (int64_t e = a; e < b; ++e) {
+    const int k = p.q2k_idx[e];
+    if (p.kv_valid[int64_t(g) * p.n_kv + k] == 0) continue;
+    atomicOr(&rev_k[(int64_t(g) * p.n_kv + k) * nqw + (q >> 5)], 1u << (q & 31));
+  }
+}
 
-__global__ __launch_bounds__(kScanThreads) void k_owners(DevProblem p, int32_t *owner_of, int32_t *pos_of,
-                                                         int32_t *own_info, int32_t *n_own) {
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned lo = __shfl_xor((unsigned)v, off), hi = __shfl_xor((unsigned)(v >> 32), off);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    v = o < v ? o : v;
+  }
+  return v;
+}
+
+// Owners of slot blockIdx.x: every full block is an owner of its own, in block order.
+// The partial blocks then fill owners one at a time: the smallest unplaced one opens an
+// owner, and while one fits, the fitting block that adds the fewest query blocks to the
+// owner's reverse neighbourhood joins it (ties to the smaller index).  The candidates of
+// each choice are scored in parallel, one or more per thread, and the choice is the
+// minimum of (new query blocks, block index) over the workgroup.  Dynamic LDS: the
+// owner's covered query blocks (nqw words), then one placed bit per block (nkw words).
+__global__ __launch_bounds__(kScanThreads) void k_owners(DevProblem p, const uint32_t *rev_k, int nqw, int nkw,
+                                                         int32_t *owner_of, int32_t *pos_of, int32_t *own_info,
+                                                         int32_t *n_own) {
   __shared__ int64_t lds[kScanThreads];
-  __shared__ int32_t s_ck[kStage];
+  __shared__ unsigned long long s_min[kScanThreads / 64];
+  __shared__ int s_pick;
+  extern __shared__ uint32_t s_dyn[];
+  uint32_t *covered = s_dyn;
+  uint32_t *placed = s_dyn + nqw;
   const int g = blockIdx.x;
+  const int tid = threadIdx.x;
   const int64_t gb = int64_t(g) * p.n_kv;
   const int32_t *ck = p.kv_valid + gb;
+  const uint32_t *rk = rev_k + gb * nqw;
+  for (int i = tid; i < nkw; i += kScanThreads) placed[i] = 0;
   int64_t carry = 0;
   for (int base = 0; base < p.n_kv; base += kScanThreads) {
-    const int k = base + threadIdx.x;
+    const int k = base + tid;
     const int c = k < p.n_kv ? ck[k] : 0;
     int64_t total;
     const int64_t pre = carry + block_scan(c == kBlockRows ? 1 : 0, lds, &total);
@@ -480,34 +514,61 @@ __global__ __launch_bounds__(kScanThreads) void k_owners(DevProblem p, int32_t *
     }
     carry += total;
   }
-  int cur = -1, used = 0, blocks = 0, n = int(carry);
-  for (int base = 0; base < p.n_kv; base += kStage) {
+  auto is_partial = [&](int k) { const int c = ck[k]; return c > 0 && c < kBlockRows; };
+  auto is_placed = [&](int k) { return (placed[k >> 5] >> (k & 31)) & 1u; };
+  int n = int(carry);
+  int scan = 0;  // every partial block below it is placed
+  for (;;) {
     __syncthreads();
-    for (int i = threadIdx.x; i < kStage; i += kScanThreads) s_ck[i] = base + i < p.n_kv ? ck[base + i] : 0;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int m = min(kStage, p.n_kv - base);
-      for (int i = 0; i < m; ++i) {
-        const int c = s_ck[i];
-        if (c == 0 || c == kBlockRows) continue;
-        const int np = pages_of(c);
-        if (cur < 0 || kOwnerSlots - used < np) {
-          if (cur >= 0) own_info[gb + cur] = pack_info(blocks, used);
-          cur = n++;
-          used = 0;
-          blocks = 0;
-        }
-        owner_of[gb + base + i] = cur;
-        pos_of[gb + base + i] = used;
-        used += np;
-        ++blocks;
-      }
+    if (tid == 0) {
+      while (scan < p.n_kv && !(is_partial(scan) && !is_placed(scan))) ++scan;
+      s_pick = scan < p.n_kv ? scan : -1;
     }
+    __syncthreads();
+    const int seed = s_pick;
+    if (seed < 0) break;
+    scan = seed + 1;
+    const int cur = n++;
+    int used = 0, blocks = 0;
+    for (int i = tid; i < nqw; i += kScanThreads) covered[i] = 0;
+    __syncthreads();
+    int k = seed;
+    for (;;) {  // place k, then look for the next block
+      if (tid == 0) {
+        owner_of[gb + k] = cur;
+        pos_of[gb + k] = used;
+        placed[k >> 5] |= 1u << (k & 31);
+      }
+      for (int i = tid; i < nqw; i += kScanThreads) covered[i] |= rk[int64_t(k) * nqw + i];
+      used += pages_of(ck[k]);
+      ++blocks;
+      __syncthreads();
+      const int free_slots = kOwnerSlots - used;
+      unsigned long long best = ~0ull;
+      if (free_slots > 0) {
+        for (int j = seed + 1 + tid; j < p.n_kv; j += kScanThreads) {
+          if (!is_partial(j) || is_placed(j) || pages_of(ck[j]) > free_slots) continue;
+          unsigned new_q = 0;
+          for (int i = 0; i < nqw; ++i) new_q += __popc(rk[int64_t(j) * nqw + i] & ~covered[i]);
+          const unsigned long long key = ((unsigned long long)new_q << 32) | unsigned(j);
+          best = key < best ? key : best;
+        }
+      }
+      best = wave_min_u64(best);
+      if ((tid & 63) == 0) s_min[tid >> 6] = best;
+      __syncthreads();
+      if (tid == 0) {
+        unsigned long long m = ~0ull;
+        for (int w = 0; w < kScanThreads / 64; ++w) m = s_min[w] < m ? s_min[w] : m;
+        s_pick = m == ~0ull ? -1 : int(m & 0xFFFFFFFFu);
+      }
+      __syncthreads();
+      if (s_pick < 0) break;
+      k = s_pick;
+    }
+    if (tid == 0) own_info[gb + cur] = pack_info(blocks, used);
   }
-  if (threadIdx.x == 0) {
-    if (cur >= 0) own_info[gb + cur] = pack_info(blocks, used);
-    n_own[g] = n;
-  }
+  if (tid == 0) n_own[g] = n;
 }
 
 // pages of slot blockIdx.x outside every block footprint: count, or (unc != NULL)
@@ -846,6 +907,12 @@ kpage_status build_backward_device(const DevProblem &p, const int32_t *page_bloc
   const int64_t n_pages = p.seq_kv / kPageRows;
   const int nkw = (p.n_kv + 31) / 32, nqw = (p.n_q + 31) / 32;
   const unsigned long long mult = p.per_head ? 1ull : (unsigned long long)p.batch * p.heads;
+  // owner packing keeps the covered query blocks and one placed bit per block in LDS
+  const size_t owners_lds = size_t(nqw + nkw) * 4;
+  if (owners_lds > size_t(kOwnersLdsMax)) {
+    *err = "too many query and key blocks for the GPU planner's owner packing";
+    return KPAGE_ERR_UNSUPPORTED;
+  }
   bool oom = false;
   auto A = [&](int64_t n, size_t elem) -> void * {
     void *q = alloc(size_t(std::max<int64_t>(n, 1)) * elem);
@@ -860,6 +927,7 @@ kpage_status build_backward_device(const DevProblem &p, const int32_t *page_bloc
   int32_t *n_unc = static_cast<int32_t *>(A(G, 4));
   uint32_t *edge = static_cast<uint32_t *>(A(GQ * nkw, 4));
   uint32_t *own_q = static_cast<uint32_t *>(A(GK * nqw, 4));
+  uint32_t *rev_k = static_cast<uint32_t *>(A(GK * nqw, 4));
   uint32_t *fullq = static_cast<uint32_t *>(A(int64_t(G) * nqw, 4));
   int64_t *rcount = static_cast<int64_t *>(A(GK, 8));
   int64_t *qlen = static_cast<int64_t *>(A(GK, 8));
@@ -889,8 +957,11 @@ kpage_status build_backward_device(const DevProblem &p, const int32_t *page_bloc
   KP_CHECK(hipMemsetAsync(d_sum, 0, sizeof(BwdSummary), st));
   KP_CHECK(hipMemsetAsync(edge, 0, size_t(std::max<int64_t>(GQ * nkw, 1)) * 4, st));
   KP_CHECK(hipMemsetAsync(own_q, 0, size_t(std::max<int64_t>(GK * nqw, 1)) * 4, st));
+  KP_CHECK(hipMemsetAsync(rev_k, 0, size_t(std::max<int64_t>(GK * nqw, 1)) * 4, st));
   KP_CHECK(hipMemsetAsync(fullq, 0, size_t(std::max<int64_t>(int64_t(G) * nqw, 1)) * 4, st));
-  hipLaunchKernelGGL(k_owners, dim3(G), dim3(kScanThreads), 0, st, p, owner_of, pos_of, own_info, n_own);
+  hipLaunchKernelGGL(k_block_revq, dim3(blocks_for(GQ, TB)), dim3(TB), 0, st, p, nqw, rev_k);
+  hipLaunchKernelGGL(k_owners, dim3(G), dim3(kScanThreads), owners_lds, st, p, rev_k, nqw, nkw, owner_of, pos_of,
+                     own_info, n_own);
   hipLaunchKernelGGL(k_uncovered, dim3(G), dim3(kScanThreads), 0, st, p, page_block, n_unc, nullptr, nullptr);
   hipLaunchKernelGGL(k_slot_scans, dim3(1), dim3(kScanThreads), 0, st, G, n_own, n_unc, t->owner_ptr,
                      t->uncovered_ptr, d_sum);

@@ -19,9 +19,12 @@ sections are missing from the text; the readings taken here:
   queues         per route, entries (b*H + h, q) by descending unpadded walk
                  length, then ascending b*H + h, then ascending q
   owners         8 page slots; each full block (c = 128) takes its own owner in
-                 ascending block order; then blocks with 0 < c < 128 are placed
-                 next-fit in ascending order, never crossing an owner; the
-                 aligned flag is set when one block with 8 pages fills the owner
+                 ascending block order; then the blocks with 0 < c < 128 fill
+                 owners one at a time, never crossing an owner: the smallest
+                 unplaced one opens an owner, and while one fits, the fitting
+                 block adding the fewest query blocks to the owner's reverse
+                 neighbourhood joins (ties to the smaller index); the aligned
+                 flag is set when one block with 8 pages fills the owner
   reverse Q      bitmap[owner(k)][q] over the graph edges with c_q, c_k > 0;
                  each owner's list is its set bits in ascending q
   Q groups       q_group = 0: one group; q_group = n > 0: G_g = the Q blocks
@@ -119,7 +122,22 @@ def _fwd_slot(c_q, c_k, o_k, rows, align64: int, align128: int):
     return routes, walks, nfull, masks
 
 
-def _owners_slot(c_k, o_k):
+def _owners_slot(c_k, o_k, c_q, rows):
+    """Owners of one graph slot (section 3.3.1 says only that partial blocks are packed;
+    reading R15): every full block (c = 128) is an owner of its own, in block order.  The
+    partial blocks (0 < c < 128) then fill owners one at a time: the unplaced partial
+    block of smallest index opens an owner; while some unplaced partial block fits into the
+    owner's free slots, the one that adds the fewest query blocks to the owner's reverse
+    neighbourhood joins it (ties to the smaller index), its pages after those already in
+    the owner.  A block's reverse neighbourhood is the set of query blocks with c_q > 0
+    that select it."""
+    R = {k: set() for k in range(len(c_k))}
+    for q, row in enumerate(rows):
+        if int(c_q[q]) == 0:
+            continue
+        for k in row:
+            if int(c_k[int(k)]) > 0:
+                R[int(k)].add(q)
     owners, aligned, owner_of = [], [], {}
     for k in range(len(c_k)):
         if int(c_k[k]) == BLOCK:
@@ -127,19 +145,33 @@ def _owners_slot(c_k, o_k):
             owner_of[k] = len(owners)
             owners.append([base + j for j in range(8)])
             aligned.append(1)
-    cur = -1
-    for k in range(len(c_k)):
-        ck = int(c_k[k])
-        if ck == 0 or ck == BLOCK:
-            continue
-        p = _pages(ck)
-        base = int(o_k[k]) // PAGE
-        if cur < 0 or 8 - len(owners[cur]) < p:
-            owners.append([])
-            aligned.append(0)
-            cur = len(owners) - 1
-        owner_of[k] = cur
-        owners[cur].extend(base + j for j in range(p))
+    left = [k for k in range(len(c_k)) if 0 < int(c_k[k]) < BLOCK]
+    while left:
+        seed = left.pop(0)
+        t = len(owners)
+        owners.append([])
+        aligned.append(0)
+        covered = set()
+
+        def place(k):
+            owner_of[k] = t
+            base = int(o_k[k]) // PAGE
+            owners[t].extend(base + j for j in range(_pages(int(c_k[k]))))
+            covered.update(R[k])
+
+        place(seed)
+        while True:
+            free = 8 - len(owners[t])
+            best, best_new = None, None
+            for k in left:
+                if _pages(int(c_k[k])) <= free:
+                    new_q = len(R[k] - covered)
+                    if best_new is None or new_q < best_new:
+                        best, best_new = k, new_q
+            if best is None:
+                break
+            left.remove(best)
+            place(best)
     for t, pages in enumerate(owners):
         if aligned[t] == 0 and len(pages) == 8:
             blocks = {owner_block for owner_block, ot in owner_of.items() if ot == t}
@@ -198,7 +230,7 @@ def oracle_plan(problem, align_q64: int = 16, align_q128: int = 8, q_group: int 
         f_ptr[g, n_q] = len(f_walk)
 
         # backward: owners, reverse Q, Q-page walks, adjacency
-        owners, aligned, owner_of = _owners_slot(c_k, o_k)
+        owners, aligned, owner_of = _owners_slot(c_k, o_k, c_q, rows)
         o_ptr[g + 1] = o_ptr[g] + len(owners)
         page_block = {}
         for k, t in owner_of.items():
