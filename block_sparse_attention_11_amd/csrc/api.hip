@@ -339,7 +339,6 @@ void make_bwd_items(const Problem &P, const BwdTables &B, std::vector<BwdItem> *
     x.n_steps = int32_t((B.qwalk_ptr[w + 1] - B.qwalk_ptr[w]) / 8);
     x.bh = bh;
     x.owner = int32_t(t);
-    x.aligned = B.aligned[t];
     x.partial = tg_local % ng;  // group, until the slots are assigned below
     items->push_back(x);
   }

@@ -179,11 +179,19 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
   const int rd_base = chunk_off<kSwzBoth, D>(l32, g);
   const int tr_base = chunk_off<kSwzBoth, D>(4 * g + (sl >> 2), 2 * (mgrp & 1) + ((sl & 3) >> 1)) + (sl & 1) * 8;
 
+  // Lane parts of the lse2 / delta reads with the stats buffer's own LDS address folded
+  // in, kept opaque: every read is then this base plus a constant that fits the 16-bit
+  // read offset (the buffer sits past the first 64 KiB of LDS).
+  uint32_t st_lse = (uint32_t)(uintptr_t)(const lds_char *)stats + 16 * g;
+  uint32_t st_del = (uint32_t)(uintptr_t)(const lds_char *)stats + ((l32 >> 4) * 64 + 16 + (l32 & 15)) * 4;
+  asm volatile("" : "+v"(st_lse), "+v"(st_del));
+
   auto half_step = [&](auto buf_c, int u, uint64_t adj) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_c)::value;
     const lds_char *qt = (const lds_char *)smem + (2 * BUF) * TILE;
     const lds_char *gt = (const lds_char *)smem + (2 * BUF + 1) * TILE;
-    const lds_char *stb = (const lds_char *)stats + BUF * STATS;
+    const lds_char *stl = (const lds_char *)(uintptr_t)st_lse + BUF * STATS;
+    const lds_char *std_ = (const lds_char *)(uintptr_t)st_del + BUF * STATS;
     // Pair mask.  Query rows without a valid key (invalid rows included) have
     // lse2 = +inf, so their P is 0 by itself.  Key validity needs no mask here: the P
     // and dS of an invalid key reach only that key's own dK / dV rows, which are
@@ -207,8 +215,8 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
       // Register r of a 32 x 32 score block holds query row 32 qb + 8 (r / 4) + 4 g +
       // r % 4 of the half-step; group j4 = r / 4 reads its 4 lse2 values as one f32x4.
       auto lse4 = [&](int j4) __attribute__((always_inline)) {
-        const int q = 32 * QB + 8 * j4 + 4 * g;
-        return *(const __attribute__((address_space(3))) f32x4 *)(stb + ((q >> 4) * 64 + (q & 15)) * 4);
+        // q = 32 qb + 8 j4 + 4 g: page 2 qb + j4 / 2, row 8 (j4 % 2) + 4 g (4 g is in stl)
+        return *(const __attribute__((address_space(3))) f32x4 *)(stl + ((2 * QB + (j4 >> 1)) * 64 + 8 * (j4 & 1)) * 4);
       };
       auto rd_row = [&](const lds_char *t, auto s_c) __attribute__((always_inline)) {
         constexpr int S = decltype(s_c)::value;
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
         constexpr int S = decltype(s_c)::value;
         read_op(ic<S + 2>{});
         if constexpr (S == DS - 2) nd = -*(const __attribute__((address_space(3))) float *)(
-                                        stb + (((32 * QB + l32) >> 4) * 64 + 16 + ((32 * QB + l32) & 15)) * 4);
+                                        std_ + 2 * QB * 64 * 4);
         if constexpr (S == DS - 4) l4[0] = lse4(0);
         if constexpr (S == DS - 3) l4[1] = lse4(1);
         sp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], kreg[S], S == 0 ? f32x16{} : sp, 0, 0, 0);
@@ -297,6 +305,12 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
       // read during the last products.
       constexpr int NOPS = 4 * ND;
       bf16x8 top[NOPS];
+      // the ND lane offsets tr_base ^ 64 n of this block's transposed reads, computed
+      // once for its 4 ND operands (8 ND reads)
+      int trx[ND];
+      static_for<ND>([&](auto n_c) __attribute__((always_inline)) {
+        trx[decltype(n_c)::value] = xor_imm<64 * decltype(n_c)::value>(tr_base);
+      });
       // operand i: tile (dO for even phase, Q for odd), hh = i / (2 ND), n = i % ND
       auto rdt = [&](auto i_c) __attribute__((always_inline)) {
         constexpr int I = decltype(i_c)::value;
@@ -304,7 +318,7 @@ __global__ __launch_bounds__(64 * kKvWaves, 2) void kpage_bwd_kv(BwdArgs a) {
           constexpr int PH = I / ND, N = I % ND, HH = PH / 2;
           constexpr int RH = RB + 16 * HH * D * 2;
           const lds_char *t = (PH & 1) ? qt : gt;
-          top[I] = tr_read8(t + RH + xor_imm<64 * N>(tr_base), t + RH + 8 * D * 2 + xor_imm<64 * (N ^ 1)>(tr_base));
+          top[I] = tr_read8(t + RH + trx[N], t + RH + 8 * D * 2 + trx[N ^ 1]);
         }
       };
       auto ds_pair = [&](auto r_c) __attribute__((always_inline)) {
@@ -504,11 +518,11 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
     bf16x8 op[2 * DS];
     auto read_op = [&](auto i_c) __attribute__((always_inline)) {
       constexpr int I = decltype(i_c)::value;
-      if constexpr (I < DS) op[I] = lds_read8(kt + xor_imm<32 * I>(rdk));
-      else if constexpr (I < 2 * DS) op[I] = lds_read8(vt + xor_imm<32 * (I - DS)>(rdv));
+      if constexpr (I < DS) op[I] = lds_read8(kt + (rdk ^ (32 * I)));
+      else if constexpr (I < 2 * DS) op[I] = lds_read8(vt + (rdv ^ (32 * (I - DS))));
     };
     uint32_t word = 0;
-    if constexpr (MASKED) word = vwords[2 * u + ((keyoff + 32 * H) >> 5)] >> (4 * g);
+    if constexpr (MASKED) word = vwords[2 * u + ((keyoff + 32 * H) >> 5)];
     read_op(ic<0>{});
     read_op(ic<1>{});
     static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
@@ -517,22 +531,17 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
       s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[S], qreg[S], S == 0 ? f32x16{} : s_acc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     });
-    // probabilities in place of the scores; key row of register r: 8 (r / 4) + 4 g +
-    // r % 4 of the sub-tile, its validity bit in the sub-tile's word (two 16-bit page
-    // masks): (r % 4) + 8 ((r / 4) % 2) + 16 (r / 8) after the shift by 4 g
+    // probabilities in place of the scores; register r holds key row acc_row(r, g) of
+    // the sub-tile, whose validity bit (the sub-tile's word: two 16-bit page masks) is
+    // wave-uniform in each lane half: a scalar lane mask selects p or 0
     auto p_slice = [&](auto j_c) __attribute__((always_inline)) {
       constexpr int J4 = decltype(j_c)::value;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * J4 + e;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[r], c2, nlse2));
-        if constexpr (MASKED) {
-          const int bit = (r & 3) + 8 * ((r >> 2) & 1) + 16 * (r >> 3);
-          s_acc[r] = ((word >> bit) & 1u) ? p : 0.f;
-        } else {
-          s_acc[r] = p;
-        }
-      }
+      static_for<4>([&](auto e_c) __attribute__((always_inline)) {
+        constexpr int R = 4 * J4 + decltype(e_c)::value;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[R], c2, nlse2));
+        if constexpr (MASKED) s_acc[R] = select_lanes(row_lane_mask<R>(word), p, 0.f);
+        else s_acc[R] = p;
+      });
     };
     static_for<DS>([&](auto s_c) __attribute__((always_inline)) {
       constexpr int S = decltype(s_c)::value;
@@ -550,7 +559,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
       constexpr int J = decltype(j_c)::value, HH = J / ND, N = J % ND;
       if constexpr (J < NOPS) {
         const lds_char *p = kt + 16 * HH * D * 2;
-        kop[J] = tr_read8(p + xor_imm<64 * N>(trk), p + 8 * D * 2 + xor_imm<64 * (N ^ 1)>(trk));
+        kop[J] = tr_read8(p + (trk ^ (64 * N)), p + 8 * D * 2 + (trk ^ (64 * (N ^ 1))));
       }
     };
     u32x4 ds[2];

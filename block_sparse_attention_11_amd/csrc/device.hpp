@@ -37,10 +37,9 @@ struct BwdItem {
   int32_t bh;
   int32_t owner;       // global owner index (row of the owner table)
   int32_t n_steps;
-  int32_t aligned;     // 1: the owner is one block of 8 contiguous pages
   int32_t partial;     // -1: write dK/dV (bf16) directly; >= 0: fp32 partial slot of
                        // an owner split over several Q groups (summed by the reduce pass)
-  int32_t pad;
+  int32_t pad[2];
 };
 
 // One owner whose Q groups were split over `count` work items: partial slots

@@ -203,12 +203,14 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
   // exact masking of invalid key rows of sub-tile `sub` (its 32 keys = one validity word)
   auto mask = [&](int sub, f32x16 &sc) __attribute__((always_inline)) {
     const int tile = sub / NH, half = sub % NH;
-    const uint32_t word = vwords[tile * (kTilePages / 2) + (keyoff >> 5) + half] >> (4 * g);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int bit = (r & 3) + 8 * ((r >> 2) & 1) + 16 * (r >> 3);
-      sc[r] = ((word >> bit) & 1u) ? sc[r] : kNegInf;
-    }
+    const uint32_t word = vwords[tile * (kTilePages / 2) + (keyoff >> 5) + half];
+    // register r holds key acc_row(r, g): its bit is wave-uniform in each lane half, so
+    // the condition is a scalar lane mask and each score costs one select
+    const float ninf = kNegInf;
+    static_for<16>([&](auto r_c) __attribute__((always_inline)) {
+      constexpr int R = decltype(r_c)::value;
+      sc[R] = select_lanes(row_lane_mask<R>(word), sc[R], ninf);
+    });
   };
   float alpha = 1.f;  // exact kernel: rescale factor owed by the last softmax
   float nm_fix = 0.f;  // fast kernel: -(fixed maximum) once the first sub-tile set it

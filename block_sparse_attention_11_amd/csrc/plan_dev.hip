@@ -819,7 +819,7 @@ __global__ void k_adj(DevProblem p, const int32_t *page_block, int64_t n_own, in
 // per (bh, owner within slot), f = that pair's index in (bh, owner) order: queue sort
 // key (steps descending, then f) and the launch item at its XCD position
 __global__ void k_bwd_items(DevProblem p, int64_t n_own, int64_t n_items, const int64_t *owner_ptr,
-                            const int64_t *qwalk_ptr, const uint8_t *aligned, unsigned long long *keys, BwdItem *items) {
+                            const int64_t *qwalk_ptr, unsigned long long *keys, BwdItem *items) {
   const int64_t f = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (f >= n_items) return;
   int bh;
@@ -838,7 +838,6 @@ __global__ void k_bwd_items(DevProblem p, int64_t n_own, int64_t n_items, const 
   x.bh = bh;
   x.owner = int32_t(tg);
   x.n_steps = steps;
-  x.aligned = aligned[tg];
   x.partial = -1;
   items[launch_position(f, n_items, p.xcd_chunk)] = x;
 }
@@ -1007,7 +1006,7 @@ kpage_status build_backward_device(const DevProblem &p, const int32_t *page_bloc
       hipLaunchKernelGGL(k_adj, dim3(blocks_for(n_steps, TB)), dim3(TB), 0, st, p, page_block, h.n_own, n_steps, mult,
                          owner_slot, t->qwalk_ptr, t->owners, t->qwalk, edge, nkw, t->adj, d_sum);
     hipLaunchKernelGGL(k_bwd_items, dim3(blocks_for(t->n_items, TB)), dim3(TB), 0, st, p, h.n_own, t->n_items,
-                       t->owner_ptr, t->qwalk_ptr, t->aligned, keys, t->items);
+                       t->owner_ptr, t->qwalk_ptr, keys, t->items);
     hipLaunchKernelGGL(k_bwd_tails, dim3(kXcds), dim3(1024), 0, st, t->items, t->n_items);
     size_t tmp_bytes = 0;
     KP_CHECK(hipcub::DeviceRadixSort::SortKeys(nullptr, tmp_bytes, keys, keys + t->n_items, int(t->n_items), 0, 64,

@@ -211,4 +211,21 @@ __device__ __forceinline__ uint32_t pinned(uint32_t x) {
 // lane half g: rows 8 (r / 4) + 4 g + r % 4.
 __device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
+// Lane mask (lanes 0..31: bit acc_row(R, 0) of `word`, lanes 32..63: bit acc_row(R, 1))
+// for accumulator register R of a result block whose 32 rows have validity bits in the
+// wave-uniform `word`: built with scalar operations.
+template <int R>
+__device__ __forceinline__ uint64_t row_lane_mask(uint32_t word) {
+  const uint64_t lo = (word >> acc_row(R, 0)) & 1u, hi = (word >> acc_row(R, 1)) & 1u;
+  return (lo * 0xFFFFFFFFull) | ((hi * 0xFFFFFFFFull) << 32);
+}
+
+// mask's bit of this lane ? x : y: one v_cndmask with the wave-uniform mask as its
+// condition (from a select on a per-lane bit test the compiler emits three VALU ops).
+// A builtin, not inline assembly, so that the compiler's wait-state checks cover the
+// select's inputs (the same select written as inline assembly gave wrong results).
+__device__ __forceinline__ float select_lanes(uint64_t mask, float x, float y) {
+  return __builtin_amdgcn_inverse_ballot_w64(mask) ? x : y;
+}
+
 }  // namespace kpage

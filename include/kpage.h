@@ -225,7 +225,8 @@ enum {
   KPAGE_T_Q128_QUEUE = 6,     /* int32 [n][2]                                         */
   KPAGE_T_OWNER_PTR = 7,      /* int64 [G + 1]: offsets into OWNERS                   */
   KPAGE_T_OWNERS = 8,         /* int32 [n_own][8]: K/V page ids, -1 = empty slot      */
-  KPAGE_T_OWNER_ALIGNED = 9,  /* uint8 [n_own]: one block of 8 contiguous pages       */
+  KPAGE_T_OWNER_ALIGNED = 9,  /* uint8 [n_own]: one block of 8 contiguous pages (plan
+                                 metadata only: the kernels read owners page by page) */
   KPAGE_T_REVQ_PTR = 10,      /* int64 [n_own + 1]                                    */
   KPAGE_T_REVQ = 11,          /* int32 Q block ids, ascending per owner               */
   KPAGE_T_QWALK_PTR = 12,     /* int64 [n_own + 1]: offsets into QWALK (multiple of 8)*/
