@@ -277,6 +277,9 @@ def main():
                     help="configuration to time (default: the metric's 3D-padded fwd+bwd workload)")
     ap.add_argument("--q-group", type=int, default=0, metavar="N",
                     help="backward Q-group size in Q blocks (0: one group, the default)")
+    ap.add_argument("--heads", type=int, default=0, metavar="N",
+                    help="time only the first N heads of the workload (one GPU's share when the heads are "
+                         "sharded over several GPUs; 0: all heads, the default)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the known-size kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -303,7 +306,9 @@ def main():
 
     dev = torch.device("cuda", 0)
     desc, tokens, cpu_heads = WORKLOADS[args.workload]
-    w = make_workload(args.workload, with_do=True)
+    w = make_workload(args.workload, heads=list(range(args.heads)) if args.heads > 0 else None, with_do=True)
+    if args.heads > 0:
+        desc += f"; first {w.heads} heads only"
     d = w.head_dim
     t0 = time.perf_counter()
     plan = K.kpage_plan(w, q_group=args.q_group)

@@ -325,10 +325,17 @@ void build_backward(const Problem &P, BwdTables *T, PairStats *S) {
       const uint8_t al = (own_blocks[t].size() == 1 && pages.size() == size_t(kOwnerSlots)) ? 1 : 0;
       while (pages.size() < size_t(kOwnerSlots)) pages.push_back(-1);
       std::vector<int> owner_steps;
+      // an owner whose reverse neighbourhood holds at most gsz Q blocks is within the
+      // bound the groups serve: its whole list is group 0, the other groups are empty
+      int n_revq = 0;
+      for (int q = 0; q < nq; ++q) n_revq += bitmap[size_t(t) * nq + q];
+      const bool split = n_revq > gsz;
       for (int grp = 0; grp < n_groups; ++grp) {
         // reverse neighbourhood of owner t inside Q group grp, ascending q
         std::vector<int32_t> R;
-        for (int q = grp * gsz; q < std::min(nq, (grp + 1) * gsz); ++q)
+        const int q_lo = split ? grp * gsz : (grp == 0 ? 0 : nq);
+        const int q_hi = split ? std::min(nq, (grp + 1) * gsz) : (grp == 0 ? nq : nq);
+        for (int q = q_lo; q < q_hi; ++q)
           if (bitmap[size_t(t) * nq + q]) R.push_back(q);
         T->revq.insert(T->revq.end(), R.begin(), R.end());
         T->revq_ptr.push_back(int64_t(T->revq.size()));

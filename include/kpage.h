@@ -72,11 +72,13 @@ typedef struct {
  * pages per iteration and the Q128 path 8, so walks are padded with dummy pages
  * to a multiple of align_q64 / align_q128 (defaults 16 / 8; multiples of those
  * values are accepted).  q_group is the Q-group size of section 3.3.2, in Q
- * blocks: 0 = one group; n > 0 splits every owner's reverse neighbourhood into
- * the groups [g n, (g + 1) n) of Q blocks, one backward work item per non-empty
- * (owner, group), which bounds the serial Q work of an item.  An owner split over
- * several items sums fp32 partials of dK/dV (in group order, deterministic) in
- * the backward workspace.  Negative values are KPAGE_ERR_INVALID.
+ * blocks: 0 = one group; n > 0 bounds the serial Q work of a backward work item
+ * at n Q blocks: an owner whose reverse neighbourhood holds more than n Q blocks
+ * is split into the groups [g n, (g + 1) n) of Q blocks, one work item per
+ * non-empty (owner, group); an owner with at most n keeps its whole list in
+ * group 0 (one item, no partials).  An owner split over several items sums fp32
+ * partials of dK/dV (in group order, deterministic) in the backward workspace.
+ * Negative values are KPAGE_ERR_INVALID.
  */
 typedef struct {
   int32_t q_group;

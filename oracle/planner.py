@@ -29,8 +29,11 @@ sections are missing from the text; the readings taken here:
                  each owner's list is its set bits in ascending q
   Q groups       q_group = 0: one group; q_group = n > 0: G_g = the Q blocks
                  [g n, (g + 1) n); the reverse neighbourhood of owner t in group
-                 g is its list restricted to G_g (section 3.3.2).  Tables are kept
-                 per (owner, group) pair, owner-major, empty pairs included
+                 g is its list restricted to G_g (section 3.3.2), except that an
+                 owner whose whole list holds at most n Q blocks is already within
+                 the bound the grouping serves and keeps its list whole in group 0.
+                 Tables are kept per (owner, group) pair, owner-major, empty pairs
+                 included
   Q-page walk    per (owner, group): pages 8q + j of full Q blocks in the list,
                  then the pages of partial Q blocks, then dummies up to a
                  multiple of 8
@@ -256,9 +259,13 @@ def oracle_plan(problem, align_q64: int = 16, align_q128: int = 8, q_group: int 
         slot_steps = []  # [owner][group]
         for t, pages in enumerate(owners):
             R_all = [int(x) for x in np.nonzero(bitmap[t])[0]]
+            split = len(R_all) > group_size  # a list of at most n Q blocks stays whole
             owner_steps = []
             for grp in range(n_groups):
-                R = [q for q in R_all if q // group_size == grp]
+                if split:
+                    R = [q for q in R_all if q // group_size == grp]
+                else:
+                    R = R_all if grp == 0 else []
                 revq.extend(R)
                 revq_ptr.append(len(revq))
                 qp = [8 * q + j for q in R if int(c_q[q]) == BLOCK for j in range(8)]

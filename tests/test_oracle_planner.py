@@ -263,9 +263,11 @@ def _group_lists(t, n_groups):
 @pytest.mark.parametrize("q_group", [1, 3, 8])
 def test_q_groups_partition_each_reverse_neighbourhood(q_group):
     """Section 3.3.2: the group lists of an owner are its one-group list cut at multiples of
-    q_group; every edge's token pairs are still visited once (bwd_useful_check == useful);
-    the work items are the non-empty (owner, group) pairs, and an owner without any keeps
-    one item for group 0."""
+    q_group, unless that list holds at most q_group Q blocks, which then stays whole in
+    group 0; no group list exceeds q_group blocks (the bound the grouping serves); every
+    edge's token pairs are still visited once (bwd_useful_check == useful); the work items
+    are the non-empty (owner, group) pairs, and an owner without any keeps one item for
+    group 0."""
     for w in (make_workload(1), make_workload(3, heads=[0]), make_workload(5, heads=[1])):
         one = oracle_plan(w)
         t = oracle_plan(w, q_group=q_group)
@@ -276,8 +278,12 @@ def test_q_groups_partition_each_reverse_neighbourhood(q_group):
         for o, r in enumerate(R1):
             parts = Rg[o * n_groups:(o + 1) * n_groups]
             assert sum(parts, []) == r
-            for grp, part in enumerate(parts):
-                assert all(grp * q_group <= q < (grp + 1) * q_group for q in part)
+            assert max(len(part) for part in parts) <= q_group
+            if len(r) <= q_group:
+                assert parts[0] == r
+            else:
+                for grp, part in enumerate(parts):
+                    assert all(grp * q_group <= q < (grp + 1) * q_group for q in part)
         assert t.stats["bwd_useful_check"] == t.stats["useful"] == one.stats["useful"]
         assert np.array_equal(t.owners, one.owners)
         # work items
@@ -319,6 +325,25 @@ def test_q_groups_worked_by_hand():
     assert t.adj.tolist() == [k0, k1, k0]
     assert t.stats["bwd_physical"] == 3 * 128 * 128
     assert full != k0
+
+
+def test_q_groups_keep_short_lists_whole_worked_by_hand():
+    """Q blocks 0..3 full, K blocks 0 and 1 full (owners 0 and 1, pages 0..7 and 8..15);
+    q1 -> k0, q2 -> k0 (owner 0: [1, 2]) and q0, q1, q3 -> k1 (owner 1: [0, 1, 3]).  With
+    q_group = 2 the ranges are {0, 1} and {2, 3}: owner 0's two blocks are within the
+    bound and stay in group 0 although they straddle the ranges; owner 1's three are cut
+    into [0, 1] and [3].  Steps: (0, 0) 2, (0, 1) 0, (1, 0) 2, (1, 1) 1; work items by
+    descending steps then owner, group: (0, 0), (0, 2), (0, 3)."""
+    p = make_problem([128] * 4, [128, 128], [[1], [0, 1], [0], [1]])
+    t = oracle_plan(p, q_group=2)
+    assert t.owners.tolist() == [list(range(8)), list(range(8, 16))]
+    assert t.revq_ptr.tolist() == [0, 2, 2, 4, 5]
+    assert t.revq.tolist() == [1, 2, 0, 1, 3]
+    assert t.qwalk_ptr.tolist() == [0, 16, 16, 32, 40]
+    assert t.qwalk.tolist() == list(range(8, 24)) + list(range(0, 16)) + list(range(24, 32))
+    assert t.bwd_queue.tolist() == [[0, 0], [0, 2], [0, 3]]
+    assert t.adj.tolist() == [(1 << 64) - 1] * 5
+    assert t.stats["bwd_physical"] == t.stats["useful"] == 5 * 128 * 128
 
 
 def _order_case(key):
