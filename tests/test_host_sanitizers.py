@@ -12,8 +12,18 @@ from block_sparse_attention_11_amd import build as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def _sanitized_library_is_current():
+    if not os.path.exists(B.SAN_OUT):
+        return False
+    built = os.path.getmtime(B.SAN_OUT)
+    csrc = os.path.join(os.path.dirname(os.path.abspath(B.__file__)), "csrc")
+    sources = [os.path.join(csrc, f) for f in os.listdir(csrc)] + [os.path.join(ROOT, "include", "kpage.h")]
+    return all(os.path.getmtime(f) <= built for f in sources)
+
+
 def test_planner_and_abi_host_code_clean_under_asan_and_ubsan():
-    lib = B.SAN_OUT if os.path.exists(B.SAN_OUT) else B.build_sanitized()
+    # rebuilt when a source changed since the last sanitized build (plain builds leave it)
+    lib = B.SAN_OUT if _sanitized_library_is_current() else B.build_sanitized()
     env = dict(os.environ, KPAGE_LIB=lib, LD_PRELOAD=B.asan_runtime(),
                ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
