@@ -277,10 +277,13 @@ kpage_status build_backward_on_device(PlanT *pl, hipStream_t stream) {
   std::string err;
   DevBwdTables &T = pl->DB;
   kpage_status s = build_backward_device(
-      pl->DP, pl->DF.page_block, stream, [pl](size_t b) { return plan_alloc(pl, b); }, &T, &err);
+      pl->DP, pl->DF.page_block, pl->P.q_group, stream, [pl](size_t b) { return plan_alloc(pl, b); }, &T, &err);
   if (s != KPAGE_OK) return fail(s, err);
   pl->d_bitems = T.items;
   pl->n_bitems = int(T.n_items);
+  pl->d_reduce = T.reduce;
+  pl->n_reduce = int(T.n_reduce);
+  pl->n_partials = T.n_partials;
   pl->d_owners = T.owners;
   pl->d_kmask = T.kmask;
   pl->d_qpages = T.qpages;
@@ -308,10 +311,12 @@ kpage_status ensure_backward_on_host(PlanT *pl) {
   const DevBwdTables &T = pl->DB;
   BwdTables &B = pl->B;
   const int64_t G = pl->P.slots;
+  const int64_t n_pairs = T.n_own * T.n_groups;  // (owner, group) pairs
+  B.n_groups = T.n_groups;
   const bool ok = copy_down(B.owner_ptr, T.owner_ptr, G + 1) &&
                   copy_down(B.owners, T.owners, T.n_own * kOwnerSlots) && copy_down(B.aligned, T.aligned, T.n_own) &&
-                  copy_down(B.revq_ptr, T.revq_ptr, T.n_own + 1) && copy_down(B.revq, T.revq, T.revq_total) &&
-                  copy_down(B.qwalk_ptr, T.qwalk_ptr, T.n_own + 1) && copy_down(B.qwalk, T.qwalk, T.qwalk_total) &&
+                  copy_down(B.revq_ptr, T.revq_ptr, n_pairs + 1) && copy_down(B.revq, T.revq, T.revq_total) &&
+                  copy_down(B.qwalk_ptr, T.qwalk_ptr, n_pairs + 1) && copy_down(B.qwalk, T.qwalk, T.qwalk_total) &&
                   copy_down(B.adj, T.adj, T.qwalk_total / kOwnerSlots) &&
                   copy_down(B.bwd_queue, T.bwd_queue, 2 * T.n_items) &&
                   copy_down(B.uncovered_ptr, T.uncovered_ptr, G + 1) &&
@@ -428,6 +433,7 @@ size_t partials_offset(size_t rows) { return (2 * rows * 4 + 255) / 256 * 256; }
 
 kpage_status count_partials(PlanT *pl) {
   if (pl->n_partials >= 0) return KPAGE_OK;
+  if (pl->device_planned) return build_backward_on_device(pl, nullptr);  // sets n_partials
   const kpage_status s = ensure_backward_on_host(pl);
   if (s != KPAGE_OK) return s;
   std::vector<BwdItem> items;
@@ -594,10 +600,6 @@ static kpage_status plan_device_body(const kpage_problem *problem, int64_t q2k_n
   if (s != KPAGE_OK) {
     delete pl;
     return fail(s, err);
-  }
-  if (pl->P.q_group != 0) {
-    delete pl;
-    return fail(KPAGE_ERR_UNSUPPORTED, "kpage_plan_device builds one Q group only (q_group = 0)");
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Problem &P = pl->P;

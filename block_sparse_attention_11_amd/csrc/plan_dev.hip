@@ -443,7 +443,29 @@ struct BwdSummary {
   int64_t n_own, revq_total, qwalk_total, uncovered_total;
   int32_t max_uncovered, pad;
   unsigned long long useful_check;
+  int64_t n_witems, n_part, n_red;  // per slot (shared graph) or in all: items, partial slots, reduces
 };
+
+// Q groups (section 3.3.2): the query blocks [lo, hi) of group grp of an owner.  An
+// owner whose reverse neighbourhood holds more than gsz query blocks is cut into the
+// ranges [grp gsz, (grp + 1) gsz); a smaller one keeps its whole list in group 0.
+__device__ __forceinline__ void group_range(bool split, int grp, int gsz, int n_q, int *lo, int *hi) {
+  if (split) {
+    *lo = grp * gsz;
+    *hi = min(n_q, (grp + 1) * gsz);
+  } else {
+    *lo = grp == 0 ? 0 : n_q;
+    *hi = n_q;
+  }
+}
+
+// bits [lo, hi) of word w of a query-block bitset
+__device__ __forceinline__ uint32_t range_word(int w, int lo, int hi) {
+  const int a = max(lo - 32 * w, 0), b = min(hi - 32 * w, 32);
+  if (b <= a) return 0u;
+  const uint32_t upto = b == 32 ? ~0u : (1u << b) - 1u;
+  return upto & ~((1u << a) - 1u);
+}
 
 __device__ __forceinline__ uint32_t page_mask(int c, int j) {
   return (j + 1) * kPageRows <= c ? kFullMask : tail_mask(c);
@@ -642,12 +664,14 @@ __global__ void k_edges(DevProblem p, const int32_t *owner_of, int nkw, int nqw,
   }
 }
 
-// per (slot, owner): reverse-Q count, Q-walk length (full query blocks first, 8 pages
-// each, then the pages of partial ones, padded to a multiple of 8), slot, alignment
-// flag and the empty page slots of the owner table
+// per (slot, owner): for each Q group, the reverse-Q count and the Q-walk length (full
+// query blocks first, 8 pages each, then the pages of partial ones, padded to a multiple
+// of 8), at (owner, group) = tg * ng + group; the owner's slot, whether it is split into
+// groups, its alignment flag and the empty page slots of the owner table
 __global__ void k_owner_counts(DevProblem p, const int64_t *owner_ptr, const int32_t *n_own, const int32_t *own_info,
-                               const uint32_t *own_q, const uint32_t *fullq, int nqw, int64_t *rcount, int64_t *qlen,
-                               int32_t *owner_slot, uint8_t *aligned, int32_t *owners, uint32_t *kmask) {
+                               const uint32_t *own_q, const uint32_t *fullq, int nqw, int gsz, int ng, int64_t *rcount,
+                               int64_t *qlen, int32_t *owner_slot, uint8_t *split_of, uint8_t *aligned,
+                               int32_t *owners, uint32_t *kmask) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= int64_t(p.slots) * p.n_kv) return;
   const int g = int(i / p.n_kv), t = int(i % p.n_kv);
@@ -655,21 +679,29 @@ __global__ void k_owner_counts(DevProblem p, const int64_t *owner_ptr, const int
   const int64_t tg = owner_ptr[g] + t;
   const uint32_t *bm = own_q + i * nqw;
   const uint32_t *fm = fullq + int64_t(g) * nqw;
-  int64_t r = 0, pages = 0;
-  for (int w = 0; w < nqw; ++w) {
-    const uint32_t bits = bm[w];
-    r += __popc(bits);
-    pages += int64_t(kOwnerSlots) * __popc(bits & fm[w]);
-    uint32_t part = bits & ~fm[w];
-    while (part) {
-      const int b = __ffs(part) - 1;
-      part &= part - 1;
-      pages += pages_of(p.q_valid[int64_t(g) * p.n_q + 32 * w + b]);
+  int64_t r_all = 0;
+  for (int w = 0; w < nqw; ++w) r_all += __popc(bm[w]);
+  const bool split = r_all > gsz;
+  for (int grp = 0; grp < ng; ++grp) {
+    int lo, hi;
+    group_range(split, grp, gsz, p.n_q, &lo, &hi);
+    int64_t r = 0, pages = 0;
+    for (int w = lo >> 5; w < nqw && 32 * w < hi; ++w) {
+      const uint32_t bits = bm[w] & range_word(w, lo, hi);
+      r += __popc(bits);
+      pages += int64_t(kOwnerSlots) * __popc(bits & fm[w]);
+      uint32_t part = bits & ~fm[w];
+      while (part) {
+        const int b = __ffs(part) - 1;
+        part &= part - 1;
+        pages += pages_of(p.q_valid[int64_t(g) * p.n_q + 32 * w + b]);
+      }
     }
+    rcount[tg * ng + grp] = r;
+    qlen[tg * ng + grp] = (pages + kOwnerSlots - 1) / kOwnerSlots * kOwnerSlots;
   }
-  rcount[tg] = r;
-  qlen[tg] = (pages + kOwnerSlots - 1) / kOwnerSlots * kOwnerSlots;
   owner_slot[tg] = g;
+  split_of[tg] = split ? 1 : 0;
   const int32_t info = own_info[i];
   const int blocks = info & 0xFFFF, np = info >> 16;
   aligned[tg] = (blocks == 1 && np == kOwnerSlots) ? 1 : 0;
@@ -696,12 +728,12 @@ __global__ void k_owner_pages(DevProblem p, const int32_t *owner_of, const int32
   }
 }
 
-// revq_ptr and qwalk_ptr over all owners
-__global__ __launch_bounds__(kScanThreads) void k_owner_scans(const BwdSummary *s, const int64_t *rcount,
+// revq_ptr and qwalk_ptr over all (owner, group) pairs
+__global__ __launch_bounds__(kScanThreads) void k_owner_scans(const BwdSummary *s, int ng, const int64_t *rcount,
                                                               const int64_t *qlen, int64_t *revq_ptr,
                                                               int64_t *qwalk_ptr, BwdSummary *out) {
   __shared__ int64_t lds[kScanThreads];
-  const int64_t n = s->n_own;
+  const int64_t n = s->n_own * ng;
   int64_t c1 = 0, c2 = 0;
   for (int64_t base = 0; base < n; base += kScanThreads) {
     const int64_t t = base + threadIdx.x;
@@ -723,21 +755,27 @@ __global__ __launch_bounds__(kScanThreads) void k_owner_scans(const BwdSummary *
   }
 }
 
-// per owner: reverse-Q list (ascending q) and Q-page walk
-__global__ void k_owner_fill(DevProblem p, int64_t n_own, const int64_t *owner_ptr, const int32_t *owner_slot,
-                             const uint32_t *own_q, const uint32_t *fullq, int nqw, const int64_t *revq_ptr,
-                             const int64_t *qwalk_ptr, int32_t *revq, int32_t *qwalk, int32_t *qpages) {
-  const int64_t tg = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (tg >= n_own) return;
+// per (owner, group): reverse-Q list (ascending q) and Q-page walk
+__global__ void k_owner_fill(DevProblem p, int64_t n_own, int gsz, int ng, const int64_t *owner_ptr,
+                             const int32_t *owner_slot, const uint8_t *split_of, const uint32_t *own_q,
+                             const uint32_t *fullq, int nqw, const int64_t *revq_ptr, const int64_t *qwalk_ptr,
+                             int32_t *revq, int32_t *qwalk, int32_t *qpages) {
+  const int64_t wi = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (wi >= n_own * ng) return;
+  const int64_t tg = wi / ng;
+  const int grp = int(wi % ng);
   const int g = owner_slot[tg];
   const int64_t t = tg - owner_ptr[g];
+  int lo, hi;
+  group_range(split_of[tg] != 0, grp, gsz, p.n_q, &lo, &hi);
   const uint32_t *bm = own_q + (int64_t(g) * p.n_kv + t) * nqw;
   const uint32_t *fm = fullq + int64_t(g) * nqw;
-  int64_t r = revq_ptr[tg];
-  for (int w = 0; w < nqw; ++w)
-    for (uint32_t bits = bm[w]; bits; bits &= bits - 1) revq[r++] = 32 * w + __ffs(bits) - 1;
-  int64_t pos = qwalk_ptr[tg];
-  const int64_t end = qwalk_ptr[tg + 1];
+  const int w0 = lo >> 5, w1 = min(nqw, (hi + 31) >> 5);
+  int64_t r = revq_ptr[wi];
+  for (int w = w0; w < w1; ++w)
+    for (uint32_t bits = bm[w] & range_word(w, lo, hi); bits; bits &= bits - 1) revq[r++] = 32 * w + __ffs(bits) - 1;
+  int64_t pos = qwalk_ptr[wi];
+  const int64_t end = qwalk_ptr[wi + 1];
   int32_t first = -1;
   auto emit = [&](int32_t qp) {
     if (first < 0) first = qp;
@@ -745,13 +783,13 @@ __global__ void k_owner_fill(DevProblem p, int64_t n_own, const int64_t *owner_p
     qpages[pos] = qp >= 0 ? qp : first;
     ++pos;
   };
-  for (int w = 0; w < nqw; ++w)  // full query blocks: all 8 pages
-    for (uint32_t bits = bm[w] & fm[w]; bits; bits &= bits - 1) {
+  for (int w = w0; w < w1; ++w)  // full query blocks: all 8 pages
+    for (uint32_t bits = bm[w] & fm[w] & range_word(w, lo, hi); bits; bits &= bits - 1) {
       const int q = 32 * w + __ffs(bits) - 1;
       for (int j = 0; j < kOwnerSlots; ++j) emit(kOwnerSlots * q + j);
     }
-  for (int w = 0; w < nqw; ++w)  // partial query blocks: their valid pages
-    for (uint32_t bits = bm[w] & ~fm[w]; bits; bits &= bits - 1) {
+  for (int w = w0; w < w1; ++w)  // partial query blocks: their valid pages
+    for (uint32_t bits = bm[w] & ~fm[w] & range_word(w, lo, hi); bits; bits &= bits - 1) {
       const int q = 32 * w + __ffs(bits) - 1;
       const int np = pages_of(p.q_valid[int64_t(g) * p.n_q + q]);
       for (int j = 0; j < np; ++j) emit(kOwnerSlots * q + j);
@@ -772,16 +810,17 @@ __device__ __forceinline__ int64_t upper_index(const int64_t *ptr, int64_t n, in
 
 // per 8-page step: adjacency word, bit 8 j + i = (Q page j of the step, owner page i)
 // belong to a selected block pair; pair count of the step for the visited-pair check
-__global__ void k_adj(DevProblem p, const int32_t *page_block, int64_t n_own, int64_t n_steps, unsigned long long mult,
-                      const int32_t *owner_slot, const int64_t *qwalk_ptr, const int32_t *owners, const int32_t *qwalk,
-                      const uint32_t *edge, int nkw, uint64_t *adj, BwdSummary *s) {
+__global__ void k_adj(DevProblem p, const int32_t *page_block, int64_t n_own, int ng, int64_t n_steps,
+                      unsigned long long mult, const int32_t *owner_slot, const int64_t *qwalk_ptr,
+                      const int32_t *owners, const int32_t *qwalk, const uint32_t *edge, int nkw, uint64_t *adj,
+                      BwdSummary *s) {
   __shared__ unsigned long long acc;
   if (threadIdx.x == 0) acc = 0;
   __syncthreads();
   const int64_t st = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (st < n_steps) {
     const int64_t pos = int64_t(kOwnerSlots) * st;
-    const int64_t tg = upper_index(qwalk_ptr, n_own, pos);
+    const int64_t tg = upper_index(qwalk_ptr, n_own * ng, pos) / ng;
     const int g = owner_slot[tg];
     const int64_t n_pages = p.seq_kv / kPageRows;
     int kb[kOwnerSlots];
@@ -816,30 +855,95 @@ __global__ void k_adj(DevProblem p, const int32_t *page_block, int64_t n_own, in
   if (threadIdx.x == 0 && acc) atomicAdd(&s->useful_check, acc);
 }
 
-// per (bh, owner within slot), f = that pair's index in (bh, owner) order: queue sort
-// key (steps descending, then f) and the launch item at its XCD position
-__global__ void k_bwd_items(DevProblem p, int64_t n_own, int64_t n_items, const int64_t *owner_ptr,
-                            const int64_t *qwalk_ptr, unsigned long long *keys, BwdItem *items) {
+// Work items (section 3.3.2): every (owner, group) with a non-empty Q walk, plus group 0
+// of an owner with none (it still writes its zero gradients), in (owner, group) order.
+// One workgroup scans the n_own * ng pairs: item_pos[w] = index of pair w among the
+// items (item_pos[n] = their number), item_w[index] = w.  Then per owner with more than
+// one item: consecutive fp32 partial slots in group order (part_base) and one reduce
+// entry (red_pos), in owner order.  Counts per graph slot for a shared graph (each
+// (b, h) repeats them), over all slots otherwise.
+__global__ __launch_bounds__(kScanThreads) void k_item_scan(const BwdSummary *s, int ng, const int64_t *qwalk_ptr,
+                                                            int64_t *item_pos, int64_t *item_w, int64_t *part_base,
+                                                            int64_t *red_pos, BwdSummary *out) {
+  __shared__ int64_t lds[kScanThreads];
+  const int64_t n_own = s->n_own, n = n_own * ng;
+  int64_t c = 0;
+  for (int64_t base = 0; base < n; base += kScanThreads) {
+    const int64_t w = base + threadIdx.x;
+    bool flag = false;
+    if (w < n) {
+      const int64_t tg = w / ng;
+      const bool empty_owner = qwalk_ptr[(tg + 1) * ng] == qwalk_ptr[tg * ng];
+      flag = qwalk_ptr[w + 1] > qwalk_ptr[w] || (w % ng == 0 && empty_owner);
+    }
+    int64_t tot;
+    const int64_t pos = c + block_scan(flag ? 1 : 0, lds, &tot);
+    if (w < n) {
+      item_pos[w] = pos;
+      if (flag) item_w[pos] = w;
+    }
+    c += tot;
+  }
+  if (threadIdx.x == 0) item_pos[n] = c;
+  __syncthreads();
+  int64_t cp = 0, cr = 0;
+  for (int64_t base = 0; base < n_own; base += kScanThreads) {
+    const int64_t tg = base + threadIdx.x;
+    const int64_t cnt = tg < n_own ? item_pos[(tg + 1) * ng] - item_pos[tg * ng] : 0;
+    int64_t tp, tr;
+    const int64_t pp = cp + block_scan(cnt > 1 ? cnt : 0, lds, &tp);
+    const int64_t pr = cr + block_scan(cnt > 1 ? 1 : 0, lds, &tr);
+    if (tg < n_own) {
+      part_base[tg] = pp;
+      red_pos[tg] = pr;
+    }
+    cp += tp;
+    cr += tr;
+  }
+  if (threadIdx.x == 0) {
+    out->n_witems = c;
+    out->n_part = cp;
+    out->n_red = cr;
+  }
+}
+
+// per work item f: queue sort key (steps descending, then f) and the launch item at its
+// XCD position, with its fp32 partial slot when its owner has more than one item
+__global__ void k_bwd_items(DevProblem p, int ng, int64_t n_w, int64_t n_items, int64_t n_part_slot,
+                            const int64_t *qwalk_ptr, const int32_t *owner_slot, const int64_t *item_pos,
+                            const int64_t *item_w, const int64_t *part_base, unsigned long long *keys,
+                            BwdItem *items) {
   const int64_t f = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (f >= n_items) return;
-  int bh;
-  int64_t tg;
-  if (p.per_head) {
-    bh = int(upper_index(owner_ptr, p.slots, f));
-    tg = f;
-  } else {
-    bh = int(f / n_own);
-    tg = f % n_own;
-  }
-  const int32_t steps = int32_t((qwalk_ptr[tg + 1] - qwalk_ptr[tg]) / kOwnerSlots);
+  const int64_t w = item_w[p.per_head ? f : f % n_w];
+  const int64_t tg = w / ng;
+  const int bh = p.per_head ? owner_slot[tg] : int(f / n_w);
+  const int32_t steps = int32_t((qwalk_ptr[w + 1] - qwalk_ptr[w]) / kOwnerSlots);
   keys[f] = ((unsigned long long)(0x7FFFFFFF - steps) << 32) | (unsigned long long)(uint32_t)f;
+  const int64_t first = item_pos[tg * ng], cnt = item_pos[(tg + 1) * ng] - first;
   BwdItem x{};
-  x.qwalk_off = qwalk_ptr[tg];
+  x.qwalk_off = qwalk_ptr[w];
   x.bh = bh;
   x.owner = int32_t(tg);
   x.n_steps = steps;
-  x.partial = -1;
+  x.partial = cnt > 1 ? int32_t((p.per_head ? 0 : int64_t(bh) * n_part_slot) + part_base[tg] + (item_pos[w] - first))
+                      : -1;
   items[launch_position(f, n_items, p.xcd_chunk)] = x;
+}
+
+// reduce entries of the owners split over several items, in (bh, owner) order
+__global__ void k_bwd_reduce_list(DevProblem p, int64_t n_own, int ng, int64_t n_part_slot, int64_t n_red_slot,
+                                  const int32_t *owner_slot, const int64_t *item_pos, const int64_t *part_base,
+                                  const int64_t *red_pos, int64_t n, BwdReduce *reduce) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int64_t tg = p.per_head ? i : i % n_own;
+  const int bh = p.per_head ? owner_slot[tg] : int(i / n_own);
+  const int64_t cnt = item_pos[(tg + 1) * ng] - item_pos[tg * ng];
+  if (cnt < 2) return;
+  const int64_t at = (p.per_head ? 0 : int64_t(bh) * n_red_slot) + red_pos[tg];
+  reduce[at] = BwdReduce{bh, int32_t(tg), int32_t((p.per_head ? 0 : int64_t(bh) * n_part_slot) + part_base[tg]),
+                         int32_t(cnt)};
 }
 
 // The last bwd_tail_len(count) items of each XCD's launch sequence (positions 8 j + x)
@@ -879,29 +983,27 @@ __global__ __launch_bounds__(1024) void k_bwd_tails(BwdItem *items, int64_t n) {
   for (int i = int(threadIdx.x); i < t; i += int(blockDim.x)) items[(j0 + i) * kXcds + x] = buf[uint32_t(key[i])];
 }
 
-__global__ void k_bwd_queue_out(DevProblem p, int64_t n_own, int64_t n_items, const int64_t *owner_ptr,
-                                const unsigned long long *keys, int32_t *queue) {
+__global__ void k_bwd_queue_out(DevProblem p, int ng, int64_t n_w, int64_t n_items, const int64_t *owner_ptr,
+                                const int32_t *owner_slot, const int64_t *item_w, const unsigned long long *keys,
+                                int32_t *queue) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n_items) return;
   const int64_t f = int64_t(keys[i] & 0xFFFFFFFFull);
-  int bh;
-  int64_t t;
-  if (p.per_head) {
-    bh = int(upper_index(owner_ptr, p.slots, f));
-    t = f - owner_ptr[bh];
-  } else {
-    bh = int(f / n_own);
-    t = f % n_own;
-  }
-  queue[2 * i] = bh;
-  queue[2 * i + 1] = int32_t(t);
+  const int64_t w = item_w[p.per_head ? f : f % n_w];
+  const int64_t tg = w / ng;
+  const int g = owner_slot[tg];
+  queue[2 * i] = p.per_head ? g : int(f / n_w);
+  queue[2 * i + 1] = int32_t((tg - owner_ptr[g]) * ng + w % ng);
 }
 
 }  // namespace
 
-kpage_status build_backward_device(const DevProblem &p, const int32_t *page_block, hipStream_t st,
+kpage_status build_backward_device(const DevProblem &p, const int32_t *page_block, int q_group, hipStream_t st,
                                    const DevAlloc &alloc, DevBwdTables *t, std::string *err) {
   const int G = p.slots;
+  const int gsz = q_group > 0 ? std::min(q_group, p.n_q) : p.n_q;
+  const int ng = (p.n_q + gsz - 1) / gsz;
+  t->n_groups = ng;
   const int64_t GK = int64_t(G) * p.n_kv, GQ = int64_t(G) * p.n_q;
   const int64_t n_pages = p.seq_kv / kPageRows;
   const int nkw = (p.n_kv + 31) / 32, nqw = (p.n_q + 31) / 32;
@@ -928,16 +1030,21 @@ kpage_status build_backward_device(const DevProblem &p, const int32_t *page_bloc
   uint32_t *own_q = static_cast<uint32_t *>(A(GK * nqw, 4));
   uint32_t *rev_k = static_cast<uint32_t *>(A(GK * nqw, 4));
   uint32_t *fullq = static_cast<uint32_t *>(A(int64_t(G) * nqw, 4));
-  int64_t *rcount = static_cast<int64_t *>(A(GK, 8));
-  int64_t *qlen = static_cast<int64_t *>(A(GK, 8));
+  int64_t *rcount = static_cast<int64_t *>(A(GK * ng, 8));
+  int64_t *qlen = static_cast<int64_t *>(A(GK * ng, 8));
   int32_t *owner_slot = static_cast<int32_t *>(A(GK, 4));
+  uint8_t *split_of = static_cast<uint8_t *>(A(GK, 1));
+  int64_t *item_pos = static_cast<int64_t *>(A(GK * ng + 1, 8));
+  int64_t *item_w = static_cast<int64_t *>(A(GK * ng, 8));
+  int64_t *part_base = static_cast<int64_t *>(A(GK, 8));
+  int64_t *red_pos = static_cast<int64_t *>(A(GK, 8));
   // owner-indexed tables at their upper bound (at most one owner per block)
   t->owner_ptr = static_cast<int64_t *>(A(G + 1, 8));
   t->owners = static_cast<int32_t *>(A(GK * kOwnerSlots, 4));
   t->kmask = static_cast<uint32_t *>(A(GK * kOwnerSlots, 4));
   t->aligned = static_cast<uint8_t *>(A(GK, 1));
-  t->revq_ptr = static_cast<int64_t *>(A(GK + 1, 8));
-  t->qwalk_ptr = static_cast<int64_t *>(A(GK + 1, 8));
+  t->revq_ptr = static_cast<int64_t *>(A(GK * ng + 1, 8));
+  t->qwalk_ptr = static_cast<int64_t *>(A(GK * ng + 1, 8));
   t->uncovered_ptr = static_cast<int64_t *>(A(G + 1, 8));
   t->uncovered = static_cast<int32_t *>(A(int64_t(G) * n_pages, 4));
   if (oom) {
@@ -968,11 +1075,14 @@ kpage_status build_backward_device(const DevProblem &p, const int32_t *page_bloc
                      t->uncovered);
   hipLaunchKernelGGL(k_edges, dim3(blocks_for(GQ, TB)), dim3(TB), 0, st, p, owner_of, nkw, nqw, edge, own_q, fullq);
   hipLaunchKernelGGL(k_owner_counts, dim3(blocks_for(GK, TB)), dim3(TB), 0, st, p, t->owner_ptr, n_own, own_info,
-                     own_q, fullq, nqw, rcount, qlen, owner_slot, t->aligned, t->owners, t->kmask);
+                     own_q, fullq, nqw, gsz, ng, rcount, qlen, owner_slot, split_of, t->aligned, t->owners,
+                     t->kmask);
   hipLaunchKernelGGL(k_owner_pages, dim3(blocks_for(GK, TB)), dim3(TB), 0, st, p, owner_of, pos_of, t->owner_ptr,
                      t->owners, t->kmask);
-  hipLaunchKernelGGL(k_owner_scans, dim3(1), dim3(kScanThreads), 0, st, d_sum, rcount, qlen, t->revq_ptr,
+  hipLaunchKernelGGL(k_owner_scans, dim3(1), dim3(kScanThreads), 0, st, d_sum, ng, rcount, qlen, t->revq_ptr,
                      t->qwalk_ptr, d_sum);
+  hipLaunchKernelGGL(k_item_scan, dim3(1), dim3(kScanThreads), 0, st, d_sum, ng, t->qwalk_ptr, item_pos, item_w,
+                     part_base, red_pos, d_sum);
   KP_CHECK(hipGetLastError());
   BwdSummary h{};
   KP_CHECK(hipMemcpyAsync(&h, d_sum, sizeof(BwdSummary), hipMemcpyDeviceToHost, st));
@@ -982,8 +1092,11 @@ kpage_status build_backward_device(const DevProblem &p, const int32_t *page_bloc
   t->qwalk_total = h.qwalk_total;
   t->uncovered_total = h.uncovered_total;
   t->max_uncovered = h.max_uncovered;
-  t->n_items = int64_t(mult) * h.n_own;
-  if (t->n_items >= (int64_t(1) << 31)) {
+  const int64_t n_w = h.n_witems;  // work items per graph slot (shared graph) or in all
+  t->n_items = int64_t(mult) * n_w;
+  t->n_partials = int64_t(mult) * h.n_part;
+  t->n_reduce = int64_t(mult) * h.n_red;
+  if (t->n_items >= (int64_t(1) << 31) || t->n_partials >= (int64_t(1) << 31)) {
     *err = "more than 2^31 backward work items";
     return KPAGE_ERR_UNSUPPORTED;
   }
@@ -995,18 +1108,25 @@ kpage_status build_backward_device(const DevProblem &p, const int32_t *page_bloc
   t->items = static_cast<BwdItem *>(A(t->n_items, sizeof(BwdItem)));
   t->bwd_queue = static_cast<int32_t *>(A(2 * t->n_items, 4));
   unsigned long long *keys = static_cast<unsigned long long *>(A(2 * t->n_items, 8));
+  t->reduce = static_cast<BwdReduce *>(A(t->n_reduce, sizeof(BwdReduce)));
   if (oom) {
     *err = "device allocation failed while planning the backward";
     return KPAGE_ERR_OOM;
   }
   if (h.n_own > 0) {
-    hipLaunchKernelGGL(k_owner_fill, dim3(blocks_for(h.n_own, TB)), dim3(TB), 0, st, p, h.n_own, t->owner_ptr,
-                       owner_slot, own_q, fullq, nqw, t->revq_ptr, t->qwalk_ptr, t->revq, t->qwalk, t->qpages);
+    hipLaunchKernelGGL(k_owner_fill, dim3(blocks_for(h.n_own * ng, TB)), dim3(TB), 0, st, p, h.n_own, gsz, ng,
+                       t->owner_ptr, owner_slot, split_of, own_q, fullq, nqw, t->revq_ptr, t->qwalk_ptr, t->revq,
+                       t->qwalk, t->qpages);
     if (n_steps > 0)
-      hipLaunchKernelGGL(k_adj, dim3(blocks_for(n_steps, TB)), dim3(TB), 0, st, p, page_block, h.n_own, n_steps, mult,
-                         owner_slot, t->qwalk_ptr, t->owners, t->qwalk, edge, nkw, t->adj, d_sum);
-    hipLaunchKernelGGL(k_bwd_items, dim3(blocks_for(t->n_items, TB)), dim3(TB), 0, st, p, h.n_own, t->n_items,
-                       t->owner_ptr, t->qwalk_ptr, keys, t->items);
+      hipLaunchKernelGGL(k_adj, dim3(blocks_for(n_steps, TB)), dim3(TB), 0, st, p, page_block, h.n_own, ng, n_steps,
+                         mult, owner_slot, t->qwalk_ptr, t->owners, t->qwalk, edge, nkw, t->adj, d_sum);
+    hipLaunchKernelGGL(k_bwd_items, dim3(blocks_for(t->n_items, TB)), dim3(TB), 0, st, p, ng, n_w, t->n_items,
+                       h.n_part, t->qwalk_ptr, owner_slot, item_pos, item_w, part_base, keys, t->items);
+    if (t->n_reduce > 0) {
+      const int64_t n_red_threads = p.per_head ? h.n_own : int64_t(mult) * h.n_own;
+      hipLaunchKernelGGL(k_bwd_reduce_list, dim3(blocks_for(n_red_threads, TB)), dim3(TB), 0, st, p, h.n_own, ng,
+                         h.n_part, h.n_red, owner_slot, item_pos, part_base, red_pos, n_red_threads, t->reduce);
+    }
     hipLaunchKernelGGL(k_bwd_tails, dim3(kXcds), dim3(1024), 0, st, t->items, t->n_items);
     size_t tmp_bytes = 0;
     KP_CHECK(hipcub::DeviceRadixSort::SortKeys(nullptr, tmp_bytes, keys, keys + t->n_items, int(t->n_items), 0, 64,
@@ -1017,8 +1137,8 @@ kpage_status build_backward_device(const DevProblem &p, const int32_t *page_bloc
       return KPAGE_ERR_OOM;
     }
     KP_CHECK(hipcub::DeviceRadixSort::SortKeys(tmp, tmp_bytes, keys, keys + t->n_items, int(t->n_items), 0, 64, st));
-    hipLaunchKernelGGL(k_bwd_queue_out, dim3(blocks_for(t->n_items, TB)), dim3(TB), 0, st, p, h.n_own, t->n_items,
-                       t->owner_ptr, keys + t->n_items, t->bwd_queue);
+    hipLaunchKernelGGL(k_bwd_queue_out, dim3(blocks_for(t->n_items, TB)), dim3(TB), 0, st, p, ng, n_w, t->n_items,
+                       t->owner_ptr, owner_slot, item_w, keys + t->n_items, t->bwd_queue);
   }
   KP_CHECK(hipGetLastError());
   KP_CHECK(hipMemcpyAsync(&h, d_sum, sizeof(BwdSummary), hipMemcpyDeviceToHost, st));

@@ -49,17 +49,20 @@ struct DevBwdTables {
   int32_t *owners = nullptr;         // [n_own][8] page ids, -1 = empty slot
   uint32_t *kmask = nullptr;         // [n_own][8] row masks of the owner pages
   uint8_t *aligned = nullptr;        // [n_own]
-  int64_t *revq_ptr = nullptr;       // [n_own + 1]
+  int64_t *revq_ptr = nullptr;       // [n_own * n_groups + 1], per (owner, group), owner-major
   int32_t *revq = nullptr;
-  int64_t *qwalk_ptr = nullptr;      // [n_own + 1]
+  int64_t *qwalk_ptr = nullptr;      // [n_own * n_groups + 1]
   int32_t *qwalk = nullptr;          // Q page ids (8 q + j), -1 = dummy
   int32_t *qpages = nullptr;         // the same with dummies pointed at the walk's first page
   uint64_t *adj = nullptr;           // one word per 8-page step
-  int32_t *bwd_queue = nullptr;      // (bh, owner within slot) pairs, queue order
-  BwdItem *items = nullptr;          // launch order (bh, owner), XCD-interleaved
+  int32_t *bwd_queue = nullptr;      // (bh, owner within slot * n_groups + group) pairs, queue order
+  BwdItem *items = nullptr;          // launch order (bh, owner, group), XCD-interleaved
+  BwdReduce *reduce = nullptr;       // owners split over several items, (bh, owner) order
   int64_t *uncovered_ptr = nullptr;  // [slots + 1]
   int32_t *uncovered = nullptr;
   int64_t n_own = 0, revq_total = 0, qwalk_total = 0, n_items = 0, uncovered_total = 0;
+  int n_groups = 1;
+  int64_t n_partials = 0, n_reduce = 0;  // fp32 partial slots and reduce entries (Q groups)
   int max_uncovered = 0;
   uint64_t bwd_physical = 0, bwd_useful_check = 0;
 };
@@ -73,9 +76,10 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
                                   const DevAlloc &alloc, DevFwdTables *t, std::string *err);
 
 // Builds the backward tables on `stream` from a descriptor already validated by
-// build_forward_device and that call's page_block table.  Synchronises `stream` twice
+// build_forward_device and that call's page_block table, with Q groups of q_group Q
+// blocks (0: one group) as the host planner builds them.  Synchronises `stream` twice
 // (table sizes, then pair counts).
-kpage_status build_backward_device(const DevProblem &p, const int32_t *page_block, hipStream_t stream,
+kpage_status build_backward_device(const DevProblem &p, const int32_t *page_block, int q_group, hipStream_t stream,
                                    const DevAlloc &alloc, DevBwdTables *t, std::string *err);
 
 }  // namespace kpage

@@ -141,11 +141,49 @@ def _bad(p, what):
     assert e2.value.status == K.KPAGE_ERR_INVALID, what
 
 
-def test_device_plan_builds_one_q_group_only():
-    p = make_problem([128, 64], [128, 40, 7], [[0, 1], [2]], heads=1, head_dim=128)
-    with pytest.raises(K.KpageError) as e:
-        K.kpage_plan_device(p, q_group=2)
-    assert e.value.status == K.KPAGE_ERR_UNSUPPORTED
+GROUP_CASES = {
+    "tiny 5x6x10 d=64, q_group 1": (lambda: make_workload(1), 1),
+    "tiny 5x6x10 d=64, q_group 3": (lambda: make_workload(1), 3),
+    "21x30x52 two heads, q_group 16": (lambda: make_workload(3, heads=[0, 1]), 16),
+    "21x45x80 top-87 two heads (per-head graphs), q_group 64": (lambda: make_workload(4, heads=[0, 1]), 64),
+    "SVG2-like partitions two heads, q_group 8": (lambda: make_workload(5, heads=[0, 1]), 8),
+    # one owner of two Q blocks straddling the ranges (kept whole), one of three (split)
+    "short lists kept whole, q_group 2": (
+        lambda: make_problem([128] * 4, [128, 128], [[1], [0, 1], [0], [1]], heads=2, head_dim=128), 2),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUP_CASES))
+def test_device_plan_q_group_tables_equal_host_plan(name):
+    make, q_group = GROUP_CASES[name]
+    _say(f"[plan] {name}")
+    h, d = same_plans(make(), name, q_group=q_group)
+    assert K.kpage_bwd_workspace_size(h) == K.kpage_bwd_workspace_size(d)
+
+
+@pytest.mark.parametrize("name,q_group", [("21x30x52 two heads", 16),
+                                          ("21x45x80 top-87 two heads (per-head graphs)", 64)])
+def test_device_plan_q_groups_attention_is_bitwise_equal(name, q_group):
+    """Q groups planned on the GPU: the same work items, fp32 partial slots and reduce
+    entries as the host plan, so the gradients are bitwise equal."""
+    w = make_workload(3 if "21x30x52" in name else 4, heads=[0, 1], with_do=True)
+    _say(f"[device plan] {name}, q_group {q_group}")
+    h, d = K.kpage_plan(w, q_group=q_group), K.kpage_plan_device(w, q_group=q_group)
+    assert K.kpage_bwd_workspace_size(h) == K.kpage_bwd_workspace_size(d)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
+    outs = []
+    for plan in (h, d):
+        o, lse = K.attn_fwd(plan, q, k, v, w.scale)
+        dq, dk, dv = K.attn_bwd(plan, q, k, v, o, lse, do, w.scale)
+        torch.cuda.synchronize()
+        outs.append([x.view(torch.int16 if x.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+                     for x in (o, lse, dq, dk, dv)])
+        del o, lse, dq, dk, dv
+    for n, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), *outs):
+        assert np.array_equal(a, b), n
+    for t in BWD_TABLES:
+        assert np.array_equal(K.kpage_plan_export(h, t), K.kpage_plan_export(d, t)), t
 
 
 def test_device_plan_rejects_malformed_descriptors():
