@@ -34,36 +34,6 @@
 namespace kpage {
 namespace {
 
-// ---------------------------------------------------------------------------
-// pre: 16 threads per query row.  Rows past c_q of their block (the plan's query sizes)
-// get lse2 = +inf and D = 0 whatever the caller's LSE and O hold there, so padded rows
-// never reach the gradients.
-template <int D>
-__global__ __launch_bounds__(256) void kpage_bwd_pre(BwdArgs a) {
-  const int64_t rows = (int64_t)a.bh_count * a.seq_q;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  if (row >= rows) return;
-  const int64_t bh = row / a.seq_q, r = row - bh * a.seq_q;
-  const int slot = a.per_head ? (int)bh : 0;
-  const bool valid = (int)(r & 127) < a.q_valid[(int64_t)slot * a.n_q + (r >> 7)];
-  constexpr int PER = D / 16;  // elements per thread
-  typedef __bf16 row_t __attribute__((ext_vector_type(PER)));
-  const row_t o = *(const row_t *)((const __bf16 *)a.o + row * D + sub * PER);
-  const row_t g = *(const row_t *)((const __bf16 *)a.dout + row * D + sub * PER);
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) s += (float)o[e] * (float)g[e];
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
-  if (sub == 0) {
-    a.delta[row] = valid ? s : 0.f;
-    const float l = a.lse[row];
-    // rows without a valid key (and rows past c_q) get +inf: exp2(x - lse2) = 0
-    a.lse2[row] = (!valid || l == kNegInf) ? __builtin_inff() : l * kLog2e;
-  }
-}
-
 // zero dK/dV on pages outside every block footprint: one block per (bh, page)
 template <int D>
 __global__ __launch_bounds__(256) void kpage_bwd_zero(BwdArgs a, int64_t pages_per_bh) {
@@ -468,13 +438,36 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
       greg[s] = qok ? gp[2 * s + g] : bf16x8{};
     }
   }
-  const float nlse2 = qok ? -a.lse2[qrow] : kNegInf;
+  // D = rowsum(dO * O) and lse2 = LSE * log2(e) of this lane's query row, from the
+  // caller's O and LSE; rows past c_q get D = 0 and lse2 = +inf whatever O and LSE hold
+  // there, and so do rows whose LSE is -inf (no valid key): exp2(x - lse2) = 0.  The
+  // K/V-owned pass, which runs after this one, reads them from the workspace: every
+  // query block is an item of this pass (empty ones as cleanup items), and its items
+  // cover every row of the query pages that the K/V-owned walks visit.
+  float dsum = 0.f;
+  if (qok) {
+    const bf16x8 *op = (const bf16x8 *)((const char *)a.o + qrow * D * 2);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const bf16x8 ov = op[2 * s + g];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)ov[e], (float)greg[s][e], dsum);
+    }
+  }
+  dsum = half_sum(dsum);  // the other half of the row's head dimension sits in lane ^ 32
+  const float lse = qok ? a.lse[qrow] : kNegInf;
+  const float lse2 = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+  if (keyoff == 0 && g == 0) {  // one lane per row (query groups repeat over key halves)
+    a.delta[qrow] = dsum;
+    a.lse2[qrow] = lse2;
+  }
+  const float nlse2 = -lse2;
   // D enters the dP^T chain as one extra k-step: A = ones in k = 0, 1 (lanes 0-31),
   // B = -D of this lane's query split into bf16 hi + lo in k = 0, 1, so the chain
   // yields dP^T - D and dS^T = P^T (dP^T - D) costs one multiply per element
   bf16x8 one_aug, nd_aug;
   {
-    const float nd = qok ? -a.delta[qrow] : 0.f;
+    const float nd = -dsum;
     const float hi = __builtin_bit_cast(float, pack_bf16(nd, 0.f) << 16);
     nd_aug = __builtin_bit_cast(bf16x8, u32x4{g ? 0u : pack_bf16(hi, nd - hi), 0u, 0u, 0u});
     one_aug = __builtin_bit_cast(bf16x8, u32x4{g ? 0u : 0x3F803F80u, 0u, 0u, 0u});
@@ -699,26 +692,11 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a) {
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
-  const int64_t rows = (int64_t)a.bh_count * a.seq_q;
-  const int64_t row_blocks = (rows + 15) / 16;
-  if (t) t->before(2, stream);
-  hipLaunchKernelGGL(kpage_bwd_pre<D>, dim3((unsigned)row_blocks), dim3(256), 0, stream, a);
-  if (t) t->after(2, stream);
   if (a.max_uncovered > 0) {
     if (t) t->before(3, stream);
     hipLaunchKernelGGL(kpage_bwd_zero<D>, dim3((unsigned)(a.bh_count * a.max_uncovered)), dim3(256), 0, stream, a,
                        (int64_t)a.max_uncovered);
     if (t) t->after(3, stream);
-  }
-  if (a.n_items > 0) {
-    if (t) t->before(4, stream);
-    hipLaunchKernelGGL(kpage_bwd_kv<D>, dim3(a.n_items), dim3(64 * kKvWaves), 0, stream, a);
-    if (t) t->after(4, stream);
-  }
-  if (a.n_reduce > 0) {
-    if (t) t->before(6, stream);
-    hipLaunchKernelGGL(kpage_bwd_kv_reduce<D>, dim3(a.n_reduce), dim3(256), 0, stream, a);
-    if (t) t->after(6, stream);
   }
   if (t && t->split_routes()) {  // profiling: one dQ launch per route
     BwdArgs only128 = a, only64 = a;
@@ -739,6 +717,17 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
     if (t) t->before(KPAGE_K_BWD_DQ, stream);
     hipLaunchKernelGGL(kpage_bwd_dq<D>, dim3(a.n_fitems128 + a.n_fitems64), dim3(64 * kDqWaves), 0, stream, a);
     if (t) t->after(KPAGE_K_BWD_DQ, stream);
+  }
+  // the K/V-owned pass reads the lse2 and D that the dQ pass wrote
+  if (a.n_items > 0) {
+    if (t) t->before(4, stream);
+    hipLaunchKernelGGL(kpage_bwd_kv<D>, dim3(a.n_items), dim3(64 * kKvWaves), 0, stream, a);
+    if (t) t->after(4, stream);
+  }
+  if (a.n_reduce > 0) {
+    if (t) t->before(6, stream);
+    hipLaunchKernelGGL(kpage_bwd_kv_reduce<D>, dim3(a.n_reduce), dim3(256), 0, stream, a);
+    if (t) t->after(6, stream);
   }
   return hipGetLastError();
 }

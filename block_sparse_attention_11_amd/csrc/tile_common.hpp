@@ -191,6 +191,13 @@ __device__ __forceinline__ float half_max(float x) {
   return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
+// x of this lane plus x of lane ^ 32 (the same sum, in the same order, in both lanes).
+__device__ __forceinline__ float half_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 // Two floats to packed bf16 (round to nearest even), a in the low half: one
 // v_cvt_pk_bf16_f32.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -269,10 +269,12 @@ enum {
                          /* then M64 x N256 items and empty-block cleanup)         */
   KPAGE_K_FWD_EXACT = 1, /* forward re-run with online rescaling of the items the  */
                          /* fixed-maximum pass marked (one launch, both routes)    */
-  KPAGE_K_BWD_PRE = 2,   /* rowsum(dO * O) and LSE * log2(e) per query row         */
+  KPAGE_K_BWD_PRE = 2,   /* reserved: rowsum(dO * O) and LSE * log2(e) per query   */
+                         /* row run inside the dQ pass; no launch, reads 0         */
   KPAGE_K_BWD_ZERO = 3,  /* dK/dV pages outside every block footprint              */
   KPAGE_K_BWD_KV = 4,    /* K/V-owned pass: dK, dV                                  */
-  KPAGE_K_BWD_DQ = 5,    /* Q-owned pass over the forward walks (both routes): dQ  */
+  KPAGE_K_BWD_DQ = 5,    /* Q-owned pass over the forward walks (both routes): dQ, */
+                         /* and rowsum(dO * O), LSE * log2(e) of every query row   */
   KPAGE_K_BWD_REDUCE = 6,/* sum of the fp32 dK/dV partials of owners split over Q groups */
   KPAGE_K_FWD_Q64 = 7,   /* timing mode 2 only: the forward's M64 x N256 launch      */
   KPAGE_K_BWD_DQ_Q64 = 8,/* timing mode 2 only: the dQ pass's M64 x N256 launch      */
