@@ -15,16 +15,17 @@
 // MI355X the owner loop would otherwise spend its LDS bandwidth on transposed dS
 // and K reads and its memory bandwidth on fp32 atomics.
 //
-// Kernels:
-//   kpage_bwd_pre   D_i = sum_d dO_id O_id and LSE_i * log2(e) (+inf for rows
-//                   without keys and rows past c_q), 16 threads per row.
+// Kernels, in launch order:
 //   kpage_bwd_zero  zero dK/dV pages that lie outside every block footprint.
+//   kpage_bwd_dq    one workgroup per forward work item (query block), both routes
+//                   in one launch: dQ; its prologue also writes the row statistics
+//                   D_i = sum_d dO_id O_id and LSE_i * log2(e) (+inf for rows without
+//                   keys and rows past c_q) of the item's rows.
 //   kpage_bwd_kv    one workgroup per (batch*head, owner), or per (batch*head,
 //                   owner, Q group) when the plan splits reverse neighbourhoods
-//                   into Q groups (section 3.3.2): dK, dV, or fp32 partials of them.
+//                   into Q groups (section 3.3.2): dK, dV, or fp32 partials of them;
+//                   reads the row statistics.
 //   kpage_bwd_kv_reduce  sums the partials of owners split over Q groups.
-//   kpage_bwd_dq    one workgroup per forward work item (query block), both routes
-//                   in one launch: dQ.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
