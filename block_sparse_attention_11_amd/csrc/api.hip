@@ -95,6 +95,7 @@ struct kpage_plan {
   bool bwd_on_device = false;
   // forward device tables
   FwdItem *d_items128 = nullptr, *d_items64 = nullptr;
+  int32_t *d_order = nullptr;  // launch position -> item of either route (NULL: M128 then M64)
   int n_items128 = 0, n_items64 = 0;
   int32_t *d_pages = nullptr;
   uint32_t *d_valid = nullptr;
@@ -219,14 +220,36 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   auto head_major = [](const FwdItem &a, const FwdItem &b) { return a.bh != b.bh ? a.bh < b.bh : a.q < b.q; };
   std::stable_sort(it128.begin(), it128.end(), head_major);
   std::stable_sort(it64.begin(), it64.end(), head_major);
-  // blocks without valid rows still own their output rows: append cleanup items (empty walk)
+  // blocks without valid rows still own their output rows: cleanup items (empty walk)
+  // after the M64 items
+  const size_t n64 = it64.size();
   for (int bh = 0; bh < P.batch * P.heads; ++bh)
     for (int q = 0; q < nq; ++q)
       if (P.q_valid[size_t(P.slot_of(bh)) * nq + q] == 0) it64.push_back(make(bh, q));
+  // Launch order: one list of both routes, head-major, each head's M128 items before its
+  // M64 items (so that they gather pages the M128 items have just brought into the
+  // caches), cleanup items last; the list position of M128 item i of head bh is i + (M64
+  // items of heads < bh), of M64 item j, j + (M128 items of heads <= bh).  The list is
+  // dealt to the XCDs by launch_position; order[b] names workgroup b's item (i, or ~j).
+  const int BH = P.batch * P.heads;
+  std::vector<int64_t> pre128(BH + 1, 0), pre64(BH + 1, 0);
+  for (const FwdItem &x : it128) ++pre128[x.bh + 1];
+  for (size_t j = 0; j < n64; ++j) ++pre64[it64[j].bh + 1];
+  for (int bh = 0; bh < BH; ++bh) {
+    pre128[bh + 1] += pre128[bh];
+    pre64[bh + 1] += pre64[bh];
+  }
   const int64_t chunk = xcd_chunk_for(P.seq_q, P.seq_kv, P.head_dim);
-  it128 = xcd_interleave(it128, chunk);
-  it64 = xcd_interleave(it64, chunk);
+  const int64_t n_all = int64_t(it128.size() + it64.size());
+  std::vector<int32_t> order(static_cast<size_t>(n_all));
+  for (size_t i = 0; i < it128.size(); ++i)
+    order[size_t(launch_position(int64_t(i) + pre64[it128[i].bh], n_all, chunk))] = int32_t(i);
+  for (size_t j = 0; j < it64.size(); ++j) {
+    const int64_t L = j < n64 ? int64_t(j) + pre128[it64[j].bh + 1] : int64_t(it128.size() + j);
+    order[size_t(launch_position(L, n_all, chunk))] = ~int32_t(j);
+  }
   kpage_status s;
+  if ((s = upload(pl, order, &pl->d_order, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, pages, &pl->d_pages, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, F.valid, &pl->d_valid, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, it128, &pl->d_items128, stream)) != KPAGE_OK) return s;
@@ -645,6 +668,7 @@ static kpage_status plan_device_body(const kpage_problem *problem, int64_t q2k_n
   pl->d_valid = pl->DF.valid;
   pl->d_items128 = pl->DF.items128;
   pl->d_items64 = pl->DF.items64;
+  pl->d_order = pl->DF.order;
   pl->n_items128 = pl->DF.n_q128;
   pl->n_items64 = pl->DF.n_q64 + pl->DF.n_zero;
   pl->fwd_on_device = true;
@@ -676,6 +700,7 @@ kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, co
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   FwdArgs a64 = a;
   a.items = plan->d_items128;
+  a.order = plan->d_order;
   a.n_items = plan->n_items128;
   a64.items = plan->d_items64;
   a64.n_items = plan->n_items64;
@@ -729,6 +754,7 @@ static kpage_status launch_backward(kpage_plan_t *plan, const void *q, const voi
                               : nullptr;
   a.fitems128 = plan->d_items128;
   a.fitems64 = plan->d_items64;
+  a.forder = plan->d_order;
   a.n_fitems128 = plan->n_items128;
   a.n_fitems64 = plan->n_items64;
   a.pages = plan->d_pages;

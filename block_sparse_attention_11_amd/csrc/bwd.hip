@@ -687,8 +687,9 @@ template <int D>
 __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * 64 * D * 2];
   const int b = blockIdx.x;
-  if (b < a.n_fitems128) dq_item<D, 128>(a, a.fitems128, b, smem);
-  else dq_item<D, 64>(a, a.fitems64, b - a.n_fitems128, smem);
+  const int t = a.forder ? a.forder[b] : (b < a.n_fitems128 ? b : ~(b - a.n_fitems128));
+  if (t >= 0) dq_item<D, 128>(a, a.fitems128, t, smem);
+  else dq_item<D, 64>(a, a.fitems64, ~t, smem);
 }
 
 template <int D>
@@ -704,6 +705,7 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
     only128.n_fitems64 = 0;
     only64.n_fitems128 = 0;
     only64.fitems128 = nullptr;
+    only128.forder = only64.forder = nullptr;
     if (a.n_fitems128 > 0) {
       t->before(KPAGE_K_BWD_DQ, stream);
       hipLaunchKernelGGL(kpage_bwd_dq<D>, dim3(a.n_fitems128), dim3(64 * kDqWaves), 0, stream, only128);

@@ -542,8 +542,9 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs a128, FwdArgs a64) {
   __shared__ FwdLds<D> lds;
   const int b = blockIdx.x;
-  if (b < a128.n_items) fwd_item<D, 128, false>(a128, b, lds);
-  else fwd_item<D, 64, false>(a64, b - a128.n_items, lds);
+  const int t = a128.order ? a128.order[b] : (b < a128.n_items ? b : ~(b - a128.n_items));
+  if (t >= 0) fwd_item<D, 128, false>(a128, t, lds);
+  else fwd_item<D, 64, false>(a64, ~t, lds);
 }
 
 // Exact re-run over the items the fast kernel marked (first LSE row = kRedoMark): a small
@@ -585,12 +586,13 @@ template <int D>
 void launch_d(const FwdArgs &a128, const FwdArgs &a64, hipStream_t stream, LaunchTimer *timer) {
   dim3 grid(a128.n_items + a64.n_items), block(kThreads);
   if (timer && timer->split_routes()) {  // profiling: one launch per route
-    FwdArgs none128 = a128, none64 = a64;
+    FwdArgs none128 = a128, none64 = a64, only128 = a128;
     none128.n_items = 0;
     none64.n_items = 0;
+    none128.order = only128.order = nullptr;  // each launch holds one route, in list order
     if (a128.n_items > 0) {
       timer->before(KPAGE_K_FWD, stream);
-      hipLaunchKernelGGL((kpage_fwd_kernel<D>), dim3(a128.n_items), block, 0, stream, a128, none64);
+      hipLaunchKernelGGL((kpage_fwd_kernel<D>), dim3(a128.n_items), block, 0, stream, only128, none64);
       timer->after(KPAGE_K_FWD, stream);
     }
     if (a64.n_items > 0) {

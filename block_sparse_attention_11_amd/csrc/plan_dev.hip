@@ -271,48 +271,83 @@ __global__ void k_queue_out(const unsigned long long *keys, int n, int n_q, int3
   queue[2 * i + 1] = int32_t(f % uint32_t(n_q));
 }
 
-// launch items in (bh, q) order per route; the Q64 list also carries the cleanup items
-// of empty query blocks after its own items
+// Launch items in (bh, q) order per route; the Q64 list also carries the cleanup items
+// of empty query blocks after its own items.  Launch order (the host planner's, in the
+// same closed form): one list of both routes, head-major, each head's M128 items before
+// its M64 items, cleanup items last; list position L of M128 item i of head bh is
+// i + (M64 items of heads < bh), of M64 item j is j + (M128 items of heads <= bh), of
+// cleanup item z is n128 + n64 + z; workgroup launch_position(L) runs that item
+// (order[] = i, or ~(index in the M64 list)).  hs128 / hs64 [BH + 1]: items of each
+// route in the heads before bh.
 __global__ __launch_bounds__(kScanThreads) void k_items(DevProblem p, const int32_t *route, const int32_t *nfull,
                                                         const int32_t *unpadded, const int64_t *walk_ptr,
-                                                        const Summary *sum, FwdItem *items128, FwdItem *items64) {
+                                                        const Summary *sum, FwdItem *items128, FwdItem *items64,
+                                                        int64_t *hs128, int64_t *hs64, int32_t *order) {
   __shared__ int64_t lds[kScanThreads];
   const int64_t n = int64_t(p.batch) * p.heads * p.n_q;
-  const int64_t n128 = sum->n_q128, n64 = sum->n_q64, nall64 = sum->n_q64 + sum->n_zero;
-  int64_t c128 = 0, c64 = 0, cz = 0;
-  for (int64_t base = 0; base < n; base += kScanThreads) {
-    const int64_t f = base + threadIdx.x;
-    int r = -1, cq = 0;
-    int64_t i = 0;
-    int bh = 0, q = 0;
-    if (f < n) {
-      bh = int(f / p.n_q);
-      q = int(f % p.n_q);
-      i = int64_t(p.per_head ? bh : 0) * p.n_q + q;
-      r = route[i];
-      cq = p.q_valid[i];
+  const int BH = p.batch * p.heads;
+  const int64_t n128 = sum->n_q128, n64 = sum->n_q64, n_all = n128 + n64 + sum->n_zero;
+  for (int pass = 0; pass < 2; ++pass) {
+    int64_t c128 = 0, c64 = 0, cz = 0;
+    for (int64_t base = 0; base < n; base += kScanThreads) {
+      const int64_t f = base + threadIdx.x;
+      int r = -1, cq = 0;
+      int64_t i = 0;
+      int bh = 0, q = 0;
+      if (f < n) {
+        bh = int(f / p.n_q);
+        q = int(f % p.n_q);
+        i = int64_t(p.per_head ? bh : 0) * p.n_q + q;
+        r = route[i];
+        cq = p.q_valid[i];
+      }
+      int64_t t128, t64, tz;
+      const int64_t p128 = c128 + block_scan(r == 128 ? 1 : 0, lds, &t128);
+      const int64_t p64 = c64 + block_scan(r == 64 ? 1 : 0, lds, &t64);
+      const int64_t pz = cz + block_scan(f < n && r == 0 && cq == 0 ? 1 : 0, lds, &tz);
+      if (pass == 0 && f < n && q == 0) {
+        hs128[bh] = p128;
+        hs64[bh] = p64;
+      }
+      if (f < n && (r != 0 || cq == 0)) {
+        if (pass == 0) {
+          FwdItem x{};
+          const int64_t wp = int64_t(p.per_head ? bh : 0) * (p.n_q + 1) + q;
+          x.walk_off = walk_ptr[wp];
+          x.walk_len = int32_t(walk_ptr[wp + 1] - x.walk_off);
+          x.bh = bh;
+          x.q = q;
+          x.n_full = nfull[i];
+          x.n_pages = unpadded[i];
+          x.c_q = cq;
+          if (r == 128) items128[p128] = x;
+          else if (r == 64) items64[p64] = x;
+          else items64[n64 + pz] = x;
+        } else {
+          int64_t L;
+          int32_t tag;
+          if (r == 128) {
+            L = p128 + hs64[bh];
+            tag = int32_t(p128);
+          } else if (r == 64) {
+            L = p64 + hs128[bh + 1];
+            tag = ~int32_t(p64);
+          } else {
+            L = n128 + n64 + pz;
+            tag = ~int32_t(n64 + pz);
+          }
+          order[launch_position(L, n_all, p.xcd_chunk)] = tag;
+        }
+      }
+      c128 += t128;
+      c64 += t64;
+      cz += tz;
     }
-    int64_t t128, t64, tz;
-    const int64_t p128 = c128 + block_scan(r == 128 ? 1 : 0, lds, &t128);
-    const int64_t p64 = c64 + block_scan(r == 64 ? 1 : 0, lds, &t64);
-    const int64_t pz = cz + block_scan(f < n && r == 0 && cq == 0 ? 1 : 0, lds, &tz);
-    if (f < n && (r != 0 || cq == 0)) {
-      FwdItem x{};
-      const int64_t wp = int64_t(p.per_head ? bh : 0) * (p.n_q + 1) + q;
-      x.walk_off = walk_ptr[wp];
-      x.walk_len = int32_t(walk_ptr[wp + 1] - x.walk_off);
-      x.bh = bh;
-      x.q = q;
-      x.n_full = nfull[i];
-      x.n_pages = unpadded[i];
-      x.c_q = cq;
-      if (r == 128) items128[launch_position(p128, n128, p.xcd_chunk)] = x;
-      else if (r == 64) items64[launch_position(p64, nall64, p.xcd_chunk)] = x;
-      else items64[launch_position(n64 + pz, nall64, p.xcd_chunk)] = x;
+    if (pass == 0 && threadIdx.x == 0) {
+      hs128[BH] = c128;
+      hs64[BH] = c64;
     }
-    c128 += t128;
-    c64 += t64;
-    cz += tz;
+    __syncthreads();  // head starts visible to the second pass
   }
 }
 
@@ -385,9 +420,11 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
   t->q128_queue = a32(2 * int64_t(h.n_q128));
   t->items128 = static_cast<FwdItem *>(alloc(size_t(std::max(h.n_q128, 1)) * sizeof(FwdItem)));
   t->items64 = static_cast<FwdItem *>(alloc(size_t(std::max(h.n_q64 + h.n_zero, 1)) * sizeof(FwdItem)));
+  t->order = a32(int64_t(h.n_q128) + h.n_q64 + h.n_zero);
+  int64_t *head_starts = static_cast<int64_t *>(alloc(size_t(2) * (size_t(p.batch) * p.heads + 1) * 8));
   unsigned long long *keys = static_cast<unsigned long long *>(alloc(size_t(std::max<int64_t>(BHQ, 1)) * 8 * 3));
   if (!t->walk || !t->pages || !t->valid || !t->q64_queue || !t->q128_queue || !t->items128 || !t->items64 ||
-      !keys) {
+      !t->order || !head_starts || !keys) {
     *err = "device allocation failed while planning";
     return KPAGE_ERR_OOM;
   }
@@ -414,7 +451,7 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
                        t->q128_queue);
   }
   hipLaunchKernelGGL(k_items, dim3(1), dim3(kScanThreads), 0, st, p, t->route, t->nfull, t->unpadded, t->walk_ptr, d_sum,
-                     t->items128, t->items64);
+                     t->items128, t->items64, head_starts, head_starts + (int64_t(p.batch) * p.heads + 1), t->order);
   KP_CHECK(hipGetLastError());
   KP_CHECK(hipMemcpyAsync(&h, d_sum, sizeof(Summary), hipMemcpyDeviceToHost, st));
   KP_CHECK(hipStreamSynchronize(st));

@@ -36,7 +36,8 @@ struct DevFwdTables {
   int32_t *pages = nullptr;   // the same with dummies pointed at the walk's first page
   uint32_t *valid = nullptr;  // two 16-bit page masks per word
   int32_t *q64_queue = nullptr, *q128_queue = nullptr;  // (bh, q) pairs, queue order
-  FwdItem *items128 = nullptr, *items64 = nullptr;      // launch order (see api.hip)
+  FwdItem *items128 = nullptr, *items64 = nullptr;      // (bh, q) order per route; cleanup items last
+  int32_t *order = nullptr;  // launch position -> item: i >= 0 M128 item i, ~j M64 item j
   int32_t *page_block = nullptr;  // [slots][seq_kv / 16] block whose footprint holds the page, -1 none
   int64_t walk_total = 0;
   int n_q64 = 0, n_q128 = 0, n_zero = 0;  // queue entries, empty query blocks
