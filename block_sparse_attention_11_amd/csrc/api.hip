@@ -248,6 +248,18 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
     const int64_t L = j < n64 ? int64_t(j) + pre128[it64[j].bh + 1] : int64_t(it128.size() + j);
     order[size_t(launch_position(L, n_all, chunk))] = ~int32_t(j);
   }
+  // each XCD's last kFwdTail entries longest-first (fwd_tail_cost, ties in launch order)
+  for (int x = 0; x < kXcds; ++x) {
+    const int64_t cnt = n_all > x ? (n_all - x + kXcds - 1) / kXcds : 0;
+    const int64_t t = std::min<int64_t>(kFwdTail, cnt);
+    std::vector<int32_t> tail;
+    for (int64_t j = cnt - t; j < cnt; ++j) tail.push_back(order[size_t(j * kXcds + x)]);
+    auto cost = [&](int32_t tag) {
+      return tag >= 0 ? fwd_tail_cost(128, it128[size_t(tag)].n_pages) : fwd_tail_cost(64, it64[size_t(~tag)].n_pages);
+    };
+    std::stable_sort(tail.begin(), tail.end(), [&](int32_t a, int32_t b) { return cost(a) > cost(b); });
+    for (int64_t j = cnt - t; j < cnt; ++j) order[size_t(j * kXcds + x)] = tail[size_t(j - (cnt - t))];
+  }
   kpage_status s;
   if ((s = upload(pl, order, &pl->d_order, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, pages, &pl->d_pages, stream)) != KPAGE_OK) return s;

@@ -126,6 +126,16 @@ __host__ __device__ inline int64_t bwd_tail_len(int64_t count) {
   return t < kMaxBwdTail ? t : kMaxBwdTail;
 }
 
+// Entries at the end of each XCD's forward (and dQ) launch sequence that run
+// longest-first: two per workgroup slot of an XCD (64 slots), so that the XCD's last
+// round does not end on a long item.  Cost of an item: its 4-page stages, weighted 3
+// for the M128 route and 2 for the M64 route (a measured per-stage time ratio of about
+// 2 : 3); ties keep their launch order.
+constexpr int kFwdTail = 128;
+__host__ __device__ inline int32_t fwd_tail_cost(int route, int n_pages) {
+  return (route == 128 ? 3 : 2) * ((n_pages + 3) / 4);
+}
+
 // Chunk length of a plan's launch order: whole-head runs per XCD (0) while one head's
 // pair of gathered tensors (K and V, or Q and dO) times 8 fits the memory-side cache,
 // else 64 entries (one XCD's two workgroups per CU).

@@ -351,6 +351,42 @@ __global__ __launch_bounds__(kScanThreads) void k_items(DevProblem p, const int3
   }
 }
 
+// The last kFwdTail entries of each XCD's launch sequence (positions 8 j + x) in
+// descending fwd_tail_cost, ties in launch order: one workgroup per XCD sorts them in
+// LDS (bitonic), the same order as the host planner's.
+__global__ __launch_bounds__(kFwdTail) void k_fwd_tails(int32_t *order, const FwdItem *items128,
+                                                        const FwdItem *items64, int64_t n) {
+  __shared__ unsigned long long key[kFwdTail];
+  __shared__ int32_t tag[kFwdTail];
+  const int x = int(blockIdx.x);
+  const int64_t cnt = n > x ? (n - x + kXcds - 1) / kXcds : 0;
+  const int64_t t = cnt < kFwdTail ? cnt : kFwdTail;
+  const int64_t j0 = cnt - t;
+  const int i = int(threadIdx.x);
+  if (i < t) {
+    const int32_t tg = order[(j0 + i) * kXcds + x];
+    const int32_t c = tg >= 0 ? fwd_tail_cost(128, items128[tg].n_pages) : fwd_tail_cost(64, items64[~tg].n_pages);
+    tag[i] = tg;
+    key[i] = ((unsigned long long)(uint32_t)(0x7FFFFFFF - c) << 32) | (unsigned long long)(uint32_t)i;
+  } else {
+    key[i] = ~0ull;
+  }
+  __syncthreads();
+  for (int k = 2; k <= kFwdTail; k <<= 1)
+    for (int h = k >> 1; h > 0; h >>= 1) {
+      const int l = i ^ h;
+      if (l > i) {
+        const unsigned long long a = key[i], b = key[l];
+        if ((a > b) == ((i & k) == 0)) {
+          key[i] = b;
+          key[l] = a;
+        }
+      }
+      __syncthreads();
+    }
+  if (i < t) order[(j0 + i) * kXcds + x] = tag[uint32_t(key[i])];
+}
+
 int blocks_for(int64_t n, int threads) { return int((n + threads - 1) / threads); }
 
 }  // namespace
@@ -452,6 +488,8 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
   }
   hipLaunchKernelGGL(k_items, dim3(1), dim3(kScanThreads), 0, st, p, t->route, t->nfull, t->unpadded, t->walk_ptr, d_sum,
                      t->items128, t->items64, head_starts, head_starts + (int64_t(p.batch) * p.heads + 1), t->order);
+  hipLaunchKernelGGL(k_fwd_tails, dim3(kXcds), dim3(kFwdTail), 0, st, t->order, t->items128, t->items64,
+                     int64_t(h.n_q128) + h.n_q64 + h.n_zero);
   KP_CHECK(hipGetLastError());
   KP_CHECK(hipMemcpyAsync(&h, d_sum, sizeof(Summary), hipMemcpyDeviceToHost, st));
   KP_CHECK(hipStreamSynchronize(st));
