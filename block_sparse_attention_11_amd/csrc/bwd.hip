@@ -688,8 +688,11 @@ __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * 64 * D * 2];
   const int b = blockIdx.x;
   const int t = a.forder ? a.forder[b] : (b < a.n_fitems128 ? b : ~(b - a.n_fitems128));
-  if (t >= 0) dq_item<D, 128>(a, a.fitems128, t, smem);
-  else dq_item<D, 64>(a, a.fitems64, ~t, smem);
+  if (t >= 0) {
+    if (a.froute_only != 64) dq_item<D, 128>(a, a.fitems128, t, smem);
+  } else if (a.froute_only != 128) {
+    dq_item<D, 64>(a, a.fitems64, ~t, smem);
+  }
 }
 
 template <int D>
@@ -700,20 +703,19 @@ hipError_t launch_bwd_d(const BwdArgs &a, hipStream_t stream, LaunchTimer *t) {
                        (int64_t)a.max_uncovered);
     if (t) t->after(3, stream);
   }
-  if (t && t->split_routes()) {  // profiling: one dQ launch per route
+  if (t && t->split_routes()) {
+    // profiling: the full dQ launch twice, one route's items each, at their positions in
+    // the combined launch (the row statistics of both routes are written by the pair)
     BwdArgs only128 = a, only64 = a;
-    only128.n_fitems64 = 0;
-    only64.n_fitems128 = 0;
-    only64.fitems128 = nullptr;
-    only128.forder = only64.forder = nullptr;
-    if (a.n_fitems128 > 0) {
+    only128.froute_only = 128;
+    only64.froute_only = 64;
+    const unsigned grid = (unsigned)(a.n_fitems128 + a.n_fitems64);
+    if (grid > 0) {
       t->before(KPAGE_K_BWD_DQ, stream);
-      hipLaunchKernelGGL(kpage_bwd_dq<D>, dim3(a.n_fitems128), dim3(64 * kDqWaves), 0, stream, only128);
+      hipLaunchKernelGGL(kpage_bwd_dq<D>, dim3(grid), dim3(64 * kDqWaves), 0, stream, only128);
       t->after(KPAGE_K_BWD_DQ, stream);
-    }
-    if (a.n_fitems64 > 0) {
       t->before(KPAGE_K_BWD_DQ_Q64, stream);
-      hipLaunchKernelGGL(kpage_bwd_dq<D>, dim3(a.n_fitems64), dim3(64 * kDqWaves), 0, stream, only64);
+      hipLaunchKernelGGL(kpage_bwd_dq<D>, dim3(grid), dim3(64 * kDqWaves), 0, stream, only64);
       t->after(KPAGE_K_BWD_DQ_Q64, stream);
     }
   } else if (a.n_fitems128 + a.n_fitems64 > 0) {

@@ -26,6 +26,8 @@ struct FwdArgs {
   // launch order of a launch holding both routes: workgroup b runs M128 item order[b]
   // when order[b] >= 0, else M64 item ~order[b]; NULL: the M128 items, then the M64 items
   const int32_t *order;
+  int32_t route_only;       // timing mode: 128 or 64 runs only that route's items (the other
+                            // route's workgroups exit at once); 0 runs both
   const int32_t *pages;     // walk entries; dummy slots point at a real page of the same walk
   const uint32_t *valid;    // two 16-bit row masks per word, indexed by walk position / 2
   int64_t seq_q, seq_kv;
@@ -73,6 +75,7 @@ struct BwdArgs {
   // Q-owned pass (dQ): the forward work items and page walks of both routes
   const FwdItem *fitems128, *fitems64;
   const int32_t *forder;      // launch order of the dQ pass, as FwdArgs::order
+  int32_t froute_only;        // as FwdArgs::route_only
   const int32_t *pages;
   const uint32_t *valid;
   int32_t n_fitems128, n_fitems64;

@@ -543,8 +543,11 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs a128, Fw
   __shared__ FwdLds<D> lds;
   const int b = blockIdx.x;
   const int t = a128.order ? a128.order[b] : (b < a128.n_items ? b : ~(b - a128.n_items));
-  if (t >= 0) fwd_item<D, 128, false>(a128, t, lds);
-  else fwd_item<D, 64, false>(a64, ~t, lds);
+  if (t >= 0) {
+    if (a128.route_only != 64) fwd_item<D, 128, false>(a128, t, lds);
+  } else if (a128.route_only != 128) {
+    fwd_item<D, 64, false>(a64, ~t, lds);
+  }
 }
 
 // Exact re-run over the items the fast kernel marked (first LSE row = kRedoMark): a small
@@ -585,21 +588,18 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_exact_kernel(FwdArgs a1
 template <int D>
 void launch_d(const FwdArgs &a128, const FwdArgs &a64, hipStream_t stream, LaunchTimer *timer) {
   dim3 grid(a128.n_items + a64.n_items), block(kThreads);
-  if (timer && timer->split_routes()) {  // profiling: one launch per route
-    FwdArgs none128 = a128, none64 = a64, only128 = a128;
-    none128.n_items = 0;
-    none64.n_items = 0;
-    none128.order = only128.order = nullptr;  // each launch holds one route, in list order
-    if (a128.n_items > 0) {
-      timer->before(KPAGE_K_FWD, stream);
-      hipLaunchKernelGGL((kpage_fwd_kernel<D>), dim3(a128.n_items), block, 0, stream, only128, none64);
-      timer->after(KPAGE_K_FWD, stream);
-    }
-    if (a64.n_items > 0) {
-      timer->before(KPAGE_K_FWD_Q64, stream);
-      hipLaunchKernelGGL((kpage_fwd_kernel<D>), dim3(a64.n_items), block, 0, stream, none128, a64);
-      timer->after(KPAGE_K_FWD_Q64, stream);
-    }
+  if (timer && timer->split_routes()) {
+    // profiling: the full launch twice, each running one route's items at the launch
+    // positions they hold in the combined launch (the other route's workgroups exit)
+    FwdArgs only128 = a128, only64 = a128;
+    only128.route_only = 128;
+    only64.route_only = 64;
+    timer->before(KPAGE_K_FWD, stream);
+    hipLaunchKernelGGL((kpage_fwd_kernel<D>), grid, block, 0, stream, only128, a64);
+    timer->after(KPAGE_K_FWD, stream);
+    timer->before(KPAGE_K_FWD_Q64, stream);
+    hipLaunchKernelGGL((kpage_fwd_kernel<D>), grid, block, 0, stream, only64, a64);
+    timer->after(KPAGE_K_FWD_Q64, stream);
   } else {
     if (timer) timer->before(KPAGE_K_FWD, stream);
     hipLaunchKernelGGL((kpage_fwd_kernel<D>), grid, block, 0, stream, a128, a64);

@@ -259,10 +259,12 @@ void kpage_plan_destroy(kpage_plan_t *plan);
  * and the number of launches of one kernel since the last read, and resets that
  * kernel's record.  Kernel ids below.  Disabled by default; enable = 1 adds two
  * event records per launch and nothing else.  enable = 2 is a profiling mode that
- * also splits the forward and dQ launches by route: the M128 x N128 items keep
- * the pass's own id and the M64 x N256 items (with the empty-block cleanup) are
- * timed as KPAGE_K_FWD_Q64 / KPAGE_K_BWD_DQ_Q64 (two launches per pass instead of
- * one, so the pass itself may run slightly slower).
+ * also splits the forward and dQ launches by route: the pass runs its full launch
+ * twice, once with only the M128 x N128 items (timed under the pass's own id) and
+ * once with only the M64 x N256 items and the empty-block cleanup (timed as
+ * KPAGE_K_FWD_Q64 / KPAGE_K_BWD_DQ_Q64); each item keeps its launch position and
+ * the other route's workgroups exit at once, so a route is timed without the
+ * other one running beside it.
  */
 enum {
   KPAGE_K_FWD = 0,       /* forward, both routes in one launch (M128 x N128 items, */
