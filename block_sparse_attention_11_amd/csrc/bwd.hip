@@ -595,7 +595,11 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
   for_range(ic<true>{}, split, n_half, iter);
 
   // ---- sum the waves that share query rows, then write dQ = scale * acc (bf16) ----
+  // The barrier alone does not order LDS accesses on this GPU (the compiler inserts no
+  // wait before it): each wave first waits for its own copies and LDS reads, and for its
+  // partial's writes before the second barrier, as the forward's merge does.
   wait_vmcnt<0>();
+  wait_lgkm0();
   barrier();
   {
     lds_char *part = (lds_char *)smem + wave * PART_BYTES;
@@ -609,6 +613,7 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
         *(__attribute__((address_space(3))) f32x4 *)(part + (l32 * D + 4 * phys) * 4) = val;
       }
   }
+  wait_lgkm0();
   barrier();
   const int64_t orow0 = bh * a.seq_q + 128 * it.q;
   const int vrows = cq < M ? cq : M;

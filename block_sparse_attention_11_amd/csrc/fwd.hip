@@ -439,12 +439,14 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
 
   // ---- merge the waves that share query rows, then write O and LSE ----
   wait_vmcnt<0>();
-  wait_lgkm0();
   if (!EXACT && tid == 0) redo_any = 0;
   // fast kernel: the fixed maximum is only safe if it existed before the row's first
   // probability (else the sums ran against 0) and no score rose more than 2^kLimit
   // above it (every probability is at most the row sum)
   if (!EXACT) over = over || (m2 == kNegInf && l_run != 0.f) || !(l_run <= __builtin_exp2f(kLimit));
+  // s_barrier does not wait for LDS writes on this GPU: the reset of the flag (and every
+  // LDS read of the loop) completes before any wave can pass and set it
+  wait_lgkm0();
   barrier();
   if (!EXACT && __builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) redo_any = 1;
   {

@@ -32,6 +32,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// s_barrier alone.  It does not wait for the wave's own LDS or memory operations, and
+// on gfx950 (which backs off barriers) the compiler inserts no wait before it either:
+// a wave must wait (wait_lgkm0 / wait_vmcnt) for the LDS writes and reads that other
+// waves depend on before calling it.
 __device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
 
 template <int V>
