@@ -280,6 +280,8 @@ def main():
     ap.add_argument("--heads", type=int, default=0, metavar="N",
                     help="time only the first N heads of the workload (one GPU's share when the heads are "
                          "sharded over several GPUs; 0: all heads, the default)")
+    ap.add_argument("--no-groups", action="store_true",
+                    help="plan every query block as its own work item (no group items of small blocks)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the known-size kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -311,7 +313,7 @@ def main():
         desc += f"; first {w.heads} heads only"
     d = w.head_dim
     t0 = time.perf_counter()
-    plan = K.kpage_plan(w, q_group=args.q_group)
+    plan = K.kpage_plan(w, q_group=args.q_group, grouped=not args.no_groups)
     plan_ms = (time.perf_counter() - t0) * 1e3
     q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
     o = torch.empty_like(q)
@@ -324,6 +326,10 @@ def main():
     torch.cuda.synchronize()
     bwd_plan_ms = (time.perf_counter() - t0) * 1e3
     stats = K.kpage_plan_stats(plan)
+    # work items that run up to four small query blocks together (one per graph slot's group
+    # and (batch, head) of the slot)
+    n_groups = K.kpage_plan_export(plan, "group_members").size // 4
+    n_group_items = n_groups if w.per_head else n_groups * w.batch * w.heads
     # the same plan built on the GPU (identical tables; the timed steps use the host-built one)
     K.kpage_plan_device(w).close()  # first use: kernel and allocator warm-up
     torch.cuda.synchronize()
@@ -398,7 +404,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": desc + (f", backward Q groups of {args.q_group} blocks" if args.q_group else ""),
+        "config": {"workload": desc + (f", backward Q groups of {args.q_group} blocks" if args.q_group else "")
+                   + (", no group items" if args.no_groups else ""),
                    "batch": 1, "heads": w.heads, "head_dim": d, "tokens": tokens,
                    "seq_physical": w.seq_q},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -412,6 +419,7 @@ def main():
                     "device_forward_incl_descriptor_upload": round(dev_plan_ms, 2),
                     "device_backward_lazy_incl_first_call": round(dev_bwd_plan_ms, 2)},
         "roofline": roofline,
+        "group_items": n_group_items,
     }
     if not args.no_route_split:
         out["routes"] = _route_split(K, plan, step, w)

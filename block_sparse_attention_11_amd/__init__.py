@@ -30,6 +30,8 @@ TABLES = {
     "owner_aligned": (9, np.uint8), "revq_ptr": (10, np.int64), "revq": (11, np.int32),
     "qwalk_ptr": (12, np.int64), "qwalk": (13, np.int32), "adj": (14, np.uint64),
     "bwd_queue": (15, np.int32), "uncovered_ptr": (16, np.int64), "uncovered": (17, np.int32),
+    "group_ptr": (18, np.int64), "group_members": (19, np.int32), "group_walk_ptr": (20, np.int64),
+    "group_walk": (21, np.int32), "group_nfull": (22, np.int32), "group_valid": (23, np.uint32),
 }
 
 EXPORTED_SYMBOLS = (
@@ -61,7 +63,8 @@ class KpageProblem(ctypes.Structure):
 
 
 class KpagePlanOpts(ctypes.Structure):
-    _fields_ = [("q_group", ctypes.c_int32), ("align_q128", ctypes.c_int32), ("align_q64", ctypes.c_int32)]
+    _fields_ = [("q_group", ctypes.c_int32), ("align_q128", ctypes.c_int32), ("align_q64", ctypes.c_int32),
+                ("ungrouped", ctypes.c_int32)]
 
 
 class KpageSelectLayout(ctypes.Structure):
@@ -160,8 +163,9 @@ def _arr(x, dtype):
     return np.ascontiguousarray(np.asarray(x, dtype=dtype))
 
 
-def kpage_plan(problem, align_q64: int = 0, align_q128: int = 0, q_group: int = 0) -> Plan:
-    """Plan for ``problem`` (any object with the workloads.Workload descriptor attributes)."""
+def kpage_plan(problem, align_q64: int = 0, align_q128: int = 0, q_group: int = 0, grouped: bool = True) -> Plan:
+    """Plan for ``problem`` (any object with the workloads.Workload descriptor attributes).
+    grouped=False runs every query block as its own work item (kpage_plan_opts.ungrouped)."""
     qv = _arr(problem.q_valid, np.int32)
     kvv = _arr(problem.kv_valid, np.int32)
     ko = None if problem.kv_offset is None else _arr(problem.kv_offset, np.int64)
@@ -175,7 +179,7 @@ def kpage_plan(problem, align_q64: int = 0, align_q128: int = 0, q_group: int = 
         per_head=1 if problem.per_head else 0,
         q_valid=qv.ctypes.data, kv_valid=kvv.ctypes.data, kv_offset=0 if ko is None else ko.ctypes.data,
         q2k_ptr=ptr.ctypes.data, q2k_idx=idx.ctypes.data)
-    opts = KpagePlanOpts(q_group=q_group, align_q128=align_q128, align_q64=align_q64)
+    opts = KpagePlanOpts(q_group=q_group, align_q128=align_q128, align_q64=align_q64, ungrouped=0 if grouped else 1)
     h = ctypes.c_void_p()
     _check(lib().kpage_plan(ctypes.byref(p), ctypes.byref(opts), ctypes.byref(h)))
     return Plan(h, problem.batch, problem.heads, problem.head_dim, problem.seq_q, problem.seq_kv)

@@ -82,6 +82,7 @@ struct kpage_plan {
   Problem P;
   FwdTables F;
   BwdTables B;
+  GroupTables GT;  // group items (host plans only)
   PairStats S;
   bool fwd_on_device = false;
   // built by kpage_plan_device: the descriptor and every table live on the device
@@ -96,6 +97,7 @@ struct kpage_plan {
   // forward device tables
   FwdItem *d_items128 = nullptr, *d_items64 = nullptr;
   int32_t *d_order = nullptr;  // launch position -> item of either route (NULL: M128 then M64)
+  FwdGroup *d_groups = nullptr;  // member tables of the group items (NULL: none)
   int n_items128 = 0, n_items64 = 0;
   int32_t *d_pages = nullptr;
   uint32_t *d_valid = nullptr;
@@ -202,6 +204,8 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   const FwdTables &F = pl->F;
   const int nq = P.n_q;
   std::vector<int32_t> pages = redirect_dummies(F.walk, F.walk_ptr);
+  const GroupTables &GT = pl->GT;
+  const bool has_groups = !GT.members.empty();
   std::vector<FwdItem> it128, it64;
   auto make = [&](int bh, int q) {
     const int g = P.slot_of(bh);
@@ -216,8 +220,57 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
     return x;
   };
   for (size_t i = 0; i < F.q128_queue.size(); i += 2) it128.push_back(make(F.q128_queue[i], F.q128_queue[i + 1]));
-  for (size_t i = 0; i < F.q64_queue.size(); i += 2) it64.push_back(make(F.q64_queue[i], F.q64_queue[i + 1]));
-  auto head_major = [](const FwdItem &a, const FwdItem &b) { return a.bh != b.bh ? a.bh < b.bh : a.q < b.q; };
+  for (size_t i = 0; i < F.q64_queue.size(); i += 2) {
+    const int bh = F.q64_queue[i], q = F.q64_queue[i + 1];
+    if (has_groups && GT.in_group[size_t(P.slot_of(bh)) * nq + q]) continue;  // runs inside its group item
+    it64.push_back(make(bh, q));
+  }
+  // group items: union walks after the plan's walks, member validity words after its
+  // words; one FwdGroup per group of a slot, shared by the (batch, head)s of the slot
+  std::vector<FwdGroup> groups;
+  std::vector<uint32_t> valid_all;
+  if (has_groups) {
+    const std::vector<int32_t> gpages = redirect_dummies(GT.walk, GT.walk_ptr);
+    const int64_t walk_base = int64_t(pages.size());
+    const int64_t valid_base = int64_t(F.valid.size());
+    pages.insert(pages.end(), gpages.begin(), gpages.end());
+    valid_all = F.valid;
+    valid_all.insert(valid_all.end(), GT.valid.begin(), GT.valid.end());
+    const size_t ng = GT.nfull.size();
+    groups.resize(ng);
+    for (size_t i = 0; i < ng; ++i) {
+      FwdGroup &gr = groups[i];
+      for (int w = 0; w < kGroupMembers; ++w) {
+        gr.q[w] = GT.members[i * kGroupMembers + size_t(w)];
+        gr.c_q[w] = 0;
+      }
+      gr.valid_off = valid_base + 2 * GT.walk_ptr[i];
+      gr.pad = 0;
+    }
+    for (int g = 0; g < P.slots; ++g)
+      for (int64_t i = GT.group_ptr[size_t(g)]; i < GT.group_ptr[size_t(g) + 1]; ++i)
+        for (int w = 0; w < kGroupMembers; ++w)
+          if (groups[size_t(i)].q[w] >= 0) groups[size_t(i)].c_q[w] = P.q_valid[size_t(g) * nq + groups[size_t(i)].q[w]];
+    for (int bh = 0; bh < P.batch * P.heads; ++bh) {
+      const int g = P.slot_of(bh);
+      for (int64_t i = GT.group_ptr[size_t(g)]; i < GT.group_ptr[size_t(g) + 1]; ++i) {
+        FwdItem x{};
+        x.walk_off = walk_base + GT.walk_ptr[size_t(i)];
+        x.walk_len = int32_t(GT.walk_ptr[size_t(i) + 1] - GT.walk_ptr[size_t(i)]);
+        x.bh = bh;
+        x.q = ~int32_t(i);
+        x.n_full = GT.nfull[size_t(i)];
+        x.n_pages = GT.npages[size_t(i)];
+        x.c_q = kBlockRows;
+        it128.push_back(x);
+      }
+    }
+  }
+  // head-major, spatial order inside a head; a head's group items after its other M128 items
+  auto head_major = [nq](const FwdItem &a, const FwdItem &b) {
+    const int64_t ka = a.q >= 0 ? a.q : int64_t(nq) + ~a.q, kb = b.q >= 0 ? b.q : int64_t(nq) + ~b.q;
+    return a.bh != b.bh ? a.bh < b.bh : ka < kb;
+  };
   std::stable_sort(it128.begin(), it128.end(), head_major);
   std::stable_sort(it64.begin(), it64.end(), head_major);
   // blocks without valid rows still own their output rows: cleanup items (empty walk)
@@ -263,7 +316,8 @@ kpage_status ensure_forward_on_device(PlanT *pl, hipStream_t stream) {
   kpage_status s;
   if ((s = upload(pl, order, &pl->d_order, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, pages, &pl->d_pages, stream)) != KPAGE_OK) return s;
-  if ((s = upload(pl, F.valid, &pl->d_valid, stream)) != KPAGE_OK) return s;
+  if ((s = upload(pl, has_groups ? valid_all : F.valid, &pl->d_valid, stream)) != KPAGE_OK) return s;
+  if (has_groups && (s = upload(pl, groups, &pl->d_groups, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, it128, &pl->d_items128, stream)) != KPAGE_OK) return s;
   if ((s = upload(pl, it64, &pl->d_items64, stream)) != KPAGE_OK) return s;
   hipError_t e = hipStreamSynchronize(stream);
@@ -600,6 +654,7 @@ kpage_status kpage_plan(const kpage_problem *problem, const kpage_plan_opts *opt
   pl->F.align128 = a128;
   try {
     build_forward(pl->P, &pl->F, &pl->S);
+    build_groups(pl->P, pl->F, &pl->GT);
   } catch (const std::bad_alloc &) {
     delete pl;
     return fail(KPAGE_ERR_OOM, "host allocation failed while planning");
@@ -710,6 +765,7 @@ kpage_status kpage_attn_fwd(kpage_plan_t *plan, const void *q, const void *k, co
   a.seq_kv = plan->P.seq_kv;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.groups = plan->d_groups;
   FwdArgs a64 = a;
   a.items = plan->d_items128;
   a.order = plan->d_order;
@@ -766,6 +822,7 @@ static kpage_status launch_backward(kpage_plan_t *plan, const void *q, const voi
                               : nullptr;
   a.fitems128 = plan->d_items128;
   a.fitems64 = plan->d_items64;
+  a.fgroups = plan->d_groups;
   a.forder = plan->d_order;
   a.n_fitems128 = plan->n_items128;
   a.n_fitems64 = plan->n_items64;
@@ -870,7 +927,7 @@ kpage_status kpage_plan_stats(const kpage_plan_t *plan, kpage_pair_stats *out) {
 kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf, size_t *bytes) {
   if (!plan || !bytes) return fail(KPAGE_ERR_INVALID, "plan or bytes is NULL");
   if (table_id < 0 || table_id >= KPAGE_T_COUNT) return fail(KPAGE_ERR_INVALID, "unknown table id");
-  if (table_id >= KPAGE_T_OWNER_PTR) {
+  if (table_id >= KPAGE_T_OWNER_PTR && table_id <= KPAGE_T_UNCOVERED) {
     const kpage_status s = guarded([&] { return ensure_backward_on_host(plan); });
     if (s != KPAGE_OK) return s;
   } else {
@@ -903,6 +960,12 @@ kpage_status kpage_plan_export(kpage_plan_t *plan, int table_id, void *host_buf,
     KPAGE_TABLE(KPAGE_T_BWD_QUEUE, plan->B.bwd_queue)
     KPAGE_TABLE(KPAGE_T_UNCOVERED_PTR, plan->B.uncovered_ptr)
     KPAGE_TABLE(KPAGE_T_UNCOVERED, plan->B.uncovered)
+    KPAGE_TABLE(KPAGE_T_GROUP_PTR, plan->GT.group_ptr)
+    KPAGE_TABLE(KPAGE_T_GROUP_MEMBERS, plan->GT.members)
+    KPAGE_TABLE(KPAGE_T_GROUP_WALK_PTR, plan->GT.walk_ptr)
+    KPAGE_TABLE(KPAGE_T_GROUP_WALK, plan->GT.walk)
+    KPAGE_TABLE(KPAGE_T_GROUP_NFULL, plan->GT.nfull)
+    KPAGE_TABLE(KPAGE_T_GROUP_VALID, plan->GT.valid)
 #undef KPAGE_TABLE
   }
   if (!host_buf) {

@@ -414,7 +414,6 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
 
   const FwdItem it = items[item];
   const int64_t bh = it.bh;
-  const int cq = it.c_q;
   const int n_half = (it.n_pages + 3) / 4;  // all-dummy half-tiles of the padding skipped
   const int full_half = it.n_full / 4;
   const int qg = wave % NQG;
@@ -423,12 +422,13 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
   const char *kh = (const char *)a.k + bh * a.seq_kv * D * 2;
   const char *vh = (const char *)a.v + bh * a.seq_kv * D * 2;
   c_i32 *walk = (c_i32 *)(a.pages + it.walk_off);
-  c_u32 *vwords = (c_u32 *)(a.valid + (it.walk_off >> 1));
-
-  // this wave's 32 query rows: Q and dO as MFMA B operands, lse2 and delta per lane
-  const int64_t qrow = bh * a.seq_q + 128 * it.q + 32 * qg + l32;
-  const bool qok = 32 * qg + l32 < cq;
-  const bool idle = 32 * qg >= cq;  // wave-uniform: no valid row in this query group
+  // this wave's 32 query rows (a group item's wave holds the rows of its own member
+  // block): Q and dO as MFMA B operands, lse2 and delta per lane
+  const WaveRows wr = wave_rows(it, a.fgroups, qg);
+  c_u32 *vwords = (c_u32 *)(a.valid + wr.valid_off);
+  const int64_t qrow = bh * a.seq_q + 128 * wr.block + wr.row0 + l32;
+  const bool qok = l32 < wr.rows;
+  const bool idle = wr.rows <= 0;  // wave-uniform: no valid row in this query group
   bf16x8 qreg[DS], greg[DS];
   {
     const bf16x8 *qp = (const bf16x8 *)((const char *)a.q + qrow * D * 2);
@@ -458,7 +458,9 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
   dsum = half_sum(dsum);  // the other half of the row's head dimension sits in lane ^ 32
   const float lse = qok ? a.lse[qrow] : kNegInf;
   const float lse2 = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
-  if (keyoff == 0 && g == 0) {  // one lane per row (query groups repeat over key halves)
+  // one lane per row (query groups repeat over key halves); a group item's wave without
+  // a member block writes nothing
+  if (keyoff == 0 && g == 0 && (it.q >= 0 || !idle)) {
     a.delta[qrow] = dsum;
     a.lse2[qrow] = lse2;
   }
@@ -615,14 +617,33 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
   }
   wait_lgkm0();
   barrier();
-  const int64_t orow0 = bh * a.seq_q + 128 * it.q;
-  const int vrows = cq < M ? cq : M;
+  // Output spans: a plain item writes the 128 dQ rows of its block (rows past c_q as 0),
+  // a group item the 128 rows of each member block, member m's valid rows from wave m.
+  const bool grouped = ROUTE == 128 && it.q < 0;
+  const int n_spans = grouped ? NQG : 1;
+  int32_t span_q[NQG], span_rows[NQG];
+  if (grouped) {
+    const FwdGroup &gr = a.fgroups[~it.q];
+#pragma unroll
+    for (int m = 0; m < NQG; ++m) {
+      span_q[m] = gr.q[m];
+      span_rows[m] = gr.c_q[m];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NQG; ++m) {
+      span_q[m] = it.q;
+      span_rows[m] = it.c_q < M ? it.c_q : M;
+    }
+  }
   constexpr int GROUPS = D / 8;
-  for (int u = tid; u < 128 * GROUPS; u += 64 * kDqWaves) {
-    const int row = u / GROUPS, grp = u % GROUPS;
+  for (int u = tid; u < n_spans * 128 * GROUPS; u += 64 * kDqWaves) {
+    const int m = u / (128 * GROUPS), row = (u / GROUPS) & 127, grp = u % GROUPS;
+    const int blk = span_q[m];
+    if (blk < 0) continue;  // a group item without member m
     float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (row < vrows) {
-      const int qr = row & 31, q_g = row >> 5;
+    if (row < span_rows[m]) {
+      const int qr = grouped ? row : row & 31, q_g = grouped ? m : row >> 5;
       for (int w = q_g; w < kDqWaves; w += NQG) {
         const lds_char *pw = (const lds_char *)smem + w * PART_BYTES;
 #pragma unroll
@@ -639,7 +660,8 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
     bf16x8 out;
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc8[e] * a.scale);
-    *(bf16x8 *)((char *)a.dq + ((orow0 + row) * D + 8 * grp) * 2) = out;
+    const int64_t orow = bh * a.seq_q + 128 * blk + row;
+    *(bf16x8 *)((char *)a.dq + (orow * D + 8 * grp) * 2) = out;
   }
 }
 

@@ -18,11 +18,56 @@ struct FwdItem {
                      // past the last 4-page tile holding a real page)
 };
 
+// A group item: up to four query blocks of one (batch, head), each with at most 32 valid
+// rows, run as one M128 x N128 work item over the union of their page walks.  Wave w
+// holds the rows of member w and masks the pages of the union that its own block did not
+// select; the item writes the 128 output rows of every member block.  Group items are
+// M128 items whose q field is ~(index into the group table).
+struct FwdGroup {
+  int32_t q[4];        // member block of wave w (-1: no member, the wave computes nothing)
+  int32_t c_q[4];      // its valid rows (1..32; 0 without a member)
+  int64_t valid_off;   // wave w's validity words start at valid_off + w * (walk_len / 2)
+  int64_t pad;
+};
+
+// The 32 query rows of query group qg (one wave's rows in the M128 route) of a work item.
+struct WaveRows {
+  int32_t block;       // query block holding them (never -1: an absent member names member 0)
+  int32_t row0;        // first of them inside the block
+  int32_t rows;        // how many are valid (0: the wave computes nothing)
+  int64_t valid_off;   // first validity word of this wave's walk
+};
+
+__device__ __forceinline__ WaveRows wave_rows(const FwdItem &it, const FwdGroup *groups, int qg) {
+  WaveRows r;
+  if (it.q >= 0) {
+    const int left = it.c_q - 32 * qg;
+    r.block = it.q;
+    r.row0 = 32 * qg;
+    r.rows = left < 0 ? 0 : (left > 32 ? 32 : left);
+    r.valid_off = it.walk_off >> 1;
+  } else {
+    const FwdGroup &gr = groups[~it.q];
+    const int32_t b = gr.q[qg];
+    r.block = b >= 0 ? b : gr.q[0];
+    r.row0 = 0;
+    r.rows = b >= 0 ? gr.c_q[qg] : 0;
+    r.valid_off = gr.valid_off + int64_t(qg) * (it.walk_len / 2);
+  }
+  return r;
+}
+
+// First output row of a work item (the row that carries the forward's re-run mark).
+__device__ __forceinline__ int32_t item_block0(const FwdItem &it, const FwdGroup *groups) {
+  return it.q >= 0 ? it.q : groups[~it.q].q[0];
+}
+
 struct FwdArgs {
   const void *q, *k, *v;
   void *o;
   float *lse;
   const FwdItem *items;
+  const FwdGroup *groups;   // member tables of the group items (NULL when there are none)
   // launch order of a launch holding both routes: workgroup b runs M128 item order[b]
   // when order[b] >= 0, else M64 item ~order[b]; NULL: the M128 items, then the M64 items
   const int32_t *order;
@@ -74,6 +119,7 @@ struct BwdArgs {
   int32_t n_reduce;
   // Q-owned pass (dQ): the forward work items and page walks of both routes
   const FwdItem *fitems128, *fitems64;
+  const FwdGroup *fgroups;    // as FwdArgs::groups
   const int32_t *forder;      // launch order of the dQ pass, as FwdArgs::order
   int32_t froute_only;        // as FwdArgs::route_only
   const int32_t *pages;

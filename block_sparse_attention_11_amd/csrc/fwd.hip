@@ -111,7 +111,6 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
 
   const FwdItem it = args.items[item];
   const int bh = it.bh;
-  const int cq = it.c_q;
   // 4-page tiles up to the last one holding a real page; the all-dummy tiles of the
   // walk's step padding are neither copied nor computed
   const int n_tiles = (it.n_pages + kTilePages - 1) / kTilePages;
@@ -119,22 +118,24 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
   const int full_tiles = it.n_full / kTilePages;  // tiles inside the fully valid prefix
   const int qg = wave % NQG;
   const int keyoff = (wave / NQG) * KW;  // first key of this wave in a tile
-  // a query group without valid rows (c_q <= 32 qg) computes nothing: the wave still
-  // copies its pages and meets every barrier (none sits inside the compute below),
-  // and its rows are written as O = 0, LSE = -inf like every row past c_q
-  const bool idle = 32 * qg >= cq;
+  // this wave's query rows (a group item's wave holds the rows of its own member block)
+  const WaveRows wr = wave_rows(it, args.groups, qg);
+  // a query group without valid rows computes nothing: the wave still copies its pages
+  // and meets every barrier (none sits inside the compute below), and its rows are
+  // written as O = 0, LSE = -inf like every row past c_q
+  const bool idle = wr.rows <= 0;
 
   const char *kh = (const char *)args.k + (int64_t)bh * args.seq_kv * D * 2;
   const char *vh = (const char *)args.v + (int64_t)bh * args.seq_kv * D * 2;
   c_i32 *walk = (c_i32 *)(args.pages + it.walk_off);
-  c_u32 *vwords = (c_u32 *)(args.valid + (it.walk_off >> 1));
+  c_u32 *vwords = (c_u32 *)(args.valid + wr.valid_off);
 
   // Q rows of this wave as MFMA B operands: qreg[s] = Q[q0 + l32][16s + 8g .. +8]
   bf16x8 qreg[DS];
   {
-    const int q0 = 128 * it.q + 32 * qg;
+    const int q0 = 128 * wr.block + wr.row0;
     const bf16x8 *qh = (const bf16x8 *)((const char *)args.q + ((int64_t)bh * args.seq_q + q0) * D * 2);
-    const bool ok = 32 * qg + l32 < cq;
+    const bool ok = l32 < wr.rows;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       bf16x8 x = qh[l32 * (D / 8) + 2 * s + g];
@@ -228,8 +229,10 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
       m2 = mnew;
       pending = __builtin_amdgcn_ballot_w64(up) != 0;
     } else {
+      // the first sub-tile with a valid key fixes the maximum; sums taken before it (in
+      // the loop's sub-iterations, against 0) would not match it: the item is re-run
       const bool first = m2 == kNegInf;
-      over = over || (!first && mx > m2 + kLimit);
+      over = over || (!first && mx > m2 + kLimit) || (first && l_run != 0.f);
       m2 = first ? mx : m2;
     }
     const float nm = m2 == kNegInf ? 0.f : -m2;
@@ -458,7 +461,7 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
   }
   wait_lgkm0();
   barrier();
-  const int64_t orow0 = (int64_t)bh * args.seq_q + 128 * it.q;
+  const int64_t orow0 = (int64_t)bh * args.seq_q + 128 * item_block0(it, args.groups);
   if (!EXACT && redo_any) {
     // the exact kernel writes this item; the mark lives in the caller's own LSE row,
     // so concurrent calls on one plan (different outputs) never see each other's
@@ -499,13 +502,46 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
   wait_lgkm0();
   barrier();
 
-  const int vrows = cq < M ? cq : M;
+  // Output spans: a plain item writes the 128 rows of its block (valid rows from the
+  // waves of their query group, the rest O = 0, LSE = -inf); a group item writes the 128
+  // rows of each member block, member m's valid rows from wave m.
+  const bool grouped = ROUTE == 128 && it.q < 0;
+  const int n_spans = grouped ? NQG : 1;
+  int32_t span_q[NQG], span_rows[NQG];
+  if (grouped) {
+    const FwdGroup &gr = args.groups[~it.q];
+#pragma unroll
+    for (int m = 0; m < NQG; ++m) {
+      span_q[m] = gr.q[m];
+      span_rows[m] = gr.c_q[m];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NQG; ++m) {
+      span_q[m] = it.q;
+      span_rows[m] = it.c_q < M ? it.c_q : M;
+    }
+  }
+  // span m, row r: (block, valid, query group, row inside the group)
+  auto span_row = [&](int m, int r, int *blk, int *q_g, int *qr) __attribute__((always_inline)) -> bool {
+    *blk = span_q[m];
+    if (grouped) {
+      *q_g = m;
+      *qr = r;
+    } else {
+      *q_g = r >> 5;
+      *qr = r & 31;
+    }
+    return *blk >= 0 && r < span_rows[m];
+  };
   constexpr int GROUPS = D / 8;
-  for (int u = tid; u < 128 * GROUPS; u += kThreads) {
-    const int row = u / GROUPS, grp = u % GROUPS;
+  for (int u = tid; u < n_spans * 128 * GROUPS; u += kThreads) {
+    const int m = u / (128 * GROUPS), row = (u / GROUPS) & 127, grp = u % GROUPS;
+    int blk, q_g, qr;
+    const bool valid = span_row(m, row, &blk, &q_g, &qr);
+    if (blk < 0) continue;  // a group item without member m
     float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (row < vrows) {
-      const int qr = row & 31, q_g = row >> 5;
+    if (valid) {
       for (int w = q_g; w < kWaves; w += NQG) {
         const lds_char *pw = (const lds_char *)smem + w * PART_BYTES;
 #pragma unroll
@@ -522,18 +558,22 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
     bf16x8 out;
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = (__bf16)acc8[e];
-    *(bf16x8 *)((char *)args.o + ((orow0 + row) * D + 8 * grp) * 2) = out;
+    const int64_t orow = (int64_t)bh * args.seq_q + 128 * blk + row;
+    *(bf16x8 *)((char *)args.o + (orow * D + 8 * grp) * 2) = out;
   }
-  if (tid < 128) {
-    const int row = tid;
+  for (int u = tid; u < n_spans * 128; u += kThreads) {
+    const int m = u >> 7, row = u & 127;
+    int blk, q_g, qr;
+    const bool valid = span_row(m, row, &blk, &q_g, &qr);
+    if (blk < 0) continue;
     float lse = kNegInf;
-    if (row < vrows) {
+    if (valid) {
       float mt;
-      const float lt = merged(row >> 5, row & 31, &mt);
+      const float lt = merged(q_g, qr, &mt);
       // LSE = ln(sum exp(scale * s)) = (m2 + log2 l) * ln 2
       if (mt != kNegInf && lt > 0.f) lse = (mt + __log2f(lt)) * 0.6931471805599453f;
     }
-    args.lse[orow0 + row] = lse;
+    args.lse[(int64_t)bh * args.seq_q + 128 * blk + row] = lse;
   }
 }
 
@@ -566,7 +606,8 @@ __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_exact_kernel(FwdArgs a1
     bool mark = false;
     if (i < n) {
       const FwdItem it = i < a128.n_items ? a128.items[i] : a64.items[i - a128.n_items];
-      mark = __builtin_bit_cast(uint32_t, a128.lse[(int64_t)it.bh * a128.seq_q + 128 * it.q]) == kRedoMark;
+      mark = __builtin_bit_cast(uint32_t, a128.lse[(int64_t)it.bh * a128.seq_q + 128 * item_block0(it, a128.groups)]) ==
+             kRedoMark;
     }
     const uint64_t m = __builtin_amdgcn_ballot_w64(mark);
     if ((tid & 63) == 0) marked[tid >> 6] = m;

@@ -71,6 +71,7 @@ kpage_status load_scalars(const kpage_problem *p, const kpage_plan_opts *o, Prob
   P.per_head = p->per_head == 1;
   P.slots = P.per_head ? P.batch * P.heads : 1;
   P.q_group = o ? o->q_group : 0;
+  P.grouped = !(o && o->ungrouped);
   return KPAGE_OK;
 }
 
@@ -208,6 +209,153 @@ void build_forward(const Problem &P, FwdTables *T, PairStats *S) {
     for (auto &x : ent) {
       out.push_back(std::get<1>(x));
       out.push_back(std::get<2>(x));
+    }
+  }
+}
+
+// Group items.  A query block of the M64 x N256 route with at most 32 valid rows leaves
+// three of its item's four waves' worth of MFMA work unused for every page it gathers:
+// its 4-page stages are bound by the gathers, not by the matrix cores.  Blocks whose
+// selections overlap share most pages, so up to four of them run as one M128 x N128 item
+// over the union of their walks (wave w computes member w's rows and masks the pages its
+// block did not select): the union is gathered once.  Greedy, per slot, in block order:
+// the first free block opens a group, which then takes, among the free blocks that share
+// a page with every member, the one with the largest share of its pages already in the
+// group's union (ties: lower block), while that share is at least one half.  A group of
+// one stays a plain item.  Union walk: the pages that
+// are full and selected by every member (in the first member's walk order; no masking
+// in their stages), then the other pages every member selected (same order), then each
+// member's remaining pages in its walk order, padded with dummies to whole 4-page stages.
+void build_groups(const Problem &P, const FwdTables &F, GroupTables *T) {
+  const int G = P.slots, nq = P.n_q;
+  T->group_ptr.assign(size_t(G) + 1, 0);
+  T->members.clear();
+  T->walk_ptr.assign(1, 0);
+  T->walk.clear();
+  T->nfull.clear();
+  T->npages.clear();
+  T->valid.clear();
+  T->in_group.assign(size_t(G) * nq, 0);
+  const int64_t n_pg = P.seq_kv / kPageRows;
+  const size_t W = size_t((n_pg + 63) / 64);
+  std::vector<uint64_t> bits, uni(W), inter(W);
+  std::vector<uint32_t> pmask(size_t(n_pg), 0);
+  for (int g = 0; g < G; ++g) {
+    T->group_ptr[size_t(g) + 1] = T->group_ptr[size_t(g)];
+    if (!P.grouped) continue;
+    std::vector<int> cand;  // eligible blocks, ascending
+    for (int q = 0; q < nq; ++q) {
+      const int cq = P.q_valid[size_t(g) * nq + q];
+      if (F.route[size_t(g) * nq + q] == 64 && cq > 0 && cq <= kGroupMaxRows && F.unpadded[size_t(g) * nq + q] > 0)
+        cand.push_back(q);
+    }
+    if (cand.size() < 2) continue;
+    // page sets as bitsets, and every page's row mask
+    bits.assign(cand.size() * W, 0);
+    std::vector<int> n_of(cand.size(), 0);
+    for (size_t c = 0; c < cand.size(); ++c) {
+      const int64_t a = F.walk_ptr[size_t(g) * (nq + 1) + cand[c]];
+      const int n = F.unpadded[size_t(g) * nq + cand[c]];
+      for (int i = 0; i < n; ++i) {
+        const int32_t pg = F.walk[size_t(a + i)];
+        bits[c * W + size_t(pg >> 6)] |= uint64_t(1) << (pg & 63);
+        pmask[size_t(pg)] = (F.valid[size_t((a + i) >> 1)] >> (16 * ((a + i) & 1))) & kFullMask;
+      }
+      n_of[c] = n;
+    }
+    std::vector<uint8_t> free_(cand.size(), 1);
+    for (size_t c0 = 0; c0 < cand.size(); ++c0) {
+      if (!free_[c0]) continue;
+      free_[c0] = 0;
+      std::vector<size_t> grp{c0};
+      std::copy(bits.begin() + c0 * W, bits.begin() + (c0 + 1) * W, uni.begin());
+      std::copy(bits.begin() + c0 * W, bits.begin() + (c0 + 1) * W, inter.begin());
+      while (grp.size() < size_t(kGroupMembers)) {
+        size_t best = cand.size();
+        int64_t best_in = 0, best_n = 1;
+        for (size_t c = c0 + 1; c < cand.size(); ++c) {
+          if (!free_[c]) continue;
+          bool shares = false;  // a page selected by every member, the candidate included
+          for (size_t w = 0; w < W && !shares; ++w) shares = (inter[w] & bits[c * W + w]) != 0;
+          if (!shares) continue;
+          int64_t in = 0;
+          for (size_t w = 0; w < W; ++w) in += __builtin_popcountll(uni[w] & bits[c * W + w]);
+          if (best == cand.size() || in * best_n > best_in * n_of[c]) {
+            best = c;
+            best_in = in;
+            best_n = n_of[c];
+          }
+        }
+        if (best == cand.size() || 2 * best_in < best_n) break;
+        free_[best] = 0;
+        grp.push_back(best);
+        for (size_t w = 0; w < W; ++w) {
+          uni[w] |= bits[best * W + w];
+          inter[w] &= bits[best * W + w];
+        }
+      }
+      if (grp.size() < 2) continue;
+      // union walk
+      auto in_member = [&](size_t c, int32_t pg) { return (bits[c * W + size_t(pg >> 6)] >> (pg & 63)) & 1u; };
+      std::vector<int32_t> order;
+      auto walk_of = [&](size_t c, int i) {
+        return F.walk[size_t(F.walk_ptr[size_t(g) * (nq + 1) + cand[c]] + i)];
+      };
+      std::vector<uint8_t> used(size_t(n_pg), 0);
+      for (int i = 0; i < n_of[grp[0]]; ++i) {
+        const int32_t pg = walk_of(grp[0], i);
+        if (pmask[size_t(pg)] != kFullMask) continue;
+        bool all = true;
+        for (size_t m = 1; m < grp.size(); ++m) all = all && in_member(grp[m], pg);
+        if (all) {
+          order.push_back(pg);
+          used[size_t(pg)] = 1;
+        }
+      }
+      const int n_full = int(order.size());
+      // then the other pages every member selected, so that the first sub-tile holds a
+      // valid key for every member whenever they share a page
+      for (int i = 0; i < n_of[grp[0]]; ++i) {
+        const int32_t pg = walk_of(grp[0], i);
+        if (used[size_t(pg)]) continue;
+        bool all = true;
+        for (size_t m = 1; m < grp.size(); ++m) all = all && in_member(grp[m], pg);
+        if (all) {
+          order.push_back(pg);
+          used[size_t(pg)] = 1;
+        }
+      }
+      for (size_t m = 0; m < grp.size(); ++m)
+        for (int i = 0; i < n_of[grp[m]]; ++i) {
+          const int32_t pg = walk_of(grp[m], i);
+          if (!used[size_t(pg)]) {
+            order.push_back(pg);
+            used[size_t(pg)] = 1;
+          }
+        }
+      const int n_real = int(order.size());
+      while (order.size() % 4) order.push_back(-1);
+      T->walk.insert(T->walk.end(), order.begin(), order.end());
+      T->walk_ptr.push_back(int64_t(T->walk.size()));
+      T->nfull.push_back(n_full);
+      T->npages.push_back(n_real);
+      for (int w = 0; w < kGroupMembers; ++w) {
+        for (size_t i = 0; i < order.size(); i += 2) {
+          uint32_t word = 0;
+          for (int h = 0; h < 2; ++h) {
+            const int32_t pg = order[i + size_t(h)];
+            if (pg >= 0 && size_t(w) < grp.size() && in_member(grp[size_t(w)], pg))
+              word |= pmask[size_t(pg)] << (16 * h);
+          }
+          T->valid.push_back(word);
+        }
+      }
+      for (int w = 0; w < kGroupMembers; ++w) {
+        const int32_t q = size_t(w) < grp.size() ? cand[grp[size_t(w)]] : -1;
+        T->members.push_back(q);
+        if (q >= 0) T->in_group[size_t(g) * nq + q] = 1;
+      }
+      T->group_ptr[size_t(g) + 1]++;
     }
   }
 }

@@ -19,6 +19,7 @@ struct Problem {
   int64_t seq_q = 0, seq_kv = 0;
   bool per_head = false;
   int q_group = 0;  // Q blocks per backward Q group; 0 = one group
+  bool grouped = true;  // run small query blocks in group items (build_groups)
   std::vector<int32_t> q_valid, kv_valid;   // [slots][n]
   std::vector<int64_t> kv_offset;           // [slots][n_kv]
   std::vector<int64_t> q2k_ptr;             // [slots][n_q + 1]
@@ -42,6 +43,23 @@ struct FwdTables {
   std::vector<int32_t> q64_queue;   // pairs (bh, q)
   std::vector<int32_t> q128_queue;  // pairs (bh, q)
   std::vector<int32_t> unpadded;    // [slots][n_q] real pages per walk
+};
+
+// Group items (launch-level, not part of the paper's tables): per graph slot, query
+// blocks of the M64 x N256 route with at most 32 valid rows whose walks overlap are run
+// four at a time as one M128 x N128 item over the union of their walks, one member per
+// wave.  Built on the host only.
+constexpr int kGroupMembers = 4;
+constexpr int kGroupMaxRows = 32;
+struct GroupTables {
+  std::vector<int64_t> group_ptr;   // [slots + 1] offsets into the group list
+  std::vector<int32_t> members;     // [n_groups][4] query blocks, -1 = none (at least 2 members)
+  std::vector<int64_t> walk_ptr;    // [n_groups + 1] union walks, multiples of 4 entries
+  std::vector<int32_t> walk;        // page ids, -1 dummy (only at the end)
+  std::vector<int32_t> nfull;       // [n_groups] leading pages that are full and in every member's walk
+  std::vector<int32_t> npages;      // [n_groups] real pages of the union walk
+  std::vector<uint32_t> valid;      // member w of group i: words [2 walk_ptr[i] + w len / 2, + len / 2)
+  std::vector<uint8_t> in_group;    // [slots][n_q] 1 when the block is a group member
 };
 
 // Backward tables, concatenated over graph slots.
@@ -69,5 +87,7 @@ kpage_status load_problem(const kpage_problem *p, const kpage_plan_opts *o, Prob
                           int *align128, std::string *err);
 void build_forward(const Problem &p, FwdTables *t, PairStats *s);
 void build_backward(const Problem &p, BwdTables *t, PairStats *s);
+// Group items of the forward and dQ launches (empty tables when p.grouped is false).
+void build_groups(const Problem &p, const FwdTables &f, GroupTables *t);
 
 }  // namespace kpage

@@ -79,11 +79,22 @@ typedef struct {
  * group 0 (one item, no partials).  An owner split over several items sums fp32
  * partials of dK/dV (in group order, deterministic) in the backward workspace.
  * Negative values are KPAGE_ERR_INVALID.
+ *
+ * ungrouped = 0 (default) lets kpage_plan() run query blocks of the Q64 route with
+ * at most 32 valid rows in group items: up to four such blocks whose K/V walks
+ * overlap share one M128 x N128 work item of the forward and dQ passes over the
+ * union of their walks (each block's rows mask the pages it did not select), so a
+ * page they share is gathered once.  This is a launch-level choice outside the
+ * paper's tables (section 3.2.2 routes such blocks to M64 x N256 one at a time):
+ * the exported tables, queues and pair counts do not change, and each row's result
+ * is the same attention up to fp32 summation order.  ungrouped = 1 runs every
+ * block as its own item.  kpage_plan_device() never groups.
  */
 typedef struct {
   int32_t q_group;
   int32_t align_q128;
   int32_t align_q64;
+  int32_t ungrouped;
 } kpage_plan_opts;
 
 /* Section 4.4 pair-capacity accounting, summed over batch, heads and non-empty
@@ -237,7 +248,16 @@ enum {
   KPAGE_T_BWD_QUEUE = 15,     /* int32 [n][2]: (b * heads + h, owner within its slot) */
   KPAGE_T_UNCOVERED_PTR = 16, /* int64 [G + 1]: offsets into UNCOVERED                */
   KPAGE_T_UNCOVERED = 17,     /* int32 K/V pages outside every block footprint, ascending */
-  KPAGE_T_COUNT = 18
+  /* group items of kpage_plan() (see kpage_plan_opts.ungrouped; empty otherwise) */
+  KPAGE_T_GROUP_PTR = 18,     /* int64 [G + 1]: offsets into the group list            */
+  KPAGE_T_GROUP_MEMBERS = 19, /* int32 [n_groups][4]: query blocks, -1 = none          */
+  KPAGE_T_GROUP_WALK_PTR = 20,/* int64 [n_groups + 1]: offsets into GROUP_WALK (x4)    */
+  KPAGE_T_GROUP_WALK = 21,    /* int32 union walk page ids, -1 = dummy (at the end)    */
+  KPAGE_T_GROUP_NFULL = 22,   /* int32 [n_groups]: leading pages full in every member  */
+  KPAGE_T_GROUP_VALID = 23,   /* uint32: member w of group i, word j at
+                                 2 GROUP_WALK_PTR[i] + w len_i / 2 + j (page masks of
+                                 the member's own selection, 0 for other pages)        */
+  KPAGE_T_COUNT = 24
 };
 
 /*

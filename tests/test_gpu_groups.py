@@ -1,0 +1,116 @@
+"""Group items on the GPU against the fp64 CPU oracle (through the C ABI).
+
+A group item runs up to four query blocks of at most 32 valid rows over the union of
+their page walks, one member per wave, each wave masking the pages its own block did
+not select; it writes every member block's 128 output rows.  Checked here: forward O and
+LSE and the gradients on layouts built to form groups of two, three and four members
+(tails, 1- and 8-row blocks, empty blocks next to members), groups whose items take the
+exact re-run, and every member block of the top-87 workload; the same problems planned
+without groups agree with the oracle too.  Tolerances as in the forward and backward
+parity tests.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_11_amd as K
+from oracle import oracle_bwd, oracle_fwd
+from tests.problems import make_problem, random_tensors
+from tests.test_gpu_bwd import check_grads, gpu_fwd_bwd
+from tests.test_gpu_fwd import abs_values_attention, check, gpu_fwd
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def group_sizes(plan):
+    m = K.kpage_plan_export(plan, "group_members").reshape(-1, 4)
+    return sorted(int(x) for x in (m >= 0).sum(axis=1))
+
+
+def small_blocks_problem(d):
+    """14 query blocks: 11 of at most 32 rows (1, 8, 16, 17, 20, 31 and 32 rows), one empty,
+    two large.  K blocks 0-5 full or with tails; the small blocks select overlapping
+    subsets of K blocks 0-4 (so they form groups of 2-4), two select disjoint ones."""
+    cq = [128, 20, 32, 8, 32, 0, 31, 1, 17, 16, 32, 100, 32, 24]
+    ck = [128, 128, 70, 128, 9, 128, 33]
+    rows = [[0, 1, 2, 3], [0, 1, 2], [0, 1, 2, 4], [0, 1], [1, 2, 0], [0], [3, 4, 2], [3, 4], [2, 3, 4, 1],
+            [4, 3], [5, 6], [0, 5, 6], [6, 5], [1, 0, 2, 6]]
+    return make_problem(cq, ck, rows, heads=3, head_dim=d, sort_rows=False)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_groups_forward_and_backward(d):
+    p = small_blocks_problem(d)
+    t = random_tensors(p, seed=70 + d)
+    plan = K.kpage_plan(p)
+    sizes = group_sizes(plan)
+    _say(f"[groups] small blocks d={d}: group sizes {sizes}")
+    assert len(sizes) >= 2 and max(sizes) >= 3
+    O, L = gpu_fwd(p, t["q"], t["k"], t["v"], plan=plan)
+    Oref, Lref = oracle_fwd(p, t["q"], t["k"], t["v"])
+    check(O, L, Oref, Lref, f"groups d={d}", Aabs=abs_values_attention(p, t["q"], t["k"], t["v"]))
+    got = gpu_fwd_bwd(p, t["q"], t["k"], t["v"], t["do"], plan=plan)
+    ref = oracle_bwd(p, t["q"], t["k"], t["v"], t["do"])[:3]
+    check_grads(got, ref, f"groups d={d}", p)
+
+
+def test_ungrouped_plan_matches_oracle_too():
+    p = small_blocks_problem(128)
+    t = random_tensors(p, seed=71)
+    plan = K.kpage_plan(p, grouped=False)
+    assert group_sizes(plan) == []
+    _say("[groups] same problem, no groups")
+    O, L = gpu_fwd(p, t["q"], t["k"], t["v"], plan=plan)
+    Oref, Lref = oracle_fwd(p, t["q"], t["k"], t["v"])
+    check(O, L, Oref, Lref, "ungrouped", Aabs=abs_values_attention(p, t["q"], t["k"], t["v"]))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_groups_take_the_exact_rerun(d):
+    """Scores that rise by far more than 2^64 (base 2) after the first pages of every walk:
+    every group item is marked and re-run by the exact kernel."""
+    p = small_blocks_problem(d)
+    t = random_tensors(p, seed=72 + d)
+    g = torch.Generator().manual_seed(73)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    amp = 30.0 * (128.0 / d) ** 0.5
+    q = t["q"].float() + amp * u
+    k = t["k"].float()
+    k[:, :, 128:] += amp * u  # every K block but block 0
+    for x, c in ((q, p.q_valid[0]), (k, p.kv_valid[0])):
+        for b, n in enumerate(c):
+            x[:, :, 128 * b + int(n):128 * (b + 1)] = 0
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    plan = K.kpage_plan(p)
+    assert group_sizes(plan)
+    _say(f"[groups] score rise d={d}")
+    O, L = gpu_fwd(p, q, k, t["v"], plan=plan)
+    Oref, Lref = oracle_fwd(p, q, k, t["v"])
+    check(O, L, Oref, Lref, f"groups score rise d={d}", Aabs=abs_values_attention(p, q, k, t["v"]))
+
+
+def test_topk_workload_every_member_block():
+    """Two heads of the 21x45x80 top-87 workload (per-head graphs): every block that runs
+    inside a group item, forward; one head's gradients."""
+    w = make_workload(4, heads=[0, 1], with_do=True)
+    plan = K.kpage_plan(w)
+    m = K.kpage_plan_export(plan, "group_members").reshape(-1, 4)
+    ptr = K.kpage_plan_export(plan, "group_ptr")
+    items = [(0, h, int(q)) for h in range(2) for i in range(int(ptr[h]), int(ptr[h + 1])) for q in m[i] if q >= 0]
+    _say(f"[groups] top-87 two heads: {len(items)} member blocks in {m.shape[0]} groups")
+    assert len(items) > 100
+    O, L = gpu_fwd(w, w.q, w.k, w.v, plan=plan)
+    Oref, Lref = oracle_fwd(w, w.q, w.k, w.v, items=items)
+    check(O, L, Oref, Lref, "top-87 group members")
+    got = gpu_fwd_bwd(w, w.q, w.k, w.v, w.do, plan=plan)
+    ref = oracle_bwd(w, w.q, w.k, w.v, w.do, heads=[1])[:3]
+    check_grads(got, ref, "top-87 groups head 1", w, heads=[1])

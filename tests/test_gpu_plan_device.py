@@ -36,7 +36,8 @@ def _say(msg):
 
 
 def same_plans(p, label, bwd=True, **opts):
-    h = K.kpage_plan(p, **opts)
+    # the GPU planner builds no group items; the host plan's launch runs ungrouped too
+    h = K.kpage_plan(p, grouped=False, **opts)
     d = K.kpage_plan_device(p, **opts)
     for t in FWD_TABLES:
         a, b = K.kpage_plan_export(h, t), K.kpage_plan_export(d, t)
@@ -116,7 +117,7 @@ def test_device_plan_full_size_attention_is_bitwise_equal():
     plan's bit for bit."""
     w = make_workload(3, with_do=True)
     _say(f"[device plan] full-size 21x30x52, {w.heads} heads")
-    h, d = K.kpage_plan(w), K.kpage_plan_device(w)
+    h, d = K.kpage_plan(w, grouped=False), K.kpage_plan_device(w)
     dev = torch.device("cuda", 0)
     q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
     outs = []
@@ -168,7 +169,7 @@ def test_device_plan_q_groups_attention_is_bitwise_equal(name, q_group):
     entries as the host plan, so the gradients are bitwise equal."""
     w = make_workload(3 if "21x30x52" in name else 4, heads=[0, 1], with_do=True)
     _say(f"[device plan] {name}, q_group {q_group}")
-    h, d = K.kpage_plan(w, q_group=q_group), K.kpage_plan_device(w, q_group=q_group)
+    h, d = K.kpage_plan(w, q_group=q_group, grouped=False), K.kpage_plan_device(w, q_group=q_group)
     assert K.kpage_bwd_workspace_size(h) == K.kpage_bwd_workspace_size(d)
     dev = torch.device("cuda", 0)
     q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))

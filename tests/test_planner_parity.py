@@ -13,6 +13,8 @@ def _assert_same(problem, **opts):
     plan = K.kpage_plan(problem, **opts)
     ref = oracle_plan(problem, **{k: v for k, v in opts.items() if v})
     for name in K.TABLES:
+        if name.startswith("group_"):  # launch-level grouping, not part of the paper's tables
+            continue
         got = K.kpage_plan_export(plan, name)
         want = getattr(ref, name).reshape(-1)
         assert got.dtype == want.dtype or got.dtype.kind == want.dtype.kind, name
