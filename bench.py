@@ -154,7 +154,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bwd_3d_padded_h40.jso
 def _measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed FETCH_SIZE / WRITE_SIZE counter
     summary (already scaled by the copy calibration), or None when the counters were taken
-    on another workload or the kernel's sources changed since they were taken."""
+    on another workload or when the kernel's sources, or the host planner and launch-list
+    code that decide its work, changed since they were taken."""
     import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
@@ -171,11 +172,20 @@ def _measured_traffic(kernel, workload):
     return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
-def _route_pairs(w):
-    """Useful pairs of the M128 x N128 and M64 x N256 routes (c_q > 64 and 1 <= c_q <= 64)."""
+def _route_pairs(w, K=None, plan=None):
+    """Useful pairs of the work items of the M128 x N128 and M64 x N256 launches: blocks with
+    c_q > 64 and the members of group items (up to four blocks of <= 32 rows run as one M128
+    item), and the other blocks with 1 <= c_q <= 64."""
     import numpy as np
     BH = w.batch * w.heads
     slots = range(BH) if w.per_head else [0]
+    grouped = set()
+    if plan is not None:
+        gptr = K.kpage_plan_export(plan, "group_ptr")
+        mem = K.kpage_plan_export(plan, "group_members").reshape(-1, 4)
+        for g in slots:
+            for i in range(int(gptr[g]), int(gptr[g + 1])):
+                grouped.update((g, int(q)) for q in mem[i] if q >= 0)
     out = {"q128": 0, "q64": 0}
     for g in slots:
         for q in range(w.n_q):
@@ -184,7 +194,7 @@ def _route_pairs(w):
                 continue
             ks = w.q2k_idx[w.q2k_ptr[g, q]:w.q2k_ptr[g, q + 1]]
             pairs = cq * int(np.asarray(w.kv_valid[g])[ks].sum())
-            out["q128" if cq > 64 else "q64"] += pairs
+            out["q128" if cq > 64 or (g, q) in grouped else "q64"] += pairs
     if not w.per_head:
         out = {k: v * BH for k, v in out.items()}
     return out
@@ -192,13 +202,14 @@ def _route_pairs(w):
 
 def _route_split(K, plan, step, w, steps=5):
     """Forward and dQ launches split by route (timing mode 2), after the timed region: per-route
-    time and useful TFLOP/s (4 d per pair for the forward, 6 d for the dQ pass)."""
+    time and useful TFLOP/s (4 d per pair for the forward, 6 d for the dQ pass); group items
+    count with the M128 x N128 route, whose launch runs them."""
     K.kpage_timing_enable(plan, 2)
     for _ in range(steps):
         step()
     kern = {n: K.kpage_timing_read(plan, n) for n in K.KERNELS}
     K.kpage_timing_enable(plan, False)
-    pairs = _route_pairs(w)
+    pairs = _route_pairs(w, K, plan)
     d = w.head_dim
     out = {}
     for name, key, route, per in (("fwd_q128", "fwd", "q128", 4), ("fwd_q64", "fwd_q64", "q64", 4),
