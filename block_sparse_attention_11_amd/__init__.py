@@ -185,7 +185,8 @@ def kpage_plan(problem, align_q64: int = 0, align_q128: int = 0, q_group: int = 
     return Plan(h, problem.batch, problem.heads, problem.head_dim, problem.seq_q, problem.seq_kv)
 
 
-def kpage_plan_device(problem, align_q64: int = 0, align_q128: int = 0, q_group: int = 0, stream=None) -> Plan:
+def kpage_plan_device(problem, align_q64: int = 0, align_q128: int = 0, q_group: int = 0, stream=None,
+                      grouped: bool = True) -> Plan:
     """Plan for ``problem`` built on the GPU from device copies of its descriptor arrays
     (kpage_plan_device).  The arrays may be numpy arrays (copied to the current device
     here) or CUDA tensors of the right dtypes."""
@@ -213,7 +214,7 @@ def kpage_plan_device(problem, align_q64: int = 0, align_q128: int = 0, q_group:
         per_head=1 if problem.per_head else 0,
         q_valid=qv.data_ptr(), kv_valid=kvv.data_ptr(), kv_offset=0 if ko is None else ko.data_ptr(),
         q2k_ptr=ptr.data_ptr(), q2k_idx=idx.data_ptr())
-    opts = KpagePlanOpts(q_group=q_group, align_q128=align_q128, align_q64=align_q64)
+    opts = KpagePlanOpts(q_group=q_group, align_q128=align_q128, align_q64=align_q64, ungrouped=0 if grouped else 1)
     h = ctypes.c_void_p()
     _check(lib().kpage_plan_device(ctypes.byref(p), nnz, ctypes.byref(opts), _stream_ptr(stream), ctypes.byref(h)))
     return Plan(h, problem.batch, problem.heads, problem.head_dim, problem.seq_q, problem.seq_kv)

@@ -348,7 +348,14 @@ kpage_status ensure_forward_on_host(PlanT *pl) {
                   copy_down(F.q64_queue, T.q64_queue, 2 * int64_t(T.n_q64)) &&
                   copy_down(F.q128_queue, T.q128_queue, 2 * int64_t(T.n_q128)) &&
                   copy_down(F.unpadded, T.unpadded, GQ);
-  if (!ok) return fail(KPAGE_ERR_HIP, "copying the forward tables to the host failed");
+  GroupTables &GT = pl->GT;
+  GT.group_ptr = T.g_group_ptr;
+  GT.walk_ptr = T.g_walk_ptr;
+  const int64_t gw = T.g_walk_ptr.empty() ? 0 : T.g_walk_ptr.back();
+  const bool gok = copy_down(GT.members, T.g_members, T.n_groups * kGroupMembers) &&
+                   copy_down(GT.nfull, T.g_nfull, T.n_groups) && copy_down(GT.npages, T.g_npages, T.n_groups) &&
+                   copy_down(GT.walk, T.g_walk, gw) && copy_down(GT.valid, T.g_valid, 2 * gw);
+  if (!ok || !gok) return fail(KPAGE_ERR_HIP, "copying the forward tables to the host failed");
   pl->fwd_on_host = true;
   return KPAGE_OK;
 }
@@ -723,7 +730,7 @@ static kpage_status plan_device_body(const kpage_problem *problem, int64_t q2k_n
   }
   pl->F.align64 = a64;
   pl->F.align128 = a128;
-  s = build_forward_device(D, a64, a128, st, alloc, &pl->DF, &err);
+  s = build_forward_device(D, a64, a128, P.grouped, st, alloc, &pl->DF, &err);
   if (s != KPAGE_OK) {
     kpage_plan_destroy(pl);
     return fail(s, err);
@@ -736,8 +743,9 @@ static kpage_status plan_device_body(const kpage_problem *problem, int64_t q2k_n
   pl->d_items128 = pl->DF.items128;
   pl->d_items64 = pl->DF.items64;
   pl->d_order = pl->DF.order;
-  pl->n_items128 = pl->DF.n_q128;
-  pl->n_items64 = pl->DF.n_q64 + pl->DF.n_zero;
+  pl->d_groups = pl->DF.groups;
+  pl->n_items128 = int(pl->DF.n_q128 + pl->DF.n_gitems);
+  pl->n_items64 = int(pl->DF.n_q64 - pl->DF.n_members + pl->DF.n_zero);
   pl->fwd_on_device = true;
   *out = pl;
   g_last_error.clear();

@@ -242,14 +242,14 @@ void build_groups(const Problem &P, const FwdTables &F, GroupTables *T) {
   std::vector<uint32_t> pmask(size_t(n_pg), 0);
   for (int g = 0; g < G; ++g) {
     T->group_ptr[size_t(g) + 1] = T->group_ptr[size_t(g)];
-    if (!P.grouped) continue;
+    if (!P.grouped || W > size_t(kGroupMaxWords)) continue;
     std::vector<int> cand;  // eligible blocks, ascending
     for (int q = 0; q < nq; ++q) {
       const int cq = P.q_valid[size_t(g) * nq + q];
       if (F.route[size_t(g) * nq + q] == 64 && cq > 0 && cq <= kGroupMaxRows && F.unpadded[size_t(g) * nq + q] > 0)
         cand.push_back(q);
     }
-    if (cand.size() < 2) continue;
+    if (cand.size() < 2 || cand.size() > size_t(kGroupMaxCands)) continue;
     // page sets as bitsets, and every page's row mask
     bits.assign(cand.size() * W, 0);
     std::vector<int> n_of(cand.size(), 0);

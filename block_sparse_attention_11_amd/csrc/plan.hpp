@@ -51,6 +51,11 @@ struct FwdTables {
 // wave.  Built on the host only.
 constexpr int kGroupMembers = 4;
 constexpr int kGroupMaxRows = 32;
+// Grouping runs where its working sets fit the GPU planner's LDS (both planners apply
+// the same limits): page bitsets of at most 2048 words (seq_kv up to 2^21 rows) and at
+// most 16384 candidate blocks per graph slot.
+constexpr int kGroupMaxWords = 2048;
+constexpr int kGroupMaxCands = 16384;
 struct GroupTables {
   std::vector<int64_t> group_ptr;   // [slots + 1] offsets into the group list
   std::vector<int32_t> members;     // [n_groups][4] query blocks, -1 = none (at least 2 members)

@@ -279,14 +279,22 @@ __global__ void k_queue_out(const unsigned long long *keys, int n, int n_q, int3
 // cleanup item z is n128 + n64 + z; workgroup launch_position(L) runs that item
 // (order[] = i, or ~(index in the M64 list)).  hs128 / hs64 [BH + 1]: items of each
 // route in the heads before bh.
+// With group items (in_group: members; hsg [BH + 1]: group items of the heads before bh,
+// NULL without groups): a head's group items follow its other M128 items (k_group_items
+// writes them), member blocks are no M64 items, and every later position shifts by the
+// group items before it.
 __global__ __launch_bounds__(kScanThreads) void k_items(DevProblem p, const int32_t *route, const int32_t *nfull,
                                                         const int32_t *unpadded, const int64_t *walk_ptr,
-                                                        const Summary *sum, FwdItem *items128, FwdItem *items64,
-                                                        int64_t *hs128, int64_t *hs64, int32_t *order) {
+                                                        const Summary *sum, const uint8_t *in_group,
+                                                        const int64_t *hsg, int64_t n_members, FwdItem *items128,
+                                                        FwdItem *items64, int64_t *hs128, int64_t *hs64,
+                                                        int32_t *order) {
   __shared__ int64_t lds[kScanThreads];
   const int64_t n = int64_t(p.batch) * p.heads * p.n_q;
   const int BH = p.batch * p.heads;
-  const int64_t n128 = sum->n_q128, n64 = sum->n_q64, n_all = n128 + n64 + sum->n_zero;
+  const int64_t n_gi = hsg ? hsg[BH] : 0;
+  const int64_t n128 = sum->n_q128, n64 = sum->n_q64 - n_members, n_all = n128 + n_gi + n64 + sum->n_zero;
+  auto gb = [&](int bh) -> int64_t { return hsg ? hsg[bh] : 0; };
   for (int pass = 0; pass < 2; ++pass) {
     int64_t c128 = 0, c64 = 0, cz = 0;
     for (int64_t base = 0; base < n; base += kScanThreads) {
@@ -300,6 +308,7 @@ __global__ __launch_bounds__(kScanThreads) void k_items(DevProblem p, const int3
         i = int64_t(p.per_head ? bh : 0) * p.n_q + q;
         r = route[i];
         cq = p.q_valid[i];
+        if (r == 64 && in_group && in_group[i]) r = -1;  // runs inside its group item
       }
       int64_t t128, t64, tz;
       const int64_t p128 = c128 + block_scan(r == 128 ? 1 : 0, lds, &t128);
@@ -309,7 +318,7 @@ __global__ __launch_bounds__(kScanThreads) void k_items(DevProblem p, const int3
         hs128[bh] = p128;
         hs64[bh] = p64;
       }
-      if (f < n && (r != 0 || cq == 0)) {
+      if (f < n && r >= 0 && (r != 0 || cq == 0)) {
         if (pass == 0) {
           FwdItem x{};
           const int64_t wp = int64_t(p.per_head ? bh : 0) * (p.n_q + 1) + q;
@@ -320,20 +329,20 @@ __global__ __launch_bounds__(kScanThreads) void k_items(DevProblem p, const int3
           x.n_full = nfull[i];
           x.n_pages = unpadded[i];
           x.c_q = cq;
-          if (r == 128) items128[p128] = x;
+          if (r == 128) items128[p128 + gb(bh)] = x;
           else if (r == 64) items64[p64] = x;
           else items64[n64 + pz] = x;
         } else {
           int64_t L;
           int32_t tag;
           if (r == 128) {
-            L = p128 + hs64[bh];
-            tag = int32_t(p128);
+            L = p128 + gb(bh) + hs64[bh];
+            tag = int32_t(p128 + gb(bh));
           } else if (r == 64) {
-            L = p64 + hs128[bh + 1];
+            L = p64 + hs128[bh + 1] + gb(bh + 1);
             tag = ~int32_t(p64);
           } else {
-            L = n128 + n64 + pz;
+            L = n128 + n_gi + n64 + pz;
             tag = ~int32_t(n64 + pz);
           }
           order[launch_position(L, n_all, p.xcd_chunk)] = tag;
@@ -387,11 +396,308 @@ __global__ __launch_bounds__(kFwdTail) void k_fwd_tails(int32_t *order, const Fw
   if (i < t) order[(j0 + i) * kXcds + x] = tag[uint32_t(key[i])];
 }
 
+// ---------------------------------------------------------------------------------
+// Group items (the host planner's build_groups: same rule, same groups, same union walks).
+// Candidates of a slot: the query blocks of the Q64 route with 1..32 valid rows and a
+// non-empty walk, in block order, each held as a bitset of its walk's pages.  One
+// workgroup per slot makes the greedy choice (the opening blocks in order; each pick a
+// parallel argmax over the free candidates, ties to the lower block); one workgroup per
+// group then writes its union walk, in the same order as the host, and the validity
+// words of its four waves.
+constexpr int kGroupThreads = 256;
+
+// row mask of page pg of slot g (a page of a walk lies in a selected block's footprint)
+__device__ __forceinline__ uint32_t dev_page_mask(const DevProblem &p, const int32_t *page_block, int g, int32_t pg) {
+  const int64_t n_pg = p.seq_kv / kPageRows;
+  const int b = page_block[int64_t(g) * n_pg + pg];
+  const int ck = p.kv_valid[int64_t(g) * p.n_kv + b];
+  const int j = pg - int(kv_off(p, g, b) / kPageRows);
+  return (j + 1) * kPageRows <= ck ? kFullMask : tail_mask(ck);
+}
+
+// candidates of slot blockIdx.x in block order; their count
+__global__ __launch_bounds__(kScanThreads) void k_group_cands(DevProblem p, const int32_t *route,
+                                                              const int32_t *unpadded, int32_t *cand,
+                                                              int32_t *n_cand) {
+  __shared__ int64_t lds[kScanThreads];
+  const int g = int(blockIdx.x);
+  int64_t c = 0;
+  for (int base = 0; base < p.n_q; base += kScanThreads) {
+    const int q = base + int(threadIdx.x);
+    bool f = false;
+    if (q < p.n_q) {
+      const int64_t i = int64_t(g) * p.n_q + q;
+      const int cq = p.q_valid[i];
+      f = route[i] == 64 && cq > 0 && cq <= kGroupMaxRows && unpadded[i] > 0;
+    }
+    int64_t tot;
+    const int64_t pos = c + block_scan(f ? 1 : 0, lds, &tot);
+    if (f) cand[int64_t(g) * p.n_q + pos] = q;
+    c += tot;
+  }
+  if (threadIdx.x == 0) n_cand[g] = int32_t(c);
+}
+
+// slot of global index i with ptr[g] <= i < ptr[g + 1] (ptr non-decreasing, ptr[0] = 0)
+__device__ __forceinline__ int slot_of_index(const int64_t *ptr, int slots, int64_t i) {
+  int lo = 0, hi = slots;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (ptr[mid] <= i) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// page bitset of candidate blockIdx.x (global candidate index; bits zeroed beforehand)
+__global__ void k_group_bits(DevProblem p, const int64_t *walk_ptr, const int32_t *walk, const int32_t *unpadded,
+                             const int32_t *cand, const int64_t *cand_off, int W, unsigned long long *bits) {
+  const int64_t ci = blockIdx.x;
+  const int g = slot_of_index(cand_off, p.slots, ci);
+  const int q = cand[int64_t(g) * p.n_q + (ci - cand_off[g])];
+  const int64_t a = walk_ptr[int64_t(g) * (p.n_q + 1) + q];
+  const int n = unpadded[int64_t(g) * p.n_q + q];
+  unsigned long long *b = bits + ci * W;
+  for (int i = int(threadIdx.x); i < n; i += int(blockDim.x)) {
+    const int32_t pg = walk[a + i];
+    atomicOr(&b[pg >> 6], 1ull << (pg & 63));
+  }
+}
+
+// the greedy choice of slot blockIdx.x; group gi of the slot: members (candidate
+// indices, -1 none) at gmem[(cand_off + gi) * 4 ..], union size at gunion[cand_off + gi]
+__global__ __launch_bounds__(kGroupThreads) void k_group_greedy(DevProblem p, const int32_t *unpadded,
+                                                                const int32_t *cand, const int32_t *n_cand,
+                                                                const int64_t *cand_off, int W,
+                                                                const unsigned long long *bits, int32_t *gmem,
+                                                                int32_t *gunion, int32_t *gcount, int32_t *gmembers) {
+  extern __shared__ unsigned long long gl[];  // union [W], intersection [W], taken flags [n_cand]
+  unsigned long long *uni = gl, *inter = gl + W;
+  uint8_t *taken = reinterpret_cast<uint8_t *>(gl + 2 * W);
+  __shared__ int64_t r_in[kGroupThreads], r_n[kGroupThreads];
+  __shared__ int32_t r_c[kGroupThreads];
+  __shared__ int32_t mem[kGroupMembers];
+  const int g = int(blockIdx.x), tid = int(threadIdx.x);
+  const int nc = n_cand[g];
+  const int64_t off = cand_off[g];
+  const unsigned long long *B = bits + off * W;
+  for (int c = tid; c < nc; c += kGroupThreads) taken[c] = 0;
+  int ng = 0, nmem = 0;
+  for (int c0 = 0; c0 < nc; ++c0) {
+    __syncthreads();
+    const bool skip = taken[c0] != 0;
+    __syncthreads();  // every wave has read the flag before thread 0 may set it
+    if (skip) continue;
+    if (tid == 0) {
+      taken[c0] = 1;
+      mem[0] = c0;
+      mem[1] = mem[2] = mem[3] = -1;
+    }
+    for (int w = tid; w < W; w += kGroupThreads) uni[w] = inter[w] = B[int64_t(c0) * W + w];
+    __syncthreads();
+    int m = 1;
+    while (m < kGroupMembers) {
+      int64_t bi = 0, bn = 1;
+      int32_t bc = -1;
+      for (int c = c0 + 1 + tid; c < nc; c += kGroupThreads) {
+        if (taken[c]) continue;
+        const unsigned long long *bb = B + int64_t(c) * W;
+        bool shares = false;  // a page selected by every member and by c
+        for (int w = 0; w < W && !shares; ++w) shares = (inter[w] & bb[w]) != 0;
+        if (!shares) continue;
+        int64_t in = 0;
+        for (int w = 0; w < W; ++w) in += __popcll(uni[w] & bb[w]);
+        const int64_t n = unpadded[int64_t(g) * p.n_q + cand[int64_t(g) * p.n_q + c]];
+        if (bc < 0 || in * bn > bi * n) {
+          bi = in;
+          bn = n;
+          bc = c;
+        }
+      }
+      r_in[tid] = bi;
+      r_n[tid] = bn;
+      r_c[tid] = bc;
+      __syncthreads();
+      for (int h = kGroupThreads / 2; h > 0; h >>= 1) {
+        if (tid < h) {
+          const int32_t c1 = r_c[tid + h], c0b = r_c[tid];
+          if (c1 >= 0) {
+            const int64_t i1 = r_in[tid + h], n1 = r_n[tid + h], i0 = r_in[tid], n0 = r_n[tid];
+            if (c0b < 0 || i1 * n0 > i0 * n1 || (i1 * n0 == i0 * n1 && c1 < c0b)) {
+              r_in[tid] = i1;
+              r_n[tid] = n1;
+              r_c[tid] = c1;
+            }
+          }
+        }
+        __syncthreads();
+      }
+      const int32_t best = r_c[0];
+      const int64_t best_in = r_in[0], best_n = r_n[0];
+      __syncthreads();  // the next round rewrites r_*
+      if (best < 0 || 2 * best_in < best_n) break;
+      if (tid == 0) {
+        taken[best] = 1;
+        mem[m] = best;
+      }
+      for (int w = tid; w < W; w += kGroupThreads) {
+        const unsigned long long x = B[int64_t(best) * W + w];
+        uni[w] |= x;
+        inter[w] &= x;
+      }
+      ++m;
+      __syncthreads();
+    }
+    if (m >= 2) {
+      int cnt = 0;
+      for (int w = tid; w < W; w += kGroupThreads) cnt += __popcll(uni[w]);
+      r_c[tid] = cnt;
+      __syncthreads();
+      for (int h = kGroupThreads / 2; h > 0; h >>= 1) {
+        if (tid < h) r_c[tid] += r_c[tid + h];
+        __syncthreads();
+      }
+      if (tid == 0) {
+        for (int j = 0; j < kGroupMembers; ++j) gmem[(off + ng) * kGroupMembers + j] = mem[j];
+        gunion[off + ng] = r_c[0];
+      }
+      ++ng;
+      nmem += m;
+    }
+  }
+  if (tid == 0) {
+    gcount[g] = ng;
+    gmembers[g] = nmem;
+  }
+}
+
+// union walk, validity words and member table of group blockIdx.x (global group index)
+__global__ __launch_bounds__(kScanThreads) void k_group_walks(
+    DevProblem p, const int32_t *page_block, const int64_t *walk_ptr, const int32_t *walk, const int32_t *unpadded,
+    const int32_t *cand, const int64_t *cand_off, int W, const unsigned long long *bits, const int32_t *gmem,
+    const int64_t *group_ptr, const int64_t *gwalk_ptr, int64_t walk_base, int64_t valid_base, FwdGroup *groups,
+    int32_t *members, int32_t *nfull, int32_t *npages, int32_t *gwalk, int32_t *pages, uint32_t *valid,
+    uint32_t *gvalid, uint8_t *in_group) {
+  extern __shared__ unsigned long long used[];  // [W]: pages already in the union walk
+  __shared__ int64_t lds[kScanThreads];
+  const int64_t i = blockIdx.x;
+  const int tid = int(threadIdx.x);
+  const int g = slot_of_index(group_ptr, p.slots, i);
+  const int64_t k = i - group_ptr[g], off = cand_off[g];
+  int32_t mc[kGroupMembers], mq[kGroupMembers];
+  int nm = 0;
+  for (int j = 0; j < kGroupMembers; ++j) {
+    mc[j] = gmem[(off + k) * kGroupMembers + j];
+    mq[j] = mc[j] >= 0 ? cand[int64_t(g) * p.n_q + mc[j]] : -1;
+    nm += mc[j] >= 0 ? 1 : 0;
+  }
+  for (int w = tid; w < W; w += kScanThreads) used[w] = 0;
+  __syncthreads();
+  const int64_t o0 = gwalk_ptr[i], len = gwalk_ptr[i + 1] - o0;
+  auto in_member = [&](int j, int32_t pg) -> bool {
+    return (bits[(off + mc[j]) * W + (pg >> 6)] >> (pg & 63)) & 1ull;
+  };
+  int64_t pos = 0;
+  // phase 0: full pages every member selected, 1: the other shared pages (both in the
+  // first member's walk order), 2: a member's pages not yet in the walk
+  auto pass = [&](int j, int phase) {
+    const int q = mq[j];
+    const int64_t a = walk_ptr[int64_t(g) * (p.n_q + 1) + q];
+    const int n = unpadded[int64_t(g) * p.n_q + q];
+    for (int base = 0; base < n; base += kScanThreads) {
+      const int e = base + tid;
+      int32_t pg = -1;
+      bool f = false;
+      if (e < n) {
+        pg = walk[a + e];
+        if (phase < 2) {
+          bool all = true;
+          for (int jj = 1; jj < nm; ++jj) all = all && in_member(jj, pg);
+          const bool full = dev_page_mask(p, page_block, g, pg) == kFullMask;
+          f = all && (phase == 0 ? full : !full);
+        } else {
+          f = !((used[pg >> 6] >> (pg & 63)) & 1ull);
+        }
+      }
+      int64_t tot;
+      const int64_t x = block_scan(f ? 1 : 0, lds, &tot);
+      if (f && pos + x < len) {  // the union size bounds the walk (the guard only keeps stores in range)
+        gwalk[o0 + pos + x] = pg;
+        atomicOr(&used[pg >> 6], 1ull << (pg & 63));
+      }
+      pos += tot;
+      __syncthreads();
+    }
+  };
+  pass(0, 0);
+  const int64_t n_full = pos;
+  pass(0, 1);
+  for (int j = 0; j < nm; ++j) pass(j, 2);
+  for (int64_t e = pos + tid; e < len; e += kScanThreads) gwalk[o0 + e] = -1;
+  __syncthreads();  // the walk, written by this workgroup, is read back below
+  const int32_t first = gwalk[o0];
+  for (int64_t e = tid; e < len; e += kScanThreads) {
+    const int32_t pg = gwalk[o0 + e];
+    pages[walk_base + o0 + e] = pg >= 0 ? pg : first;
+  }
+  const int64_t half = len / 2;
+  for (int64_t e = tid; e < kGroupMembers * half; e += kScanThreads) {
+    const int w = int(e / half);
+    const int64_t j = e % half;
+    uint32_t word = 0;
+    if (mc[w] >= 0)
+      for (int h = 0; h < 2; ++h) {
+        const int32_t pg = gwalk[o0 + 2 * j + h];
+        if (pg >= 0 && in_member(w, pg)) word |= dev_page_mask(p, page_block, g, pg) << (16 * h);
+      }
+    valid[valid_base + 2 * o0 + e] = word;
+    gvalid[2 * o0 + e] = word;
+  }
+  if (tid < kGroupMembers) {
+    FwdGroup &gr = groups[i];
+    gr.q[tid] = mq[tid];
+    gr.c_q[tid] = mq[tid] >= 0 ? p.q_valid[int64_t(g) * p.n_q + mq[tid]] : 0;
+    members[i * kGroupMembers + tid] = mq[tid];
+    if (mq[tid] >= 0) in_group[int64_t(g) * p.n_q + mq[tid]] = 1;
+    if (tid == 0) {
+      gr.valid_off = valid_base + 2 * o0;
+      gr.pad = 0;
+      nfull[i] = int32_t(n_full);
+      npages[i] = int32_t(pos);
+    }
+  }
+}
+
+// group item k of head bh: M128 item hs128[bh + 1] + hsg[bh] + k (after the head's other
+// M128 items), list position that + hs64[bh]; one thread per group item
+__global__ void k_group_items(DevProblem p, const int64_t *group_ptr, const int64_t *gwalk_ptr,
+                              const int32_t *nfull, const int32_t *npages, int64_t walk_base, const int64_t *hs128,
+                              const int64_t *hs64, const int64_t *hsg, int64_t n_all, FwdItem *items128,
+                              int32_t *order) {
+  const int BH = p.batch * p.heads;
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= hsg[BH]) return;
+  const int bh = slot_of_index(hsg, BH, t);
+  const int g = p.per_head ? bh : 0;
+  const int64_t k = t - hsg[bh], gi = group_ptr[g] + k;
+  FwdItem x{};
+  x.walk_off = walk_base + gwalk_ptr[gi];
+  x.walk_len = int32_t(gwalk_ptr[gi + 1] - gwalk_ptr[gi]);
+  x.bh = bh;
+  x.q = ~int32_t(gi);
+  x.n_full = nfull[gi];
+  x.n_pages = npages[gi];
+  x.c_q = kBlockRows;
+  const int64_t idx = hs128[bh + 1] + hsg[bh] + k;
+  items128[idx] = x;
+  order[launch_position(idx + hs64[bh], n_all, p.xcd_chunk)] = int32_t(idx);
+}
+
 int blocks_for(int64_t n, int threads) { return int((n + threads - 1) / threads); }
 
 }  // namespace
 
-kpage_status build_forward_device(const DevProblem &p, int align64, int align128, hipStream_t st,
+kpage_status build_forward_device(const DevProblem &p, int align64, int align128, bool grouped, hipStream_t st,
                                   const DevAlloc &alloc, DevFwdTables *t, std::string *err) {
   const int64_t GQ = int64_t(p.slots) * p.n_q, GK = int64_t(p.slots) * p.n_kv;
   const int64_t BHQ = int64_t(p.batch) * p.heads * p.n_q;
@@ -454,13 +760,9 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
   t->valid = static_cast<uint32_t *>(alloc(size_t(std::max<int64_t>(h.walk_total / 2, 1)) * 4));
   t->q64_queue = a32(2 * int64_t(h.n_q64));
   t->q128_queue = a32(2 * int64_t(h.n_q128));
-  t->items128 = static_cast<FwdItem *>(alloc(size_t(std::max(h.n_q128, 1)) * sizeof(FwdItem)));
-  t->items64 = static_cast<FwdItem *>(alloc(size_t(std::max(h.n_q64 + h.n_zero, 1)) * sizeof(FwdItem)));
-  t->order = a32(int64_t(h.n_q128) + h.n_q64 + h.n_zero);
   int64_t *head_starts = static_cast<int64_t *>(alloc(size_t(2) * (size_t(p.batch) * p.heads + 1) * 8));
   unsigned long long *keys = static_cast<unsigned long long *>(alloc(size_t(std::max<int64_t>(BHQ, 1)) * 8 * 3));
-  if (!t->walk || !t->pages || !t->valid || !t->q64_queue || !t->q128_queue || !t->items128 || !t->items64 ||
-      !t->order || !head_starts || !keys) {
+  if (!t->walk || !t->pages || !t->valid || !t->q64_queue || !t->q128_queue || !head_starts || !keys) {
     *err = "device allocation failed while planning";
     return KPAGE_ERR_OOM;
   }
@@ -486,10 +788,129 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
     hipLaunchKernelGGL(k_queue_out, dim3(blocks_for(h.n_q128, TB)), dim3(TB), 0, st, ksorted, h.n_q128, p.n_q,
                        t->q128_queue);
   }
+  // group items (the host planner's build_groups)
+  const int BH = p.batch * p.heads;
+  const int64_t W = (n_pages + 63) / 64;
+  uint8_t *in_group = nullptr;
+  int64_t *d_hsg = nullptr, *d_gptr = nullptr, *d_gwptr = nullptr;
+  t->g_group_ptr.assign(size_t(p.slots) + 1, 0);
+  t->g_walk_ptr.assign(1, 0);
+  if (grouped && W <= kGroupMaxWords) {
+    int32_t *cand = a32(GQ), *n_cand = a32(p.slots);
+    if (!cand || !n_cand) {
+      *err = "device allocation failed while planning";
+      return KPAGE_ERR_OOM;
+    }
+    hipLaunchKernelGGL(k_group_cands, dim3(p.slots), dim3(kScanThreads), 0, st, p, t->route, t->unpadded, cand,
+                       n_cand);
+    std::vector<int32_t> hc(static_cast<size_t>(p.slots));
+    KP_CHECK(hipMemcpyAsync(hc.data(), n_cand, hc.size() * 4, hipMemcpyDeviceToHost, st));
+    KP_CHECK(hipStreamSynchronize(st));
+    // slots with fewer than 2 or more than kGroupMaxCands candidates form no group
+    std::vector<int64_t> coff(size_t(p.slots) + 1, 0);
+    int max_nc = 0;
+    for (int g = 0; g < p.slots; ++g) {
+      if (hc[size_t(g)] < 2 || hc[size_t(g)] > kGroupMaxCands) hc[size_t(g)] = 0;
+      coff[size_t(g) + 1] = coff[size_t(g)] + hc[size_t(g)];
+      max_nc = std::max(max_nc, hc[size_t(g)]);
+    }
+    const int64_t n_cand_all = coff[size_t(p.slots)];
+    if (n_cand_all > 0) {
+      int64_t *d_coff = a64(p.slots + 1);
+      int32_t *d_nc = a32(p.slots);
+      unsigned long long *bits = static_cast<unsigned long long *>(alloc(size_t(n_cand_all * W) * 8));
+      int32_t *gmem = a32(n_cand_all * kGroupMembers), *gunion = a32(n_cand_all);
+      int32_t *gcount = a32(p.slots), *gmembers = a32(p.slots);
+      if (!d_coff || !d_nc || !bits || !gmem || !gunion || !gcount || !gmembers) {
+        *err = "device allocation failed while planning";
+        return KPAGE_ERR_OOM;
+      }
+      KP_CHECK(hipMemcpyAsync(d_coff, coff.data(), coff.size() * 8, hipMemcpyHostToDevice, st));
+      KP_CHECK(hipMemcpyAsync(d_nc, hc.data(), hc.size() * 4, hipMemcpyHostToDevice, st));
+      KP_CHECK(hipMemsetAsync(bits, 0, size_t(n_cand_all * W) * 8, st));
+      hipLaunchKernelGGL(k_group_bits, dim3(unsigned(n_cand_all)), dim3(256), 0, st, p, t->walk_ptr, t->walk,
+                         t->unpadded, cand, d_coff, int(W), bits);
+      const size_t lds = size_t(2 * W) * 8 + size_t((max_nc + 7) / 8) * 8;
+      hipLaunchKernelGGL(k_group_greedy, dim3(p.slots), dim3(kGroupThreads), lds, st, p, t->unpadded, cand, d_nc,
+                         d_coff, int(W), bits, gmem, gunion, gcount, gmembers);
+      KP_CHECK(hipGetLastError());
+      std::vector<int32_t> hgc(static_cast<size_t>(p.slots)), hgm(static_cast<size_t>(p.slots)),
+          hgu(static_cast<size_t>(n_cand_all));
+      KP_CHECK(hipMemcpyAsync(hgc.data(), gcount, hgc.size() * 4, hipMemcpyDeviceToHost, st));
+      KP_CHECK(hipMemcpyAsync(hgm.data(), gmembers, hgm.size() * 4, hipMemcpyDeviceToHost, st));
+      KP_CHECK(hipMemcpyAsync(hgu.data(), gunion, hgu.size() * 4, hipMemcpyDeviceToHost, st));
+      KP_CHECK(hipStreamSynchronize(st));
+      int64_t n_mem_slot = 0;
+      for (int g = 0; g < p.slots; ++g) {
+        t->g_group_ptr[size_t(g) + 1] = t->g_group_ptr[size_t(g)] + hgc[size_t(g)];
+        for (int k = 0; k < hgc[size_t(g)]; ++k)
+          t->g_walk_ptr.push_back(t->g_walk_ptr.back() + (int64_t(hgu[size_t(coff[size_t(g)] + k)]) + 3) / 4 * 4);
+      }
+      t->n_groups = t->g_group_ptr[size_t(p.slots)];
+      if (t->n_groups > 0) {
+        const int64_t gw_total = t->g_walk_ptr.back();
+        std::vector<int64_t> hsg(size_t(BH) + 1, 0);
+        for (int bh = 0; bh < BH; ++bh) {
+          const int g = p.per_head ? bh : 0;
+          hsg[size_t(bh) + 1] = hsg[size_t(bh)] + (t->g_group_ptr[size_t(g) + 1] - t->g_group_ptr[size_t(g)]);
+          n_mem_slot += hgm[size_t(g)];
+        }
+        t->n_gitems = hsg[size_t(BH)];
+        t->n_members = n_mem_slot;
+        d_gptr = a64(p.slots + 1);
+        d_gwptr = a64(t->n_groups + 1);
+        d_hsg = a64(BH + 1);
+        t->groups = static_cast<FwdGroup *>(alloc(size_t(t->n_groups) * sizeof(FwdGroup)));
+        t->g_members = a32(t->n_groups * kGroupMembers);
+        t->g_nfull = a32(t->n_groups);
+        t->g_npages = a32(t->n_groups);
+        t->g_walk = a32(gw_total);
+        t->g_valid = static_cast<uint32_t *>(alloc(size_t(2 * gw_total) * 4));
+        in_group = static_cast<uint8_t *>(alloc(size_t(GQ)));
+        // the union walks and their words follow the plan's walks and words
+        int32_t *pages2 = a32(h.walk_total + gw_total);
+        uint32_t *valid2 = static_cast<uint32_t *>(alloc(size_t(h.walk_total / 2 + 2 * gw_total) * 4));
+        if (!d_gptr || !d_gwptr || !d_hsg || !t->groups || !t->g_members || !t->g_nfull || !t->g_npages ||
+            !t->g_walk || !t->g_valid || !in_group || !pages2 || !valid2) {
+          *err = "device allocation failed while planning";
+          return KPAGE_ERR_OOM;
+        }
+        KP_CHECK(hipMemcpyAsync(d_gptr, t->g_group_ptr.data(), t->g_group_ptr.size() * 8, hipMemcpyHostToDevice, st));
+        KP_CHECK(hipMemcpyAsync(d_gwptr, t->g_walk_ptr.data(), t->g_walk_ptr.size() * 8, hipMemcpyHostToDevice, st));
+        KP_CHECK(hipMemcpyAsync(d_hsg, hsg.data(), hsg.size() * 8, hipMemcpyHostToDevice, st));
+        KP_CHECK(hipMemsetAsync(in_group, 0, size_t(GQ), st));
+        if (h.walk_total > 0) {
+          KP_CHECK(hipMemcpyAsync(pages2, t->pages, size_t(h.walk_total) * 4, hipMemcpyDeviceToDevice, st));
+          KP_CHECK(hipMemcpyAsync(valid2, t->valid, size_t(h.walk_total / 2) * 4, hipMemcpyDeviceToDevice, st));
+        }
+        t->pages = pages2;
+        t->valid = valid2;
+        hipLaunchKernelGGL(k_group_walks, dim3(unsigned(t->n_groups)), dim3(kScanThreads), size_t(W) * 8, st, p,
+                           t->page_block, t->walk_ptr, t->walk, t->unpadded, cand, d_coff, int(W), bits, gmem, d_gptr,
+                           d_gwptr, h.walk_total, h.walk_total / 2, t->groups, t->g_members, t->g_nfull,
+                           t->g_npages, t->g_walk, t->pages, t->valid, t->g_valid, in_group);
+        KP_CHECK(hipGetLastError());
+      }
+    }
+  }
+  const int64_t n_items128 = int64_t(h.n_q128) + t->n_gitems;
+  const int64_t n_items64 = int64_t(h.n_q64) - t->n_members + h.n_zero;
+  const int64_t n_all = n_items128 + n_items64;
+  t->items128 = static_cast<FwdItem *>(alloc(size_t(std::max<int64_t>(n_items128, 1)) * sizeof(FwdItem)));
+  t->items64 = static_cast<FwdItem *>(alloc(size_t(std::max<int64_t>(n_items64, 1)) * sizeof(FwdItem)));
+  t->order = a32(n_all);
+  if (!t->items128 || !t->items64 || !t->order) {
+    *err = "device allocation failed while planning";
+    return KPAGE_ERR_OOM;
+  }
+  int64_t *hs128 = head_starts, *hs64 = head_starts + (int64_t(BH) + 1);
   hipLaunchKernelGGL(k_items, dim3(1), dim3(kScanThreads), 0, st, p, t->route, t->nfull, t->unpadded, t->walk_ptr, d_sum,
-                     t->items128, t->items64, head_starts, head_starts + (int64_t(p.batch) * p.heads + 1), t->order);
-  hipLaunchKernelGGL(k_fwd_tails, dim3(kXcds), dim3(kFwdTail), 0, st, t->order, t->items128, t->items64,
-                     int64_t(h.n_q128) + h.n_q64 + h.n_zero);
+                     in_group, d_hsg, t->n_members, t->items128, t->items64, hs128, hs64, t->order);
+  if (t->n_gitems > 0)
+    hipLaunchKernelGGL(k_group_items, dim3(blocks_for(t->n_gitems, TB)), dim3(TB), 0, st, p, d_gptr,
+                       d_gwptr, t->g_nfull, t->g_npages, h.walk_total, hs128, hs64, d_hsg, n_all,
+                       t->items128, t->order);
+  hipLaunchKernelGGL(k_fwd_tails, dim3(kXcds), dim3(kFwdTail), 0, st, t->order, t->items128, t->items64, n_all);
   KP_CHECK(hipGetLastError());
   KP_CHECK(hipMemcpyAsync(&h, d_sum, sizeof(Summary), hipMemcpyDeviceToHost, st));
   KP_CHECK(hipStreamSynchronize(st));

@@ -42,6 +42,16 @@ struct DevFwdTables {
   int64_t walk_total = 0;
   int n_q64 = 0, n_q128 = 0, n_zero = 0;  // queue entries, empty query blocks
   PairStats stats;
+  // Group items (plan.hpp, GroupTables), the same groups as the host planner's.  The
+  // union walks follow the plan's walks in `pages` and their validity words follow the
+  // plan's words in `valid`; g_walk / g_valid hold the exported copies.
+  FwdGroup *groups = nullptr;                       // [n_groups], shared by a slot's (b, h)s
+  int32_t *g_members = nullptr;                     // [n_groups][4] query blocks, -1 none
+  int32_t *g_nfull = nullptr, *g_npages = nullptr;  // [n_groups]
+  int32_t *g_walk = nullptr;                        // union walks, -1 dummies
+  uint32_t *g_valid = nullptr;                      // member validity words
+  std::vector<int64_t> g_group_ptr, g_walk_ptr;     // host copies: [slots + 1], [n_groups + 1]
+  int64_t n_groups = 0, n_gitems = 0, n_members = 0;  // groups, group items over (b, h), member items
 };
 
 // Device backward tables (section 3.3), same contents and order as BwdTables.
@@ -72,8 +82,9 @@ using DevAlloc = std::function<void *(size_t)>;
 
 // Builds the forward tables on `stream`.  Validates the descriptor on the device first
 // (KPAGE_ERR_INVALID with `err` set on a malformed one).  Synchronises `stream` twice:
-// once for the table sizes, once at the end for the queue lengths and pair counts.
-kpage_status build_forward_device(const DevProblem &p, int align64, int align128, hipStream_t stream,
+// once for the table sizes, once at the end for the queue lengths and pair counts; with
+// `grouped`, twice more for the group items (candidate counts, then group sizes).
+kpage_status build_forward_device(const DevProblem &p, int align64, int align128, bool grouped, hipStream_t stream,
                                   const DevAlloc &alloc, DevFwdTables *t, std::string *err);
 
 // Builds the backward tables on `stream` from a descriptor already validated by

@@ -88,7 +88,10 @@ typedef struct {
  * paper's tables (section 3.2.2 routes such blocks to M64 x N256 one at a time):
  * the exported tables, queues and pair counts do not change, and each row's result
  * is the same attention up to fp32 summation order.  ungrouped = 1 runs every
- * block as its own item.  kpage_plan_device() never groups.
+ * block as its own item.  kpage_plan_device() builds the same groups as kpage_plan()
+ * (with ungrouped = 1, none).  Grouping applies where the page bitsets fit the GPU
+ * planner's LDS: seq_kv up to 2^21 rows and at most 16384 candidate blocks per graph
+ * slot (both planners use these limits).
  */
 typedef struct {
   int32_t q_group;

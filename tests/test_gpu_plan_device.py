@@ -23,7 +23,8 @@ from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
 
-FWD_TABLES = ("fwd_route", "fwd_walk_ptr", "fwd_walk", "fwd_nfull", "fwd_valid", "q64_queue", "q128_queue")
+FWD_TABLES = ("fwd_route", "fwd_walk_ptr", "fwd_walk", "fwd_nfull", "fwd_valid", "q64_queue", "q128_queue",
+              "group_ptr", "group_members", "group_walk_ptr", "group_walk", "group_nfull", "group_valid")
 BWD_TABLES = ("owner_ptr", "owners", "owner_aligned", "revq_ptr", "revq", "qwalk_ptr", "qwalk", "adj", "bwd_queue",
               "uncovered_ptr", "uncovered")
 FWD_STATS = ("useful", "whole_block", "paged_m128", "nominal", "scheduled")
@@ -36,8 +37,7 @@ def _say(msg):
 
 
 def same_plans(p, label, bwd=True, **opts):
-    # the GPU planner builds no group items; the host plan's launch runs ungrouped too
-    h = K.kpage_plan(p, grouped=False, **opts)
+    h = K.kpage_plan(p, **opts)
     d = K.kpage_plan_device(p, **opts)
     for t in FWD_TABLES:
         a, b = K.kpage_plan_export(h, t), K.kpage_plan_export(d, t)
@@ -111,13 +111,31 @@ def test_device_plan_attention_is_bitwise_equal():
     assert sh["bwd_physical"] == sd["bwd_physical"] and sh["bwd_useful_check"] == sd["bwd_useful_check"]
 
 
+@pytest.mark.parametrize("cfg,heads", [(3, [0, 1]), (4, [0, 1])])
+def test_device_plan_groups_equal_host_groups(cfg, heads):
+    """Group items built on the GPU: the same groups, union walks and member words as the
+    host planner's, and none when both are planned ungrouped."""
+    w = make_workload(cfg, heads=heads)
+    h, d = K.kpage_plan(w), K.kpage_plan_device(w)
+    assert K.kpage_plan_export(h, "group_members").size > 0
+    for t in FWD_TABLES:
+        a, b = K.kpage_plan_export(h, t), K.kpage_plan_export(d, t)
+        assert a.dtype == b.dtype and np.array_equal(a, b), (cfg, t)
+    h0, d0 = K.kpage_plan(w, grouped=False), K.kpage_plan_device(w, grouped=False)
+    for x in (h0, d0):
+        assert K.kpage_plan_export(x, "group_members").size == 0
+        gp = K.kpage_plan_export(x, "group_ptr")
+        assert gp.size == (len(heads) if w.per_head else 1) + 1 and not gp.any()
+    _say(f"  workload {cfg}: {K.kpage_plan_export(d, 'group_members').size // 4} groups equal")
+
+
 def test_device_plan_full_size_attention_is_bitwise_equal():
     """All 40 heads of the 21x30x52 workload (10,320 backward items, so every XCD's
     longest-first tail holds 64 owners): outputs of the GPU-built plan equal the host
     plan's bit for bit."""
     w = make_workload(3, with_do=True)
     _say(f"[device plan] full-size 21x30x52, {w.heads} heads")
-    h, d = K.kpage_plan(w, grouped=False), K.kpage_plan_device(w)
+    h, d = K.kpage_plan(w), K.kpage_plan_device(w)
     dev = torch.device("cuda", 0)
     q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))
     outs = []
@@ -169,7 +187,7 @@ def test_device_plan_q_groups_attention_is_bitwise_equal(name, q_group):
     entries as the host plan, so the gradients are bitwise equal."""
     w = make_workload(3 if "21x30x52" in name else 4, heads=[0, 1], with_do=True)
     _say(f"[device plan] {name}, q_group {q_group}")
-    h, d = K.kpage_plan(w, q_group=q_group, grouped=False), K.kpage_plan_device(w, q_group=q_group)
+    h, d = K.kpage_plan(w, q_group=q_group), K.kpage_plan_device(w, q_group=q_group)
     assert K.kpage_bwd_workspace_size(h) == K.kpage_bwd_workspace_size(d)
     dev = torch.device("cuda", 0)
     q, k, v, do = (x.to(dev) for x in (w.q, w.k, w.v, w.do))

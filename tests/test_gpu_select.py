@@ -99,7 +99,7 @@ def test_select_then_plan_then_attention():
             idx.extend(rows[h][qb])
             ptr[h, qb + 1] = len(idx)
     w.q2k_ptr, w.q2k_idx = ptr, np.asarray(idx, dtype=np.int32)
-    plan_host = K.kpage_plan(w, grouped=False)  # the GPU planner builds no group items
+    plan_host = K.kpage_plan(w)
     o1, l1 = K.attn_fwd(plan_dev, q, k, v, w.scale)
     o2, l2 = K.attn_fwd(plan_host, q, k, v, w.scale)
     torch.cuda.synchronize()
