@@ -82,7 +82,7 @@ struct kpage_plan {
   Problem P;
   FwdTables F;
   BwdTables B;
-  GroupTables GT;  // group items (host plans only)
+  GroupTables GT;  // group items (device-planned plans: host copies for export)
   PairStats S;
   bool fwd_on_device = false;
   // built by kpage_plan_device: the descriptor and every table live on the device

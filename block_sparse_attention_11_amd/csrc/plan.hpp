@@ -48,7 +48,7 @@ struct FwdTables {
 // Group items (launch-level, not part of the paper's tables): per graph slot, query
 // blocks of the M64 x N256 route with at most 32 valid rows whose walks overlap are run
 // four at a time as one M128 x N128 item over the union of their walks, one member per
-// wave.  Built on the host only.
+// wave.  The GPU planner builds the same tables (plan_dev.hip).
 constexpr int kGroupMembers = 4;
 constexpr int kGroupMaxRows = 32;
 // Grouping runs where its working sets fit the GPU planner's LDS (both planners apply
