@@ -502,11 +502,17 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_greedy(DevProblem p, co
       for (int c = c0 + 1 + tid; c < nc; c += kGroupThreads) {
         if (taken[c]) continue;
         const unsigned long long *bb = B + int64_t(c) * W;
-        bool shares = false;  // a page selected by every member and by c
-        for (int w = 0; w < W && !shares; ++w) shares = (inter[w] & bb[w]) != 0;
-        if (!shares) continue;
+        // one pass over the words (independent loads): pages shared with every member, and
+        // pages already in the union
+        unsigned long long sh = 0;
         int64_t in = 0;
-        for (int w = 0; w < W; ++w) in += __popcll(uni[w] & bb[w]);
+#pragma unroll 8
+        for (int w = 0; w < W; ++w) {
+          const unsigned long long x = bb[w];
+          sh |= inter[w] & x;
+          in += __popcll(uni[w] & x);
+        }
+        if (sh == 0) continue;  // no page selected by every member and by c
         const int64_t n = unpadded[int64_t(g) * p.n_q + cand[int64_t(g) * p.n_q + c]];
         if (bc < 0 || in * bn > bi * n) {
           bi = in;
