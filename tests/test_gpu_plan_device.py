@@ -290,3 +290,14 @@ def test_device_plan_random_layouts():
                     q2k_ptr=ptr, q2k_idx=np.asarray(idx, dtype=np.int32))
         align = [(0, 0), (32, 16)][trial % 2]
         same_plans(p, f"random layout {trial}", align_q64=align[0], align_q128=align[1])
+
+
+@pytest.mark.parametrize("rows_past", [0, 16])
+def test_device_plan_grouping_limit_equals_host(rows_past):
+    """At and one page past the page-bitset limit of the grouping (2^21 K/V rows), the GPU
+    planner groups exactly as the host planner does (a group, then none)."""
+    seq_kv = 2048 * 64 * 16 + rows_past
+    p = make_problem([20, 32, 8], [128, 128, 128], [[0, 1], [0, 1], [0, 2]], heads=1, head_dim=64,
+                     kv_offset=[0, 128, seq_kv - 128], seq_kv=seq_kv)
+    h, d = same_plans(p, f"seq_kv {seq_kv}", bwd=False)
+    assert K.kpage_plan_export(d, "group_members").size == (4 if rows_past == 0 else 0)

@@ -188,3 +188,21 @@ def test_random_layouts_follow_the_rule():
             rows.append(sorted(set(base[:int(rng.integers(1, len(base) + 1))] + extra)))
         p = make_problem(cq, ck, rows, heads=2, head_dim=64)
         check_groups(p)
+
+
+@pytest.mark.parametrize("rows_past,grouped", [(0, True), (16, False)])
+def test_grouping_stops_past_the_page_bitset_limit(rows_past, grouped):
+    """Both planners group only while a page bitset fits 2048 words (seq_kv up to 2^21
+    rows); one page more and every block runs alone."""
+    limit = 2048 * 64 * 16
+    seq_kv = limit + rows_past
+    # K blocks 0 and 1 at the start, block 2 ending at seq_kv
+    p = make_problem([20, 32, 8], [128, 128, 128], [[0, 1], [0, 1], [0, 2]], heads=1, head_dim=64,
+                     kv_offset=[0, 128, seq_kv - 128], seq_kv=seq_kv)
+    plan = K.kpage_plan(p)
+    members = K.kpage_plan_export(plan, "group_members")
+    if grouped:
+        assert members.tolist() == [0, 1, 2, -1]
+        check_groups(p, plan)
+    else:
+        assert members.size == 0
