@@ -5,9 +5,10 @@ their page walks, one member per wave, each wave masking the pages its own block
 not select; it writes every member block's 128 output rows.  Checked here: forward O and
 LSE and the gradients on layouts built to form groups of two, three and four members
 (tails, 1- and 8-row blocks, empty blocks next to members), groups whose items take the
-exact re-run, and every member block of the top-87 workload; the same problems planned
-without groups agree with the oracle too.  Tolerances as in the forward and backward
-parity tests.
+exact re-run, every member block of the top-87 workload, and batch 2 with a shared graph
+and with one graph per (batch, head) (there also the GPU planner's groups against the
+host's); the same problems planned without groups agree with the oracle too.  Tolerances
+as in the forward and backward parity tests.
 """
 import sys
 
@@ -17,9 +18,10 @@ import torch
 
 import block_sparse_attention_11_amd as K
 from oracle import oracle_bwd, oracle_fwd
-from tests.problems import make_problem, random_tensors
+from tests.problems import Problem, make_problem, random_tensors
 from tests.test_gpu_bwd import check_grads, gpu_fwd_bwd
 from tests.test_gpu_fwd import abs_values_attention, check, gpu_fwd
+from tests.test_gpu_plan_device import same_plans
 from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +37,7 @@ def group_sizes(plan):
     return sorted(int(x) for x in (m >= 0).sum(axis=1))
 
 
-def small_blocks_problem(d):
+def small_blocks_problem(d, batch=1):
     """14 query blocks: 11 of at most 32 rows (1, 8, 16, 17, 20, 31 and 32 rows), one empty,
     two large.  K blocks 0-5 full or with tails; the small blocks select overlapping
     subsets of K blocks 0-4 (so they form groups of 2-4), two select disjoint ones."""
@@ -43,7 +45,7 @@ def small_blocks_problem(d):
     ck = [128, 128, 70, 128, 9, 128, 33]
     rows = [[0, 1, 2, 3], [0, 1, 2], [0, 1, 2, 4], [0, 1], [1, 2, 0], [0], [3, 4, 2], [3, 4], [2, 3, 4, 1],
             [4, 3], [5, 6], [0, 5, 6], [6, 5], [1, 0, 2, 6]]
-    return make_problem(cq, ck, rows, heads=3, head_dim=d, sort_rows=False)
+    return make_problem(cq, ck, rows, heads=3, batch=batch, head_dim=d, sort_rows=False)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -114,3 +116,45 @@ def test_topk_workload_every_member_block():
     got = gpu_fwd_bwd(w, w.q, w.k, w.v, w.do, plan=plan)
     ref = oracle_bwd(w, w.q, w.k, w.v, w.do, heads=[1])[:3]
     check_grads(got, ref, "top-87 groups head 1", w, heads=[1])
+
+
+def per_slot_small_blocks(batch, heads, d, seed):
+    """One graph per (batch, head): mostly blocks of at most 32 rows whose selections share a
+    random base set of K blocks, so that every slot forms its own groups."""
+    rng = np.random.default_rng(seed)
+    G, n_q, n_kv = batch * heads, 9, 7
+    qv = rng.choice([20, 32, 8, 1, 31, 16, 128, 64, 0], size=(G, n_q)).astype(np.int32)
+    kv = rng.choice([128, 128, 77, 64, 16, 3], size=(G, n_kv)).astype(np.int32)
+    off = np.tile(np.arange(n_kv, dtype=np.int64) * 128, (G, 1))
+    ptr = np.zeros((G, n_q + 1), dtype=np.int64)
+    idx = []
+    for g in range(G):
+        base = rng.permutation(n_kv)[:3].tolist()
+        ptr[g, 0] = len(idx)
+        for q in range(n_q):
+            extra = rng.permutation(n_kv)[:int(rng.integers(0, 3))].tolist()
+            idx.extend(rng.permutation(sorted(set(base + extra))).tolist())
+            ptr[g, q + 1] = len(idx)
+    return Problem(batch=batch, heads=heads, head_dim=d, n_q=n_q, n_kv=n_kv, seq_q=128 * n_q,
+                   seq_kv=128 * n_kv, per_head=True, q_valid=qv, kv_valid=kv, kv_offset=off,
+                   q2k_ptr=ptr, q2k_idx=np.asarray(idx, dtype=np.int32))
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+def test_groups_batch2(per_head):
+    """Batch 2 x 3 heads: group items of a graph shared by every (batch, head), and of one graph
+    per (batch, head); forward and backward against the oracle, and the GPU planner's groups
+    equal the host's."""
+    p = per_slot_small_blocks(2, 3, 128, seed=77) if per_head else small_blocks_problem(128, batch=2)
+    t = random_tensors(p, seed=78)
+    plan = K.kpage_plan(p)
+    sizes = group_sizes(plan)
+    _say(f"[groups] batch 2, per_head={per_head}: group sizes {sizes}")
+    assert len(sizes) >= 3
+    O, L = gpu_fwd(p, t["q"], t["k"], t["v"], plan=plan)
+    Oref, Lref = oracle_fwd(p, t["q"], t["k"], t["v"])
+    check(O, L, Oref, Lref, f"groups batch 2 per_head={per_head}", Aabs=abs_values_attention(p, t["q"], t["k"], t["v"]))
+    got = gpu_fwd_bwd(p, t["q"], t["k"], t["v"], t["do"], plan=plan)
+    ref = oracle_bwd(p, t["q"], t["k"], t["v"], t["do"])[:3]
+    check_grads(got, ref, f"groups batch 2 per_head={per_head}", p)
+    same_plans(p, f"groups batch 2 per_head={per_head}", bwd=False)
