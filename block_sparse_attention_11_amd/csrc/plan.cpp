@@ -240,16 +240,27 @@ void build_groups(const Problem &P, const FwdTables &F, GroupTables *T) {
   const size_t W = size_t((n_pg + 63) / 64);
   std::vector<uint64_t> bits, uni(W), inter(W);
   std::vector<uint32_t> pmask(size_t(n_pg), 0);
-  for (int g = 0; g < G; ++g) {
-    T->group_ptr[size_t(g) + 1] = T->group_ptr[size_t(g)];
-    if (!P.grouped || W > size_t(kGroupMaxWords)) continue;
-    std::vector<int> cand;  // eligible blocks, ascending
+  auto candidates = [&](int g) {  // eligible blocks of slot g, ascending; none past the limits
+    std::vector<int> cand;
     for (int q = 0; q < nq; ++q) {
       const int cq = P.q_valid[size_t(g) * nq + q];
       if (F.route[size_t(g) * nq + q] == 64 && cq > 0 && cq <= kGroupMaxRows && F.unpadded[size_t(g) * nq + q] > 0)
         cand.push_back(q);
     }
-    if (cand.size() < 2 || cand.size() > size_t(kGroupMaxCands)) continue;
+    if (cand.size() < 2 || cand.size() > size_t(kGroupMaxCands)) cand.clear();
+    return cand;
+  };
+  bool grouped = P.grouped && W <= size_t(kGroupMaxWords);
+  if (grouped) {
+    int64_t words = 0;
+    for (int g = 0; g < G; ++g) words += int64_t(candidates(g).size()) * int64_t(W);
+    grouped = words <= kGroupMaxBitsetWords;
+  }
+  for (int g = 0; g < G; ++g) {
+    T->group_ptr[size_t(g) + 1] = T->group_ptr[size_t(g)];
+    if (!grouped) continue;
+    const std::vector<int> cand = candidates(g);
+    if (cand.empty()) continue;
     // page sets as bitsets, and every page's row mask
     bits.assign(cand.size() * W, 0);
     std::vector<int> n_of(cand.size(), 0);

@@ -56,6 +56,9 @@ constexpr int kGroupMaxRows = 32;
 // most 16384 candidate blocks per graph slot.
 constexpr int kGroupMaxWords = 2048;
 constexpr int kGroupMaxCands = 16384;
+// and the page bitsets of all slots' candidates together at most 2^25 words (256 MiB of
+// device memory while the GPU planner groups); beyond that no slot groups
+constexpr int64_t kGroupMaxBitsetWords = int64_t(1) << 25;
 struct GroupTables {
   std::vector<int64_t> group_ptr;   // [slots + 1] offsets into the group list
   std::vector<int32_t> members;     // [n_groups][4] query blocks, -1 = none (at least 2 members)

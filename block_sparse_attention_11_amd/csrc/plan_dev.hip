@@ -821,7 +821,8 @@ kpage_status build_forward_device(const DevProblem &p, int align64, int align128
       max_nc = std::max(max_nc, hc[size_t(g)]);
     }
     const int64_t n_cand_all = coff[size_t(p.slots)];
-    if (n_cand_all > 0) {
+    // no slot groups when all the page bitsets together pass the limit (as on the host)
+    if (n_cand_all > 0 && n_cand_all * W <= kGroupMaxBitsetWords) {
       int64_t *d_coff = a64(p.slots + 1);
       int32_t *d_nc = a32(p.slots);
       unsigned long long *bits = static_cast<unsigned long long *>(alloc(size_t(n_cand_all * W) * 8));

@@ -90,8 +90,9 @@ typedef struct {
  * is the same attention up to fp32 summation order.  ungrouped = 1 runs every
  * block as its own item.  kpage_plan_device() builds the same groups as kpage_plan()
  * (with ungrouped = 1, none).  Grouping applies where the page bitsets fit the GPU
- * planner's LDS: seq_kv up to 2^21 rows and at most 16384 candidate blocks per graph
- * slot (both planners use these limits).
+ * planner: seq_kv up to 2^21 rows, at most 16384 candidate blocks per graph slot, and
+ * all slots' candidate bitsets together at most 2^25 64-bit words (both planners use
+ * these limits).
  */
 typedef struct {
   int32_t q_group;

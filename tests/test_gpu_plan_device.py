@@ -301,3 +301,11 @@ def test_device_plan_grouping_limit_equals_host(rows_past):
                      kv_offset=[0, 128, seq_kv - 128], seq_kv=seq_kv)
     h, d = same_plans(p, f"seq_kv {seq_kv}", bwd=False)
     assert K.kpage_plan_export(d, "group_members").size == (4 if rows_past == 0 else 0)
+
+
+def test_device_plan_total_bitset_limit_equals_host():
+    """Past the limit on all slots' page bitsets together the GPU planner, like the host
+    planner, builds no group items."""
+    from tests.test_groups import many_small_blocks_problem
+    h, d = same_plans(many_small_blocks_problem(8193), "2 x 8193 small blocks over 2^21 K/V rows", bwd=False)
+    assert K.kpage_plan_export(d, "group_members").size == 0

@@ -206,3 +206,27 @@ def test_grouping_stops_past_the_page_bitset_limit(rows_past, grouped):
         check_groups(p, plan)
     else:
         assert members.size == 0
+
+
+def many_small_blocks_problem(per_slot):
+    """Two graph slots of `per_slot` 8-row query blocks that all select K block 0, over a
+    K/V sequence of 2^21 rows (page bitsets of 2048 words each)."""
+    from tests.problems import Problem
+    seq_kv = 2048 * 64 * 16
+    G, n_kv = 2, 2
+    qv = np.full((G, per_slot), 8, dtype=np.int32)
+    kv = np.full((G, n_kv), 128, dtype=np.int32)
+    off = np.tile(np.array([0, seq_kv - 128], dtype=np.int64), (G, 1))
+    ptr = np.tile(np.arange(per_slot + 1, dtype=np.int64), (G, 1))
+    ptr[1] += per_slot
+    idx = np.zeros(G * per_slot, dtype=np.int32)
+    return Problem(batch=1, heads=G, head_dim=64, n_q=per_slot, n_kv=n_kv, seq_q=128 * per_slot, seq_kv=seq_kv,
+                   per_head=True, q_valid=qv, kv_valid=kv, kv_offset=off, q2k_ptr=ptr, q2k_idx=idx)
+
+
+def test_grouping_stops_past_the_total_bitset_limit():
+    """2 x 8193 candidates of 2048-word bitsets pass the 2^25-word limit of all slots'
+    bitsets together: no slot groups."""
+    plan = K.kpage_plan(many_small_blocks_problem(8193))
+    assert K.kpage_plan_export(plan, "group_members").size == 0
+    assert K.kpage_plan_export(plan, "group_ptr").tolist() == [0, 0, 0]
