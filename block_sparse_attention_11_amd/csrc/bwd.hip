@@ -706,10 +706,9 @@ __global__ __launch_bounds__(256) void kpage_bwd_kv_reduce(BwdArgs a) {
   }
 }
 
-// dQ over both routes in one launch: workgroups [0, n128) take the M128 items, the rest
-// the M64 items (and cleanup items), so the shorter M64 items fill the end of the M128
-// work.  K half-tiles 0/1 and V half-tiles 0/1 in LDS; at the end the per-wave dQ
-// partials.
+// dQ over both routes in one launch, in the forward's launch order (order table: M128
+// item i >= 0, else M64 or cleanup item ~i).  K half-tiles 0/1 and V half-tiles 0/1 in
+// LDS; at the end the per-wave dQ partials.
 template <int D>
 __global__ __launch_bounds__(64 * kDqWaves, 2) void kpage_bwd_dq(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * 64 * D * 2];

@@ -6,9 +6,11 @@
 // a contiguous 16-row run of the original K/V tensors and is copied straight from
 // global memory into LDS with 16-byte direct-to-LDS loads (section 3.2.3); no
 // compacted copy exists in HBM.  The consumer is a flash-attention step on the
-// assembled tile: bf16 MFMA for Q K^T and P V with fp32 accumulation, and an
-// online softmax (section 3.2.4: invalid rows are set to -inf before the row
-// maximum, and only on tiles at or past the end of the fully valid prefix).
+// assembled tile: bf16 MFMA for Q K^T and P V with fp32 accumulation, and a softmax
+// over the walk (section 3.2.4: invalid rows are set to -inf before the row maximum,
+// and only on tiles at or past the end of the fully valid prefix) whose maximum is
+// fixed by the first sub-tile, with an exact re-run for the rare item that needs a
+// running maximum (below).
 //
 // Work split.  A workgroup has 4 waves and two workgroups share a CU, so every
 // SIMD runs two waves of different items that drift apart: one wave's vector
@@ -18,8 +20,10 @@
 // 4 query groups, every wave takes all 64 keys of a tile (2 sub-tiles).  Route
 // M64 x N256: 2 query groups x 2 key halves, 1 sub-tile per wave per tile.  Each
 // wave keeps its own running maximum, sum and output; waves that share query
-// rows are merged once at the end.  One launch covers both routes: the first
-// workgroups take the M128 items, the rest the M64 items.
+// rows are merged once at the end.  A group item (up to four query blocks of at most
+// 32 rows over the union of their walks) runs on the M128 route with one member per
+// wave.  One launch covers both routes, in the launch order of the plan's order table
+// (per head its M128 items, then its M64 items).
 //
 // Matrix layout per wave (v_mfma_f32_32x32x16_bf16, 32 cycles each):
 //   S^T (key x query) = K . Q^T : A = K rows from LDS, B = Q rows kept in VGPRs.
@@ -577,9 +581,10 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
   }
 }
 
-// Both routes in one launch: workgroups [0, n128) take the M128 x N128 items, the rest
-// the M64 x N256 items (and the cleanup items of empty blocks), so the shorter M64 items
-// fill the end of the M128 work instead of starting after its last workgroup.
+// Both routes in one launch: workgroup b runs M128 x N128 item order[b] when that is
+// >= 0, else M64 x N256 item ~order[b] (or a cleanup item of an empty block); without an
+// order table the M128 items come first.  Per head the M64 items follow the M128 items,
+// so they fill the end of that work and find its pages in the caches.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void kpage_fwd_kernel(FwdArgs a128, FwdArgs a64) {
   __shared__ FwdLds<D> lds;
