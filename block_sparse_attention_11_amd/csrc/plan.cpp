@@ -286,11 +286,15 @@ void build_groups(const Problem &P, const FwdTables &F, GroupTables *T) {
         int64_t best_in = 0, best_n = 1;
         for (size_t c = c0 + 1; c < cand.size(); ++c) {
           if (!free_[c]) continue;
-          bool shares = false;  // a page selected by every member, the candidate included
-          for (size_t w = 0; w < W && !shares; ++w) shares = (inter[w] & bits[c * W + w]) != 0;
-          if (!shares) continue;
+          // one pass: pages shared with every member, and pages already in the union
+          const uint64_t *bc = &bits[c * W];
+          uint64_t sh = 0;
           int64_t in = 0;
-          for (size_t w = 0; w < W; ++w) in += __builtin_popcountll(uni[w] & bits[c * W + w]);
+          for (size_t w = 0; w < W; ++w) {
+            sh |= inter[w] & bc[w];
+            in += __builtin_popcountll(uni[w] & bc[w]);
+          }
+          if (sh == 0) continue;  // no page selected by every member and by the candidate
           if (best == cand.size() || in * best_n > best_in * n_of[c]) {
             best = c;
             best_in = in;
