@@ -47,3 +47,23 @@ def test_more_than_one_gpu_is_refused():
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_route_pairs_count_group_members_with_the_m128_launch():
+    """The per-route split attributes the pairs of blocks that run inside group items to the
+    M128 launch; the two routes together hold every useful pair of the plan."""
+    import numpy as np
+    import block_sparse_attention_11_amd as K
+    from workloads import make_workload
+    w = make_workload(3, heads=[0])
+    plan = K.kpage_plan(w)
+    members = K.kpage_plan_export(plan, "group_members")
+    members = members[members >= 0]
+    assert members.size > 0
+    with_groups = bench._route_pairs(w, K, plan)
+    plain = bench._route_pairs(w)
+    useful = K.kpage_plan_stats(plan)["useful"]
+    assert with_groups["q128"] + with_groups["q64"] == useful == plain["q128"] + plain["q64"]
+    moved = sum(int(w.q_valid[0, q]) * int(np.asarray(w.kv_valid[0])[w.q2k_idx[w.q2k_ptr[0, q]:w.q2k_ptr[0, q + 1]]].sum())
+                for q in members)
+    assert with_groups["q128"] - plain["q128"] == moved
