@@ -5,7 +5,8 @@ their page walks, one member per wave, each wave masking the pages its own block
 not select; it writes every member block's 128 output rows.  Checked here: forward O and
 LSE and the gradients on layouts built to form groups of two, three and four members
 (tails, 1- and 8-row blocks, empty blocks next to members), groups whose items take the
-exact re-run, every member block of the top-87 workload, and batch 2 with a shared graph
+exact re-run, every member block of the top-87 workload, a group over both ends of a
+2^21-row K/V sequence (the longest the grouping takes), and batch 2 with a shared graph
 and with one graph per (batch, head) (there also the GPU planner's groups against the
 host's); the same problems planned without groups agree with the oracle too.  Tolerances
 as in the forward and backward parity tests.
@@ -116,6 +117,27 @@ def test_topk_workload_every_member_block():
     got = gpu_fwd_bwd(w, w.q, w.k, w.v, w.do, plan=plan)
     ref = oracle_bwd(w, w.q, w.k, w.v, w.do, heads=[1])[:3]
     check_grads(got, ref, "top-87 groups head 1", w, heads=[1])
+
+
+def test_groups_at_the_page_bitset_limit():
+    """K/V of 2^21 rows, the longest sequence whose page bitsets (2048 words) the grouping
+    takes: three small blocks form one group item whose union walk holds pages at both ends
+    of the sequence (page ids up to 2^17 - 1); forward and backward against the oracle."""
+    seq_kv = 2048 * 64 * 16
+    p = make_problem([20, 32, 8], [128, 128, 128], [[0, 1], [0, 1], [0, 2]], heads=1, head_dim=64,
+                     kv_offset=[0, 128, seq_kv - 128], seq_kv=seq_kv)
+    t = random_tensors(p, seed=79)
+    plan = K.kpage_plan(p)
+    assert group_sizes(plan) == [3]
+    assert int(K.kpage_plan_export(plan, "group_walk").max()) == seq_kv // 16 - 1
+    _say(f"[groups] seq_kv {seq_kv}: one group of 3 over both ends of K/V")
+    O, L = gpu_fwd(p, t["q"], t["k"], t["v"], plan=plan)
+    Oref, Lref = oracle_fwd(p, t["q"], t["k"], t["v"])
+    check(O, L, Oref, Lref, "groups at the page-bitset limit",
+          Aabs=abs_values_attention(p, t["q"], t["k"], t["v"]))
+    got = gpu_fwd_bwd(p, t["q"], t["k"], t["v"], t["do"], plan=plan)
+    ref = oracle_bwd(p, t["q"], t["k"], t["v"], t["do"])[:3]
+    check_grads(got, ref, "groups at the page-bitset limit", p)
 
 
 def per_slot_small_blocks(batch, heads, d, seed):
