@@ -518,7 +518,12 @@ __device__ __forceinline__ void dq_item(const BwdArgs &a, const FwdItem *items, 
       else if constexpr (I < 2 * DS) op[I] = lds_read8(vt + (rdv ^ (32 * (I - DS))));
     };
     uint32_t word = 0;
-    if constexpr (MASKED) word = vwords[2 * u + ((keyoff + 32 * H) >> 5)];
+    if constexpr (MASKED) {
+      word = vwords[2 * u + ((keyoff + 32 * H) >> 5)];
+      // no key of the sub-tile is valid for this wave's rows (pages a group member did not
+      // select, dummy pages): P and dS are 0, the sub-tile adds nothing to dQ
+      if (word == 0u) return;
+    }
     read_op(ic<0>{});
     read_op(ic<1>{});
     static_for<DS>([&](auto s_c) __attribute__((always_inline)) {

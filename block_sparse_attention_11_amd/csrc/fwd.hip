@@ -205,10 +205,13 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
       }
     }
   };
+  // validity word of sub-tile `sub` for this wave's keys (its 32 keys, 16 bits per page)
+  auto sub_word = [&](int sub) __attribute__((always_inline)) -> uint32_t {
+    return vwords[(sub / NH) * (kTilePages / 2) + (keyoff >> 5) + sub % NH];
+  };
   // exact masking of invalid key rows of sub-tile `sub` (its 32 keys = one validity word)
   auto mask = [&](int sub, f32x16 &sc) __attribute__((always_inline)) {
-    const int tile = sub / NH, half = sub % NH;
-    const uint32_t word = vwords[tile * (kTilePages / 2) + (keyoff >> 5) + half];
+    const uint32_t word = sub_word(sub);
     // register r holds key acc_row(r, g): its bit is wave-uniform in each lane half, so
     // the condition is a scalar lane mask and each score costs one select
     const float ninf = kNegInf;
@@ -264,9 +267,11 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
   // of S_i is cut into slices placed between them.  A scheduling fence closes every
   // second chunk, so the order written here is the order issued.  K and V operands
   // are read from LDS two products ahead of their MFMAs.
-  auto fused = [&](auto par, const lds_char *kb, int khalf, const lds_char *vb, int vhalf)
+  auto fused = [&](auto par, const lds_char *kb, int khalf, const lds_char *vb, int vhalf, auto probs_only)
                    __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
+    // probabilities of S_i only: S_{i+1} and P_{i-1} are known to hold no key of this wave
+    constexpr bool ONLY_P = decltype(probs_only)::value;
     constexpr int VOPS = 2 * ND, NM = DS + VOPS;
     constexpr int SLICES = 4;  // probabilities of 4 scores each
     static_assert(DS == VOPS, "QK and PV products alternate one to one");
@@ -308,6 +313,12 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
         for (int e = 0; e < 4; ++e) po[R / 8][R % 8 + e] = (__bf16)p[e];
       }
     };
+    if constexpr (ONLY_P) {
+      static_for<SLICES>([&](auto k_c) __attribute__((always_inline)) { slice(k_c); });
+      l_run += rs0 + rs1;
+      sn = f32x16{};  // S_{i+1}: every key masked by the next sub-iteration
+      return;
+    }
     read_k(ic<0>{});
     read_k(ic<1>{});
     read_v(ic<0>{});
@@ -347,7 +358,15 @@ __device__ __forceinline__ void fwd_item(const FwdArgs &args, int item, FwdLds<D
     if (MASK == kMaskAlways || (MASK == kMaskCheck && i / NH >= full_tiles)) mask(i, sacc[P]);
     __builtin_amdgcn_sched_barrier(0);
     if (!EXACT && HAS_QK && HAS_PV) {
-      fused(par, kb, (i + 1) % NH, vb, (i - 1 + NH) % NH);
+      // Past the valid prefix a run of sub-tiles may hold no key of this wave (pages a
+      // group member did not select, dummy pages): their probabilities are exactly 0.
+      // When sub-tiles i - 1 and i + 1 both hold none, S_{i+1} (masked to -inf by the
+      // next sub-iteration) and P_{i-1} V_{i-1} are skipped; the probabilities of S_i
+      // are still taken.  M128 route only: with both variants the M64 loop spills.
+      if (NH == 2 && MASK == kMaskAlways && sub_word(i + 1) == 0u && sub_word(i - 1) == 0u)
+        fused(par, kb, (i + 1) % NH, vb, (i - 1 + NH) % NH, ic<1>{});
+      else
+        fused(par, kb, (i + 1) % NH, vb, (i - 1 + NH) % NH, ic<0>{});
     } else {
       if (HAS_QK) qk(kb, (i + 1) % NH, sacc[1 - P]);
       softmax(sacc[P], pacc[P]);
